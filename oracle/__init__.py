@@ -1,0 +1,122 @@
+"""fp64 CPU oracle for the Kimi Delta Attention (KDA) recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package; the product path (the HIP library and
+its binding) never does, and this package imports nothing from it.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, libm ``exp``); this
+module only builds it with gcc, converts arrays to contiguous fp64 and calls
+it through ctypes.  It follows the state-update equation of the section
+"Kimi Delta Attention (KDA)" on the page "Kimi Linear 高效注意力架构":
+``S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T`` with
+``alpha_t = exp(log_alpha_t)`` per key channel, and the readout
+``o_t = S_t^T q_t`` after the token's write.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, special cases, exact rational arithmetic and an explicit-matrix brute
+force; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compiles kda_oracle.c with gcc -O2 (no fast-math) into libkda_oracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+             "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.kda_oracle_forward.argtypes = [
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+            i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
+        lib.kda_oracle_forward.restype = ctypes.c_int
+        lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp]
+        lib.kda_oracle_decode_step.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """Contiguous fp64 numpy copy/view of an array-like (torch tensors included)."""
+    if hasattr(x, "detach"):  # torch tensor: widen exactly on the host
+        x = x.detach().to("cpu")
+        if x.dtype != __import__("torch").float64:
+            x = x.double()
+        x = x.numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_threads=None):
+    """Runs the recurrence token by token in fp64.
+
+    q, k, log_alpha: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
+    init_state: [N, H, Dk, Dv] or None (zeros); cu_seqlens: int [N+1] or None.
+    Returns (o [B, T, H, Dv], final_state [N, H, Dk, Dv]) as fp64 numpy arrays.
+    """
+    q, k, v, la, be = (_f64(a) for a in (q, k, v, log_alpha, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    assert k.shape == q.shape and la.shape == q.shape
+    assert v.shape == (B, T, H, Dv) and be.shape == (B, T, H)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens), dtype=np.int32)
+        N = cu.size - 1
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        cu, N, cu_p = None, B, None
+    s0 = None if init_state is None else _f64(init_state)
+    if s0 is not None:
+        assert s0.shape == (N, H, Dk, Dv)
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    fs = np.zeros((N, H, Dk, Dv), dtype=np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    rc = _load().kda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+                                    cu_p, B, T, H, Dk, Dv, N, _ptr(o), _ptr(fs), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_forward failed with code {rc}")
+    return o, fs
+
+
+def decode_step(q, k, v, log_alpha, beta, state):
+    """One recurrence step per (n, h); q, k, log_alpha [N,H,Dk], v [N,H,Dv],
+    beta [N,H], state [N,H,Dk,Dv].  Returns (o [N,H,Dv], new_state), fp64."""
+    q, k, v, la, be = (_f64(a) for a in (q, k, v, log_alpha, beta))
+    st = _f64(state).copy()
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    assert st.shape == (N, H, Dk, Dv)
+    o = np.zeros((N, H, Dv), dtype=np.float64)
+    rc = _load().kda_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be),
+                                        _ptr(st), N, H, Dk, Dv, _ptr(o))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_decode_step failed with code {rc}")
+    return o, st

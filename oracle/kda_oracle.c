@@ -1,0 +1,191 @@
+/*
+ * kda_oracle.c -- plain fp64 CPU oracle for the Kimi Delta Attention (KDA)
+ * recurrence.  TEST INFRASTRUCTURE ONLY: nothing in the product path links,
+ * loads or calls this file.  It shares no code, header, table or constant with
+ * the HIP kernels or the C-ABI library.
+ *
+ * What it computes (per sequence n, per head h, tokens t of that sequence in
+ * order), following the state-update equation in the section "Kimi Delta
+ * Attention (KDA)" of the page "Kimi Linear 高效注意力架构" (chenshi221 wiki):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *
+ * with the channel-wise decay alpha_t in [0,1]^{d_k} of the bullet on
+ * channel-wise decay in the same section (alpha_t = exp(log_alpha_t); a
+ * log_alpha of -inf is alpha = 0 exactly), and the readout o_t = S_t^T q_t
+ * taken after the token's own write (the pages print no readout; this is the
+ * operator's defined output).
+ *
+ * The product (I - b k k^T) Diag(a) S is expanded once, in the order the
+ * equation writes it: first the decay Diag(a) S, then the erase/write
+ *     S <- S' - b k (k^T S') + b k v^T  =  S' + b k (v - S'^T k)^T.
+ * Nothing else is reordered, blocked or fused.  All arithmetic is IEEE fp64
+ * with libm exp; build without -ffast-math.
+ *
+ * Layouts (dense, row-major, element strides):
+ *   q, k       [B, T, H, Dk]     v, o  [B, T, H, Dv]
+ *   log_alpha  [B, T, H, Dk]     beta  [B, T, H]
+ *   states     [N, H, Dk, Dv]    (row c of a head's state is key channel c)
+ * With cu_seqlens (int32 [N+1], host memory) the batch is one packed row
+ * (B == 1) and sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ * Without it there are N = B sequences of T tokens each.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *beta, *init_state;
+    const int32_t *cu_seqlens;
+    int64_t B, T, H, Dk, Dv, N;
+    double *o, *final_state;
+    int64_t next_unit;      /* work counter, guarded by lock */
+    pthread_mutex_t lock;
+} oracle_job;
+
+/* One token of the recurrence on one head's state S [Dk x Dv] (fp64).
+ * p is caller scratch of length Dv.  Writes o_t (length Dv). */
+static void token_update(double *S, int64_t Dk, int64_t Dv,
+                         const double *q, const double *k, const double *v,
+                         const double *log_alpha, double beta,
+                         double *p, double *o_t)
+{
+    /* Diag(alpha_t) S_{t-1}: row c scaled by alpha_c = exp(log_alpha_c). */
+    for (int64_t c = 0; c < Dk; ++c) {
+        double a = exp(log_alpha[c]);
+        for (int64_t j = 0; j < Dv; ++j) S[c * Dv + j] *= a;
+    }
+    /* p = S'^T k  (what the decayed memory returns for key k). */
+    for (int64_t j = 0; j < Dv; ++j) p[j] = 0.0;
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < Dv; ++j) p[j] += S[c * Dv + j] * k[c];
+    /* S = S' + beta k (v - p)^T  ==  (I - beta k k^T) S' + beta k v^T. */
+    for (int64_t c = 0; c < Dk; ++c) {
+        double bk = beta * k[c];
+        for (int64_t j = 0; j < Dv; ++j) S[c * Dv + j] += bk * (v[j] - p[j]);
+    }
+    /* o_t = S_t^T q_t. */
+    for (int64_t j = 0; j < Dv; ++j) o_t[j] = 0.0;
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < Dv; ++j) o_t[j] += S[c * Dv + j] * q[c];
+}
+
+/* Runs the whole token loop of one (sequence n, head h) unit. */
+static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, double *p)
+{
+    const int64_t Dk = J->Dk, Dv = J->Dv, H = J->H;
+    int64_t b, t0, t1;
+    if (J->cu_seqlens) { b = 0; t0 = J->cu_seqlens[n]; t1 = J->cu_seqlens[n + 1]; }
+    else               { b = n; t0 = 0;               t1 = J->T; }
+
+    const size_t sidx = (size_t)(n * H + h) * (size_t)(Dk * Dv);
+    if (J->init_state) memcpy(S, J->init_state + sidx, sizeof(double) * (size_t)(Dk * Dv));
+    else               memset(S, 0, sizeof(double) * (size_t)(Dk * Dv));
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const size_t row = (size_t)((b * J->T + t) * H + h);
+        token_update(S, Dk, Dv,
+                     J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
+                     J->v + row * (size_t)Dv, J->log_alpha + row * (size_t)Dk,
+                     J->beta[row], p, J->o + row * (size_t)Dv);
+    }
+    if (J->final_state) memcpy(J->final_state + sidx, S, sizeof(double) * (size_t)(Dk * Dv));
+}
+
+static void *worker(void *arg)
+{
+    oracle_job *J = (oracle_job *)arg;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(J->Dk * J->Dv));
+    double *p = (double *)malloc(sizeof(double) * (size_t)J->Dv);
+    if (!S || !p) { free(S); free(p); return (void *)1; }
+    const int64_t units = J->N * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t u = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (u >= units) break;
+        run_unit(J, u / J->H, u % J->H, S, p);
+    }
+    free(S);
+    free(p);
+    return NULL;
+}
+
+/*
+ * kda_oracle_forward: the recurrence over every (sequence, head) unit.
+ * All pointers are host memory.  init_state and final_state may be NULL
+ * (zeros in / no state out); cu_seqlens may be NULL (dense batch).  Units are
+ * independent and are spread over n_threads POSIX threads (<= 0 means 1);
+ * each unit is computed by exactly one thread in token order, so results do
+ * not depend on n_threads.  Returns 0 on success, -1 on a bad argument,
+ * -2 when a thread or allocation fails.
+ */
+int kda_oracle_forward(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const double *init_state, const int32_t *cu_seqlens,
+                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                       int64_t n_seqs, double *o, double *final_state, int n_threads)
+{
+    if (!q || !k || !v || !log_alpha || !beta || !o) return -1;
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta;
+    J.init_state = init_state; J.cu_seqlens = cu_seqlens;
+    J.B = B; J.T = T; J.H = H; J.Dk = Dk; J.Dv = Dv;
+    J.o = o; J.final_state = final_state;
+    if (cu_seqlens) {
+        if (B != 1 || n_seqs < 1) return -1;
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != T) return -1;
+        for (int64_t n = 0; n < n_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+        J.N = n_seqs;
+    } else {
+        J.N = B;
+    }
+    pthread_mutex_init(&J.lock, NULL);
+    if (n_threads < 1) n_threads = 1;
+    if ((int64_t)n_threads > J.N * H) n_threads = (int)(J.N * H);
+    int rc = 0;
+    pthread_t *tid = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    int started = 0;
+    if (!tid) rc = -2;
+    for (int i = 0; i < n_threads && rc == 0; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, &J) != 0) rc = -2;
+        else ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret) rc = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}
+
+/*
+ * kda_oracle_decode_step: one token for each of N independent states, the
+ * state updated in place.  q, k [N, H, Dk]; v, o [N, H, Dv];
+ * log_alpha [N, H, Dk]; beta [N, H]; state [N, H, Dk, Dv].  This is the same
+ * token_update as above, applied once per (n, h).
+ */
+int kda_oracle_decode_step(const double *q, const double *k, const double *v,
+                           const double *log_alpha, const double *beta,
+                           double *state, int64_t N, int64_t H, int64_t Dk,
+                           int64_t Dv, double *o)
+{
+    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return -1;
+    if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    double *p = (double *)malloc(sizeof(double) * (size_t)Dv);
+    if (!p) return -2;
+    for (int64_t u = 0; u < N * H; ++u)
+        token_update(state + (size_t)u * (size_t)(Dk * Dv), Dk, Dv,
+                     q + (size_t)u * (size_t)Dk, k + (size_t)u * (size_t)Dk,
+                     v + (size_t)u * (size_t)Dv, log_alpha + (size_t)u * (size_t)Dk,
+                     beta[u], p, o + (size_t)u * (size_t)Dv);
+    free(p);
+    return 0;
+}
