@@ -1,0 +1,88 @@
+// kda_internal.h -- launcher interface between the C-ABI host code and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    float *state, *o;
+    int32_t N, H, Dk, Dv;
+    bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kda
+
+namespace kda {
+
+// Byte layout of one intra-chunk package (one chunk of one head) in the
+// prefill workspace.  Sections are 256-byte aligned.  Fragment layouts are the
+// register layouts the state pass feeds to the matrix cores, so its loads are
+// contiguous 1 KB (16-bit operands) or 2 KB (fp32 operands) per wave:
+//   WQ  A operand of [W; Q'] S: rows 2C (W then Q'), K = Dk.
+//       block (row tile rt, k-step ks) = 64 lanes x 8 values, lane l holding
+//       row 16 rt + l%16, k = 32 ks + 8 (l/16) + e; order [rt][ks][lane][8].
+//   KT  A operand of Ktilde^T U: rows Dk (channels), K = C tokens (padded to
+//       32); order [ct][ks][part][lane][8] with part = hi, lo (16-bit path).
+//   UP  U' in accumulator layout: tile (col tile ct, row tile rt), lane l
+//       holding rows 4 (l/16) + r of the tile, column 16 ct + l%16;
+//       order [ct][rt][lane][4] fp32.
+//   OI  the intra-chunk output P U', same layout as UP.
+//   GL  Gamma of the chunk's last token per key channel, fp32 [Dk].
+struct PackageLayout {
+    size_t wq, kt, up, oi, gl, bytes;  // offsets of sections and total size
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline PackageLayout package_layout(int C, int Dk, int Dv, bool bf16) {
+    const size_t osz = bf16 ? 2 : 4;                   // matrix-core operand bytes
+    const size_t dkp = Dk < 32 ? 32 : Dk;              // K padded to a 32-wide step
+    const size_t cp = C < 32 ? 32 : C;
+    const size_t parts = bf16 ? 2 : 1;                 // hi/lo split of Ktilde
+    PackageLayout L;
+    size_t off = 0;
+    L.wq = off; off += align256(2 * (size_t)C * dkp * osz);
+    L.kt = off; off += align256((size_t)Dk * cp * osz * parts);
+    L.up = off; off += align256((size_t)C * Dv * 4);
+    L.oi = off; off += align256((size_t)C * Dv * 4);
+    L.gl = off; off += align256((size_t)Dk * 4);
+    L.bytes = off;
+    return L;
+}
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *init_state;
+    const int32_t *cu_seqlens;  // nullable
+    int32_t B, H, Dk, Dv, N, C;
+    int64_t T;
+    bool bf16;
+    float *o, *final_state;     // final_state nullable
+    char *workspace;
+    int64_t n_slots;            // chunk slots in the workspace
+    size_t pkg_bytes;
+    int32_t *chunk_offsets;     // varlen: [N + 1] in the workspace
+};
+
+// Chunk slots the workspace reserves: every chunk of every sequence.
+inline int64_t prefill_slots(int32_t B, int64_t T, int32_t N, int32_t C, bool varlen) {
+    const int64_t per = (T + C - 1) / C;
+    return varlen ? per + N : per * B;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Chunk size the kernels use for a requested one (the fp32 path at d = 128 is
+// limited to 32 tokens by LDS capacity).  Results do not depend on it beyond
+// rounding.
+int prefill_effective_chunk(int C, int Dk, int Dv, bool bf16);
+
+}  // namespace kda

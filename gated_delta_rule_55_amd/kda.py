@@ -1,0 +1,118 @@
+"""Python binding of libkda.so (ctypes).
+
+Argument marshalling only: every step of the operator runs in the library's
+HIP kernels.  torch provides device memory (tensors, ``data_ptr()``) and the
+current HIP stream; there is no fallback path -- if the library is missing or
+a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+_lib = None
+
+
+class KdaError(RuntimeError):
+    pass
+
+
+def load():
+    """Loads libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KdaError(f"{LIB_PATH} is missing: build it with gated_delta_rule_55_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int, i32]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32,
+                                  ctypes.c_int, i32, fp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, fp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        raise KdaError(f"{lib.kda_status_string(rc).decode()}: {lib.kda_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise KdaError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(B, T, H, Dk, Dv, n_seqs=0, dtype=torch.bfloat16, chunk_size=64) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, code, chunk_size))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk_size=64,
+              out=None, final_state=None, output_final_state=True, workspace=None, stream=None):
+    """Chunked prefill.  q, k [B,T,H,Dk]; v [B,T,H,Dv]; log_alpha [B,T,H,Dk] fp32;
+    beta [B,T,H] fp32; init_state [N,H,Dk,Dv] fp32 or None; cu_seqlens int32 [N+1]
+    (device) or None.  Returns (o [B,T,H,Dv] fp32, final_state [N,H,Dk,Dv] or None)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = B if cu_seqlens is None else n_seqs
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, code, chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs, code,
+                             chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
+    """One step per (n, h); state [N,H,Dk,Dv] fp32 is updated in place.
+    Returns o [N,H,Dv] fp32."""
+    lib = load()
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               _ptr(state), N, H, Dk, Dv, _dtype_code(q), _ptr(out),
+                               _stream(stream)))
+    return out

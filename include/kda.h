@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * The operator is the gated delta-rule recurrence of the section
+ * "Kimi Delta Attention (KDA)" on the page "Kimi Linear 高效注意力架构":
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *
+ * with one state S of d_k x d_v per (sequence, head), a channel-wise decay
+ * alpha_t in [0,1]^{d_k} (bullet on channel-wise decay, same section) passed
+ * as log_alpha = log(alpha) (-inf encodes alpha = 0), a scalar beta_t per
+ * (token, head), and the output o_t = S_t^T q_t read after the token's write
+ * (the page prints no readout; this is the operator's defined output, with no
+ * 1/sqrt(d_k) scale -- callers may pre-scale q).  The chunked prefill follows
+ * the bullet on the hardware-efficient chunked algorithm (DPLR with a = b = k)
+ * and the complexity table O(T d_k d_v + T C d_h + T C^2) of the comparison
+ * table on the same page; the decode step keeps the fixed-size d_k x d_v state
+ * of the linear-complexity bullet.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc'd memory of the current device)
+ *     unless stated otherwise, 16-byte aligned, dense and row-major.
+ *   - Layouts: q, k, log_alpha [B, T, H, Dk]; v, o [B, T, H, Dv];
+ *     beta [B, T, H]; states [N, H, Dk, Dv] (row c of a head's state is key
+ *     channel c).  bf16 inputs are raw IEEE bfloat16 bit patterns.
+ *   - Accumulation and states are fp32; o is always fp32.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory, keeps no pointer after returning, and never
+ *     synchronises: work is enqueued on `stream` and runs asynchronously.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued (no HIP call, no pointer dereference); on any error nothing is
+ *     written and a status other than KDA_OK is returned, with a detail
+ *     message in kda_last_error().  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Determinism: identical inputs give bit-identical outputs on one device.
+ *   - Thread safety: no global mutable state except the thread-local error
+ *     message; calls on different streams may overlap if they share no
+ *     output or workspace buffer.
+ *   - Numerical preconditions: log_alpha <= 0 (alpha in [0,1]); q and k are
+ *     expected L2-normalised as the KDA layer produces them (not checked);
+ *     NaN inputs propagate.  On the bf16 path the state and the per-chunk
+ *     innovation U = beta (v - ...) are fed to fp16 matrix cores and must stay
+ *     below 65504 in magnitude.  A log_alpha of -inf on every channel of a
+ *     token is an exact state reset; -inf on only some channels is taken as
+ *     -88 (alpha ~ 6e-39).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, aliasing   */
+    KDA_ERR_UNSUPPORTED = 2, /* Dk/Dv outside {16,32,64,128}, chunk size, dtype */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+    KDA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError)      */
+} kda_status;
+
+typedef enum {
+    KDA_BF16 = 0, /* q, k, v are bfloat16                              */
+    KDA_F32 = 1   /* q, k, v are float32 (fp32 matrix-core path)       */
+} kda_dtype;
+
+/*
+ * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
+ * needs for these sizes (host only, pure; 0 for invalid arguments).  The
+ * workspace holds one intra-chunk package per (chunk, head): the WY factors
+ * W, the folded readout operator Q' = Q*Gamma - P W, the decayed keys, U' and
+ * the intra-chunk output, all computed from the chunk alone.
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                    int32_t n_seqs, kda_dtype in_dtype, int32_t chunk_size);
+
+/*
+ * kda_chunk_fwd -- chunked prefill over whole sequences.
+ *
+ *   q, k        [B, T, H, Dk] in_dtype           queries / keys
+ *   v           [B, T, H, Dv] in_dtype           values
+ *   log_alpha   [B, T, H, Dk] fp32               per-channel log decay (<= 0)
+ *   beta        [B, T, H]     fp32               write strength
+ *   init_state  [N, H, Dk, Dv] fp32, nullable    incoming state (NULL: zeros)
+ *   cu_seqlens  [N + 1] int32, nullable          packed sequence offsets (device)
+ *   B, T, H, Dk, Dv                              sizes; Dk, Dv in {16, 32, 64, 128}
+ *   n_seqs      N when cu_seqlens is given (then B must be 1), else ignored (N = B)
+ *   in_dtype    KDA_BF16 or KDA_F32
+ *   chunk_size  16, 32 or 64 (0 selects 64); results do not depend on it
+ *               beyond rounding
+ *   o           [B, T, H, Dv] fp32 output; must not overlap any input
+ *   final_state [N, H, Dk, Dv] fp32, nullable; may alias init_state
+ *   workspace   device scratch of at least kda_chunk_fwd_workspace_size()
+ *               bytes (256-byte aligned); contents on entry are ignored
+ *   stream      HIP stream the kernels are enqueued on
+ *
+ * cu_seqlens must satisfy cu[0] = 0, cu[N] = T and be non-decreasing (the
+ * device-side contents are the caller's contract and are not read by the
+ * host).  Zero-length sequences keep their initial state.  Chunks restart at
+ * each sequence start; the last chunk of a sequence may be partial.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                         kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_decode_step -- one token for each of N independent sequences, the state
+ * updated in place (the fixed d_k x d_v per-head state of the linear-complexity
+ * bullet of the same section).
+ *
+ *   q, k        [N, H, Dk] in_dtype
+ *   v           [N, H, Dv] in_dtype
+ *   log_alpha   [N, H, Dk] fp32
+ *   beta        [N, H]     fp32
+ *   state       [N, H, Dk, Dv] fp32, read and written in place
+ *   o           [N, H, Dv] fp32 output; must not overlap any input or state
+ *
+ * Each state is streamed from HBM once and written back once; the arithmetic
+ * is fp32 throughout.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
+                           int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream);
+
+/* Static name of a status code ("KDA_OK", ...). */
+const char *kda_status_string(kda_status status);
+
+/* Detail message of the last failing call on this host thread ("" if none). */
+const char *kda_last_error(void);
+
+/* KDA_VERSION of the built library. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,76 @@
+"""The chunked algorithm the HIP prefill implements, modelled in fp64 on the CPU,
+against the token-loop oracle: pins the derivation (WY/UT form, sub-block
+exponent references, reset masks, partial chunks) before any kernel runs."""
+import numpy as np
+import pytest
+
+import oracle
+from chunk_model import chunk_forward
+
+
+def _inputs(rng, T, H, Dk, Dv, shift=0.0, B=1, resets=0.0, neg_inf_channels=0.0, state=True,
+            gate_scale=1.0):
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, Dv))
+    la = -gate_scale * np.log1p(np.exp(rng.standard_normal((B, T, H, Dk)) + shift))
+    be = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    if resets:
+        la[:, rng.random(T) < resets] = -np.inf
+    if neg_inf_channels:
+        la[rng.random(la.shape) < neg_inf_channels] = -np.inf
+    s0 = 0.02 * rng.standard_normal((B, H, Dk, Dv)) if state else None
+    return q, k, v, la, be, s0
+
+
+def _check(ref, got, tol=1e-11):
+    o_r, s_r = ref
+    o_g, s_g = got
+    scale_o = np.sqrt(np.mean(o_r ** 2)) + 1e-300
+    scale_s = np.sqrt(np.mean(s_r ** 2)) + 1e-300
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(s_g))
+    assert np.max(np.abs(o_g - o_r)) <= tol * scale_o
+    assert np.max(np.abs(s_g - s_r)) <= tol * scale_s
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("shift", [0.0, 2.0, 3.0])
+@pytest.mark.parametrize("fold", [False, True])
+def test_chunked_equals_token_loop(C, shift, fold):
+    rng = np.random.default_rng(int(C + 10 * shift))
+    args = _inputs(rng, 157, 2, 32, 24, shift=shift)
+    _check(oracle.forward(*args), chunk_forward(*args, chunk=C, fold=fold))
+
+
+def test_chunked_varlen_resets_partial_chunks():
+    rng = np.random.default_rng(3)
+    lens = [1, 64, 65, 130, 7, 0, 200]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, la, be, _ = _inputs(rng, int(cu[-1]), 2, 32, 16, resets=0.05)
+    s0 = 0.02 * rng.standard_normal((len(lens), 2, 32, 16))
+    args = (q, k, v, la, be, s0)
+    _check(oracle.forward(*args, cu_seqlens=cu), chunk_forward(*args, cu_seqlens=cu, chunk=64, fold=True))
+
+
+def test_chunked_reset_on_first_and_last_token_of_chunk():
+    rng = np.random.default_rng(4)
+    q, k, v, la, be, s0 = _inputs(rng, 128, 1, 16, 16)
+    for t in (0, 15, 16, 63, 64, 127):
+        la[0, t] = -np.inf
+    _check(oracle.forward(q, k, v, la, be, s0), chunk_forward(q, k, v, la, be, s0, chunk=64, fold=True))
+
+
+def test_chunked_extreme_decay_takes_exact_path():
+    """Gates far below the configs' range push diagonal-tile half-spans past the
+    safe bound; those channels take the per-element path."""
+    rng = np.random.default_rng(5)
+    args = _inputs(rng, 96, 1, 16, 8, gate_scale=12.0)
+    _check(oracle.forward(*args), chunk_forward(*args, chunk=64))
+
+
+def test_chunked_partial_neg_inf_channels():
+    rng = np.random.default_rng(6)
+    args = _inputs(rng, 100, 2, 16, 8, neg_inf_channels=0.03)
+    _check(oracle.forward(*args), chunk_forward(*args, chunk=32))

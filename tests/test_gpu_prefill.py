@@ -1,0 +1,213 @@
+"""Chunked prefill on the GPU (through the C-ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_55_amd import kda, workloads
+from kda_testlib import TAU, assert_parity, host64, log, oracle_threads, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp, chunk=None, poison=True, init_state="inp"):
+    q = inp["q"]
+    B, T, H, Dk = q.shape
+    Dv = inp["v"].shape[-1]
+    N = inp["N"]
+    o = torch.full((B, T, H, Dv), float("nan"), device="cuda") if poison else None
+    fs = torch.full((N, H, Dk, Dv), float("nan"), device="cuda") if poison else None
+    s0 = inp["init_state"] if init_state == "inp" else init_state
+    o, fs = kda.chunk_fwd(q, inp["k"], inp["v"], inp["log_alpha"], inp["beta"], s0,
+                          inp["cu_seqlens"], chunk or inp["chunk"], out=o, final_state=fs)
+    torch.cuda.synchronize()
+    return o, fs
+
+
+def _oracle(inp, heads=None, T=None):
+    sl = (lambda x: x) if heads is None else (lambda x: x[:, :, heads])
+    tcut = (lambda x: x) if T is None else (lambda x: x[:, :T])
+    s0 = inp["init_state"]
+    if s0 is not None and heads is not None:
+        s0 = s0[:, heads]
+    return oracle.forward(tcut(sl(inp["q"])), tcut(sl(inp["k"])), tcut(sl(inp["v"])),
+                          tcut(sl(inp["log_alpha"])), tcut(sl(inp["beta"])), s0,
+                          inp["cu_seqlens"], n_threads=oracle_threads())
+
+
+def _check(inp, o, fs, tau, heads=None, label=""):
+    o_ref, s_ref = _oracle(inp, heads)
+    og = o if heads is None else o[:, :, heads]
+    fg = fs if heads is None else fs[:, heads]
+    e1 = assert_parity(og, o_ref, tau, f"{label} o")
+    e2 = assert_parity(fg, s_ref, tau, f"{label} final state")
+    return e1, e2
+
+
+def test_tiny_fp32_workload():
+    """fp32 inputs, T=64, H=1, d=16, 16-token chunks: the 1e-4 bar."""
+    inp = workloads.make_prefill("tiny", "cuda", 0)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.float32], label="tiny")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_ragged_small(dtype, D, C):
+    """T not a multiple of any chunk size, several heads, random initial state."""
+    log(f"ragged dtype={dtype} D={D} C={C}")
+    inp = workloads.make_prefill("prefill", "cuda", seed=D + C, T=157, H=3, dtype=dtype)
+    if D != 128:
+        inp = _shrink(inp, D)
+    o, fs = _gpu(inp, chunk=C)
+    tau = TAU[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    _check(inp, o, fs, tau, label=f"{dtype} D={D} C={C}")
+
+
+def _shrink(inp, D):
+    """Keeps the first D channels (re-normalising q, k) for smaller head dims."""
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name][..., :D].float()
+        out[name] = (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(inp[name].dtype)
+    out["v"] = inp["v"][..., :D].contiguous()
+    out["log_alpha"] = inp["log_alpha"][..., :D].contiguous()
+    if inp["init_state"] is not None:
+        out["init_state"] = inp["init_state"][:, :, :D, :D].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("shift", [0.0, 2.0, 3.0])
+def test_gate_ranges_bf16(shift):
+    inp = workloads.make_prefill("prefill", "cuda", seed=11, T=700, H=4, shift=shift)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label=f"shift={shift}")
+
+
+def test_prefill_workload_full():
+    """T=4096, H=32, d=128, bf16, random initial state: every output checked."""
+    log("prefill workload T=4096 H=32")
+    inp = workloads.make_prefill("prefill", "cuda", 0)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label="prefill 4096x32")
+
+
+def test_varlen_small_with_resets():
+    lens = [1, 64, 65, 130, 7, 0, 200, 33]
+    inp = workloads.make_prefill("varlen", "cuda", seed=5, H=3, lengths=lens)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    inp["init_state"] = 0.02 * torch.randn((len(lens), 3, 128, 128), device="cuda", generator=g)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label="varlen small")
+
+
+def test_varlen_workload_sampled_heads():
+    """16 packed sequences (~131k tokens), 5% resets, H=32: all outputs of 4 heads."""
+    inp = workloads.make_prefill("varlen", "cuda", 0)
+    log(f"varlen workload T={inp['T']}")
+    o, fs = _gpu(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(fs).all()
+    _check(inp, o, fs, TAU[torch.bfloat16], heads=[0, 9, 22, 31], label="varlen 4 heads")
+
+
+@pytest.mark.timeout(600)
+def test_long_workload_sampled():
+    """T=1,048,576, H=32: o of 8 heads over the first 32768 tokens and, for 2
+    heads, every output and the final state over the full length."""
+    inp = workloads.make_prefill("long", "cuda", 0)
+    log("long workload T=1M H=32")
+    o, fs = _gpu(inp, poison=False)
+    assert torch.isfinite(fs).all()
+    heads = [0, 5, 11, 16, 20, 26, 30, 31]
+    Tp = 32768
+    o_ref, _ = _oracle(inp, heads=heads, T=Tp)
+    assert_parity(o[:, :Tp, heads], o_ref, TAU[torch.bfloat16], "long o (8 heads, 32k tokens)")
+    del o_ref
+    _check(inp, o, fs, TAU[torch.bfloat16], heads=[3, 29], label="long 2 heads full")
+
+
+def test_chunk_size_invariance():
+    inp = workloads.make_prefill("prefill", "cuda", seed=3, T=333, H=2)
+    res = [_gpu(inp, chunk=C) for C in (16, 32, 64)]
+    for C, (o, fs) in zip((32, 64), res[1:]):
+        assert rel_err(o, host64(res[0][0])) < 5e-3, C
+        assert rel_err(fs, host64(res[0][1])) < 5e-3, C
+
+
+def test_split_resume_and_final_state_alias():
+    inp = workloads.make_prefill("prefill", "cuda", seed=4, T=400, H=2)
+    o, fs = _gpu(inp)
+    T1 = 150
+    a = {k: (v[:, :T1].contiguous() if k in ("q", "k", "v", "log_alpha", "beta") else v)
+         for k, v in inp.items()}
+    b = {k: (v[:, T1:].contiguous() if k in ("q", "k", "v", "log_alpha", "beta") else v)
+         for k, v in inp.items()}
+    oa, fa = _gpu(a)
+    # continue in place: final_state aliases init_state
+    ob, fb = kda.chunk_fwd(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], fa, None, 64,
+                           final_state=fa)
+    torch.cuda.synchronize()
+    o2 = torch.cat([oa, ob], dim=1)
+    assert rel_err(o2, host64(o)) < 5e-3
+    assert rel_err(fb, host64(fs)) < 5e-3
+    assert fb.data_ptr() == fa.data_ptr()
+
+
+def test_prefill_equals_decode_steps():
+    inp = workloads.make_prefill("prefill", "cuda", seed=6, T=96, H=2)
+    o, fs = _gpu(inp)
+    st = inp["init_state"].clone()
+    outs = []
+    for t in range(96):
+        outs.append(kda.decode_step(inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(),
+                                    inp["v"][:, t].contiguous(), inp["log_alpha"][:, t].contiguous(),
+                                    inp["beta"][:, t].contiguous(), st))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, dim=1)
+    assert rel_err(o, host64(od)) < 5e-3
+    assert rel_err(fs, host64(st)) < 5e-3
+
+
+def test_varlen_equals_separate_calls():
+    lens = [70, 1, 129, 64]
+    inp = workloads.make_prefill("varlen", "cuda", seed=7, H=2, lengths=lens)
+    o, fs = _gpu(inp)
+    cu = inp["cu_seqlens"].cpu().tolist()
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        sub = {k: (v[:, a:b].contiguous() if k in ("q", "k", "v", "log_alpha", "beta") else v)
+               for k, v in inp.items()}
+        sub["cu_seqlens"] = None
+        sub["N"] = 1
+        on, fn = _gpu(sub)
+        assert torch.equal(on, o[:, a:b]), n
+        assert torch.equal(fn[0], fs[n]), n
+
+
+def test_deterministic_and_all_outputs_written():
+    inp = workloads.make_prefill("varlen", "cuda", seed=8, H=2, lengths=[100, 37, 0, 64])
+    o1, f1 = _gpu(inp)
+    o2, f2 = _gpu(inp)
+    assert torch.isfinite(o1).all() and torch.isfinite(f1).all()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_extreme_decay_and_partial_neg_inf():
+    """Gates far outside the workloads' range (exact per-element path for
+    diagonal tiles) and -inf on scattered channels (clamped to -88)."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=12, T=200, H=2)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    inp["log_alpha"] = inp["log_alpha"] * 12.0
+    mask = torch.rand(inp["log_alpha"].shape, device="cuda", generator=g) < 0.03
+    inp["log_alpha"][mask] = float("-inf")
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label="extreme decay")
+
+
+def test_zero_length_and_empty():
+    # T = 0: final state equals the initial state, o is empty
+    inp = workloads.make_prefill("prefill", "cuda", seed=13, T=0, H=2)
+    o, fs = _gpu(inp)
+    assert o.numel() == 0
+    assert torch.equal(fs, inp["init_state"])
