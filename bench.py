@@ -1,0 +1,241 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill (kda_chunk_fwd) over the 1M-token workload
+(B=1, T=1,048,576, H=32, d_k=d_v=128, 64-token chunks, bf16 q/k/v, fp32 gates)
+followed by the 64 consecutive decode steps (kda_decode_step) of the decode
+workload (256 sequences x 32 heads, 128x128 fp32 states).  Inputs are seeded
+synthetic tensors already resident in HBM; outputs and workspaces are
+preallocated.  `value` is prefill tokens/s; the decode step's HBM GB/s is
+reported next to it.  Times come from HIP events on the stream the kernels run
+on.  The fp64 CPU oracle is timed on a bounded sample of the same prefill
+workload on the host cores (cpu_baseline).
+
+python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # MI355X HBM3E bytes/s
+BF16_PEAK = 2.5e15       # MI355X dense bf16/fp16 matrix flop/s
+
+
+def prefill_alg_bytes(T, H, Dk, Dv, N, in_bytes=2, init=False):
+    """Algorithmic HBM bytes of one prefill: q, k, v read, log_alpha and beta
+    read, o written, final state written (and the initial state read)."""
+    per_tok_head = in_bytes * (2 * Dk + Dv) + 4 * Dk + 4 + 4 * Dv
+    state = N * H * Dk * Dv * 4
+    return T * H * per_tok_head + state * (2 if init else 1)
+
+
+def prefill_alg_flops(T, H, Dk, Dv, C):
+    """6 d_k d_v + C (3 d_k + 2 d_v) + C^2 / 3 per token and head (the three
+    state contractions, the intra-chunk products counted on their triangles,
+    and the triangular inverse)."""
+    return T * H * (6 * Dk * Dv + C * (3 * Dk + 2 * Dv) + C * C / 3)
+
+
+def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2):
+    """State read and written once, plus the token's q, k, v, log_alpha, beta, o."""
+    return N * H * (8 * Dk * Dv + in_bytes * (2 * Dk + Dv) + 4 * Dk + 4 + 4 * Dv)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_55_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, heads, T_sample, threads):
+    import oracle
+    sl = lambda x: x[:, :T_sample, heads].detach().to("cpu").double().numpy()
+    args = [sl(inp[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
+    t0 = time.perf_counter()
+    oracle.forward(*args, None, None, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the KDA operator here runs on a single "
+              f"MI355X (got --gpus {args.gpus}); heads and sequences would shard across "
+              f"GPUs with no communication, which this benchmark does not launch.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_55_amd import kda, workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    lib = kda.load()
+
+    # ---- inputs (seeded, synthetic, resident in HBM) ----------------------------
+    pin = workloads.make_prefill("long", dev, 0)
+    w = pin["workload"]
+    T, H, Dk, Dv, C, N = pin["T"], w.H, w.Dk, w.Dv, w.chunk, pin["N"]
+    o = torch.empty((1, T, H, Dv), dtype=torch.float32, device=dev)
+    fs = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    ws_bytes = kda.workspace_size(1, T, H, Dk, Dv, 0, torch.bfloat16, C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    din = workloads.make_decode("decode", dev, 0)
+    dw = din["workload"]
+    dsteps = args.decode_steps or dw.steps
+    state0 = din["state"]
+    state = state0.clone()
+    od = torch.empty((dw.N, dw.H, dw.Dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        kda.chunk_fwd(pin["q"], pin["k"], pin["v"], pin["log_alpha"], pin["beta"], None, None, C,
+                      out=o, final_state=fs, workspace=ws)
+
+    def decode(t):
+        kda.decode_step(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t],
+                        din["beta"][t], state, out=od)
+
+    for _ in range(args.warmup):
+        prefill()
+        for t in range(dsteps):
+            decode(t)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    pre_ms, dec_ms = [], []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        de = [ev() for _ in range(dsteps + 1)]
+        de[0].record(stream)
+        for t in range(dsteps):
+            decode(t)
+            de[t + 1].record(stream)
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+        dec_ms.extend(de[t].elapsed_time(de[t + 1]) for t in range(dsteps))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    pre_ms.sort()
+    dec_sorted = sorted(dec_ms)
+    t_pre = sum(pre_ms) / len(pre_ms) / 1e3
+    t_dec = sum(dec_ms) / len(dec_ms) / 1e3
+    tok_s = T / t_pre
+    pb = prefill_alg_bytes(T, H, Dk, Dv, N)
+    pf = prefill_alg_flops(T, H, Dk, Dv, C)
+    db = decode_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv)
+    dec_gbs = db / t_dec / 1e9
+
+    result = {
+        "metric": "KDA prefill tokens/s (H=32,d=128, T=1M) + decode step HBM GB/s, 1 MI355X",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "KDA long prefill B=1 T=1048576 H=32 d_k=d_v=128 chunk=64 bf16 q/k/v, "
+                        "fp32 gates/state, log_alpha=-softplus(N(0,1)+3); then KDA decode "
+                        "256 seqs x 32 heads x 128x128 fp32 state, 64 steps",
+            "T": T, "H": H, "d_k": Dk, "d_v": Dv, "chunk": C,
+            "decode_states": dw.N * dw.H, "decode_steps": dsteps,
+        },
+        "prefill": {
+            "ms_mean": t_pre * 1e3, "ms_median": pre_ms[len(pre_ms) // 2],
+            "tokens_per_s": tok_s,
+            "hbm_frac_algorithmic": pb / t_pre / HBM_PEAK,
+            "mfma_frac_algorithmic": pf / t_pre / BF16_PEAK,
+            "alg_bytes": pb, "alg_flops": pf,
+        },
+        "decode": {
+            "us_per_step_mean": t_dec * 1e6,
+            "us_per_step_median": dec_sorted[len(dec_sorted) // 2] * 1e3,
+            "GB_per_s": dec_gbs,
+            "hbm_frac": db / t_dec / HBM_PEAK,
+            "alg_bytes_per_step": db,
+        },
+        "roofline": {
+            "kernel": "kda_chunk_fwd (intra_kernel + state_kernel)",
+            "bound": "hbm",
+            "achieved": pb / t_pre / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": pb / t_pre / HBM_PEAK,
+            "traffic": measured_traffic("prefill_long"),
+        },
+        "decode_roofline": {
+            "kernel": "decode_step_kernel<128,128,bf16>",
+            "bound": "hbm",
+            "achieved": dec_gbs,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": db / t_dec / HBM_PEAK,
+            "traffic": measured_traffic("decode"),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        heads = list(range(16))
+        T_s = 65536
+        dt = cpu_baseline(pin, heads, T_s, threads)
+        # the metric's unit is tokens/s at H=32: token-heads/s divided by 32
+        result["cpu_baseline"] = {
+            "value": T_s * len(heads) / dt / H,
+            "unit": "tokens/s",
+            "cores": min(threads, len(heads)),
+            "kind": "oracle",
+            "sample": f"fp64 token loop on heads 0-15 x first {T_s} tokens of the long "
+                      f"prefill workload ({dt:.1f} s wall), scaled to H=32 tokens/s",
+        }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,8 @@ bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
 };
@@ -85,7 +87,9 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     const char *names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
     for (int i = 0; i < 7; ++i) {
         if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", names[i]);
-        if (!aligned16(ptrs[i])) return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+        const bool scalar = i == 4;  // beta is read element by element
+        if (scalar ? !aligned4(ptrs[i]) : !aligned16(ptrs[i]))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", names[i], scalar ? 4 : 16);
     }
     const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
     size_t bq, bv, bg, bb, bs, bo;
@@ -176,14 +180,17 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const char *nn[] = {"q", "k", "v", "log_alpha", "beta", "o"};
     for (int i = 0; i < 6; ++i) {
         if (!need[i] && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", nn[i]);
-        if (need[i] && !aligned16(need[i]))
-            return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", nn[i]);
+        const bool scalar = i == 4;  // beta is read element by element
+        if (need[i] && (scalar ? !aligned4(need[i]) : !aligned16(need[i])))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", nn[i], scalar ? 4 : 16);
     }
     const void *opt[] = {init_state, cu_seqlens, final_state};
     const char *on[] = {"init_state", "cu_seqlens", "final_state"};
-    for (int i = 0; i < 3; ++i)
-        if (opt[i] && !aligned16(opt[i]))
-            return fail(KDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", on[i]);
+    for (int i = 0; i < 3; ++i) {
+        const bool scalar = i == 1;  // cu_seqlens: int32 offsets
+        if (opt[i] && (scalar ? !aligned4(opt[i]) : !aligned16(opt[i])))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", on[i], scalar ? 4 : 16);
+    }
     const bool bf16 = in_dtype == KDA_BF16;
     size_t need_ws = 0, pkg = 0;
     int64_t slots = 0;

@@ -19,7 +19,9 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are device pointers (hipMalloc'd memory of the current device)
- *     unless stated otherwise, 16-byte aligned, dense and row-major.
+ *     unless stated otherwise, dense and row-major, 16-byte aligned except
+ *     beta and cu_seqlens (4-byte aligned), so a slice of a larger tensor
+ *     along tokens or heads may be passed directly.
  *   - Layouts: q, k, log_alpha [B, T, H, Dk]; v, o [B, T, H, Dv];
  *     beta [B, T, H]; states [N, H, Dk, Dv] (row c of a head's state is key
  *     channel c).  bf16 inputs are raw IEEE bfloat16 bit patterns.
@@ -61,7 +63,8 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, aliasing   */
-    KDA_ERR_UNSUPPORTED = 2, /* Dk/Dv outside {16,32,64,128}, chunk size, dtype */
+    KDA_ERR_UNSUPPORTED = 2, /* Dk/Dv outside {16,32,64,128} (prefill: Dk != Dv),
+                                chunk size, dtype                             */
     KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
     KDA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError)      */
 } kda_status;
@@ -90,11 +93,12 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
  *   beta        [B, T, H]     fp32               write strength
  *   init_state  [N, H, Dk, Dv] fp32, nullable    incoming state (NULL: zeros)
  *   cu_seqlens  [N + 1] int32, nullable          packed sequence offsets (device)
- *   B, T, H, Dk, Dv                              sizes; Dk, Dv in {16, 32, 64, 128}
+ *   B, T, H, Dk, Dv                              sizes; Dk == Dv in {16, 32, 64, 128}
  *   n_seqs      N when cu_seqlens is given (then B must be 1), else ignored (N = B)
  *   in_dtype    KDA_BF16 or KDA_F32
  *   chunk_size  16, 32 or 64 (0 selects 64); results do not depend on it
- *               beyond rounding
+ *               beyond rounding (the fp32 path at d = 128 uses at most 32,
+ *               which kda_chunk_fwd_workspace_size accounts for)
  *   o           [B, T, H, Dv] fp32 output; must not overlap any input
  *   final_state [N, H, Dk, Dv] fp32, nullable; may alias init_state
  *   workspace   device scratch of at least kda_chunk_fwd_workspace_size()

@@ -125,12 +125,21 @@ def _decode(lib, **kw):
     (dict(N=-1), INVALID),
     (dict(H=0), INVALID),
     (dict(state=None), INVALID),
-    (dict(beta=FAKE + 0x4000004), INVALID),
+    (dict(beta=FAKE + 0x4000002), INVALID),   # beta needs 4-byte alignment only
+    (dict(q=FAKE + 4), INVALID),
     (dict(o=FAKE + 0x5000000), INVALID),   # o aliases the state
     (dict(state=FAKE + 0x1000000), INVALID),  # state aliases k
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def test_beta_and_cu_seqlens_need_only_natural_alignment(lib):
+    # both still fail later validation on purpose (workspace missing), which
+    # shows the alignment checks accepted them
+    assert _chunk(lib, beta=FAKE + 0x4000004, ws=None) == WORKSPACE
+    assert _chunk(lib, cu_seqlens=FAKE + 0x8000004, n_seqs=2, ws=None) == WORKSPACE
+    assert _chunk(lib, beta=FAKE + 0x4000002) == INVALID
 
 
 def test_empty_decode_is_a_no_op(lib):
