@@ -170,23 +170,42 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t *__restrict__ c
 // -----------------------------------------------------------------------------
 // intra-chunk package
 // -----------------------------------------------------------------------------
+// Layout conventions shared with state_kernel:
+//   * the WQ fragment for row tile rt and 32-channel step ks gives lane l the
+//     token 16 rt + l%16 and the channels 32 ks + 4 (l/16) + e (e < 4) and
+//     32 ks + 16 + 4 (l/16) + (e - 4) (e >= 4); the state pass stores its state
+//     slab with the same channel order, so the pairing of k values matches.
+//   * T' = T Diag(beta) and R = P T' are stored as one 128 x 64 operand
+//     M = [T'; -R], so [W; Q'] = [0; Q*Gamma] + M (K*Gamma) and
+//     [U'; -O_intra] = M V; M is lower triangular in the token index.
 template <int C, int DK, int DV, bool BF>
 __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     using F = Cfg<C, DK, DV, BF>;
     using In = typename F::In;
     using Op = typename F::Op;
     constexpr int NT16 = F::NT16, CP = F::CP, DKP = F::DKP;
+    constexpr int AS = CP + 8;                       // fp32 row stride of A/T and P/R
+    constexpr int MS = BF ? CP + 8 : CP + 4;         // row stride of M (elements)
+    constexpr int SEG = 256 / DK;                    // token segments of the cumsum
+    constexpr int TPS = (C + SEG - 1) / SEG;         // tokens per segment
+    constexpr int KSK = DKP / 32, KSC = CP / 32;
+    constexpr int PARTS = BF ? 2 : 1;
+    using MT = std::conditional_t<BF, __bf16, float>;
 
     __shared__ __align__(16) float sG[C][F::GS];
     __shared__ __align__(16) In sK[C][F::KS];
     __shared__ __align__(16) In sQ[C][F::KS];
     __shared__ __align__(16) In sV[C][F::VS];
-    __shared__ __align__(16) float sA[C][F::AS];
-    __shared__ __align__(16) float sP[C][F::AS];
-    __shared__ __align__(16) float sX[4][32][F::XS];
+    __shared__ __align__(16) float sAP[2][C][AS];  // A -> T and P -> R (fp32); then M
     __shared__ float sBeta[C];
     __shared__ int sLru[C];
+    __shared__ int sAllInf[C];
+    __shared__ float sSeg[SEG][DK];
     __shared__ int sLastReset;
+    static_assert(sizeof(MT) * PARTS * 2 * C * MS <= sizeof(float) * 2 * C * AS, "M overlay");
+    MT *Mp = reinterpret_cast<MT *>(&sAP[0][0][0]);  // [PARTS][2C][MS]
+    float(*sA)[AS] = sAP[0];
+    float(*sP)[AS] = sAP[1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
@@ -198,17 +217,17 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     const int H = p.H;
     char *pkg = p.ws + (static_cast<size_t>(x) * H + h) * p.pkg_bytes;
 
-    // ---- 1. stage the chunk in LDS; pad rows >= nvalid with identity tokens
+    // ---- 1. stage k, q, v in LDS (rows >= nvalid are identity tokens: zeros);
+    //         this thread's log_alpha values go to registers for the cumsum
+    const int cc = tid % DK, seg = tid / DK;
+    float gr[TPS];
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const int i = seg * TPS + u;
+        gr[u] = (i < nvalid) ? p.log_alpha[((tok0 + i) * H + h) * DK + cc] : 0.f;
+    }
     {
-        constexpr int GV4 = DK / 4;
-        for (int idx = tid; idx < C * GV4; idx += 256) {
-            const int i = idx / GV4, c4 = idx % GV4;
-            f32x4 g = {0.f, 0.f, 0.f, 0.f};
-            if (i < nvalid)
-                g = *reinterpret_cast<const f32x4 *>(p.log_alpha + ((tok0 + i) * H + h) * DK + 4 * c4);
-            *reinterpret_cast<f32x4 *>(&sG[i][4 * c4]) = g;
-        }
-        constexpr int EPV = 16 / sizeof(In);  // elements per 16-byte vector
+        constexpr int EPV = 16 / sizeof(In);
         constexpr int KV = DK / EPV, VV = DV / EPV;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         for (int idx = tid; idx < C * KV; idx += 256) {
@@ -230,21 +249,22 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                                                       ((tok0 + i) * H + h) * DV + c);
             *reinterpret_cast<f32x4 *>(&sV[i][c]) = vv;
         }
-        for (int idx = tid; idx < C * F::AS; idx += 256) {
-            (&sA[0][0])[idx] = 0.f;
-            (&sP[0][0])[idx] = 0.f;
+        for (int i = tid; i < C; i += 256) {
+            sBeta[i] = i < nvalid ? p.beta[(tok0 + i) * H + h] : 0.f;
+            sAllInf[i] = i < nvalid ? 1 : 0;
         }
-        for (int i = tid; i < C; i += 256) sBeta[i] = i < nvalid ? p.beta[(tok0 + i) * H + h] : 0.f;
     }
     __syncthreads();
 
-    // ---- 2. resets (log_alpha = -inf on every channel) and their masks
+    // ---- 2. resets: a token whose log_alpha is -inf on every channel
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const int i = seg * TPS + u;
+        if (i < C && !(gr[u] == kNegInf)) sAllInf[i] = 0;
+    }
+    __syncthreads();
     if (w == 0) {
-        bool reset = false;
-        if (lane < nvalid) {
-            reset = true;
-            for (int c = 0; c < DK; ++c) reset = reset && (sG[lane][c] == kNegInf);
-        }
+        const bool reset = lane < C && sAllInf[lane] != 0;
         const uint64_t mask = __ballot(reset);
         if (lane < C) {
             const uint64_t upto = lane == 63 ? mask : (mask & ((uint64_t(1) << (lane + 1)) - 1));
@@ -253,27 +273,55 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
         if (lane == 0) sLastReset = mask ? 63 - __clzll(mask) : -1;
     }
     __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += 256) {
-        const int i = idx / DK, c = idx % DK;
-        const float g = sG[i][c];
-        sG[i][c] = (sLru[i] == i) ? 0.f : fmaxf(g, kGFloor) * kLog2e;
+
+    // ---- 3. cumulative log2-decay per channel (segmented scan in registers)
+    {
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = seg * TPS + u;
+            const float g = (i < C && sLru[i] == i) ? 0.f : fmaxf(gr[u], kGFloor) * kLog2e;
+            run += g;
+            gr[u] = run;
+        }
+        sSeg[seg][cc] = run;
     }
     __syncthreads();
-    // cumulative log2-decay per channel
-    if (tid < DK) {
-        float run = 0.f;
-        for (int i = 0; i < C; ++i) {
-            run += sG[i][tid];
-            sG[i][tid] = run;
+    {
+        float base = 0.f;
+        for (int s2 = 0; s2 < seg; ++s2) base += sSeg[s2][cc];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = seg * TPS + u;
+            if (i < C) sG[i][cc] = gr[u] + base;
         }
     }
+    for (int idx = tid; idx < 2 * C * AS; idx += 256) (&sAP[0][0][0])[idx] = 0.f;
     __syncthreads();
 
     auto Kf = [&](int i, int c) { return in_to_f32<BF>(sK[i][c]); };
     auto Qf = [&](int i, int c) { return in_to_f32<BF>(sQ[i][c]); };
     auto Vf = [&](int i, int c) { return in_to_f32<BF>(sV[i][c]); };
+    auto ld8f = [&](const float *src, float (&o)[8]) {
+        const f32x4 a = reinterpret_cast<const f32x4 *>(src)[0];
+        const f32x4 b = reinterpret_cast<const f32x4 *>(src)[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[e] = a[e];
+            o[4 + e] = b[e];
+        }
+    };
+    auto ld8in = [&](const In *src, float (&o)[8]) {
+        if constexpr (BF) {
+            const u16x8 r = *reinterpret_cast<const u16x8 *>(src);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32(r[e]);
+        } else {
+            ld8f(src, o);
+        }
+    };
 
-    // ---- 3. A and P, 16x16 tiles on the lower triangle
+    // ---- 4. A and P, 16x16 tiles on the lower triangle (factored exponents)
     {
         constexpr int NTILES = NT16 * (NT16 + 1) / 2;
         for (int t = w; t < NTILES; t += 4) {
@@ -286,27 +334,37 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
             bool unsafe_any = false;
 #pragma unroll
             for (int ks = 0; ks < DKP / 32; ++ks) {
+                const int c0 = 32 * ks + 8 * kg;
                 float xk[8], xq[8], y[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = 32 * ks + 8 * kg + e;
-                    xk[e] = xq[e] = y[e] = 0.f;
-                    if (c < DK) {
-                        const float gm = sG[m][c];
-                        float fa = fast_exp2(sG[ia][c] - gm);
-                        float fb = fast_exp2(gm - sG[jb][c]);
-                        if (diag) {
-                            const float span = fmaxf(sG[16 * I][c] - gm, gm - sG[16 * I + 15][c]);
-                            if (!(span <= kSafeSpan2)) {
-                                fa = 0.f;
-                                fb = 0.f;
-                                unsafe_any = true;
-                            }
-                        }
-                        xk[e] = Kf(ia, c) * fa;
-                        xq[e] = Qf(ia, c) * fa;
-                        y[e] = Kf(jb, c) * fb;
+                if (c0 < DK) {
+                    float gi[8], gm[8], gj[8], ki[8], qi[8], kj[8];
+                    ld8f(&sG[ia][c0], gi);
+                    ld8f(&sG[m][c0], gm);
+                    ld8f(&sG[jb][c0], gj);
+                    ld8in(&sK[ia][c0], ki);
+                    ld8in(&sQ[ia][c0], qi);
+                    ld8in(&sK[jb][c0], kj);
+                    float gf[8], gl[8];
+                    if (diag) {
+                        ld8f(&sG[16 * I][c0], gf);
+                        ld8f(&sG[16 * I + 15][c0], gl);
                     }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float fa = fast_exp2(gi[e] - gm[e]);
+                        float fb = fast_exp2(gm[e] - gj[e]);
+                        if (diag && !(fmaxf(gf[e] - gm[e], gm[e] - gl[e]) <= kSafeSpan2)) {
+                            fa = 0.f;
+                            fb = 0.f;
+                            unsafe_any = true;
+                        }
+                        xk[e] = ki[e] * fa;
+                        xq[e] = qi[e] * fa;
+                        y[e] = kj[e] * fb;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xk[e] = xq[e] = y[e] = 0.f;
                 }
                 mma<F::kIntra>(accA, xk, y);
                 mma<F::kIntra>(accP, xq, y);
@@ -338,7 +396,7 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     }
     __syncthreads();
 
-    // ---- 4. T = (I + A)^-1 in place (unit lower triangular), then T' = T Diag(beta)
+    // ---- 5. T = (I + A)^-1 (unit lower triangular), in place over A
     if (w < NT16 && lane < 16) {
         const int base = 16 * w, col = lane;
         float t[16];
@@ -354,225 +412,328 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
             if (i >= col) sA[base + i][base + col] = t[i];
     }
     __syncthreads();
+    // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ  (fp32 matrix cores)
     for (int I = 1; I < NT16; ++I) {
-        float *X = &sX[0][0][0];  // I blocks of 16x16 scratch
-        const int i = tid >> 4, j = tid & 15;
-        for (int J = 0; J < I; ++J) {
-            float acc = 0.f;
-            for (int K = J; K < I; ++K)
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        const int J = w;
+        if (J < I) {
+            f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+            for (int K = J; K < I; ++K) {
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    acc += sA[16 * I + i][16 * K + kk] * sA[16 * K + kk][16 * J + j];
-            X[J * 256 + i * 16 + j] = acc;
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int kk = 4 * s4 + kg;
+                    xv = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * I + l16][16 * K + kk],
+                                                               sA[16 * K + kk][16 * J + l16], xv, 0, 0, 0);
+                }
+            }
+            // y = T_II x, with x's rows 4 kg + r held by this lane as xv[r]
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * I + l16][16 * I + 4 * kg + r], xv[r], y,
+                                                          0, 0, 0);
         }
         __syncthreads();
-        for (int J = 0; J < I; ++J) {
-            float acc = 0.f;
+        if (J < I) {
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) acc += sA[16 * I + i][16 * I + kk] * X[J * 256 + kk * 16 + j];
-            sA[16 * I + i][16 * J + j] = -acc;
+            for (int r = 0; r < 4; ++r) sA[16 * I + 4 * kg + r][16 * J + l16] = -y[r];
         }
         __syncthreads();
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int i = idx / C, j = idx % C;
-        sA[i][j] *= sBeta[j];
+
+    // ---- 6. R = P T' and M = [T'; -R] (T' = T Diag(beta)) as matrix-core operands
+    {
+        constexpr int NB = NT16 * (NT16 + 1) / 2;
+        constexpr int BPW = (NB + 3) / 4;
+        f32x4 tv[BPW], rv[BPW];
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int t = w + 4 * b;
+            tv[b] = rv[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < NB) {
+                int I = 0, J = t;
+                while (J > I) { J -= I + 1; ++I; }
+                const float bj = sBeta[16 * J + l16];
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K <= I; ++K) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int kk = 4 * s4 + kg;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[16 * I + l16][16 * K + kk],
+                                                                    sA[16 * K + kk][16 * J + l16], acc, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    rv[b][r] = -acc[r] * bj;
+                    tv[b][r] = sA[16 * I + 4 * kg + r][16 * J + l16] * bj;
+                }
+            }
+        }
+        __syncthreads();  // every fp32 read of A/T and P is done: M overlays them
+        for (int idx = tid; idx < PARTS * 2 * C * MS; idx += 256) Mp[idx] = static_cast<MT>(0.f);
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int t = w + 4 * b;
+            if (t < NB) {
+                int I = 0, J = t;
+                while (J > I) { J -= I + 1; ++I; }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * I + 4 * kg + r, col = 16 * J + l16;
+                    const float vals[2] = {tv[b][r], rv[b][r]};
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const size_t o = static_cast<size_t>(hh * C + row) * MS + col;
+                        if constexpr (BF) {
+                            const __bf16 hi = static_cast<__bf16>(vals[hh]);
+                            Mp[o] = hi;
+                            Mp[static_cast<size_t>(2 * C) * MS + o] =
+                                static_cast<__bf16>(vals[hh] - static_cast<float>(hi));
+                        } else {
+                            Mp[o] = vals[hh];
+                        }
+                    }
+                }
+            }
+        }
     }
     __syncthreads();
 
-    // ---- 5/6. per-wave jobs: channel groups (W, Q') and value groups (U', O_intra)
-    float(*X)[F::XS] = sX[w];
-    auto a_frag = [&](const float(*M)[F::AS], int I, int s, float (&a)[8]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = M[16 * I + l16][32 * s + 8 * kg + e];
+    // ---- 7. package: [W; Q'] fragments, Kt fragments, U', O_intra, Gamma_last
+    const int last_reset = sLastReset;
+    // B fragment of M^T for row tile rt and token step s: row 16 rt + l16 of M
+    auto m_frag_bf = [&](int rt, int s, bf16x8 &hi, bf16x8 &lo) {
+        const size_t o = static_cast<size_t>(16 * rt + l16) * MS + 32 * s + 8 * kg;
+        hi = *reinterpret_cast<const bf16x8 *>(Mp + o);
+        lo = *reinterpret_cast<const bf16x8 *>(Mp + static_cast<size_t>(2 * C) * MS + o);
     };
-    for (int job = w; job < F::GK + F::GV; job += 4) {
-        if (job < F::GK) {
-            const int g = job;
-            // W = T' (K * Gamma) for the 32 channels of group g, kept transposed in X
-            for (int hc = 0; hc < 2; ++hc) {
-                const int ct = 2 * g + hc;
-                if (16 * ct >= DK) break;
-                const int c = 16 * ct + l16;
-#pragma unroll
-                for (int I = 0; I < NT16; ++I) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < CP / 32; ++s) {
-                        float a[8], b[8];
-                        a_frag(sA, I, s, a);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int j = 32 * s + 8 * kg + e;
-                            b[e] = (j < C && sLru[j] < 0) ? Kf(j, c) * fast_exp2(sG[j][c]) : 0.f;
-                        }
-                        mma<F::kIntra>(acc, a, b);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) X[16 * hc + l16][16 * I + 4 * kg + r] = acc[r];
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            // Q' = Q * Gamma - P W   (registers)
-            f32x4 qp[2][NT16];
+    auto m_frag_f = [&](int rt, int s, float (&a)[8]) {
+        ld8f(reinterpret_cast<const float *>(Mp) + static_cast<size_t>(16 * rt + l16) * MS + 32 * s + 8 * kg, a);
+    };
+    Op *wq = reinterpret_cast<Op *>(pkg + p.L.wq);
+    Op *kt = reinterpret_cast<Op *>(pkg + p.L.kt);
+    constexpr int NJOBS = KSK + DV / 16;
+    for (int job = w; job < NJOBS; job += 4) {
+        if (job < KSK) {
+            // channels 32 ks .. 32 ks + 31: W^T = Kg^T T'^T and Q'^T = Qg^T + Kg^T (-R)^T
+            const int ks = job;
+            bf16x8 ka_hi[2][KSC], ka_lo[2][KSC];
+            float ka_f[2][KSC][8];
 #pragma unroll
             for (int hc = 0; hc < 2; ++hc) {
-                const int ct = 2 * g + hc;
-                const int c = 16 * ct + l16;
+                const int c = 32 * ks + 16 * hc + l16;
 #pragma unroll
-                for (int I = 0; I < NT16; ++I) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (16 * ct < DK) {
+                for (int s = 0; s < KSC; ++s) {
+                    float kgv[8], ktv[8];
 #pragma unroll
-                        for (int s = 0; s < CP / 32; ++s) {
-                            float a[8], b[8];
-                            a_frag(sP, I, s, a);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const int j = 32 * s + 8 * kg + e;
-                                b[e] = j < C ? X[16 * hc + l16][j] : 0.f;
-                            }
-                            mma<F::kIntra>(acc, a, b);
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int i = 16 * I + 4 * kg + r;
-                            const float qg = sLru[i] < 0 ? Qf(i, c) * fast_exp2(sG[i][c]) : 0.f;
-                            acc[r] = qg - acc[r];
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * s + 8 * kg + e;
+                        kgv[e] = ktv[e] = 0.f;
+                        if (c < DK && j < C) {
+                            const float kk = Kf(j, c), gj = sG[j][c];
+                            kgv[e] = sLru[j] < 0 ? kk * fast_exp2(gj) : 0.f;
+                            ktv[e] = j >= last_reset ? kk * fast_exp2(sG[C - 1][c] - gj) : 0.f;
                         }
                     }
-                    qp[hc][I] = acc;
+                    if (c < DK) {
+                        const int ct = 2 * ks + hc;
+                        Op *dst = kt + ((static_cast<size_t>(ct) * KSC + s) * PARTS * 64 + lane) * 8;
+                        if constexpr (BF) {
+                            f16x8 hi, lo;
+                            split_f16(ktv, hi, lo);
+                            *reinterpret_cast<f16x8 *>(dst) = hi;
+                            *reinterpret_cast<f16x8 *>(dst + 64 * 8) = lo;
+                        } else {
+                            store8(dst, ktv);
+                        }
+                    }
+                    if constexpr (BF) split_bf16(kgv, ka_hi[hc][s], ka_lo[hc][s]);
+                    else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ka_f[hc][s][e] = kgv[e];
+                    }
                 }
             }
-            // WQ fragments, W part: row 16 I + l16, channels 32 g + 8 kg + e
-            Op *wq = reinterpret_cast<Op *>(pkg + p.L.wq);
 #pragma unroll
-            for (int I = 0; I < NT16; ++I) {
+            for (int rt = 0; rt < 2 * NT16; ++rt) {
+                const int I = rt < NT16 ? rt : rt - NT16;
+                const int nks = (16 * I + 15) / 32 + 1;  // token steps with nonzeros
+                f32x4 acc[2];
+#pragma unroll
+                for (int hc = 0; hc < 2; ++hc) {
+                    acc[hc] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int c0 = 32 * ks + 16 * hc + 4 * kg;
+                    if (rt >= NT16 && c0 < DK) {  // Q * Gamma for token 16 I + l16
+                        const int i = 16 * I + l16;
+                        if (sLru[i] < 0) {
+                            const f32x4 gv = *reinterpret_cast<const f32x4 *>(&sG[i][c0]);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[hc][r] = Qf(i, c0 + r) * fast_exp2(gv[r]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < KSC; ++s) {
+                    if (s >= nks) break;
+                    if constexpr (BF) {
+                        bf16x8 mh, ml;
+                        m_frag_bf(rt, s, mh, ml);
+#pragma unroll
+                        for (int hc = 0; hc < 2; ++hc) {
+                            acc[hc] = mfma_bf16(ka_lo[hc][s], mh, acc[hc]);
+                            acc[hc] = mfma_bf16(ka_hi[hc][s], ml, acc[hc]);
+                            acc[hc] = mfma_bf16(ka_hi[hc][s], mh, acc[hc]);
+                        }
+                    } else {
+                        float mf[8];
+                        m_frag_f(rt, s, mf);
+#pragma unroll
+                        for (int hc = 0; hc < 2; ++hc) mma<Prec::F32>(acc[hc], ka_f[hc][s], mf);
+                    }
+                }
                 float v8[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int cl = 8 * kg + e;
-                    v8[e] = (32 * g + cl < DK) ? X[cl][16 * I + l16] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    v8[r] = acc[0][r];
+                    v8[4 + r] = acc[1][r];
                 }
-                store8(wq + ((static_cast<size_t>(I) * (DKP / 32) + g) * 64 + lane) * 8, v8);
+                store8(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8, v8);
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-            for (int hc = 0; hc < 2; ++hc)
-#pragma unroll
-                for (int I = 0; I < NT16; ++I)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) X[16 * hc + l16][16 * I + 4 * kg + r] = qp[hc][I][r];
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-            for (int I = 0; I < NT16; ++I) {
-                float v8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int cl = 8 * kg + e;
-                    v8[e] = (32 * g + cl < DK) ? X[cl][16 * I + l16] : 0.f;
-                }
-                store8(wq + ((static_cast<size_t>(NT16 + I) * (DKP / 32) + g) * 64 + lane) * 8, v8);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         } else {
-            const int g = job - F::GK;
+            // value columns 16 ct .. 16 ct + 15: [U'; -O_intra] = M V
+            const int ct = job - KSK;
+            const int c = 16 * ct + l16;
+            float vb[KSC][8];
+#pragma unroll
+            for (int s = 0; s < KSC; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * s + 8 * kg + e;
+                    vb[s][e] = j < C ? Vf(j, c) : 0.f;
+                }
             f32x4 *up = reinterpret_cast<f32x4 *>(pkg + p.L.up);
             f32x4 *oi = reinterpret_cast<f32x4 *>(pkg + p.L.oi);
-            // U' = T' V for the 32 value columns of group g
-            for (int hc = 0; hc < 2; ++hc) {
-                const int ct = 2 * g + hc;
-                if (16 * ct >= DV) break;
-                const int c = 16 * ct + l16;
 #pragma unroll
-                for (int I = 0; I < NT16; ++I) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 2 * NT16; ++rt) {
+                const int I = rt < NT16 ? rt : rt - NT16;
+                const int nks = (16 * I + 15) / 32 + 1;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < CP / 32; ++s) {
-                        float a[8], b[8];
-                        a_frag(sA, I, s, a);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int j = 32 * s + 8 * kg + e;
-                            b[e] = j < C ? Vf(j, c) : 0.f;
-                        }
-                        mma<F::kIntraV>(acc, a, b);
+                for (int s = 0; s < KSC; ++s) {
+                    if (s >= nks) break;
+                    if constexpr (BF) {
+                        bf16x8 mh, ml;
+                        m_frag_bf(rt, s, mh, ml);
+                        const bf16x8 vv = pack_bf16(vb[s]);
+                        acc = mfma_bf16(ml, vv, acc);
+                        acc = mfma_bf16(mh, vv, acc);
+                    } else {
+                        float mf[8];
+                        m_frag_f(rt, s, mf);
+                        mma<Prec::F32>(acc, mf, vb[s]);
                     }
-                    up[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane] = acc;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) X[16 * hc + l16][16 * I + 4 * kg + r] = acc[r];
                 }
+                if (rt < NT16) up[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane] = acc;
+                else oi[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane] = -acc;
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            // O_intra = P U'
-            for (int hc = 0; hc < 2; ++hc) {
-                const int ct = 2 * g + hc;
-                if (16 * ct >= DV) break;
-#pragma unroll
-                for (int I = 0; I < NT16; ++I) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < CP / 32; ++s) {
-                        float a[8], b[8];
-                        a_frag(sP, I, s, a);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int j = 32 * s + 8 * kg + e;
-                            b[e] = j < C ? X[16 * hc + l16][j] : 0.f;
-                        }
-                        mma<F::kIntra>(acc, a, b);
-                    }
-                    oi[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane] = acc;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
-
-    // ---- 7. decayed keys Kt (A operand of Kt^T U) and Gamma_last
-    {
-        const int last_reset = sLastReset;
-        constexpr int NKT = (DK / 16) * (CP / 32);
-        Op *kt = reinterpret_cast<Op *>(pkg + p.L.kt);
-        constexpr int PARTS = BF ? 2 : 1;
-        for (int blk = w; blk < NKT; blk += 4) {
-            const int ct = blk / (CP / 32), ks = blk % (CP / 32);
-            const int c = 16 * ct + l16;
-            const float glast = sG[C - 1][c];
-            float val[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = 32 * ks + 8 * kg + e;
-                val[e] = (j < C && j >= last_reset) ? Kf(j, c) * fast_exp2(glast - sG[j][c]) : 0.f;
-            }
-            Op *dst = kt + ((static_cast<size_t>(ct) * (CP / 32) + ks) * PARTS * 64 + lane) * 8;
-            if constexpr (BF) {
-                f16x8 hi, lo;
-                split_f16(val, hi, lo);
-                *reinterpret_cast<f16x8 *>(dst) = hi;
-                *reinterpret_cast<f16x8 *>(dst + 64 * 8) = lo;
-            } else {
-                store8(dst, val);
-            }
-        }
-        float *gl = reinterpret_cast<float *>(pkg + p.L.gl);
-        for (int c = tid; c < DK; c += 256) gl[c] = last_reset >= 0 ? 0.f : fast_exp2(sG[C - 1][c]);
-    }
+    float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
+    for (int c = tid; c < DK; c += 256) glp[c] = last_reset >= 0 ? 0.f : fast_exp2(sG[C - 1][c]);
 }
 
 // -----------------------------------------------------------------------------
 // sequential state pass: one workgroup per (sequence, head, 16-column slab)
 // -----------------------------------------------------------------------------
+// 8 matrix-core operand values of one lane: fp16 (bf16 path) or fp32.
+template <bool BF>
+struct Vec8;
+template <>
+struct Vec8<true> {
+    f16x8 v;
+};
+template <>
+struct Vec8<false> {
+    f32x4 a, b;
+};
+
+template <bool BF>
+__device__ __forceinline__ Vec8<BF> ld_vec8(const void *p) {
+    Vec8<BF> r;
+    if constexpr (BF) {
+        r.v = *reinterpret_cast<const f16x8 *>(p);
+    } else {
+        r.a = reinterpret_cast<const f32x4 *>(p)[0];
+        r.b = reinterpret_cast<const f32x4 *>(p)[1];
+    }
+    return r;
+}
+
+__device__ __forceinline__ void unpack8(const Vec8<false> &x, float (&o)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[e] = x.a[e];
+        o[4 + e] = x.b[e];
+    }
+}
+
+// The part of one chunk's package a wave of the state pass consumes, held in
+// registers so the next chunk's loads are in flight while this one computes.
+template <int C, int DK, int DV, bool BF>
+struct StateFrags {
+    using F = Cfg<C, DK, DV, BF>;
+    static constexpr int NTK = DK / 16, SPW = (NTK + 3) / 4;
+    static constexpr int NRT = 2 * F::NT16, RPW = (NRT + 3) / 4;
+    static constexpr int KSK = F::DKP / 32, KSC = F::CP / 32, PARTS = BF ? 2 : 1;
+    Vec8<BF> wq[RPW][KSK];
+    f32x4 uo[RPW];
+    Vec8<BF> kt[SPW][KSC][PARTS];
+    f32x4 gl[SPW];
+
+    __device__ __forceinline__ void load(const char *pkg, const PackageLayout &L, int w, int lane,
+                                         int ct) {
+        using Op = typename F::Op;
+        constexpr int NT16 = F::NT16;
+        const Op *wqp = reinterpret_cast<const Op *>(pkg + L.wq);
+#pragma unroll
+        for (int rw = 0; rw < RPW; ++rw) {
+            const int rt = w + 4 * rw;
+            if (rt < NRT) {
+#pragma unroll
+                for (int ks = 0; ks < KSK; ++ks)
+                    wq[rw][ks] = ld_vec8<BF>(wqp + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8);
+                const size_t off = rt < NT16 ? L.up : L.oi;
+                const int I = rt < NT16 ? rt : rt - NT16;
+                uo[rw] = reinterpret_cast<const f32x4 *>(pkg + off)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane];
+            }
+        }
+        const Op *ktp = reinterpret_cast<const Op *>(pkg + L.kt);
+        const float *glp = reinterpret_cast<const float *>(pkg + L.gl);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+#pragma unroll
+                for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+                    for (int pt = 0; pt < PARTS; ++pt)
+                        kt[sl][ks][pt] = ld_vec8<BF>(
+                            ktp + (((static_cast<size_t>(tk) * KSC + ks) * PARTS + pt) * 64 + lane) * 8);
+                gl[sl] = *reinterpret_cast<const f32x4 *>(glp + 16 * tk + 4 * (lane >> 4));
+            }
+        }
+    }
+};
+
 template <int C, int DK, int DV, bool BF>
 __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     using F = Cfg<C, DK, DV, BF>;
     using Op = typename F::Op;
+    using Frags = StateFrags<C, DK, DV, BF>;
     constexpr int NT16 = F::NT16, CP = F::CP, DKP = F::DKP;
-    constexpr int NTK = DK / 16;                 // 16-row tiles of the state
-    constexpr int SPW = (NTK + 3) / 4;           // state tiles per wave
-    constexpr int NRT = 2 * NT16;                // row tiles of [W; Q']
-    constexpr int RPW = (NRT + 3) / 4;           // [W; Q'] row tiles per wave
-    constexpr int PARTS = BF ? 2 : 1;
+    constexpr int NTK = Frags::NTK, SPW = Frags::SPW, NRT = Frags::NRT, RPW = Frags::RPW;
+    constexpr int KSK = Frags::KSK, KSC = Frags::KSC, PARTS = Frags::PARTS;
     constexpr int SSS = DKP + 8;                 // LDS strides (elements)
     constexpr int SUS = CP + 8;
 
@@ -595,6 +756,9 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
         slot_base = static_cast<int64_t>(n) * ((p.T + C - 1) / C);
     }
     const int64_t nchunks = (L + C - 1) / C;
+    auto pkg_of = [&](int64_t c) {
+        return p.ws + (static_cast<size_t>(slot_base + c) * H + h) * p.pkg_bytes;
+    };
 
     for (int idx = tid; idx < 16 * SSS; idx += 256) (&sS[0][0])[idx] = static_cast<Op>(0.f);
     for (int idx = tid; idx < PARTS * 16 * SUS; idx += 256) (&sU[0][0][0])[idx] = static_cast<Op>(0.f);
@@ -613,20 +777,24 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
         }
     }
     __syncthreads();
+    // The state slab is stored [col][channel] with the channel order of the WQ
+    // fragments: within each 32-channel step, position 8 g + 4 half + r holds
+    // channel 16 half + 4 g + r.
     auto put_state = [&]() {
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
             if (tk < NTK) {
+                const int pos = 32 * (tk >> 1) + 8 * kg + 4 * (tk & 1);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sS[l16][16 * tk + 4 * kg + r] = static_cast<Op>(S[sl][r]);
+                for (int r = 0; r < 4; ++r) sS[l16][pos + r] = static_cast<Op>(S[sl][r]);
             }
         }
     };
     put_state();
 
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const char *pkg = p.ws + (static_cast<size_t>(slot_base + c) * H + h) * p.pkg_bytes;
+    // one chunk of the recurrence on this slab, operands from registers
+    auto step = [&](const Frags &f, int64_t c) {
         const int64_t rem = L - c * C;
         const int nvalid = static_cast<int>(rem < C ? rem : C);
         __syncthreads();  // sS holds this chunk's incoming state
@@ -637,27 +805,21 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
             const int rt = w + 4 * rw;
             if (rt >= NRT) break;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const Op *wq = reinterpret_cast<const Op *>(pkg + p.L.wq);
 #pragma unroll
-            for (int ks = 0; ks < DKP / 32; ++ks) {
-                const Op *af = wq + ((static_cast<size_t>(rt) * (DKP / 32) + ks) * 64 + lane) * 8;
+            for (int ks = 0; ks < KSK; ++ks) {
                 if constexpr (BF) {
-                    const f16x8 a = *reinterpret_cast<const f16x8 *>(af);
                     const f16x8 b = *reinterpret_cast<const f16x8 *>(&sS[l16][32 * ks + 8 * kg]);
-                    acc = mfma_f16(a, b, acc);
+                    acc = mfma_f16(f.wq[rw][ks].v, b, acc);
                 } else {
                     float a[8], b[8];
+                    unpack8(f.wq[rw][ks], a);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        a[e] = af[e];
-                        b[e] = sS[l16][32 * ks + 8 * kg + e];
-                    }
+                    for (int e = 0; e < 8; ++e) b[e] = sS[l16][32 * ks + 8 * kg + e];
                     mma<Prec::F32>(acc, a, b);
                 }
             }
             if (rt < NT16) {
-                const f32x4 upv = reinterpret_cast<const f32x4 *>(pkg + p.L.up)[(static_cast<size_t>(ct) * NT16 + rt) * 64 + lane];
-                const f32x4 u = upv - acc;
+                const f32x4 u = f.uo[rw] - acc;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * rt + 4 * kg + r;
@@ -667,8 +829,7 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
                 }
             } else {
                 const int I = rt - NT16;
-                const f32x4 oiv = reinterpret_cast<const f32x4 *>(pkg + p.L.oi)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane];
-                const f32x4 ov = oiv + acc;
+                const f32x4 ov = f.uo[rw] + acc;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * I + 4 * kg + r;
@@ -679,40 +840,43 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
         __syncthreads();  // sU complete; all reads of sS done
 
         // (c) S1 = Diag(Gamma_last) S0 + Kt^T U for this wave's state tiles
-        const float *gl = reinterpret_cast<const float *>(pkg + p.L.gl);
-        const Op *kt = reinterpret_cast<const Op *>(pkg + p.L.kt);
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
             if (tk >= NTK) break;
-            f32x4 acc;
+            f32x4 acc = f.gl[sl] * S[sl];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gl[16 * tk + 4 * kg + r] * S[sl][r];
-#pragma unroll
-            for (int ks = 0; ks < CP / 32; ++ks) {
-                const Op *af = kt + ((static_cast<size_t>(tk) * (CP / 32) + ks) * PARTS * 64 + lane) * 8;
+            for (int ks = 0; ks < KSC; ++ks) {
                 if constexpr (BF) {
-                    const f16x8 ah = *reinterpret_cast<const f16x8 *>(af);
-                    const f16x8 al = *reinterpret_cast<const f16x8 *>(af + 64 * 8);
                     const f16x8 bh = *reinterpret_cast<const f16x8 *>(&sU[0][l16][32 * ks + 8 * kg]);
                     const f16x8 bl = *reinterpret_cast<const f16x8 *>(&sU[1][l16][32 * ks + 8 * kg]);
-                    acc = mfma_f16(al, bh, acc);
-                    acc = mfma_f16(ah, bl, acc);
-                    acc = mfma_f16(ah, bh, acc);
+                    acc = mfma_f16(f.kt[sl][ks][1].v, bh, acc);
+                    acc = mfma_f16(f.kt[sl][ks][0].v, bl, acc);
+                    acc = mfma_f16(f.kt[sl][ks][0].v, bh, acc);
                 } else {
                     float a[8], b[8];
+                    unpack8(f.kt[sl][ks][0], a);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        a[e] = af[e];
-                        b[e] = sU[0][l16][32 * ks + 8 * kg + e];
-                    }
+                    for (int e = 0; e < 8; ++e) b[e] = sU[0][l16][32 * ks + 8 * kg + e];
                     mma<Prec::F32>(acc, a, b);
                 }
             }
             S[sl] = acc;
         }
         put_state();
+    };
+
+    // software pipeline: the package of chunk c + 1 loads while chunk c computes
+    Frags fa, fb;
+    if (nchunks > 0) fa.load(pkg_of(0), p.L, w, lane, ct);
+    int64_t c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        fb.load(pkg_of(c + 1), p.L, w, lane, ct);
+        step(fa, c);
+        if (c + 2 < nchunks) fa.load(pkg_of(c + 2), p.L, w, lane, ct);
+        step(fb, c + 1);
     }
+    if (c < nchunks) step(fa, c);
 
     if (p.final_state) {
 #pragma unroll
