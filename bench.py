@@ -88,6 +88,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the KDA operator here runs on a single "
@@ -106,7 +107,7 @@ def main():
     # ---- inputs (seeded, synthetic, resident in HBM) ----------------------------
     pin = workloads.make_prefill("long", dev, 0)
     w = pin["workload"]
-    T, H, Dk, Dv, C, N = pin["T"], w.H, w.Dk, w.Dv, w.chunk, pin["N"]
+    T, H, Dk, Dv, C, N = pin["T"], w.H, w.Dk, w.Dv, (args.chunk or w.chunk), pin["N"]
     o = torch.empty((1, T, H, Dv), dtype=torch.float32, device=dev)
     fs = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
     ws_bytes = kda.workspace_size(1, T, H, Dk, Dv, 0, torch.bfloat16, C)

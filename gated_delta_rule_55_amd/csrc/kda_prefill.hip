@@ -36,6 +36,7 @@
 // Operand precision (fp32 accumulation everywhere): with bf16 inputs the
 // intra products use bf16 hi/lo splits (three products), [W; Q'] S uses fp16,
 // Kt^T U uses fp16 hi/lo splits; with fp32 inputs every product is fp32.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_common.h"
@@ -47,6 +48,7 @@ namespace kda {
 constexpr float kGFloor = -88.0f;               // clamp for partial -inf decays
 constexpr float kSafeSpan2 = 110.0f;            // max |exponent| (log2) of a factor
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kIntraThreads = 256;               // 4 waves
 
 struct IntraParams {
     const void *q, *k, *v;
@@ -178,18 +180,105 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t *__restrict__ c
 //   * T' = T Diag(beta) and R = P T' are stored as one 128 x 64 operand
 //     M = [T'; -R], so [W; Q'] = [0; Q*Gamma] + M (K*Gamma) and
 //     [U'; -O_intra] = M V; M is lower triangular in the token index.
+// One chunk's inputs as held in registers by one thread (the kernel loads the
+// next work item's inputs while it computes the current one).
 template <int C, int DK, int DV, bool BF>
-__global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
+struct IntraInputs {
+    using In = typename Cfg<C, DK, DV, BF>::In;
+    static constexpr int SEG = kIntraThreads / DK, TPS = (C + SEG - 1) / SEG;
+    static constexpr int EPV = 16 / sizeof(In);
+    static constexpr int KV = DK / EPV, VV = DV / EPV;
+    static constexpr int NKV = (C * KV + kIntraThreads - 1) / kIntraThreads;
+    static constexpr int NVV = (C * VV + kIntraThreads - 1) / kIntraThreads;
+    float g[TPS];
+    f32x4 k[NKV], q[NKV], v[NVV];
+    float beta;
+    int64_t tok0;
+    int nvalid;
+    bool valid;
+
+    __device__ __forceinline__ void load(const IntraParams &p, int64_t item, int tid) {
+        const int H = p.H;
+        const int64_t slot = item / H;
+        const int h = static_cast<int>(item % H);
+        valid = locate_chunk(slot, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid);
+        if (!valid) nvalid = 0;
+        const int cc = tid % DK, seg = tid / DK;
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = seg * TPS + u;
+            g[u] = (i < nvalid) ? p.log_alpha[((tok0 + i) * H + h) * DK + cc] : 0.f;
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < NKV; ++r) {
+            const int idx = tid + kIntraThreads * r;
+            const int i = idx / KV, c = (idx % KV) * EPV;
+            k[r] = q[r] = z;
+            if (idx < C * KV && i < nvalid) {
+                const int64_t off = ((tok0 + i) * H + h) * DK + c;
+                k[r] = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.k) + off);
+                q[r] = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.q) + off);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NVV; ++r) {
+            const int idx = tid + kIntraThreads * r;
+            const int i = idx / VV, c = (idx % VV) * EPV;
+            v[r] = z;
+            if (idx < C * VV && i < nvalid)
+                v[r] = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.v) +
+                                                        ((tok0 + i) * H + h) * DV + c);
+        }
+        beta = (tid < nvalid) ? p.beta[(tok0 + tid) * H + h] : 0.f;
+    }
+};
+
+// Reads one 32-bit word of each 128-byte line of the next work item's q, k,
+// v and log_alpha rows, so that those lines are in L2 when the item starts.
+// Returns the sum of the words (only to keep the loads alive).
+template <int C, int DK, int DV, bool BF>
+__device__ __forceinline__ float touch_next_item(const IntraParams &p, int64_t item, int64_t n_items,
+                                                 int tid) {
+    using In = typename Cfg<C, DK, DV, BF>::In;
+    if (item >= n_items) return 0.f;
+    const int H = p.H;
+    int64_t tok0;
+    int nvalid;
+    if (!locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return 0.f;
+    const int h = static_cast<int>(item % H);
+    constexpr int LK = DK * sizeof(In) / 128 > 0 ? DK * sizeof(In) / 128 : 1;  // lines per q/k row
+    constexpr int LV = DV * sizeof(In) / 128 > 0 ? DV * sizeof(In) / 128 : 1;
+    constexpr int LG = DK * 4 / 128 > 0 ? DK * 4 / 128 : 1;
+    constexpr int PER_ROW = 2 * LK + LV + LG;
+    float acc = 0.f;
+    for (int idx = tid; idx < nvalid * PER_ROW; idx += kIntraThreads) {
+        const int i = idx / PER_ROW, l = idx % PER_ROW;
+        const int64_t row = (tok0 + i) * H + h;
+        const float *src;
+        if (l < LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.q) + row * DK) + l * 32;
+        else if (l < 2 * LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.k) + row * DK) + (l - LK) * 32;
+        else if (l < 2 * LK + LV) src = reinterpret_cast<const float *>(static_cast<const In *>(p.v) + row * DV) + (l - 2 * LK) * 32;
+        else src = p.log_alpha + row * DK + (l - 2 * LK - LV) * 32;
+        acc += *src;
+    }
+    return acc;
+}
+
+template <int C, int DK, int DV, bool BF>
+__global__ void __launch_bounds__(kIntraThreads) intra_kernel(IntraParams p, int64_t n_items) {
     using F = Cfg<C, DK, DV, BF>;
     using In = typename F::In;
     using Op = typename F::Op;
+    using Inputs = IntraInputs<C, DK, DV, BF>;
     constexpr int NT16 = F::NT16, CP = F::CP, DKP = F::DKP;
     constexpr int AS = CP + 8;                       // fp32 row stride of A/T and P/R
     constexpr int MS = BF ? CP + 8 : CP + 4;         // row stride of M (elements)
-    constexpr int SEG = 256 / DK;                    // token segments of the cumsum
-    constexpr int TPS = (C + SEG - 1) / SEG;         // tokens per segment
+    constexpr int SEG = Inputs::SEG;                 // token segments of the cumsum
+    constexpr int TPS = Inputs::TPS;                 // tokens per segment
     constexpr int KSK = DKP / 32, KSC = CP / 32;
     constexpr int PARTS = BF ? 2 : 1;
+    constexpr int NW = kIntraThreads / kWave;
     using MT = std::conditional_t<BF, __bf16, float>;
 
     __shared__ __align__(16) float sG[C][F::GS];
@@ -201,6 +290,8 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     __shared__ int sLru[C];
     __shared__ int sAllInf[C];
     __shared__ float sSeg[SEG][DK];
+    __shared__ uint32_t sNotInf[SEG];
+    __shared__ int sUnsafe[NT16];
     __shared__ int sLastReset;
     static_assert(sizeof(MT) * PARTS * 2 * C * MS <= sizeof(float) * 2 * C * AS, "M overlay");
     MT *Mp = reinterpret_cast<MT *>(&sAP[0][0][0]);  // [PARTS][2C][MS]
@@ -209,58 +300,64 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int h = blockIdx.y;
-    const int64_t x = blockIdx.x;
-    int64_t tok0;
-    int nvalid;
-    if (!locate_chunk(x, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return;
-    const int H = p.H;
-    char *pkg = p.ws + (static_cast<size_t>(x) * H + h) * p.pkg_bytes;
-
-    // ---- 1. stage k, q, v in LDS (rows >= nvalid are identity tokens: zeros);
-    //         this thread's log_alpha values go to registers for the cumsum
     const int cc = tid % DK, seg = tid / DK;
-    float gr[TPS];
+
+    int64_t item = blockIdx.x;
+    const int64_t stride = gridDim.x;
+    for (; item < n_items; item += stride) {
+      const int64_t item_next = item + stride;
+      Inputs cur;
+      cur.load(p, item, tid);
+      if (cur.valid) {
+        const int nvalid = cur.nvalid;
+        float gr[TPS];
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const int i = seg * TPS + u;
-        gr[u] = (i < nvalid) ? p.log_alpha[((tok0 + i) * H + h) * DK + cc] : 0.f;
-    }
+        for (int u = 0; u < TPS; ++u) gr[u] = cur.g[u];
+        char *pkg = p.ws + static_cast<size_t>(item) * p.pkg_bytes;
+        __syncthreads();  // the previous chunk's LDS reads are done
+
+    // ---- 1. stage k, q, v in LDS from registers (rows >= nvalid hold zeros)
     {
-        constexpr int EPV = 16 / sizeof(In);
-        constexpr int KV = DK / EPV, VV = DV / EPV;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        for (int idx = tid; idx < C * KV; idx += 256) {
-            const int i = idx / KV, c = (idx % KV) * EPV;
-            f32x4 kv = z, qv = z;
-            if (i < nvalid) {
-                const int64_t off = ((tok0 + i) * H + h) * DK + c;
-                kv = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.k) + off);
-                qv = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.q) + off);
+#pragma unroll
+        for (int r = 0; r < Inputs::NKV; ++r) {
+            const int idx = tid + kIntraThreads * r;
+            if (idx < C * Inputs::KV) {
+                const int i = idx / Inputs::KV, c = (idx % Inputs::KV) * Inputs::EPV;
+                *reinterpret_cast<f32x4 *>(&sK[i][c]) = cur.k[r];
+                *reinterpret_cast<f32x4 *>(&sQ[i][c]) = cur.q[r];
             }
-            *reinterpret_cast<f32x4 *>(&sK[i][c]) = kv;
-            *reinterpret_cast<f32x4 *>(&sQ[i][c]) = qv;
         }
-        for (int idx = tid; idx < C * VV; idx += 256) {
-            const int i = idx / VV, c = (idx % VV) * EPV;
-            f32x4 vv = z;
-            if (i < nvalid)
-                vv = *reinterpret_cast<const f32x4 *>(static_cast<const In *>(p.v) +
-                                                      ((tok0 + i) * H + h) * DV + c);
-            *reinterpret_cast<f32x4 *>(&sV[i][c]) = vv;
+#pragma unroll
+        for (int r = 0; r < Inputs::NVV; ++r) {
+            const int idx = tid + kIntraThreads * r;
+            if (idx < C * Inputs::VV) {
+                const int i = idx / Inputs::VV, c = (idx % Inputs::VV) * Inputs::EPV;
+                *reinterpret_cast<f32x4 *>(&sV[i][c]) = cur.v[r];
+            }
         }
-        for (int i = tid; i < C; i += 256) {
-            sBeta[i] = i < nvalid ? p.beta[(tok0 + i) * H + h] : 0.f;
-            sAllInf[i] = i < nvalid ? 1 : 0;
+        if (tid < C) {
+            sBeta[tid] = cur.beta;
+            sAllInf[tid] = tid < nvalid ? 1 : 0;
         }
+        if (tid < SEG) sNotInf[tid] = 0u;
     }
     __syncthreads();
 
     // ---- 2. resets: a token whose log_alpha is -inf on every channel
+    {
+        static_assert(TPS <= 32, "one bit per token of a segment");
+        uint32_t notinf = 0;
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const int i = seg * TPS + u;
-        if (i < C && !(gr[u] == kNegInf)) sAllInf[i] = 0;
+        for (int u = 0; u < TPS; ++u) notinf |= static_cast<uint32_t>(!(gr[u] == kNegInf)) << u;
+        // OR over the lanes of this wave holding the same segment (DK or 64 lanes)
+#pragma unroll
+        for (int off = 1; off < (DK < kWave ? DK : kWave); off <<= 1) notinf |= __shfl_xor(notinf, off);
+        if ((tid & ((DK < kWave ? DK : kWave) - 1)) == 0) atomicOr(&sNotInf[seg], notinf);
+    }
+    __syncthreads();
+    if (tid < C) {
+        const int sg = tid / TPS, u = tid % TPS;
+        if ((sNotInf[sg] >> u) & 1u) sAllInf[tid] = 0;
     }
     __syncthreads();
     if (w == 0) {
@@ -296,7 +393,16 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
             if (i < C) sG[i][cc] = gr[u] + base;
         }
     }
-    for (int idx = tid; idx < 2 * C * AS; idx += 256) (&sAP[0][0][0])[idx] = 0.f;
+    for (int idx = tid; idx < 2 * C * AS / 4; idx += kIntraThreads)
+        reinterpret_cast<f32x4 *>(&sAP[0][0][0])[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid < NT16) sUnsafe[tid] = 0;
+    __syncthreads();
+    // diagonal tiles whose half-span exceeds the safe factor range on some channel
+    for (int idx = tid; idx < NT16 * DK; idx += kIntraThreads) {
+        const int I = idx / DK, c = idx % DK;
+        const float gm = sG[16 * I + 7][c];
+        if (!(fmaxf(sG[16 * I][c] - gm, gm - sG[16 * I + 15][c]) <= kSafeSpan2)) sUnsafe[I] = 1;
+    }
     __syncthreads();
 
     auto Kf = [&](int i, int c) { return in_to_f32<BF>(sK[i][c]); };
@@ -322,21 +428,21 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     };
 
     // ---- 4. A and P, 16x16 tiles on the lower triangle (factored exponents)
+    // First touch one word of every 128-byte line of the next item's inputs so
+    // that its loads hit L2 when it starts (the words are consumed at the end).
+    const float touch = touch_next_item<C, DK, DV, BF>(p, item_next, n_items, tid);
     {
         constexpr int NTILES = NT16 * (NT16 + 1) / 2;
-        for (int t = w; t < NTILES; t += 4) {
-            int I = 0, J = t;
-            while (J > I) { J -= I + 1; ++I; }
-            const bool diag = I == J;
-            const int m = diag ? 16 * I + 7 : 16 * J + 15;
+        // factored tile product; kSlow also drops channels whose diagonal-tile
+        // half-span is outside the safe factor range (added exactly below)
+        auto tile_ap = [&](int I, int J, int m, f32x4 &accA, f32x4 &accP, auto slow_tag) {
+            constexpr bool kSlow = decltype(slow_tag)::value;
             const int ia = 16 * I + l16, jb = 16 * J + l16;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            bool unsafe_any = false;
-#pragma unroll
+#pragma unroll 1
             for (int ks = 0; ks < DKP / 32; ++ks) {
                 const int c0 = 32 * ks + 8 * kg;
                 float xk[8], xq[8], y[8];
-                if (c0 < DK) {
+                if (DK >= 32 || c0 < DK) {
                     float gi[8], gm[8], gj[8], ki[8], qi[8], kj[8];
                     ld8f(&sG[ia][c0], gi);
                     ld8f(&sG[m][c0], gm);
@@ -345,7 +451,7 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                     ld8in(&sQ[ia][c0], qi);
                     ld8in(&sK[jb][c0], kj);
                     float gf[8], gl[8];
-                    if (diag) {
+                    if constexpr (kSlow) {
                         ld8f(&sG[16 * I][c0], gf);
                         ld8f(&sG[16 * I + 15][c0], gl);
                     }
@@ -353,10 +459,10 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                     for (int e = 0; e < 8; ++e) {
                         float fa = fast_exp2(gi[e] - gm[e]);
                         float fb = fast_exp2(gm[e] - gj[e]);
-                        if (diag && !(fmaxf(gf[e] - gm[e], gm[e] - gl[e]) <= kSafeSpan2)) {
-                            fa = 0.f;
-                            fb = 0.f;
-                            unsafe_any = true;
+                        if constexpr (kSlow) {
+                            const bool uns = !(fmaxf(gf[e] - gm[e], gm[e] - gl[e]) <= kSafeSpan2);
+                            fa = uns ? 0.f : fa;
+                            fb = uns ? 0.f : fb;
                         }
                         xk[e] = ki[e] * fa;
                         xq[e] = qi[e] * fa;
@@ -366,11 +472,19 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) xk[e] = xq[e] = y[e] = 0.f;
                 }
-                mma<F::kIntra>(accA, xk, y);
-                mma<F::kIntra>(accP, xq, y);
+                mma<Prec::F32>(accA, xk, y);
+                mma<Prec::F32>(accP, xq, y);
             }
-            if (diag && __ballot(unsafe_any)) {
-                // exact per-element terms for channels taken out above
+        };
+        for (int t = w; t < NTILES; t += NW) {
+            int I = 0, J = t;
+            while (J > I) { J -= I + 1; ++I; }
+            const bool diag = I == J;
+            const int m = diag ? 16 * I + 7 : 16 * J + 15;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            if (diag && sUnsafe[I]) {
+                tile_ap(I, J, m, accA, accP, std::true_type{});
+                // exact per-element terms for the channels taken out
                 for (int c = 0; c < DK; ++c) {
                     const float gm = sG[m][c];
                     const float span = fmaxf(sG[16 * I][c] - gm, gm - sG[16 * I + 15][c]);
@@ -384,6 +498,8 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                         accP[r] += Qf(i, c) * Kf(j, c) * ex;
                     }
                 }
+            } else {
+                tile_ap(I, J, m, accA, accP, std::false_type{});
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -443,11 +559,11 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     // ---- 6. R = P T' and M = [T'; -R] (T' = T Diag(beta)) as matrix-core operands
     {
         constexpr int NB = NT16 * (NT16 + 1) / 2;
-        constexpr int BPW = (NB + 3) / 4;
+        constexpr int BPW = (NB + NW - 1) / NW;
         f32x4 tv[BPW], rv[BPW];
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const int t = w + 4 * b;
+            const int t = w + NW * b;
             tv[b] = rv[b] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (t < NB) {
                 int I = 0, J = t;
@@ -470,11 +586,12 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
             }
         }
         __syncthreads();  // every fp32 read of A/T and P is done: M overlays them
-        for (int idx = tid; idx < PARTS * 2 * C * MS; idx += 256) Mp[idx] = static_cast<MT>(0.f);
+        for (int idx = tid; idx < PARTS * 2 * C * MS * static_cast<int>(sizeof(MT)) / 16; idx += kIntraThreads)
+            reinterpret_cast<f32x4 *>(Mp)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
-            const int t = w + 4 * b;
+            const int t = w + NW * b;
             if (t < NB) {
                 int I = 0, J = t;
                 while (J > I) { J -= I + 1; ++I; }
@@ -514,7 +631,7 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
     Op *wq = reinterpret_cast<Op *>(pkg + p.L.wq);
     Op *kt = reinterpret_cast<Op *>(pkg + p.L.kt);
     constexpr int NJOBS = KSK + DV / 16;
-    for (int job = w; job < NJOBS; job += 4) {
+    for (int job = w; job < NJOBS; job += NW) {
         if (job < KSK) {
             // channels 32 ks .. 32 ks + 31: W^T = Kg^T T'^T and Q'^T = Qg^T + Kg^T (-R)^T
             const int ks = job;
@@ -555,7 +672,7 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                     }
                 }
             }
-#pragma unroll
+#pragma unroll 2
             for (int rt = 0; rt < 2 * NT16; ++rt) {
                 const int I = rt < NT16 ? rt : rt - NT16;
                 const int nks = (16 * I + 15) / 32 + 1;  // token steps with nonzeros
@@ -614,7 +731,7 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
                 }
             f32x4 *up = reinterpret_cast<f32x4 *>(pkg + p.L.up);
             f32x4 *oi = reinterpret_cast<f32x4 *>(pkg + p.L.oi);
-#pragma unroll
+#pragma unroll 2
             for (int rt = 0; rt < 2 * NT16; ++rt) {
                 const int I = rt < NT16 ? rt : rt - NT16;
                 const int nks = (16 * I + 15) / 32 + 1;
@@ -640,7 +757,10 @@ __global__ void __launch_bounds__(256) intra_kernel(IntraParams p) {
         }
     }
     float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
-    for (int c = tid; c < DK; c += 256) glp[c] = last_reset >= 0 ? 0.f : fast_exp2(sG[C - 1][c]);
+    for (int c = tid; c < DK; c += kIntraThreads) glp[c] = last_reset >= 0 ? 0.f : fast_exp2(sG[C - 1][c]);
+    if (n_items < 0) glp[0] = touch;  // never true: keeps the touch loads alive
+      }  // cur.valid
+    }
 }
 
 // -----------------------------------------------------------------------------
@@ -699,7 +819,7 @@ struct StateFrags {
 #pragma unroll
         for (int rw = 0; rw < RPW; ++rw) {
             const int rt = w + 4 * rw;
-            if (rt < NRT) {
+            if (NRT % 4 == 0 || rt < NRT) {  // compile-time true when tiles divide evenly
 #pragma unroll
                 for (int ks = 0; ks < KSK; ++ks)
                     wq[rw][ks] = ld_vec8<BF>(wqp + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8);
@@ -713,7 +833,7 @@ struct StateFrags {
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
-            if (tk < NTK) {
+            if (NTK % 4 == 0 || tk < NTK) {
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks)
 #pragma unroll
@@ -793,8 +913,12 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     };
     put_state();
 
-    // one chunk of the recurrence on this slab, operands from registers
-    auto step = [&](const Frags &f, int64_t c) {
+    // one chunk of the recurrence on this slab, operands from registers;
+    // kPartial: the sequence's last chunk has fewer than C tokens (its o stores
+    // are masked; full chunks store unconditionally so the hot loop has no
+    // data-dependent branches around memory operations)
+    auto step = [&](const Frags &f, int64_t c, auto partial_tag) {
+        constexpr bool kPartial = decltype(partial_tag)::value;
         const int64_t rem = L - c * C;
         const int nvalid = static_cast<int>(rem < C ? rem : C);
         __syncthreads();  // sS holds this chunk's incoming state
@@ -803,7 +927,7 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
 #pragma unroll
         for (int rw = 0; rw < RPW; ++rw) {
             const int rt = w + 4 * rw;
-            if (rt >= NRT) break;
+            if (NRT % 4 != 0 && rt >= NRT) break;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KSK; ++ks) {
@@ -830,10 +954,14 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
             } else {
                 const int I = rt - NT16;
                 const f32x4 ov = f.uo[rw] + acc;
+                float *orow = p.o + ((tok_base + c * C + 16 * I + 4 * kg) * H + h) * DV + col;
+                if constexpr (!kPartial) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * kg + r;
-                    if (i < nvalid) p.o[((tok_base + c * C + i) * H + h) * DV + col] = ov[r];
+                    for (int r = 0; r < 4; ++r) orow[static_cast<size_t>(r) * H * DV] = ov[r];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * I + 4 * kg + r < nvalid) orow[static_cast<size_t>(r) * H * DV] = ov[r];
                 }
             }
         }
@@ -843,7 +971,7 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
-            if (tk >= NTK) break;
+            if (NTK % 4 != 0 && tk >= NTK) break;
             f32x4 acc = f.gl[sl] * S[sl];
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) {
@@ -867,16 +995,25 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     };
 
     // software pipeline: the package of chunk c + 1 loads while chunk c computes
+    using Full = std::false_type;
+    using Part = std::true_type;
+    const int64_t nfull = L / C;  // chunks with C valid tokens
     Frags fa, fb;
     if (nchunks > 0) fa.load(pkg_of(0), p.L, w, lane, ct);
     int64_t c = 0;
-    for (; c + 1 < nchunks; c += 2) {
+    for (; c + 2 < nfull; c += 2) {  // two full chunks per trip, chunk c + 2 exists
         fb.load(pkg_of(c + 1), p.L, w, lane, ct);
-        step(fa, c);
-        if (c + 2 < nchunks) fa.load(pkg_of(c + 2), p.L, w, lane, ct);
-        step(fb, c + 1);
+        step(fa, c, Full{});
+        fa.load(pkg_of(c + 2), p.L, w, lane, ct);
+        step(fb, c + 1, Full{});
     }
-    if (c < nchunks) step(fa, c);
+    // tail: at most two full chunks and one partial chunk remain; fa holds chunk c
+    for (; c < nchunks; ++c) {
+        if (c + 1 < nchunks) fb.load(pkg_of(c + 1), p.L, w, lane, ct);
+        if (c < nfull) step(fa, c, Full{});
+        else step(fa, c, Part{});
+        fa = fb;
+    }
 
     if (p.final_state) {
 #pragma unroll
@@ -895,6 +1032,19 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
 // -----------------------------------------------------------------------------
 // launch
 // -----------------------------------------------------------------------------
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+    static thread_local int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 template <int C, int DK, int DV, bool BF>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     const PackageLayout L = package_layout(C, DK, DV, BF);
@@ -905,8 +1055,20 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     if (a.n_slots > 0) {
         IntraParams ip{a.q, a.k, a.v, a.log_alpha, a.beta, a.cu_seqlens, a.chunk_offsets,
                        a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
-        hipLaunchKernelGGL((intra_kernel<C, DK, DV, BF>), dim3(static_cast<unsigned>(a.n_slots), a.H),
-                           dim3(256), 0, stream, ip);
+        // persistent: a few workgroups per compute unit walk the (chunk, head)
+        // items, each loading the next item's inputs while computing one
+        const int64_t n_items = a.n_slots * a.H;
+        static thread_local int per_cu = 0;  // resident workgroups per CU for this instantiation
+        if (per_cu == 0) {
+            int nb = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_kernel<C, DK, DV, BF>, kIntraThreads, 0) !=
+                    hipSuccess || nb <= 0)
+                nb = 1;
+            per_cu = nb;
+        }
+        const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
+        hipLaunchKernelGGL((intra_kernel<C, DK, DV, BF>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0,
+                           stream, ip, n_items);
     }
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state,
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
