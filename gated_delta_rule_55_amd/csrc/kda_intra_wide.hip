@@ -1,0 +1,570 @@
+// kda_intra_wide.hip -- intra-chunk package for 64-token chunks at
+// d_k = d_v = 128 with bf16 inputs, computed with the chunk held in registers.
+//
+// It writes the same package, bit layout for bit layout, as intra_kernel in
+// kda_prefill.hip (the WY/UT quantities of the chunked form in the section
+// "Kimi Delta Attention (KDA)" of the page "Kimi Linear 高效注意力架构": W,
+// Q' = Q*Gamma - P W, Kt, U' and O_intra).  What differs is the work split:
+// intra_kernel stages k, q, v and the fp32 cumulative decay G of the whole
+// chunk in LDS (about 124 KB, one workgroup per compute unit), while here
+// wave w of the four owns key channels 32w .. 32w + 31 (and value columns
+// 32w .. 32w + 31) and keeps them in registers:
+//
+//   lane l holds, for each 16-token tile t (token 16 t + l%16), the channels
+//       ch(e) = 32 w + 16 (e / 4) + 4 (l / 16) + e % 4,   e = 0 .. 7,
+//   of k, q, v (bf16 bits) and of G (fp32).
+//
+// That is the k-slot layout of the fp32 16x16x4 matrix instruction for the
+// Gram tiles (a sum over channels may take them in any order as long as both
+// operands agree), so every wave forms its channels' share of all ten Gram
+// tiles without touching LDS.  It is also the row layout of the [W; Q']
+// fragments, so Q*Gamma adds into Q' in place.  The cumulative decay is a scan
+// over the 16 lanes of a row (DPP) plus a carry over the four tiles.  The four
+// shares of each Gram tile are summed in a fixed order through LDS, then T, R
+// and M = [T'; -R] are formed as in intra_kernel.  About 74 KB of LDS in all,
+// so two workgroups share a compute unit.
+#include <algorithm>
+
+#include "kda_prefill.h"
+
+namespace kda {
+namespace {
+
+constexpr int kWC = 64;                           // chunk
+constexpr int kWD = 128;                          // d_k = d_v
+constexpr int kAS = kWC + 8;                      // fp32 row stride of A/T and P/R; bf16 stride of M
+constexpr int kXS = kWC + 8;                      // 16-bit row stride of a wave's transpose buffer
+constexpr int kApBytes = 2 * kWC * kAS * 4;       // A and P (fp32), later M (bf16 hi/lo)
+constexpr int kXBytes = 2 * 32 * kXS * 2;         // one wave's transpose buffer
+constexpr int kSmemBytes = kApBytes + 4 * kXBytes;
+constexpr int kRedBytes = 20 * 3 * 64 * 16;       // Gram shares in flight
+static_assert(2 * 2 * kWC * kAS * 2 == kApBytes, "M overlays A and P");
+static_assert(kRedBytes <= kSmemBytes, "Gram shares overlay A, P and the transpose buffers");
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
+                                                                 true));
+}
+// inclusive prefix sum over the 16 lanes of each row
+__device__ __forceinline__ float row_scan(float x) {
+    x += dpp_f<0x111>(x);  // row_shr:1
+    x += dpp_f<0x112>(x);  // row_shr:2
+    x += dpp_f<0x114>(x);  // row_shr:4
+    x += dpp_f<0x118>(x);  // row_shr:8
+    return x;
+}
+// value of lane N of each row of 16 lanes
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return dpp_f<0x150 + N>(x);  // row_newbcast:N
+}
+
+// element e of 8 packed bf16 values
+__device__ __forceinline__ float bf_at(const uint32_t (&u)[4], int e) {
+    const uint32_t w = u[e >> 1];
+    return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+__device__ __forceinline__ uint16_t bf_bits(const uint32_t (&u)[4], int e) {
+    const uint32_t w = u[e >> 1];
+    return static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// orders this wave's LDS accesses around a change of a buffer's role
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bits of tokens (j, i] of a 64-bit token mask (empty when j >= i).
+__device__ __forceinline__ uint64_t tokens_between(int j, int i) {
+    if (j >= i) return 0;
+    const uint64_t upto_i = i >= 63 ? ~uint64_t(0) : ((uint64_t(1) << (i + 1)) - 1);
+    const uint64_t upto_j = (uint64_t(1) << (j + 1)) - 1;  // j < i <= 63
+    return upto_i & ~upto_j;
+}
+
+// (I, J) of lower-triangular 16x16 tile index ti = I (I + 1) / 2 + J
+__host__ __device__ constexpr int tile_i(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
+__host__ __device__ constexpr int tile_j(int ti) { return ti - tile_i(ti) * (tile_i(ti) + 1) / 2; }
+
+__global__ void __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+intra_wide_kernel(IntraParams p, int64_t n_items) {
+    constexpr int C = kWC, D = kWD, NT16 = 4, PARTS = 2, MS = kAS;
+    __shared__ __align__(16) unsigned char smem[kSmemBytes];
+    __shared__ float sBeta[C];
+    __shared__ uint64_t sRst[4];
+
+    float(*sA)[kAS] = reinterpret_cast<float(*)[kAS]>(smem);
+    float(*sP)[kAS] = reinterpret_cast<float(*)[kAS]>(smem + kWC * kAS * 4);
+    __bf16 *Mp = reinterpret_cast<__bf16 *>(smem);  // [PARTS][2C][MS]
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem);   // [20 tile matrices][3 senders][64 lanes]
+    const int H = p.H;
+
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        // Lane-dependent addresses and masks are recomputed per item: hoisted out
+        // of the loop they would outnumber the registers two workgroups leave.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int t16 = lane & 15, kg = lane >> 4;
+        uint16_t *xb = reinterpret_cast<uint16_t *>(smem + kApBytes + w * kXBytes);  // [2][32][kXS]
+        const int64_t item_next = item + gridDim.x;
+        const int h = static_cast<int>(item % H);
+        int64_t tok0;
+        int nvalid;
+        if (!locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) continue;
+        char *pkg = p.ws + static_cast<size_t>(item) * p.pkg_bytes;
+
+        // ---- load this lane's tokens and channels; tokens >= nvalid read the last
+        //      valid row (always in bounds) and are zeroed after the load
+        uint32_t kr[4][4], qr[4][4], vr[4][4];
+        float G[4][8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = 16 * t + t16;
+            const bool ok = i < nvalid;
+            const int64_t row = (tok0 + (ok ? i : nvalid - 1)) * H + h;
+            const int64_t off = row * D + 32 * w + 4 * kg;
+            const uint16_t *kb = static_cast<const uint16_t *>(p.k) + off;
+            const uint16_t *qb = static_cast<const uint16_t *>(p.q) + off;
+            const uint16_t *vb = static_cast<const uint16_t *>(p.v) + off;
+            const uint2 k0 = *reinterpret_cast<const uint2 *>(kb), k1 = *reinterpret_cast<const uint2 *>(kb + 16);
+            const uint2 q0 = *reinterpret_cast<const uint2 *>(qb), q1 = *reinterpret_cast<const uint2 *>(qb + 16);
+            const uint2 v0 = *reinterpret_cast<const uint2 *>(vb), v1 = *reinterpret_cast<const uint2 *>(vb + 16);
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off);
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off + 16);
+            const uint32_t m = ok ? 0xffffffffu : 0u;
+            kr[t][0] = k0.x & m; kr[t][1] = k0.y & m; kr[t][2] = k1.x & m; kr[t][3] = k1.y & m;
+            qr[t][0] = q0.x & m; qr[t][1] = q0.y & m; qr[t][2] = q1.x & m; qr[t][3] = q1.y & m;
+            vr[t][0] = v0.x & m; vr[t][1] = v0.y & m; vr[t][2] = v1.x & m; vr[t][3] = v1.y & m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                G[t][e] = ok ? l0[e] : 0.f;
+                G[t][4 + e] = ok ? l1[e] : 0.f;
+            }
+            if (w == 0 && kg == 0) {
+                const float bv = p.beta[row];
+                sBeta[i] = ok ? bv : 0.f;
+            }
+        }
+        auto Kf = [&](int t, int e) { return bf_at(kr[t], e); };
+        auto Qf = [&](int t, int e) { return bf_at(qr[t], e); };
+
+        // ---- resets: tokens whose log_alpha is -inf on all channels
+        {
+            uint64_t mine = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bool all = 16 * t + t16 < nvalid;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) all = all && G[t][e] == kNegInf;
+                const uint64_t m = __ballot(all);
+                mine |= ((m & (m >> 16) & (m >> 32) & (m >> 48)) & 0xffffu) << (16 * t);
+            }
+            if (lane == 0) sRst[w] = mine;
+        }
+        __syncthreads();  // also: every wave is done with the previous item's LDS
+        const uint64_t rst = sRst[0] & sRst[1] & sRst[2] & sRst[3];
+        const int first_rst = rst ? __builtin_ctzll(rst) : C;  // tokens before it see the incoming state
+        const int last_rst = rst ? 63 - __builtin_clzll(rst) : -1;
+
+        // ---- cumulative log2-decay: scan within each 16-token tile, then carry
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool r = (rst >> (16 * t + t16)) & 1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) G[t][e] = row_scan(r ? 0.f : fmaxf(G[t][e], kGFloor) * kLog2e);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float carry = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float tot = row_bcast<15>(G[t][e]);
+                G[t][e] += carry;
+                carry += tot;
+            }
+        }
+
+        // ---- this wave's share of the Gram tiles A' (k k) and P (q k), factored exponents
+        f32x4 accA[10], accP[10];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            float gm[8];  // G at token 16 J + 15
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gm[e] = row_bcast<15>(G[J][e]);
+            if (J < 3) {  // tiles below the diagonal, reference = last token of column tile J
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = Kf(J, e) * fast_exp2(gm[e] - G[J][e]);
+#pragma unroll
+                for (int I = J + 1; I < 4; ++I) {
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float fa = fast_exp2(G[I][e] - gm[e]);
+                        a = __builtin_amdgcn_mfma_f32_16x16x4f32(Kf(I, e) * fa, y[e], a, 0, 0, 0);
+                        pq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qf(I, e) * fa, y[e], pq, 0, 0, 0);
+                    }
+                    accA[I * (I + 1) / 2 + J] = a;
+                    accP[I * (I + 1) / 2 + J] = pq;
+                }
+            }
+            // diagonal tile, reference = token 16 J + 7; a channel whose half-span
+            // there exceeds the safe range is left out and added exactly below
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+            uint32_t unsafe = 0;  // bit lc = 16 (e / 4) + 4 kg + e % 4 of this wave's channels
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float g7 = row_bcast<7>(G[J][e]);
+                const float g0 = row_bcast<0>(G[J][e]);
+                const bool uns = !(fmaxf(g0 - g7, g7 - gm[e]) <= kSafeSpan2);
+                const float d = G[J][e] - g7;
+                const float fa = uns ? 0.f : fast_exp2(d);
+                const float fb = uns ? 0.f : fast_exp2(-d);
+                const float kb = Kf(J, e) * fb;
+                a = __builtin_amdgcn_mfma_f32_16x16x4f32(Kf(J, e) * fa, kb, a, 0, 0, 0);
+                pq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qf(J, e) * fa, kb, pq, 0, 0, 0);
+                const uint64_t b = __ballot(uns);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if ((b >> (16 * r)) & 1) unsafe |= 1u << (16 * (e >> 2) + 4 * r + (e & 3));
+            }
+            if (unsafe) {
+                // rare: stage the tile's k, q, G of this wave's channels in its
+                // transpose buffer and add the exact terms of the unsafe channels
+                float *xs = reinterpret_cast<float *>(xb);  // [3][16][33]
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int lc = 16 * (e >> 2) + 4 * kg + (e & 3);
+                    xs[(0 * 16 + t16) * 33 + lc] = Kf(J, e);
+                    xs[(1 * 16 + t16) * 33 + lc] = Qf(J, e);
+                    xs[(2 * 16 + t16) * 33 + lc] = G[J][e];
+                }
+                wave_sync();
+                for (int lc = 0; lc < 32; ++lc) {
+                    if (!((unsafe >> lc) & 1)) continue;
+                    const float kj = xs[(0 * 16 + t16) * 33 + lc], gj = xs[(2 * 16 + t16) * 33 + lc];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * kg + r;
+                        const float ex = fast_exp2(fminf(xs[(2 * 16 + i) * 33 + lc] - gj, 0.f));
+                        a[r] += xs[(0 * 16 + i) * 33 + lc] * kj * ex;
+                        pq[r] += xs[(1 * 16 + i) * 33 + lc] * kj * ex;
+                    }
+                }
+                wave_sync();
+            }
+            accA[J * (J + 1) / 2 + J] = a;
+            accP[J * (J + 1) / 2 + J] = pq;
+        }
+        // warm L2 with the next item's inputs (consumed at the end)
+        const float touch = touch_next_item<C, D, D, true>(p, item_next, n_items, tid);
+
+        // ---- sum the four shares: tile matrix tm (A tiles 0..9, P tiles 10..19)
+        //      belongs to wave tm % 4, which adds the other three in a fixed order
+        __syncthreads();  // the shares overlay the transpose buffers (used by the exact terms)
+        auto share = [&](int tm) -> f32x4 { return tm < 10 ? accA[tm] : accP[tm - 10]; };
+#pragma unroll
+        for (int tm = 0; tm < 20; ++tm) {
+            const int owner = tm & 3;
+            if (owner != w) red[(tm * 3 + ((w - owner + 3) & 3)) * 64 + lane] = share(tm);
+        }
+        f32x4 fin[5];  // this wave's own shares of tile matrices w, w + 4, ..., selected in registers
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            fin[k] = share(4 * k);
+#pragma unroll
+            for (int o = 1; o < 4; ++o)
+                if (w == o) fin[k] = share(4 * k + o);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int tm = 4 * k + w;
+#pragma unroll
+            for (int j = 0; j < 3; ++j) fin[k] += red[(tm * 3 + j) * 64 + lane];
+        }
+        __syncthreads();  // the shares overlay A and P
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int tm = 4 * k + w;
+            const int ti = tm < 10 ? tm : tm - 10;
+            const int I = tile_i(ti), J = tile_j(ti);
+            const int j = 16 * J + t16;
+            float(*dst)[kAS] = tm < 10 ? sA : sP;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * kg + r;
+                const bool keep = (rst & tokens_between(j, i)) == 0;  // no reset in (j, i]
+                const bool lower = tm < 10 ? j < i : j <= i;
+                dst[i][j] = (lower && keep) ? (tm < 10 ? sBeta[i] : 1.f) * fin[k][r] : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- Kt = K e^{G_last - G} (fp16 hi/lo) and Gamma_last, stored now; K Gamma
+        //      (bf16 hi/lo) parked in this wave's transpose buffer; Q Gamma kept in
+        //      registers.  Transposes go through the buffer: row = channel, k = token.
+        {
+            using Op = _Float16;
+            Op *kt = reinterpret_cast<Op *>(pkg + p.L.kt);
+            float gl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gl[e] = row_bcast<15>(G[3][e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int lc = 16 * (e >> 2) + 4 * kg + (e & 3);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int i = 16 * t + t16;
+                    const float v = i >= last_rst ? Kf(t, e) * fast_exp2(gl[e] - G[t][e]) : 0.f;
+                    const Op hi = static_cast<Op>(v);
+                    const Op lo = static_cast<Op>(v - static_cast<float>(hi));
+                    xb[(0 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, hi);
+                    xb[(1 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, lo);
+                }
+            }
+            wave_sync();
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int pt = 0; pt < PARTS; ++pt) {
+                        const int ct = 2 * w + hc;
+                        const f16x8 v = *reinterpret_cast<const f16x8 *>(&xb[(pt * 32 + 16 * hc + t16) * kXS + 32 * s + 8 * kg]);
+                        *reinterpret_cast<f16x8 *>(kt + (((static_cast<size_t>(ct) * 2 + s) * PARTS + pt) * 64 + lane) * 8) = v;
+                    }
+            wave_sync();
+            float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
+            if (t16 == 0) {
+                f32x4 g0, g1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    g0[r] = last_rst >= 0 ? 0.f : fast_exp2(gl[r]);
+                    g1[r] = last_rst >= 0 ? 0.f : fast_exp2(gl[4 + r]);
+                }
+                *reinterpret_cast<f32x4 *>(glp + 32 * w + 4 * kg) = g0;
+                *reinterpret_cast<f32x4 *>(glp + 32 * w + 16 + 4 * kg) = g1;
+            }
+            if (n_items < 0) glp[0] = touch;  // never true: keeps the touch loads alive
+        }
+        float qg[4][8];  // Q Gamma (0 from the first reset on)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = 16 * t + t16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int lc = 16 * (e >> 2) + 4 * kg + (e & 3);
+                const float eg = fast_exp2(G[t][e]);
+                const float v = i < first_rst ? Kf(t, e) * eg : 0.f;
+                qg[t][e] = i < first_rst ? Qf(t, e) * eg : 0.f;
+                const __bf16 hi = static_cast<__bf16>(v);
+                const __bf16 lo = static_cast<__bf16>(v - static_cast<float>(hi));
+                xb[(0 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, hi);
+                xb[(1 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, lo);
+            }
+        }
+
+        // ---- T = (I + A)^-1 (unit lower triangular), in place over A
+        if (lane < 16) {
+            const int base = 16 * w, col = lane;
+            float tv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float val = (i == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) val -= sA[base + i][base + j] * tv[j];
+                tv[i] = val;
+                __builtin_amdgcn_sched_barrier(0);  // keep the row loads from piling up
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (i >= col) sA[base + i][base + col] = tv[i];
+        }
+        __syncthreads();
+        // off-diagonal blocks: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ  (fp32 matrix cores)
+        for (int I = 1; I < NT16; ++I) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            const int J = w;
+            if (J < I) {
+                f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int kk = 4 * s4 + kg;
+                        xv = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * I + t16][16 * K + kk],
+                                                                   sA[16 * K + kk][16 * J + t16], xv, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * I + t16][16 * I + 4 * kg + r], xv[r], y, 0,
+                                                              0, 0);
+            }
+            __syncthreads();
+            if (J < I) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sA[16 * I + 4 * kg + r][16 * J + t16] = -y[r];
+            }
+            __syncthreads();
+        }
+
+        // ---- R = P T' and M = [T'; -R] (T' = T Diag(beta)) as bf16 hi/lo operands
+        {
+            constexpr int NB = NT16 * (NT16 + 1) / 2;
+            constexpr int BPW = (NB + 3) / 4;
+            f32x4 tv[BPW], rv[BPW];
+#pragma unroll
+            for (int b = 0; b < BPW; ++b) {
+                const int t = w + 4 * b;
+                tv[b] = rv[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (t < NB) {
+                    int I = 0, J = t;
+                    while (J > I) { J -= I + 1; ++I; }
+                    const float bj = sBeta[16 * J + t16];
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int K = J; K <= I; ++K) {
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const int kk = 4 * s4 + kg;
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[16 * I + t16][16 * K + kk],
+                                                                        sA[16 * K + kk][16 * J + t16], acc, 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        rv[b][r] = -acc[r] * bj;
+                        tv[b][r] = sA[16 * I + 4 * kg + r][16 * J + t16] * bj;
+                    }
+                }
+            }
+            __syncthreads();  // every fp32 read of A/T and P is done: M overlays them
+            for (int idx = tid; idx < PARTS * 2 * C * MS * 2 / 16; idx += kIntraThreads)
+                reinterpret_cast<f32x4 *>(Mp)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < BPW; ++b) {
+                const int t = w + 4 * b;
+                if (t < NB) {
+                    int I = 0, J = t;
+                    while (J > I) { J -= I + 1; ++I; }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * I + 4 * kg + r, col = 16 * J + t16;
+                        const float vals[2] = {tv[b][r], rv[b][r]};
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const size_t o = static_cast<size_t>(hh * C + row) * MS + col;
+                            const __bf16 hi = static_cast<__bf16>(vals[hh]);
+                            Mp[o] = hi;
+                            Mp[static_cast<size_t>(2 * C) * MS + o] = static_cast<__bf16>(vals[hh] - static_cast<float>(hi));
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- [W; Q'] = [0; Q Gamma] + M (K Gamma) (computed transposed: rows =
+        //      channels) and [U'; -O_intra] = M V, for this wave's 32 channels
+        auto m_frag = [&](int rt, int s, bf16x8 &hi, bf16x8 &lo) {  // B operand: row 16 rt + l%16 of M
+            const size_t o = static_cast<size_t>(16 * rt + t16) * MS + 32 * s + 8 * kg;
+            hi = *reinterpret_cast<const bf16x8 *>(Mp + o);
+            lo = *reinterpret_cast<const bf16x8 *>(Mp + static_cast<size_t>(2 * C) * MS + o);
+        };
+        bf16x8 ka_hi[2][2], ka_lo[2][2], vb[2][2];
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                ka_hi[hc][s] = *reinterpret_cast<const bf16x8 *>(&xb[(0 * 32 + 16 * hc + t16) * kXS + 32 * s + 8 * kg]);
+                ka_lo[hc][s] = *reinterpret_cast<const bf16x8 *>(&xb[(1 * 32 + 16 * hc + t16) * kXS + 32 * s + 8 * kg]);
+            }
+        wave_sync();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = 16 * t + t16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xb[(16 * (e >> 2) + 4 * kg + (e & 3)) * kXS + i] = bf_bits(vr[t], e);
+        }
+        wave_sync();
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                vb[hc][s] = *reinterpret_cast<const bf16x8 *>(&xb[(16 * hc + t16) * kXS + 32 * s + 8 * kg]);
+        {
+            _Float16 *wq = reinterpret_cast<_Float16 *>(pkg + p.L.wq);
+            f32x4 *up = reinterpret_cast<f32x4 *>(pkg + p.L.up);
+            f32x4 *oi = reinterpret_cast<f32x4 *>(pkg + p.L.oi);
+#pragma unroll
+            for (int I = 0; I < NT16; ++I) {
+                constexpr int kMaxS = 2;
+                const int nks = I >= 2 ? 2 : 1;  // token steps with nonzeros
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {  // W / U' rows, then Q' / -O_intra rows
+                    const int rt = I + NT16 * half;
+                    f32x4 aw[2], au[2];
+#pragma unroll
+                    for (int hc = 0; hc < 2; ++hc) {
+                        au[hc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) aw[hc][r] = half ? qg[I][4 * hc + r] : 0.f;
+                    }
+#pragma unroll
+                    for (int s = 0; s < kMaxS; ++s) {
+                        if (s >= nks) break;
+                        bf16x8 mh, ml;
+                        m_frag(rt, s, mh, ml);
+#pragma unroll
+                        for (int hc = 0; hc < 2; ++hc) {
+                            aw[hc] = mfma_bf16(ka_lo[hc][s], mh, aw[hc]);
+                            aw[hc] = mfma_bf16(ka_hi[hc][s], ml, aw[hc]);
+                            aw[hc] = mfma_bf16(ka_hi[hc][s], mh, aw[hc]);
+                            au[hc] = mfma_bf16(ml, vb[hc][s], au[hc]);
+                            au[hc] = mfma_bf16(mh, vb[hc][s], au[hc]);
+                        }
+                    }
+                    float v8[8];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v8[r] = aw[0][r];
+                        v8[4 + r] = aw[1][r];
+                    }
+                    store8(wq + ((static_cast<size_t>(rt) * 4 + w) * 64 + lane) * 8, v8);
+#pragma unroll
+                    for (int hc = 0; hc < 2; ++hc) {
+                        const size_t o = (static_cast<size_t>(2 * w + hc) * NT16 + I) * 64 + lane;
+                        if (half == 0) up[o] = au[hc];
+                        else oi[o] = -au[hc];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    static thread_local int per_cu = 0;
+    if (per_cu == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_wide_kernel, kIntraThreads, 0) != hipSuccess ||
+            nb <= 0)
+            nb = 1;
+        per_cu = nb;
+    }
+    const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
+    hipLaunchKernelGGL(intra_wide_kernel, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream, p,
+                       n_items);
+    return hipGetLastError();
+}
+
+}  // namespace kda

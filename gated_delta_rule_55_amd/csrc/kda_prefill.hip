@@ -37,107 +37,10 @@
 // intra products use bf16 hi/lo splits (three products), [W; Q'] S uses fp16,
 // Kt^T U uses fp16 hi/lo splits; with fp32 inputs every product is fp32.
 #include <algorithm>
-#include <type_traits>
 
-#include "kda_common.h"
-#include "kda_internal.h"
-#include "kda_mma.h"
+#include "kda_prefill.h"
 
 namespace kda {
-
-constexpr float kGFloor = -88.0f;               // clamp for partial -inf decays
-constexpr float kSafeSpan2 = 110.0f;            // max |exponent| (log2) of a factor
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kIntraThreads = 256;               // 4 waves
-
-struct IntraParams {
-    const void *q, *k, *v;
-    const float *log_alpha, *beta;
-    const int32_t *cu_seqlens, *chunk_offsets;  // varlen only
-    int64_t T;
-    int32_t H, N;
-    char *ws;
-    size_t pkg_bytes;
-    PackageLayout L;
-};
-
-struct StateParams {
-    const float *init_state;
-    const int32_t *cu_seqlens, *chunk_offsets;
-    float *o, *final_state;
-    int64_t T;
-    int32_t H, N;
-    const char *ws;
-    size_t pkg_bytes;
-    PackageLayout L;
-};
-
-template <int C, int DK, int DV, bool BF>
-struct Cfg {
-    static constexpr int NT16 = C / 16;            // 16-token row tiles of a chunk
-    static constexpr int CP = C < 32 ? 32 : C;     // token dimension padded to a K step
-    static constexpr int DKP = DK < 32 ? 32 : DK;
-    static constexpr int DVP = DV < 32 ? 32 : DV;
-    static constexpr int GK = DKP / 32;            // 32-wide channel groups
-    static constexpr int GV = DVP / 32;
-    static constexpr int GS = DK + 4;              // LDS row strides (elements)
-    static constexpr int KS = DK + 8;
-    static constexpr int VS = DV + 8;
-    static constexpr int AS = CP + 4;
-    static constexpr int XS = CP + 4;
-    using In = std::conditional_t<BF, uint16_t, float>;
-    using Op = std::conditional_t<BF, _Float16, float>;  // stored operand type
-    static constexpr Prec kIntra = BF ? Prec::BF16X3 : Prec::F32;
-    static constexpr Prec kIntraV = BF ? Prec::BF16X2A : Prec::F32;
-};
-
-// Stores 8 operand values (converted to the package's operand type) as one
-// 16-byte (fp16) or two 16-byte (fp32) vector stores.
-template <typename Op>
-__device__ __forceinline__ void store8(Op *dst, const float (&v)[8]) {
-    if constexpr (sizeof(Op) == 2) {
-        f16x8 h;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[e]);
-        *reinterpret_cast<f16x8 *>(dst) = h;
-    } else {
-        *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
-}
-
-template <bool BF>
-__device__ __forceinline__ float in_to_f32(typename std::conditional_t<BF, uint16_t, float> x) {
-    if constexpr (BF) return bf16_bits_to_f32(x);
-    else return x;
-}
-
-// Locates the chunk handled by slot x: its first flattened token and length.
-// Returns false when x is past the last chunk (varlen grids are an upper bound).
-__device__ __forceinline__ bool locate_chunk(int64_t x, int C, int64_t T, int32_t N,
-                                             const int32_t *cu, const int32_t *off,
-                                             int64_t &tok0, int &nvalid) {
-    if (cu == nullptr) {
-        const int64_t cps = (T + C - 1) / C;
-        const int64_t n = x / cps, c = x % cps;
-        tok0 = n * T + c * C;
-        const int64_t rem = T - c * C;
-        nvalid = static_cast<int>(rem < C ? rem : C);
-        return true;
-    }
-    if (x >= off[N]) return false;
-    int lo = 0, hi = N;  // off[lo] <= x < off[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (off[mid] <= x) lo = mid;
-        else hi = mid;
-    }
-    const int64_t c = x - off[lo];
-    tok0 = cu[lo] + c * C;
-    const int64_t rem = cu[lo + 1] - tok0;
-    nvalid = static_cast<int>(rem < C ? rem : C);
-    return true;
-}
 
 // -----------------------------------------------------------------------------
 // varlen plan: chunk_offsets[n] = sum_{m<n} ceil(len_m / C)
@@ -234,36 +137,6 @@ struct IntraInputs {
     }
 };
 
-// Reads one 32-bit word of each 128-byte line of the next work item's q, k,
-// v and log_alpha rows, so that those lines are in L2 when the item starts.
-// Returns the sum of the words (only to keep the loads alive).
-template <int C, int DK, int DV, bool BF>
-__device__ __forceinline__ float touch_next_item(const IntraParams &p, int64_t item, int64_t n_items,
-                                                 int tid) {
-    using In = typename Cfg<C, DK, DV, BF>::In;
-    if (item >= n_items) return 0.f;
-    const int H = p.H;
-    int64_t tok0;
-    int nvalid;
-    if (!locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return 0.f;
-    const int h = static_cast<int>(item % H);
-    constexpr int LK = DK * sizeof(In) / 128 > 0 ? DK * sizeof(In) / 128 : 1;  // lines per q/k row
-    constexpr int LV = DV * sizeof(In) / 128 > 0 ? DV * sizeof(In) / 128 : 1;
-    constexpr int LG = DK * 4 / 128 > 0 ? DK * 4 / 128 : 1;
-    constexpr int PER_ROW = 2 * LK + LV + LG;
-    float acc = 0.f;
-    for (int idx = tid; idx < nvalid * PER_ROW; idx += kIntraThreads) {
-        const int i = idx / PER_ROW, l = idx % PER_ROW;
-        const int64_t row = (tok0 + i) * H + h;
-        const float *src;
-        if (l < LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.q) + row * DK) + l * 32;
-        else if (l < 2 * LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.k) + row * DK) + (l - LK) * 32;
-        else if (l < 2 * LK + LV) src = reinterpret_cast<const float *>(static_cast<const In *>(p.v) + row * DV) + (l - 2 * LK) * 32;
-        else src = p.log_alpha + row * DK + (l - 2 * LK - LV) * 32;
-        acc += *src;
-    }
-    return acc;
-}
 
 template <int C, int DK, int DV, bool BF>
 __global__ void __launch_bounds__(kIntraThreads) intra_kernel(IntraParams p, int64_t n_items) {
@@ -1032,19 +905,6 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
 // -----------------------------------------------------------------------------
 // launch
 // -----------------------------------------------------------------------------
-// Compute units of the current device (queried once per device).
-static int device_cu_count() {
-    static thread_local int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
 template <int C, int DK, int DV, bool BF>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     const PackageLayout L = package_layout(C, DK, DV, BF);
@@ -1058,6 +918,10 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
         // persistent: a few workgroups per compute unit walk the (chunk, head)
         // items, each loading the next item's inputs while computing one
         const int64_t n_items = a.n_slots * a.H;
+        if constexpr (C == 64 && DK == 128 && DV == 128 && BF) {
+            const hipError_t e = launch_intra_wide(ip, n_items, stream);
+            if (e != hipSuccess) return e;
+        } else {
         static thread_local int per_cu = 0;  // resident workgroups per CU for this instantiation
         if (per_cu == 0) {
             int nb = 0;
@@ -1069,6 +933,7 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
         const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
         hipLaunchKernelGGL((intra_kernel<C, DK, DV, BF>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0,
                            stream, ip, n_items);
+        }
     }
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state,
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
