@@ -24,6 +24,7 @@
 // and M = [T'; -R] are formed as in intra_kernel.  About 74 KB of LDS in all,
 // so two workgroups share a compute unit.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_prefill.h"
 
@@ -85,13 +86,59 @@ __device__ __forceinline__ uint64_t tokens_between(int j, int i) {
     return upto_i & ~upto_j;
 }
 
+// f(std::integral_constant<int, B>{}), ..., f(std::integral_constant<int, E - 1>{})
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // (I, J) of lower-triangular 16x16 tile index ti = I (I + 1) / 2 + J
 __host__ __device__ constexpr int tile_i(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
 __host__ __device__ constexpr int tile_j(int ti) { return ti - tile_i(ti) * (tile_i(ti) + 1) / 2; }
 
+// One work item's raw inputs as this lane holds them (layout above).  Rows
+// past the chunk's end are loaded from its last token (always in bounds) and
+// zeroed when the item is unpacked, so no wait sits between the loads.
+struct WideRaw {
+    uint32_t k[4][4], q[4][4], v[4][4];
+    float la[4][8];
+    float beta[4];
+};
+
+__device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, int nvalid, int h, int w, int t16,
+                                           int kg, WideRaw &r) {
+    const int H = p.H;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int i = 16 * t + t16;
+        const int64_t row = (tok0 + (i < nvalid ? i : nvalid - 1)) * H + h;
+        const int64_t off = row * kWD + 32 * w + 4 * kg;
+        const uint16_t *kb = static_cast<const uint16_t *>(p.k) + off;
+        const uint16_t *qb = static_cast<const uint16_t *>(p.q) + off;
+        const uint16_t *vb = static_cast<const uint16_t *>(p.v) + off;
+        const uint2 k0 = *reinterpret_cast<const uint2 *>(kb), k1 = *reinterpret_cast<const uint2 *>(kb + 16);
+        const uint2 q0 = *reinterpret_cast<const uint2 *>(qb), q1 = *reinterpret_cast<const uint2 *>(qb + 16);
+        const uint2 v0 = *reinterpret_cast<const uint2 *>(vb), v1 = *reinterpret_cast<const uint2 *>(vb + 16);
+        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off);
+        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off + 16);
+        r.k[t][0] = k0.x; r.k[t][1] = k0.y; r.k[t][2] = k1.x; r.k[t][3] = k1.y;
+        r.q[t][0] = q0.x; r.q[t][1] = q0.y; r.q[t][2] = q1.x; r.q[t][3] = q1.y;
+        r.v[t][0] = v0.x; r.v[t][1] = v0.y; r.v[t][2] = v1.x; r.v[t][3] = v1.y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r.la[t][e] = l0[e];
+            r.la[t][4 + e] = l1[e];
+        }
+        r.beta[t] = p.beta[row];
+    }
+}
+
 __global__ void __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 intra_wide_kernel(IntraParams p, int64_t n_items) {
-    constexpr int C = kWC, D = kWD, NT16 = 4, PARTS = 2, MS = kAS;
+    constexpr int C = kWC, NT16 = 4, PARTS = 2, MS = kAS;
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
     __shared__ float sBeta[C];
     __shared__ uint64_t sRst[4];
@@ -102,7 +149,18 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
     f32x4 *red = reinterpret_cast<f32x4 *>(smem);   // [20 tile matrices][3 senders][64 lanes]
     const int H = p.H;
 
-    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // work items are visited in order; varlen grids end with empty slots, so
+    // the first empty slot ends the walk
+    int64_t item = blockIdx.x;
+    int64_t tok0;
+    int nvalid;
+    if (item >= n_items || !locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return;
+    WideRaw raw;
+    {
+        const int tid = threadIdx.x;
+        fetch_item(p, tok0, nvalid, static_cast<int>(item % H), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
+    }
+    for (;;) {
         // Lane-dependent addresses and masks are recomputed per item: hoisted out
         // of the loop they would outnumber the registers two workgroups leave.
         int tid = threadIdx.x;
@@ -110,44 +168,25 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int t16 = lane & 15, kg = lane >> 4;
         uint16_t *xb = reinterpret_cast<uint16_t *>(smem + kApBytes + w * kXBytes);  // [2][32][kXS]
-        const int64_t item_next = item + gridDim.x;
-        const int h = static_cast<int>(item % H);
-        int64_t tok0;
-        int nvalid;
-        if (!locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) continue;
         char *pkg = p.ws + static_cast<size_t>(item) * p.pkg_bytes;
 
-        // ---- load this lane's tokens and channels; tokens >= nvalid read the last
-        //      valid row (always in bounds) and are zeroed after the load
+        // ---- unpack this lane's tokens and channels (tokens >= nvalid are zeros)
         uint32_t kr[4][4], qr[4][4], vr[4][4];
         float G[4][8];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int i = 16 * t + t16;
             const bool ok = i < nvalid;
-            const int64_t row = (tok0 + (ok ? i : nvalid - 1)) * H + h;
-            const int64_t off = row * D + 32 * w + 4 * kg;
-            const uint16_t *kb = static_cast<const uint16_t *>(p.k) + off;
-            const uint16_t *qb = static_cast<const uint16_t *>(p.q) + off;
-            const uint16_t *vb = static_cast<const uint16_t *>(p.v) + off;
-            const uint2 k0 = *reinterpret_cast<const uint2 *>(kb), k1 = *reinterpret_cast<const uint2 *>(kb + 16);
-            const uint2 q0 = *reinterpret_cast<const uint2 *>(qb), q1 = *reinterpret_cast<const uint2 *>(qb + 16);
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(vb), v1 = *reinterpret_cast<const uint2 *>(vb + 16);
-            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off);
-            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off + 16);
             const uint32_t m = ok ? 0xffffffffu : 0u;
-            kr[t][0] = k0.x & m; kr[t][1] = k0.y & m; kr[t][2] = k1.x & m; kr[t][3] = k1.y & m;
-            qr[t][0] = q0.x & m; qr[t][1] = q0.y & m; qr[t][2] = q1.x & m; qr[t][3] = q1.y & m;
-            vr[t][0] = v0.x & m; vr[t][1] = v0.y & m; vr[t][2] = v1.x & m; vr[t][3] = v1.y & m;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                G[t][e] = ok ? l0[e] : 0.f;
-                G[t][4 + e] = ok ? l1[e] : 0.f;
+            for (int x = 0; x < 4; ++x) {
+                kr[t][x] = raw.k[t][x] & m;
+                qr[t][x] = raw.q[t][x] & m;
+                vr[t][x] = raw.v[t][x] & m;
             }
-            if (w == 0 && kg == 0) {
-                const float bv = p.beta[row];
-                sBeta[i] = ok ? bv : 0.f;
-            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) G[t][e] = ok ? raw.la[t][e] : 0.f;
+            if (w == 0 && kg == 0) sBeta[i] = ok ? raw.beta[t] : 0.f;
         }
         auto Kf = [&](int t, int e) { return bf_at(kr[t], e); };
         auto Qf = [&](int t, int e) { return bf_at(qr[t], e); };
@@ -188,19 +227,26 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             }
         }
 
-        // ---- this wave's share of the Gram tiles A' (k k) and P (q k), factored exponents
-        f32x4 accA[10], accP[10];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        // ---- this wave's share of the Gram tiles A' (k k) and P (q k), factored
+        //      exponents.  Tile matrix tm (A tiles 0..9, P tiles 10..19) belongs to
+        //      wave tm % 4; the other waves leave their shares in LDS for it.
+        f32x4 fin[5];
+        auto emit = [&](auto tmc, const f32x4 &v) {
+            constexpr int tm = decltype(tmc)::value, owner = tm & 3;
+            if (owner == w) fin[tm >> 2] = v;
+            else red[(tm * 3 + ((w - owner + 3) & 3)) * 64 + lane] = v;
+        };
+        static_for<0, 4>([&](auto Jc) {
+            constexpr int J = decltype(Jc)::value;
             float gm[8];  // G at token 16 J + 15
 #pragma unroll
             for (int e = 0; e < 8; ++e) gm[e] = row_bcast<15>(G[J][e]);
-            if (J < 3) {  // tiles below the diagonal, reference = last token of column tile J
+            if constexpr (J < 3) {  // tiles below the diagonal, reference = last token of column tile J
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = Kf(J, e) * fast_exp2(gm[e] - G[J][e]);
-#pragma unroll
-                for (int I = J + 1; I < 4; ++I) {
+                static_for<J + 1, 4>([&](auto Ic) {
+                    constexpr int I = decltype(Ic)::value;
                     f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -208,14 +254,14 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                         a = __builtin_amdgcn_mfma_f32_16x16x4f32(Kf(I, e) * fa, y[e], a, 0, 0, 0);
                         pq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qf(I, e) * fa, y[e], pq, 0, 0, 0);
                     }
-                    accA[I * (I + 1) / 2 + J] = a;
-                    accP[I * (I + 1) / 2 + J] = pq;
-                }
+                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, a);
+                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, pq);
+                });
             }
             // diagonal tile, reference = token 16 J + 7; a channel whose half-span
             // there exceeds the safe range is left out and added exactly below
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-            uint32_t unsafe = 0;  // bit lc = 16 (e / 4) + 4 kg + e % 4 of this wave's channels
+            uint32_t unsafe = 0;  // bit 16 (e / 4) + 4 kg + e % 4 of this wave's channels
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float g7 = row_bcast<7>(G[J][e]);
@@ -233,53 +279,39 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                     if ((b >> (16 * r)) & 1) unsafe |= 1u << (16 * (e >> 2) + 4 * r + (e & 3));
             }
             if (unsafe) {
-                // rare: stage the tile's k, q, G of this wave's channels in its
-                // transpose buffer and add the exact terms of the unsafe channels
-                float *xs = reinterpret_cast<float *>(xb);  // [3][16][33]
+                // rare: exact terms of the channels left out, with the tile's values
+                // of channel (e, row kgs) fetched from lanes 16 kgs + token
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int lc = 16 * (e >> 2) + 4 * kg + (e & 3);
-                    xs[(0 * 16 + t16) * 33 + lc] = Kf(J, e);
-                    xs[(1 * 16 + t16) * 33 + lc] = Qf(J, e);
-                    xs[(2 * 16 + t16) * 33 + lc] = G[J][e];
-                }
-                wave_sync();
-                for (int lc = 0; lc < 32; ++lc) {
-                    if (!((unsafe >> lc) & 1)) continue;
-                    const float kj = xs[(0 * 16 + t16) * 33 + lc], gj = xs[(2 * 16 + t16) * 33 + lc];
+                    const uint32_t ub = (unsafe >> (16 * (e >> 2) + (e & 3))) & 0x1111u;
+                    if (!ub) continue;
+                    const float kv = Kf(J, e), qv = Qf(J, e), gv = G[J][e];
+                    for (int kgs = 0; kgs < 4; ++kgs) {
+                        if (!((ub >> (4 * kgs)) & 1)) continue;
+                        const float kj = __shfl(kv, 16 * kgs + t16), gj = __shfl(gv, 16 * kgs + t16);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 4 * kg + r;
-                        const float ex = fast_exp2(fminf(xs[(2 * 16 + i) * 33 + lc] - gj, 0.f));
-                        a[r] += xs[(0 * 16 + i) * 33 + lc] * kj * ex;
-                        pq[r] += xs[(1 * 16 + i) * 33 + lc] * kj * ex;
+                        for (int r = 0; r < 4; ++r) {
+                            const int src = 16 * kgs + 4 * kg + r;
+                            const float ki = __shfl(kv, src), qi = __shfl(qv, src), gi = __shfl(gv, src);
+                            const float ex = fast_exp2(fminf(gi - gj, 0.f));
+                            a[r] += ki * kj * ex;
+                            pq[r] += qi * kj * ex;
+                        }
                     }
                 }
-                wave_sync();
             }
-            accA[J * (J + 1) / 2 + J] = a;
-            accP[J * (J + 1) / 2 + J] = pq;
-        }
-        // warm L2 with the next item's inputs (consumed at the end)
-        const float touch = touch_next_item<C, D, D, true>(p, item_next, n_items, tid);
+            emit(std::integral_constant<int, J * (J + 1) / 2 + J>{}, a);
+            emit(std::integral_constant<int, 10 + J * (J + 1) / 2 + J>{}, pq);
+        });
 
-        // ---- sum the four shares: tile matrix tm (A tiles 0..9, P tiles 10..19)
-        //      belongs to wave tm % 4, which adds the other three in a fixed order
-        __syncthreads();  // the shares overlay the transpose buffers (used by the exact terms)
-        auto share = [&](int tm) -> f32x4 { return tm < 10 ? accA[tm] : accP[tm - 10]; };
-#pragma unroll
-        for (int tm = 0; tm < 20; ++tm) {
-            const int owner = tm & 3;
-            if (owner != w) red[(tm * 3 + ((w - owner + 3) & 3)) * 64 + lane] = share(tm);
-        }
-        f32x4 fin[5];  // this wave's own shares of tile matrices w, w + 4, ..., selected in registers
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            fin[k] = share(4 * k);
-#pragma unroll
-            for (int o = 1; o < 4; ++o)
-                if (w == o) fin[k] = share(4 * k + o);
-        }
+        // ---- the next item (located now, fetched once this one's stores are issued)
+        const int64_t next = item + gridDim.x;
+        int64_t tok0_n = 0;
+        int nvalid_n = 0;
+        const bool more =
+            next < n_items && locate_chunk(next / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0_n, nvalid_n);
+
+        // ---- sum the shares in a fixed order; apply masks and beta
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 5; ++k) {
@@ -339,8 +371,8 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                         *reinterpret_cast<f16x8 *>(kt + (((static_cast<size_t>(ct) * 2 + s) * PARTS + pt) * 64 + lane) * 8) = v;
                     }
             wave_sync();
-            float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
             if (t16 == 0) {
+                float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
                 f32x4 g0, g1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -350,7 +382,6 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 *reinterpret_cast<f32x4 *>(glp + 32 * w + 4 * kg) = g0;
                 *reinterpret_cast<f32x4 *>(glp + 32 * w + 16 + 4 * kg) = g1;
             }
-            if (n_items < 0) glp[0] = touch;  // never true: keeps the touch loads alive
         }
         float qg[4][8];  // Q Gamma (0 from the first reset on)
 #pragma unroll
@@ -546,6 +577,11 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 }
             }
         }
+        if (!more) break;
+        item = next;
+        tok0 = tok0_n;
+        nvalid = nvalid_n;
+        fetch_item(p, tok0, nvalid, static_cast<int>(item % H), w, t16, kg, raw);
     }
 }
 
