@@ -11,6 +11,14 @@ on.  The fp64 CPU oracle is timed on a bounded sample of the same prefill
 workload on the host cores (cpu_baseline).
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Profiling helpers (the commands that made the summaries under profiles/):
+  python bench.py --only prefill|decode|copy ...   one part only, for rocprofv3
+      (copy: a plain device-to-device copy of COPY_BYTES, the counter calibration)
+  python bench.py --summarize-trace DIR            markdown table of rocprofv3
+      --kernel-trace --stats output (DIR/run_kernel_stats.csv)
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+      writes profiles/traffic.json from four rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
@@ -25,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12        # MI355X HBM3E bytes/s
+COPY_BYTES = 1 << 31     # size of the calibration copy (read once, written once)
 BF16_PEAK = 2.5e15       # MI355X dense bf16/fp16 matrix flop/s
 
 
@@ -57,18 +66,106 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def measured_traffic(key):
+    """HBM bytes per launch (fetch + write, copy-calibrated) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get(kernel_key)
-    if not ent or ent.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest():
         return None
-    return ent.get("hbm_bytes_per_launch")
+    ent = rec.get("launches", {}).get(key)
+    return None if ent is None else ent.get("hbm_bytes")
+
+
+def _short(name):
+    """Kernel name without return type, anonymous namespace and parameter list."""
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def _kernel_rows(csv_path):
+    import csv
+    with open(csv_path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(d):
+    """Markdown table of the library's kernels from rocprofv3 --stats output."""
+    rows = _kernel_rows(os.path.join(d, "run_kernel_stats.csv"))
+    print("| kernel | calls | total us | avg us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"]
+        if "kda::" not in name:
+            continue
+        short = _short(name)
+        print(f"| `{short}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+              f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+
+
+def _last_dispatch_counters(d, counter):
+    """{kernel short name: value of `counter` (summed over instances) in its last dispatch}."""
+    import glob
+    (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    per = {}
+    for r in _kernel_rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    last = {}
+    for (disp, name), v in sorted(per.items()):
+        last[name] = v
+    return last
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    fetch = _last_dispatch_counters(fetch_dir, "FETCH_SIZE")
+    write = _last_dispatch_counters(write_dir, "WRITE_SIZE")
+    cf = _last_dispatch_counters(copy_fetch_dir, "FETCH_SIZE")
+    cw = _last_dispatch_counters(copy_write_dir, "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)  # the calibration copy is the largest dispatch
+    fetch_scale = COPY_BYTES / (cf[copy_name] * 1024.0)
+    write_scale = COPY_BYTES / (cw[copy_name] * 1024.0)
+    kernels = {}
+    for name in sorted(set(fetch) | set(write)):
+        if "kda::" not in name:
+            continue
+        short = _short(name)
+        fb = fetch.get(name, 0.0) * 1024.0 * fetch_scale
+        wb = write.get(name, 0.0) * 1024.0 * write_scale
+        kernels[short] = {"fetch_kib_raw": fetch.get(name), "write_kib_raw": write.get(name),
+                          "fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb}
+    launches = {}
+    pre = [k for k in kernels if "intra" in k or "state_kernel" in k]
+    if pre:
+        launches["kda_chunk_fwd"] = {"kernels": pre, "hbm_bytes": sum(kernels[k]["hbm_bytes"] for k in pre)}
+    dec = [k for k in kernels if "decode_step_kernel" in k]
+    if dec:
+        launches["kda_decode_step"] = {"kernels": dec, "hbm_bytes": sum(kernels[k]["hbm_bytes"] for k in dec)}
+    rec = {"source_digest": source_digest(),
+           "commands": [
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
+               "gpurun_out/prof/pmc_bench_FETCH_SIZE -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 0 "
+               "--no-cpu-baseline   (likewise WRITE_SIZE)",
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
+               "gpurun_out/prof/pmc_copy_FETCH_SIZE -o run -- python3 $GRAFT_REPO_ROOT/bench.py --only copy --steps 2"
+               "   (likewise WRITE_SIZE)",
+               "python bench.py --summarize-counters gpurun_out/prof/pmc_bench_FETCH_SIZE gpurun_out/prof/"
+               "pmc_bench_WRITE_SIZE gpurun_out/prof/pmc_copy_FETCH_SIZE gpurun_out/prof/pmc_copy_WRITE_SIZE"],
+           "note": "per-launch bytes of the last dispatch of each kernel; each counter scaled by what it reads "
+                   "for a plain device copy of copy_bytes (read once, written once)",
+           "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": _short(copy_name),
+                           "fetch_kib": cf[copy_name], "write_kib": cw[copy_name],
+                           "fetch_scale": fetch_scale, "write_scale": write_scale},
+           "kernels": kernels, "launches": launches}
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(inp, heads, T_sample, threads):
@@ -89,7 +186,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one part only (for profilers); prints no JSON line")
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None)
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the KDA operator here runs on a single "
               f"MI355X (got --gpus {args.gpus}); heads and sequences would shard across "
@@ -103,6 +210,14 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     lib = kda.load()
+
+    if args.only == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return
 
     # ---- inputs (seeded, synthetic, resident in HBM) ----------------------------
     pin = workloads.make_prefill("long", dev, 0)
@@ -130,6 +245,16 @@ def main():
     def decode(t):
         kda.decode_step(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t],
                         din["beta"][t], state, out=od)
+
+    if args.only:
+        for _ in range(args.warmup + args.steps):
+            if args.only == "prefill":
+                prefill()
+            else:
+                for t in range(dsteps):
+                    decode(t)
+        torch.cuda.synchronize()
+        return
 
     for _ in range(args.warmup):
         prefill()
@@ -202,13 +327,13 @@ def main():
             "alg_bytes_per_step": db,
         },
         "roofline": {
-            "kernel": "kda_chunk_fwd (intra_kernel + state_kernel)",
+            "kernel": "kda_chunk_fwd (intra_wide_kernel + state_kernel<64,128,128,bf16>)",
             "bound": "hbm",
             "achieved": pb / t_pre / 1e9,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": pb / t_pre / HBM_PEAK,
-            "traffic": measured_traffic("prefill_long"),
+            "traffic": measured_traffic("kda_chunk_fwd"),
         },
         "decode_roofline": {
             "kernel": "decode_step_kernel<128,128,bf16>",
@@ -217,14 +342,14 @@ def main():
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": db / t_dec / HBM_PEAK,
-            "traffic": measured_traffic("decode"),
+            "traffic": measured_traffic("kda_decode_step"),
         },
     }
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         heads = list(range(16))
-        T_s = 65536
+        T_s = 262144
         dt = cpu_baseline(pin, heads, T_s, threads)
         # the metric's unit is tokens/s at H=32: token-heads/s divided by 32
         result["cpu_baseline"] = {

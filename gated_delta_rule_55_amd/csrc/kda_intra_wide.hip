@@ -320,21 +320,26 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             for (int j = 0; j < 3; ++j) fin[k] += red[(tm * 3 + j) * 64 + lane];
         }
         __syncthreads();  // the shares overlay A and P
+        auto finalize = [&](auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            const int tm = 4 * k + w;
-            const int ti = tm < 10 ? tm : tm - 10;
-            const int I = tile_i(ti), J = tile_j(ti);
-            const int j = 16 * J + t16;
-            float(*dst)[kAS] = tm < 10 ? sA : sP;
+            for (int k = 0; k < 5; ++k) {
+                const int tm = 4 * k + w;
+                const int ti = tm < 10 ? tm : tm - 10;
+                const int I = tile_i(ti), J = tile_j(ti);
+                const int j = 16 * J + t16;
+                float(*dst)[kAS] = tm < 10 ? sA : sP;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * kg + r;
-                const bool keep = (rst & tokens_between(j, i)) == 0;  // no reset in (j, i]
-                const bool lower = tm < 10 ? j < i : j <= i;
-                dst[i][j] = (lower && keep) ? (tm < 10 ? sBeta[i] : 1.f) * fin[k][r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * kg + r;
+                    bool keep = tm < 10 ? j < i : j <= i;
+                    if constexpr (kMasked) keep = keep && (rst & tokens_between(j, i)) == 0;  // no reset in (j, i]
+                    dst[i][j] = keep ? (tm < 10 ? sBeta[i] : 1.f) * fin[k][r] : 0.f;
+                }
             }
-        }
+        };
+        if (rst == 0) finalize(std::false_type{});  // most chunks have no reset
+        else finalize(std::true_type{});
         __syncthreads();
 
         // ---- Kt = K e^{G_last - G} (fp16 hi/lo) and Gamma_last, stored now; K Gamma
@@ -573,7 +578,6 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                         if (half == 0) up[o] = au[hc];
                         else oi[o] = -au[hc];
                     }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }

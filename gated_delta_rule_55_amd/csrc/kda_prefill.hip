@@ -867,25 +867,31 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
         put_state();
     };
 
-    // software pipeline: the package of chunk c + 1 loads while chunk c computes
+    // software pipeline, three packages deep: chunk c + 2 loads while chunk c
+    // computes (a ring of three register buffers, so no buffer is copied while
+    // its loads are in flight)
     using Full = std::false_type;
     using Part = std::true_type;
     const int64_t nfull = L / C;  // chunks with C valid tokens
-    Frags fa, fb;
-    if (nchunks > 0) fa.load(pkg_of(0), p.L, w, lane, ct);
+    Frags f0, f1, f2;
+    if (nchunks > 0) f0.load(pkg_of(0), p.L, w, lane, ct);
+    if (nchunks > 1) f1.load(pkg_of(1), p.L, w, lane, ct);
     int64_t c = 0;
-    for (; c + 2 < nfull; c += 2) {  // two full chunks per trip, chunk c + 2 exists
-        fb.load(pkg_of(c + 1), p.L, w, lane, ct);
-        step(fa, c, Full{});
-        fa.load(pkg_of(c + 2), p.L, w, lane, ct);
-        step(fb, c + 1, Full{});
+    for (; c + 4 < nfull; c += 3) {  // chunks c .. c + 2 are full; c + 3 and c + 4 exist
+        f2.load(pkg_of(c + 2), p.L, w, lane, ct);
+        step(f0, c, Full{});
+        f0.load(pkg_of(c + 3), p.L, w, lane, ct);
+        step(f1, c + 1, Full{});
+        f1.load(pkg_of(c + 4), p.L, w, lane, ct);
+        step(f2, c + 2, Full{});
     }
-    // tail: at most two full chunks and one partial chunk remain; fa holds chunk c
+    // tail: f0 holds chunk c and f1 chunk c + 1 (when it exists)
     for (; c < nchunks; ++c) {
-        if (c + 1 < nchunks) fb.load(pkg_of(c + 1), p.L, w, lane, ct);
-        if (c < nfull) step(fa, c, Full{});
-        else step(fa, c, Part{});
-        fa = fb;
+        if (c + 2 < nchunks) f2.load(pkg_of(c + 2), p.L, w, lane, ct);
+        if (c < nfull) step(f0, c, Full{});
+        else step(f0, c, Part{});
+        f0 = f1;
+        f1 = f2;
     }
 
     if (p.final_state) {
