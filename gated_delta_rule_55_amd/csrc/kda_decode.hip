@@ -12,7 +12,7 @@
 //   S   = S' + k u^T                              == (I - b k k^T) S' + b k v^T
 //   o   = S^T q = r + (k . q) u
 //
-// One workgroup of min(256, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
+// One workgroup of min(512, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
 // (one float4) of RPT rows spaced RG apart, so each wave reads and writes whole
 // contiguous rows (coalesced 16-byte accesses).  Reductions: butterfly
 // shuffles inside a wave over the lanes that share a column group, then LDS
@@ -22,14 +22,16 @@
 
 namespace kda {
 
+constexpr int kDecodeThreads = 512;
+
 template <int DK, int DV, bool kBf16>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kDecodeThreads)
 decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
                    const void *__restrict__ v, const float *__restrict__ log_alpha,
                    const float *__restrict__ beta, float *__restrict__ state,
                    float *__restrict__ o) {
     constexpr int CG = DV / 4;                                  // float4 column groups
-    constexpr int NT = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;  // active threads
+    constexpr int NT = (DK * DV / 4 < kDecodeThreads) ? DK * DV / 4 : kDecodeThreads;  // threads
     constexpr int RG = NT / CG;                                 // row groups
     constexpr int RPT = DK / RG;                                // rows per thread
     constexpr int NW = (NT + kWave - 1) / kWave;                // waves holding rows
@@ -42,6 +44,18 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
 
     const int t = threadIdx.x;
     const int64_t unit = blockIdx.x;  // n * H + h
+    const int cg = t % CG;
+    const int rg = t / CG;
+    f32x4 *S = reinterpret_cast<f32x4 *>(state + unit * DK * DV);
+
+    // the state stream is issued first; the token's vectors load under it
+    f32x4 sv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
+    const float b = beta[unit];
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(v, unit * DV + 4 * cg + e);
     const float *gp = log_alpha + unit * DK;
     for (int c = t; c < DK; c += blockDim.x) {
         s_k[c] = load_in<kBf16>(k, unit * DK + c);
@@ -49,14 +63,6 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
         s_a[c] = fast_exp2(gp[c] * kLog2e);  // exp(-inf) -> 0
     }
     __syncthreads();
-
-    const int cg = t % CG;
-    const int rg = t / CG;
-    f32x4 *S = reinterpret_cast<f32x4 *>(state + unit * DK * DV);
-
-    f32x4 sv[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
 
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f;
@@ -96,10 +102,6 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
         r += s_red[ww][cg][1];
         kq += s_kq[ww][cg];
     }
-    const float b = beta[unit];
-    f32x4 vv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(v, unit * DV + 4 * cg + e);
     const f32x4 u = b * (vv - p);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -111,7 +113,7 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
 
 template <int DK, int DV, bool kBf16>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
-    constexpr int NT = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;
+    constexpr int NT = (DK * DV / 4 < kDecodeThreads) ? DK * DV / 4 : kDecodeThreads;
     const dim3 grid(static_cast<unsigned>(a.N * a.H));
     hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16>), grid, dim3(NT), 0, stream, a.q, a.k,
                        a.v, a.log_alpha, a.beta, a.state, a.o);
