@@ -30,7 +30,7 @@ namespace kda {
 //       block (row tile rt, k-step ks) = 64 lanes x 8 values, lane l holding
 //       row 16 rt + l%16, k = 32 ks + 8 (l/16) + e; order [rt][ks][lane][8].
 //   KT  A operand of Ktilde^T U: rows Dk (channels), K = C tokens (padded to
-//       32); order [ct][ks][part][lane][8] with part = hi, lo (16-bit path).
+//       32); order [ct][ks][lane][8] (fp16 on the 16-bit path, fp32 otherwise).
 //   UP  U' in accumulator layout: tile (col tile ct, row tile rt), lane l
 //       holding rows 4 (l/16) + r of the tile, column 16 ct + l%16;
 //       order [ct][rt][lane][4] fp32.
@@ -46,11 +46,10 @@ __host__ __device__ inline PackageLayout package_layout(int C, int Dk, int Dv, b
     const size_t osz = bf16 ? 2 : 4;                   // matrix-core operand bytes
     const size_t dkp = Dk < 32 ? 32 : Dk;              // K padded to a 32-wide step
     const size_t cp = C < 32 ? 32 : C;
-    const size_t parts = bf16 ? 2 : 1;                 // hi/lo split of Ktilde
     PackageLayout L;
     size_t off = 0;
     L.wq = off; off += align256(2 * (size_t)C * dkp * osz);
-    L.kt = off; off += align256((size_t)Dk * cp * osz * parts);
+    L.kt = off; off += align256((size_t)Dk * cp * osz);
     L.up = off; off += align256((size_t)C * Dv * 4);
     L.oi = off; off += align256((size_t)C * Dv * 4);
     L.gl = off; off += align256((size_t)Dk * 4);

@@ -342,7 +342,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         else finalize(std::true_type{});
         __syncthreads();
 
-        // ---- Kt = K e^{G_last - G} (fp16 hi/lo) and Gamma_last, stored now; K Gamma
+        // ---- Kt = K e^{G_last - G} (fp16) and Gamma_last, stored now; K Gamma
         //      (bf16 hi/lo) parked in this wave's transpose buffer; Q Gamma kept in
         //      registers.  Transposes go through the buffer: row = channel, k = token.
         {
@@ -358,23 +358,18 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 for (int t = 0; t < 4; ++t) {
                     const int i = 16 * t + t16;
                     const float v = i >= last_rst ? Kf(t, e) * fast_exp2(gl[e] - G[t][e]) : 0.f;
-                    const Op hi = static_cast<Op>(v);
-                    const Op lo = static_cast<Op>(v - static_cast<float>(hi));
-                    xb[(0 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, hi);
-                    xb[(1 * 32 + lc) * kXS + i] = __builtin_bit_cast(uint16_t, lo);
+                    xb[lc * kXS + i] = __builtin_bit_cast(uint16_t, static_cast<Op>(v));
                 }
             }
             wave_sync();
 #pragma unroll
             for (int hc = 0; hc < 2; ++hc)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int pt = 0; pt < PARTS; ++pt) {
-                        const int ct = 2 * w + hc;
-                        const f16x8 v = *reinterpret_cast<const f16x8 *>(&xb[(pt * 32 + 16 * hc + t16) * kXS + 32 * s + 8 * kg]);
-                        *reinterpret_cast<f16x8 *>(kt + (((static_cast<size_t>(ct) * 2 + s) * PARTS + pt) * 64 + lane) * 8) = v;
-                    }
+                for (int s = 0; s < 2; ++s) {
+                    const int ct = 2 * w + hc;
+                    const f16x8 v = *reinterpret_cast<const f16x8 *>(&xb[(16 * hc + t16) * kXS + 32 * s + 8 * kg]);
+                    *reinterpret_cast<f16x8 *>(kt + ((static_cast<size_t>(ct) * 2 + s) * 64 + lane) * 8) = v;
+                }
             wave_sync();
             if (t16 == 0) {
                 float *glp = reinterpret_cast<float *>(pkg + p.L.gl);

@@ -35,7 +35,8 @@
 //
 // Operand precision (fp32 accumulation everywhere): with bf16 inputs the
 // intra products use bf16 hi/lo splits (three products), [W; Q'] S uses fp16,
-// Kt^T U uses fp16 hi/lo splits; with fp32 inputs every product is fp32.
+// Kt^T U uses fp16 Kt and fp16 hi/lo U (two products); with fp32 inputs every
+// product is fp32.
 #include <algorithm>
 
 #include "kda_prefill.h"
@@ -528,15 +529,7 @@ __global__ void __launch_bounds__(kIntraThreads) intra_kernel(IntraParams p, int
                     }
                     if (c < DK) {
                         const int ct = 2 * ks + hc;
-                        Op *dst = kt + ((static_cast<size_t>(ct) * KSC + s) * PARTS * 64 + lane) * 8;
-                        if constexpr (BF) {
-                            f16x8 hi, lo;
-                            split_f16(ktv, hi, lo);
-                            *reinterpret_cast<f16x8 *>(dst) = hi;
-                            *reinterpret_cast<f16x8 *>(dst + 64 * 8) = lo;
-                        } else {
-                            store8(dst, ktv);
-                        }
+                        store8(kt + ((static_cast<size_t>(ct) * KSC + s) * 64 + lane) * 8, ktv);
                     }
                     if constexpr (BF) split_bf16(kgv, ka_hi[hc][s], ka_lo[hc][s]);
                     else {
@@ -678,10 +671,10 @@ struct StateFrags {
     using F = Cfg<C, DK, DV, BF>;
     static constexpr int NTK = DK / 16, SPW = (NTK + 3) / 4;
     static constexpr int NRT = 2 * F::NT16, RPW = (NRT + 3) / 4;
-    static constexpr int KSK = F::DKP / 32, KSC = F::CP / 32, PARTS = BF ? 2 : 1;
+    static constexpr int KSK = F::DKP / 32, KSC = F::CP / 32, PARTS = BF ? 2 : 1;  // U hi/lo
     Vec8<BF> wq[RPW][KSK];
     f32x4 uo[RPW];
-    Vec8<BF> kt[SPW][KSC][PARTS];
+    Vec8<BF> kt[SPW][KSC];
     f32x4 gl[SPW];
 
     __device__ __forceinline__ void load(const char *pkg, const PackageLayout &L, int w, int lane,
@@ -709,10 +702,7 @@ struct StateFrags {
             if (NTK % 4 == 0 || tk < NTK) {
 #pragma unroll
                 for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-                    for (int pt = 0; pt < PARTS; ++pt)
-                        kt[sl][ks][pt] = ld_vec8<BF>(
-                            ktp + (((static_cast<size_t>(tk) * KSC + ks) * PARTS + pt) * 64 + lane) * 8);
+                    kt[sl][ks] = ld_vec8<BF>(ktp + ((static_cast<size_t>(tk) * KSC + ks) * 64 + lane) * 8);
                 gl[sl] = *reinterpret_cast<const f32x4 *>(glp + 16 * tk + 4 * (lane >> 4));
             }
         }
@@ -851,12 +841,11 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
                 if constexpr (BF) {
                     const f16x8 bh = *reinterpret_cast<const f16x8 *>(&sU[0][l16][32 * ks + 8 * kg]);
                     const f16x8 bl = *reinterpret_cast<const f16x8 *>(&sU[1][l16][32 * ks + 8 * kg]);
-                    acc = mfma_f16(f.kt[sl][ks][1].v, bh, acc);
-                    acc = mfma_f16(f.kt[sl][ks][0].v, bl, acc);
-                    acc = mfma_f16(f.kt[sl][ks][0].v, bh, acc);
+                    acc = mfma_f16(f.kt[sl][ks].v, bl, acc);
+                    acc = mfma_f16(f.kt[sl][ks].v, bh, acc);
                 } else {
                     float a[8], b[8];
-                    unpack8(f.kt[sl][ks][0], a);
+                    unpack8(f.kt[sl][ks], a);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) b[e] = sU[0][l16][32 * ks + 8 * kg + e];
                     mma<Prec::F32>(acc, a, b);

@@ -51,7 +51,7 @@ def test_workspace_size(lib):
     # one package per (chunk, head); 4096 tokens, 64-token chunks, 32 heads
     per = ws(1, 4096, 32, 128, 128, 0, BF16, 64) // (64 * 32)
     assert per * 64 * 32 == ws(1, 4096, 32, 128, 128, 0, BF16, 64)
-    assert per >= 2 * 64 * 128 * 2 + 128 * 64 * 2 * 2 + 2 * 64 * 128 * 4 + 128 * 4
+    assert per >= 2 * 64 * 128 * 2 + 128 * 64 * 2 + 2 * 64 * 128 * 4 + 128 * 4
     assert ws(1, 4096, 32, 128, 128, 0, BF16, 0) == ws(1, 4096, 32, 128, 128, 0, BF16, 64)
     # a partial chunk still takes a slot; varlen reserves one extra slot per sequence
     assert ws(1, 4097, 1, 16, 16, 0, F32, 16) == ws(1, 4112, 1, 16, 16, 0, F32, 16)
