@@ -14,10 +14,10 @@
 //       ch(e) = 32 w + 16 (e / 4) + 4 (l / 16) + e % 4,   e = 0 .. 7,
 //   of k, q, v (bf16 bits) and of G (fp32).
 //
-// That is the k-slot layout of the fp32 16x16x4 matrix instruction for the
+// That is the k-slot layout of the 16x16x32 bf16 matrix instruction for the
 // Gram tiles (a sum over channels may take them in any order as long as both
-// operands agree), so every wave forms its channels' share of all ten Gram
-// tiles without touching LDS.  It is also the row layout of the [W; Q']
+// operands agree; operands split in bf16 hi/lo, three products), so every
+// wave forms its channels' share of all ten Gram tiles without touching LDS.  It is also the row layout of the [W; Q']
 // fragments, so Q*Gamma adds into Q' in place.  The cumulative decay is a scan
 // over the 16 lanes of a row (DPP) plus a carry over the four tiles.  The four
 // shares of each Gram tile are summed in a fixed order through LDS, then T, R
@@ -98,6 +98,18 @@ __device__ __forceinline__ void static_for(F &&f) {
 // (I, J) of lower-triangular 16x16 tile index ti = I (I + 1) / 2 + J
 __host__ __device__ constexpr int tile_i(int ti) { return ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3; }
 __host__ __device__ constexpr int tile_j(int ti) { return ti - tile_i(ti) * (tile_i(ti) + 1) / 2; }
+
+// One wave's share of a 16x16 Gram tile over its 32 channels: x (8 channels
+// of this lane's row token) against y (split as yh + yl) with bf16 hi/lo
+// operands, three 16x16x32 products (the lo x lo term is below fp32 rounding).
+__device__ __forceinline__ f32x4 gram_bf16x3(const float (&x)[8], const bf16x8 &yh, const bf16x8 &yl) {
+    bf16x8 xh, xl;
+    split_bf16(x, xh, xl);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma_bf16(xl, yh, acc);
+    acc = mfma_bf16(xh, yl, acc);
+    return mfma_bf16(xh, yh, acc);
+}
 
 // One work item's raw inputs as this lane holds them (layout above).  Rows
 // past the chunk's end are loaded from its last token (always in bounds) and
@@ -245,23 +257,25 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = Kf(J, e) * fast_exp2(gm[e] - G[J][e]);
+                bf16x8 yh, yl;
+                split_bf16(y, yh, yl);
                 static_for<J + 1, 4>([&](auto Ic) {
                     constexpr int I = decltype(Ic)::value;
-                    f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+                    float xk[8], xq[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float fa = fast_exp2(G[I][e] - gm[e]);
-                        a = __builtin_amdgcn_mfma_f32_16x16x4f32(Kf(I, e) * fa, y[e], a, 0, 0, 0);
-                        pq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qf(I, e) * fa, y[e], pq, 0, 0, 0);
+                        xk[e] = Kf(I, e) * fa;
+                        xq[e] = Qf(I, e) * fa;
                     }
-                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, a);
-                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, pq);
+                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, gram_bf16x3(xk, yh, yl));
+                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, gram_bf16x3(xq, yh, yl));
                 });
             }
             // diagonal tile, reference = token 16 J + 7; a channel whose half-span
             // there exceeds the safe range is left out and added exactly below
-            f32x4 a = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
             uint32_t unsafe = 0;  // bit 16 (e / 4) + 4 kg + e % 4 of this wave's channels
+            float xk[8], xq[8], kb[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float g7 = row_bcast<7>(G[J][e]);
@@ -270,14 +284,17 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 const float d = G[J][e] - g7;
                 const float fa = uns ? 0.f : fast_exp2(d);
                 const float fb = uns ? 0.f : fast_exp2(-d);
-                const float kb = Kf(J, e) * fb;
-                a = __builtin_amdgcn_mfma_f32_16x16x4f32(Kf(J, e) * fa, kb, a, 0, 0, 0);
-                pq = __builtin_amdgcn_mfma_f32_16x16x4f32(Qf(J, e) * fa, kb, pq, 0, 0, 0);
+                kb[e] = Kf(J, e) * fb;
+                xk[e] = Kf(J, e) * fa;
+                xq[e] = Qf(J, e) * fa;
                 const uint64_t b = __ballot(uns);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if ((b >> (16 * r)) & 1) unsafe |= 1u << (16 * (e >> 2) + 4 * r + (e & 3));
             }
+            bf16x8 kbh, kbl;
+            split_bf16(kb, kbh, kbl);
+            f32x4 a = gram_bf16x3(xk, kbh, kbl), pq = gram_bf16x3(xq, kbh, kbl);
             if (unsafe) {
                 // rare: exact terms of the channels left out, with the tile's values
                 // of channel (e, row kgs) fetched from lanes 16 kgs + token
