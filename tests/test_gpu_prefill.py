@@ -211,3 +211,26 @@ def test_zero_length_and_empty():
     o, fs = _gpu(inp)
     assert o.numel() == 0
     assert torch.equal(fs, inp["init_state"])
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (32, "f32")])
+def test_dense_batch_with_resets(D, dtype):
+    """B = 3 independent sequences in one dense call (partial last chunk, random
+    initial states, full-token resets) against the oracle's dense batch."""
+    log(f"dense batch D={D} {dtype}")
+    parts = [workloads.make_prefill("prefill", "cuda", seed=40 + b, T=200, H=3, dtype=dtype) for b in range(3)]
+    inp = {k: torch.cat([p_[k] for p_ in parts], dim=0) for k in ("q", "k", "v", "log_alpha", "beta")}
+    if D != 128:
+        for k in ("q", "k"):
+            x = inp[k][..., :D].float()
+            inp[k] = (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(inp[k].dtype)
+        inp["v"] = inp["v"][..., :D].contiguous()
+        inp["log_alpha"] = inp["log_alpha"][..., :D].contiguous()
+    g = torch.Generator(device="cuda").manual_seed(17)
+    inp["log_alpha"][1, 37] = float("-inf")     # a reset inside a chunk of sequence 1
+    inp["log_alpha"][2, 64] = float("-inf")     # a reset on a chunk boundary of sequence 2
+    inp["init_state"] = 0.02 * torch.randn((3, 3, D, D), device="cuda", generator=g)
+    inp.update(cu_seqlens=None, chunk=64, N=3)
+    o, fs = _gpu(inp)
+    tau = TAU[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    _check(inp, o, fs, tau, label=f"dense batch D={D} {dtype}")
