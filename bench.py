@@ -122,7 +122,7 @@ def _last_dispatch_counters(d, counter):
     return last
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None):
     fetch = _last_dispatch_counters(fetch_dir, "FETCH_SIZE")
     write = _last_dispatch_counters(write_dir, "WRITE_SIZE")
     cf = _last_dispatch_counters(copy_fetch_dir, "FETCH_SIZE")
@@ -139,6 +139,11 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
         wb = write.get(name, 0.0) * 1024.0 * write_scale
         kernels[short] = {"fetch_kib_raw": fetch.get(name), "write_kib_raw": write.get(name),
                           "fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb}
+    if mfma_dir:  # rocprofv3's MfmaUtil: matrix-core busy cycles / (GPU active cycles x SIMDs), percent
+        util = _last_dispatch_counters(mfma_dir, "MfmaUtil")
+        for name, v in util.items():
+            if _short(name) in kernels:
+                kernels[_short(name)]["mfma_busy_pct"] = v
     launches = {}
     pre = [k for k in kernels if "intra" in k or "state_kernel" in k]
     if pre:
@@ -154,8 +159,12 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
                "gpurun_out/prof/pmc_copy_FETCH_SIZE -o run -- python3 $GRAFT_REPO_ROOT/bench.py --only copy --steps 2"
                "   (likewise WRITE_SIZE)",
+               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc MfmaUtil --output-format csv -d $GRAFT_REPO_ROOT/"
+               "gpurun_out/prof/pmc_bench_MfmaUtil -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 0 "
+               "--no-cpu-baseline",
                "python bench.py --summarize-counters gpurun_out/prof/pmc_bench_FETCH_SIZE gpurun_out/prof/"
-               "pmc_bench_WRITE_SIZE gpurun_out/prof/pmc_copy_FETCH_SIZE gpurun_out/prof/pmc_copy_WRITE_SIZE"],
+               "pmc_bench_WRITE_SIZE gpurun_out/prof/pmc_copy_FETCH_SIZE gpurun_out/prof/pmc_copy_WRITE_SIZE "
+               "gpurun_out/prof/pmc_bench_MfmaUtil"],
            "note": "per-launch bytes of the last dispatch of each kernel; each counter scaled by what it reads "
                    "for a plain device copy of copy_bytes (read once, written once)",
            "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": _short(copy_name),
@@ -166,6 +175,19 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def measured_mfma_busy():
+    """{kernel: rocprofv3 MfmaUtil percent} from the committed counter summary
+    when it matches the current kernel sources, else {}."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return {}
+    return {k: v["mfma_busy_pct"] for k, v in rec.get("kernels", {}).items() if "mfma_busy_pct" in v}
 
 
 def cpu_baseline(inp, heads, T_sample, threads):
@@ -189,7 +211,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run one part only (for profilers); prints no JSON line")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None)
-    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR", default=None)
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
+                    help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_UTIL_DIR]")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
@@ -317,6 +340,7 @@ def main():
             "tokens_per_s": tok_s,
             "hbm_frac_algorithmic": pb / t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / t_pre / BF16_PEAK,
+            "mfma_busy_pct_counter": measured_mfma_busy() or None,
             "alg_bytes": pb, "alg_flops": pf,
         },
         "decode": {

@@ -166,11 +166,13 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
     int64_t item = blockIdx.x;
     int64_t tok0;
     int nvalid;
-    if (item >= n_items || !locate_chunk(item / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return;
+    int64_t slot, h0;
+    divmod_nonneg(item, H, slot, h0);
+    if (item >= n_items || !locate_chunk(slot, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return;
     WideRaw raw;
     {
         const int tid = threadIdx.x;
-        fetch_item(p, tok0, nvalid, static_cast<int>(item % H), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
+        fetch_item(p, tok0, nvalid, static_cast<int>(h0), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
     }
     for (;;) {
         // Lane-dependent addresses and masks are recomputed per item: hoisted out
@@ -323,10 +325,12 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
 
         // ---- the next item (located now, fetched once this one's stores are issued)
         const int64_t next = item + gridDim.x;
+        int64_t slot_n, h_n;
+        divmod_nonneg(next, H, slot_n, h_n);
         int64_t tok0_n = 0;
         int nvalid_n = 0;
         const bool more =
-            next < n_items && locate_chunk(next / H, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0_n, nvalid_n);
+            next < n_items && locate_chunk(slot_n, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0_n, nvalid_n);
 
         // ---- sum the shares in a fixed order; apply masks and beta
         __syncthreads();
@@ -597,7 +601,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         item = next;
         tok0 = tok0_n;
         nvalid = nvalid_n;
-        fetch_item(p, tok0, nvalid, static_cast<int>(item % H), w, t16, kg, raw);
+        fetch_item(p, tok0, nvalid, static_cast<int>(h_n), w, t16, kg, raw);
     }
 }
 

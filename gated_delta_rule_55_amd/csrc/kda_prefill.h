@@ -79,12 +79,27 @@ __device__ __forceinline__ float in_to_f32(typename std::conditional_t<BF, uint1
 
 // Locates the chunk handled by slot x: its first flattened token and length.
 // Returns false when x is past the last chunk (varlen grids are an upper bound).
+// q = a / b, r = a % b for a >= 0, b > 0; 32-bit division when both fit
+// (int64 division is a long software sequence on the GPU).
+__device__ __forceinline__ void divmod_nonneg(int64_t a, int64_t b, int64_t &q, int64_t &r) {
+    if (((a | b) >> 32) == 0) {
+        const uint32_t a32 = static_cast<uint32_t>(a), b32 = static_cast<uint32_t>(b);
+        const uint32_t q32 = a32 / b32;
+        q = q32;
+        r = a32 - q32 * b32;
+    } else {
+        q = a / b;
+        r = a - q * b;
+    }
+}
+
 __device__ __forceinline__ bool locate_chunk(int64_t x, int C, int64_t T, int32_t N,
                                              const int32_t *cu, const int32_t *off,
                                              int64_t &tok0, int &nvalid) {
     if (cu == nullptr) {
         const int64_t cps = (T + C - 1) / C;
-        const int64_t n = x / cps, c = x % cps;
+        int64_t n, c;
+        divmod_nonneg(x, cps, n, c);
         tok0 = n * T + c * C;
         const int64_t rem = T - c * C;
         nvalid = static_cast<int>(rem < C ? rem : C);
