@@ -177,9 +177,10 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfm
     print(json.dumps(rec, indent=1))
 
 
-def measured_mfma_busy():
-    """{kernel: rocprofv3 MfmaUtil percent} from the committed counter summary
-    when it matches the current kernel sources, else {}."""
+def measured_mfma_busy(launch):
+    """{kernel: rocprofv3 MfmaUtil percent} for the kernels of one C-ABI launch,
+    from the committed counter summary when it matches the current kernel
+    sources, else {}."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return {}
@@ -187,7 +188,9 @@ def measured_mfma_busy():
         rec = json.load(f)
     if rec.get("source_digest") != source_digest():
         return {}
-    return {k: v["mfma_busy_pct"] for k, v in rec.get("kernels", {}).items() if "mfma_busy_pct" in v}
+    names = rec.get("launches", {}).get(launch, {}).get("kernels", [])
+    kern = rec.get("kernels", {})
+    return {k: kern[k]["mfma_busy_pct"] for k in names if "mfma_busy_pct" in kern.get(k, {})}
 
 
 def cpu_baseline(inp, heads, T_sample, threads):
@@ -340,7 +343,7 @@ def main():
             "tokens_per_s": tok_s,
             "hbm_frac_algorithmic": pb / t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / t_pre / BF16_PEAK,
-            "mfma_busy_pct_counter": measured_mfma_busy() or None,
+            "mfma_busy_pct_counter": measured_mfma_busy("kda_chunk_fwd") or None,
             "alg_bytes": pb, "alg_flops": pf,
         },
         "decode": {
