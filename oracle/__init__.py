@@ -12,9 +12,17 @@ it through ctypes.  It follows the state-update equation of the section
 ``alpha_t = exp(log_alpha_t)`` per key channel, and the readout
 ``o_t = S_t^T q_t`` after the token's write.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
-forms, special cases, exact rational arithmetic and an explicit-matrix brute
-force; none is "parity unpinned".
+``gdn_forward`` and ``gdn_decode_step`` run Gated DeltaNet (GDN), the
+scalar-gate recurrence the same page sets KDA against (one head-wise
+``alpha_t``; KDA replaces it by a per-channel diagonal):
+``S_t = (I - beta_t k_t k_t^T) alpha_t S_{t-1} + beta_t k_t v_t^T``, with
+``log_alpha`` of shape [B, T, H] (prefill) or [N, H] (decode).  Its C update
+shares no arithmetic with the KDA one.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_pins_gdn.py`` against closed forms, special cases, exact
+rational arithmetic and explicit-matrix brute force; none is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -53,8 +61,12 @@ def _load():
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
             i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
         lib.kda_oracle_forward.restype = ctypes.c_int
+        lib.gdn_oracle_forward.argtypes = lib.kda_oracle_forward.argtypes
+        lib.gdn_oracle_forward.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.gdn_oracle_decode_step.argtypes = lib.kda_oracle_decode_step.argtypes
+        lib.gdn_oracle_decode_step.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -74,16 +86,29 @@ def _ptr(a):
 
 
 def forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_threads=None):
-    """Runs the recurrence token by token in fp64.
+    """Runs the KDA recurrence token by token in fp64.
 
     q, k, log_alpha: [B, T, H, Dk]; v: [B, T, H, Dv]; beta: [B, T, H];
     init_state: [N, H, Dk, Dv] or None (zeros); cu_seqlens: int [N+1] or None.
     Returns (o [B, T, H, Dv], final_state [N, H, Dk, Dv]) as fp64 numpy arrays.
     """
+    return _forward(False, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_threads)
+
+
+def gdn_forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_threads=None):
+    """Runs the GDN (scalar-gate) recurrence token by token in fp64.
+
+    As ``forward`` except log_alpha: [B, T, H] (one gate per token and head).
+    """
+    return _forward(True, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_threads)
+
+
+def _forward(scalar_gate, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_threads):
     q, k, v, la, be = (_f64(a) for a in (q, k, v, log_alpha, beta))
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
-    assert k.shape == q.shape and la.shape == q.shape
+    assert k.shape == q.shape
+    assert la.shape == ((B, T, H) if scalar_gate else q.shape)
     assert v.shape == (B, T, H, Dv) and be.shape == (B, T, H)
     if cu_seqlens is not None:
         cu = np.ascontiguousarray(np.asarray(
@@ -99,24 +124,37 @@ def forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_thread
     fs = np.zeros((N, H, Dk, Dv), dtype=np.float64)
     if n_threads is None:
         n_threads = os.cpu_count() or 1
-    rc = _load().kda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
-                                    cu_p, B, T, H, Dk, Dv, N, _ptr(o), _ptr(fs), int(n_threads))
+    lib = _load()
+    fn = lib.gdn_oracle_forward if scalar_gate else lib.kda_oracle_forward
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
+            cu_p, B, T, H, Dk, Dv, N, _ptr(o), _ptr(fs), int(n_threads))
     if rc != 0:
-        raise ValueError(f"kda_oracle_forward failed with code {rc}")
+        raise ValueError(f"{'gdn' if scalar_gate else 'kda'}_oracle_forward failed with code {rc}")
     return o, fs
 
 
 def decode_step(q, k, v, log_alpha, beta, state):
-    """One recurrence step per (n, h); q, k, log_alpha [N,H,Dk], v [N,H,Dv],
+    """One KDA step per (n, h); q, k, log_alpha [N,H,Dk], v [N,H,Dv],
     beta [N,H], state [N,H,Dk,Dv].  Returns (o [N,H,Dv], new_state), fp64."""
+    return _decode(False, q, k, v, log_alpha, beta, state)
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, state):
+    """One GDN step per (n, h); as ``decode_step`` except log_alpha [N,H]."""
+    return _decode(True, q, k, v, log_alpha, beta, state)
+
+
+def _decode(scalar_gate, q, k, v, log_alpha, beta, state):
     q, k, v, la, be = (_f64(a) for a in (q, k, v, log_alpha, beta))
     st = _f64(state).copy()
     N, H, Dk = q.shape
     Dv = v.shape[2]
     assert st.shape == (N, H, Dk, Dv)
+    assert la.shape == ((N, H) if scalar_gate else (N, H, Dk))
     o = np.zeros((N, H, Dv), dtype=np.float64)
-    rc = _load().kda_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be),
-                                        _ptr(st), N, H, Dk, Dv, _ptr(o))
+    lib = _load()
+    fn = lib.gdn_oracle_decode_step if scalar_gate else lib.kda_oracle_decode_step
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(st), N, H, Dk, Dv, _ptr(o))
     if rc != 0:
-        raise ValueError(f"kda_oracle_decode_step failed with code {rc}")
+        raise ValueError(f"{'gdn' if scalar_gate else 'kda'}_oracle_decode_step failed with code {rc}")
     return o, st

@@ -29,6 +29,19 @@
  * With cu_seqlens (int32 [N+1], host memory) the batch is one packed row
  * (B == 1) and sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
  * Without it there are N = B sequences of T tokens each.
+ *
+ * Gated DeltaNet (GDN), the scalar-gate recurrence the same page sets KDA
+ * against (bullet on channel-wise decay in the KDA section: GDN has one
+ * head-wise scalar alpha_t; the list of related work: GDN is DeltaNet with a
+ * scalar forget gate; KDA's positioning: KDA turns that scalar into a
+ * per-channel diagonal), is computed by gdn_token_update below from its own
+ * equation, with alpha_t = exp(log_alpha_t) one number per (token, head):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) alpha_t S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * and log_alpha laid out [B, T, H] (prefill) or [N, H] (decode).  It shares no
+ * arithmetic with token_update, so the two can be checked against each other.
  */
 #include <math.h>
 #include <pthread.h>
@@ -40,6 +53,7 @@ typedef struct {
     const double *q, *k, *v, *log_alpha, *beta, *init_state;
     const int32_t *cu_seqlens;
     int64_t B, T, H, Dk, Dv, N;
+    int scalar_gate;        /* 0: KDA, log_alpha [.., Dk]; 1: GDN, log_alpha [..] */
     double *o, *final_state;
     int64_t next_unit;      /* work counter, guarded by lock */
     pthread_mutex_t lock;
@@ -72,6 +86,31 @@ static void token_update(double *S, int64_t Dk, int64_t Dv,
         for (int64_t j = 0; j < Dv; ++j) o_t[j] += S[c * Dv + j] * q[c];
 }
 
+/* One token of the GDN recurrence: the whole state is scaled by the head's
+ * scalar alpha_t, then the same delta-rule erase/write, then the readout.
+ * The rank-1 terms are formed explicitly from (I - beta k k^T) S':
+ * e = k^T S' (a row vector), S = S' - beta k e + beta k v^T. */
+static void gdn_token_update(double *S, int64_t Dk, int64_t Dv,
+                             const double *q, const double *k, const double *v,
+                             double log_alpha, double beta, double *e, double *o_t)
+{
+    const double a = exp(log_alpha);
+    for (int64_t i = 0; i < Dk * Dv; ++i) S[i] = a * S[i];
+    for (int64_t j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) acc += k[c] * S[c * Dv + j];
+        e[j] = acc;
+    }
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < Dv; ++j)
+            S[c * Dv + j] = S[c * Dv + j] - beta * k[c] * e[j] + beta * k[c] * v[j];
+    for (int64_t j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) acc += q[c] * S[c * Dv + j];
+        o_t[j] = acc;
+    }
+}
+
 /* Runs the whole token loop of one (sequence n, head h) unit. */
 static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, double *p)
 {
@@ -86,10 +125,16 @@ static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, doubl
 
     for (int64_t t = t0; t < t1; ++t) {
         const size_t row = (size_t)((b * J->T + t) * H + h);
-        token_update(S, Dk, Dv,
-                     J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
-                     J->v + row * (size_t)Dv, J->log_alpha + row * (size_t)Dk,
-                     J->beta[row], p, J->o + row * (size_t)Dv);
+        if (J->scalar_gate)
+            gdn_token_update(S, Dk, Dv,
+                             J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
+                             J->v + row * (size_t)Dv, J->log_alpha[row],
+                             J->beta[row], p, J->o + row * (size_t)Dv);
+        else
+            token_update(S, Dk, Dv,
+                         J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
+                         J->v + row * (size_t)Dv, J->log_alpha + row * (size_t)Dk,
+                         J->beta[row], p, J->o + row * (size_t)Dv);
     }
     if (J->final_state) memcpy(J->final_state + sidx, S, sizeof(double) * (size_t)(Dk * Dv));
 }
@@ -122,16 +167,18 @@ static void *worker(void *arg)
  * not depend on n_threads.  Returns 0 on success, -1 on a bad argument,
  * -2 when a thread or allocation fails.
  */
-int kda_oracle_forward(const double *q, const double *k, const double *v,
-                       const double *log_alpha, const double *beta,
-                       const double *init_state, const int32_t *cu_seqlens,
-                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                       int64_t n_seqs, double *o, double *final_state, int n_threads)
+static int forward_impl(const double *q, const double *k, const double *v,
+                        const double *log_alpha, const double *beta,
+                        const double *init_state, const int32_t *cu_seqlens,
+                        int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                        int64_t n_seqs, double *o, double *final_state, int n_threads,
+                        int scalar_gate)
 {
     if (!q || !k || !v || !log_alpha || !beta || !o) return -1;
     if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return -1;
     oracle_job J;
     memset(&J, 0, sizeof(J));
+    J.scalar_gate = scalar_gate;
     J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta;
     J.init_state = init_state; J.cu_seqlens = cu_seqlens;
     J.B = B; J.T = T; J.H = H; J.Dk = Dk; J.Dv = Dv;
@@ -166,6 +213,31 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
     return rc;
 }
 
+int kda_oracle_forward(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const double *init_state, const int32_t *cu_seqlens,
+                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                       int64_t n_seqs, double *o, double *final_state, int n_threads)
+{
+    return forward_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv,
+                        n_seqs, o, final_state, n_threads, 0);
+}
+
+/*
+ * gdn_oracle_forward: the GDN recurrence over every (sequence, head) unit,
+ * with log_alpha [B, T, H] (one scalar per token and head).  Everything else
+ * (layouts, cu_seqlens, threads, return codes) is as in kda_oracle_forward.
+ */
+int gdn_oracle_forward(const double *q, const double *k, const double *v,
+                       const double *log_alpha, const double *beta,
+                       const double *init_state, const int32_t *cu_seqlens,
+                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                       int64_t n_seqs, double *o, double *final_state, int n_threads)
+{
+    return forward_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv,
+                        n_seqs, o, final_state, n_threads, 1);
+}
+
 /*
  * kda_oracle_decode_step: one token for each of N independent states, the
  * state updated in place.  q, k [N, H, Dk]; v, o [N, H, Dv];
@@ -187,5 +259,28 @@ int kda_oracle_decode_step(const double *q, const double *k, const double *v,
                      v + (size_t)u * (size_t)Dv, log_alpha + (size_t)u * (size_t)Dk,
                      beta[u], p, o + (size_t)u * (size_t)Dv);
     free(p);
+    return 0;
+}
+
+/*
+ * gdn_oracle_decode_step: one GDN token for each of N independent states, the
+ * state updated in place; log_alpha [N, H], the other layouts as in
+ * kda_oracle_decode_step.
+ */
+int gdn_oracle_decode_step(const double *q, const double *k, const double *v,
+                           const double *log_alpha, const double *beta,
+                           double *state, int64_t N, int64_t H, int64_t Dk,
+                           int64_t Dv, double *o)
+{
+    if (!q || !k || !v || !log_alpha || !beta || !state || !o) return -1;
+    if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    double *e = (double *)malloc(sizeof(double) * (size_t)Dv);
+    if (!e) return -2;
+    for (int64_t u = 0; u < N * H; ++u)
+        gdn_token_update(state + (size_t)u * (size_t)(Dk * Dv), Dk, Dv,
+                         q + (size_t)u * (size_t)Dk, k + (size_t)u * (size_t)Dk,
+                         v + (size_t)u * (size_t)Dv, log_alpha[u],
+                         beta[u], e, o + (size_t)u * (size_t)Dv);
+    free(e);
     return 0;
 }
