@@ -10,6 +10,11 @@ reported next to it.  Times come from HIP events on the stream the kernels run
 on.  The fp64 CPU oracle is timed on a bounded sample of the same prefill
 workload on the host cores (cpu_baseline).
 
+After the timed KDA steps, the Gated DeltaNet (scalar-gate) variant is timed
+on the same tensors with one log gate per (token, head) -- gdn_chunk_fwd over
+the 1M-token workload and 64 gdn_decode_step calls -- and reported in the
+"gdn" object of the same JSON line.
+
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 Profiling helpers (the commands that made the summaries under profiles/):
@@ -37,10 +42,12 @@ COPY_BYTES = 1 << 31     # size of the calibration copy (read once, written once
 BF16_PEAK = 2.5e15       # MI355X dense bf16/fp16 matrix flop/s
 
 
-def prefill_alg_bytes(T, H, Dk, Dv, N, in_bytes=2, init=False):
+def prefill_alg_bytes(T, H, Dk, Dv, N, in_bytes=2, init=False, gate_per_head=None):
     """Algorithmic HBM bytes of one prefill: q, k, v read, log_alpha and beta
-    read, o written, final state written (and the initial state read)."""
-    per_tok_head = in_bytes * (2 * Dk + Dv) + 4 * Dk + 4 + 4 * Dv
+    read, o written, final state written (and the initial state read).
+    gate_per_head: fp32 gates per (token, head) -- Dk for KDA, 1 for GDN."""
+    g = Dk if gate_per_head is None else gate_per_head
+    per_tok_head = in_bytes * (2 * Dk + Dv) + 4 * g + 4 + 4 * Dv
     state = N * H * Dk * Dv * 4
     return T * H * per_tok_head + state * (2 if init else 1)
 
@@ -52,9 +59,11 @@ def prefill_alg_flops(T, H, Dk, Dv, C):
     return T * H * (6 * Dk * Dv + C * (3 * Dk + 2 * Dv) + C * C / 3)
 
 
-def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2):
-    """State read and written once, plus the token's q, k, v, log_alpha, beta, o."""
-    return N * H * (8 * Dk * Dv + in_bytes * (2 * Dk + Dv) + 4 * Dk + 4 + 4 * Dv)
+def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
+    """State read and written once, plus the token's q, k, v, log_alpha, beta, o
+    (gate_per_head: Dk for KDA, 1 for GDN)."""
+    g = Dk if gate_per_head is None else gate_per_head
+    return N * H * (8 * Dk * Dv + in_bytes * (2 * Dk + Dv) + 4 * g + 4 + 4 * Dv)
 
 
 def source_digest():
@@ -79,6 +88,23 @@ def measured_traffic(key):
         return None
     ent = rec.get("launches", {}).get(key)
     return None if ent is None else ent.get("hbm_bytes")
+
+
+# Kernels of each C-ABI launch on the 1M-token prefill / 256x32-state decode
+# workloads (rocprofv3 names, shortened).  The state pass is one kernel for
+# both prefill variants: its last dispatch in a bench run is the GDN one, and
+# its traffic is the same for both (the package does not depend on the gate).
+KDA_INTRA = "kda::intra_wide_kernel<false>"
+GDN_INTRA = "kda::intra_wide_kernel<true>"
+STATE = "kda::state_kernel<64, 128, 128, true>"
+KDA_DECODE = "kda::decode_step_kernel<128, 128, true, false>"
+GDN_DECODE = "kda::decode_step_kernel<128, 128, true, true>"
+LAUNCH_KERNELS = {
+    "kda_chunk_fwd": (KDA_INTRA, STATE),
+    "kda_decode_step": (KDA_DECODE,),
+    "gdn_chunk_fwd": (GDN_INTRA, STATE),
+    "gdn_decode_step": (GDN_DECODE,),
+}
 
 
 def _short(name):
@@ -145,12 +171,10 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfm
             if _short(name) in kernels:
                 kernels[_short(name)]["mfma_busy_pct"] = v
     launches = {}
-    pre = [k for k in kernels if "intra" in k or "state_kernel" in k]
-    if pre:
-        launches["kda_chunk_fwd"] = {"kernels": pre, "hbm_bytes": sum(kernels[k]["hbm_bytes"] for k in pre)}
-    dec = [k for k in kernels if "decode_step_kernel" in k]
-    if dec:
-        launches["kda_decode_step"] = {"kernels": dec, "hbm_bytes": sum(kernels[k]["hbm_bytes"] for k in dec)}
+    for launch, names in LAUNCH_KERNELS.items():
+        if all(n in kernels for n in names):
+            launches[launch] = {"kernels": list(names),
+                                "hbm_bytes": sum(kernels[n]["hbm_bytes"] for n in names)}
     rec = {"source_digest": source_digest(),
            "commands": [
                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
@@ -282,31 +306,54 @@ def main():
         torch.cuda.synchronize()
         return
 
-    for _ in range(args.warmup):
-        prefill()
-        for t in range(dsteps):
-            decode(t)
-    torch.cuda.synchronize()
-
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    pre_ms, dec_ms = [], []
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        prefill()
-        e1.record(stream)
-        de = [ev() for _ in range(dsteps + 1)]
-        de[0].record(stream)
-        for t in range(dsteps):
-            decode(t)
-            de[t + 1].record(stream)
+
+    def warm(prefill_fn, decode_fn):
+        for _ in range(args.warmup):
+            prefill_fn()
+            for t in range(dsteps):
+                decode_fn(t)
         torch.cuda.synchronize()
-        pre_ms.append(e0.elapsed_time(e1))
-        dec_ms.extend(de[t].elapsed_time(de[t + 1]) for t in range(dsteps))
+
+    def timed(prefill_fn, decode_fn):
+        """K timed passes: per-call prefill ms and per-step decode ms (HIP events)."""
+        pre, dec = [], []
+        for _ in range(args.steps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            prefill_fn()
+            e1.record(stream)
+            de = [ev() for _ in range(dsteps + 1)]
+            de[0].record(stream)
+            for t in range(dsteps):
+                decode_fn(t)
+                de[t + 1].record(stream)
+            torch.cuda.synchronize()
+            pre.append(e0.elapsed_time(e1))
+            dec.extend(de[t].elapsed_time(de[t + 1]) for t in range(dsteps))
+        return pre, dec
+
+    warm(prefill, decode)
+    t_start = time.perf_counter()
+    pre_ms, dec_ms = timed(prefill, decode)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+
+    # ---- Gated DeltaNet on the same tensors: one log gate per (token, head) ----
+    gdn_la = workloads.scalar_log_alpha((1, T, H), w.shift, dev, seed=1)
+    gdn_dla = workloads.scalar_log_alpha((dsteps, dw.N, dw.H), dw.shift, dev, seed=2)
+    gstate = state0.clone()
+
+    def gdn_prefill():
+        kda.gdn_chunk_fwd(pin["q"], pin["k"], pin["v"], gdn_la, pin["beta"], None, None, C,
+                          out=o, final_state=fs, workspace=ws)
+
+    def gdn_decode(t):
+        kda.gdn_decode_step(din["q"][t], din["k"][t], din["v"][t], gdn_dla[t],
+                            din["beta"][t], gstate, out=od)
+
+    warm(gdn_prefill, gdn_decode)
+    g_pre_ms, g_dec_ms = timed(gdn_prefill, gdn_decode)
 
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
@@ -317,6 +364,13 @@ def main():
     pf = prefill_alg_flops(T, H, Dk, Dv, C)
     db = decode_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv)
     dec_gbs = db / t_dec / 1e9
+
+    g_pre_ms.sort()
+    g_dec_sorted = sorted(g_dec_ms)
+    g_t_pre = sum(g_pre_ms) / len(g_pre_ms) / 1e3
+    g_t_dec = sum(g_dec_ms) / len(g_dec_ms) / 1e3
+    g_pb = prefill_alg_bytes(T, H, Dk, Dv, N, gate_per_head=1)
+    g_db = decode_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv, gate_per_head=1)
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128, T=1M) + decode step HBM GB/s, 1 MI355X",
@@ -354,7 +408,7 @@ def main():
             "alg_bytes_per_step": db,
         },
         "roofline": {
-            "kernel": "kda_chunk_fwd (intra_wide_kernel + state_kernel<64,128,128,bf16>)",
+            "kernel": "kda_chunk_fwd (intra_wide_kernel<false> + state_kernel<64,128,128,bf16>)",
             "bound": "hbm",
             "achieved": pb / t_pre / 1e9,
             "peak": HBM_PEAK / 1e9,
@@ -363,13 +417,39 @@ def main():
             "traffic": measured_traffic("kda_chunk_fwd"),
         },
         "decode_roofline": {
-            "kernel": "decode_step_kernel<128,128,bf16>",
+            "kernel": "decode_step_kernel<128,128,bf16,false>",
             "bound": "hbm",
             "achieved": dec_gbs,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": db / t_dec / HBM_PEAK,
             "traffic": measured_traffic("kda_decode_step"),
+        },
+    }
+
+    result["gdn"] = {
+        "workload": "Gated DeltaNet (one log gate per token and head, -softplus(N(0,1)+3)) on the "
+                    "same q/k/v/beta tensors: gdn_chunk_fwd over the 1M-token prefill, then 64 "
+                    "gdn_decode_step calls on 256 seqs x 32 heads",
+        "prefill": {
+            "ms_mean": g_t_pre * 1e3, "ms_median": g_pre_ms[len(g_pre_ms) // 2],
+            "tokens_per_s": T / g_t_pre,
+            "hbm_frac_algorithmic": g_pb / g_t_pre / HBM_PEAK,
+            "mfma_frac_algorithmic": pf / g_t_pre / BF16_PEAK,
+            "alg_bytes": g_pb, "alg_flops": pf,
+            "roofline": {"kernel": "gdn_chunk_fwd (intra_wide_kernel<true> + state_kernel)",
+                         "bound": "hbm", "achieved": g_pb / g_t_pre / 1e9,
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": g_pb / g_t_pre / HBM_PEAK,
+                         "traffic": measured_traffic("gdn_chunk_fwd")},
+        },
+        "decode": {
+            "us_per_step_mean": g_t_dec * 1e6,
+            "us_per_step_median": g_dec_sorted[len(g_dec_sorted) // 2] * 1e3,
+            "GB_per_s": g_db / g_t_dec / 1e9,
+            "hbm_frac": g_db / g_t_dec / HBM_PEAK,
+            "alg_bytes_per_step": g_db,
+            "traffic": measured_traffic("gdn_decode_step"),
         },
     }
 

@@ -71,9 +71,10 @@ const char *kda_last_error(void) { return g_err; }
 
 int kda_version(void) { return KDA_VERSION; }
 
-kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
-                           const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
-                           int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
+static kda_status decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                              const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
+                              int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream,
+                              bool scalar_gate) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -87,7 +88,8 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     const char *names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
     for (int i = 0; i < 7; ++i) {
         if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", names[i]);
-        const bool scalar = i == 4;  // beta is read element by element
+        // beta and a scalar gate are read element by element
+        const bool scalar = i == 4 || (i == 3 && scalar_gate);
         if (scalar ? !aligned4(ptrs[i]) : !aligned16(ptrs[i]))
             return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", names[i], scalar ? 4 : 16);
     }
@@ -95,7 +97,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     size_t bq, bv, bg, bb, bs, bo;
     if (!bytes_of(bq, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk}, esz) ||
         !bytes_of(bv, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, esz) ||
-        !bytes_of(bg, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk}, 4) ||
+        !bytes_of(bg, {(uint64_t)N, (uint64_t)H, scalar_gate ? 1u : (uint64_t)Dk}, 4) ||
         !bytes_of(bb, {(uint64_t)N, (uint64_t)H}, 4) ||
         !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
         !bytes_of(bo, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, 4))
@@ -109,10 +111,22 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     }
     if (overlap(ro, rs)) return fail(KDA_ERR_INVALID_ARG, "o overlaps state");
 
-    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, N, H, Dk, Dv, in_dtype == KDA_BF16};
+    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, N, H, Dk, Dv, in_dtype == KDA_BF16, scalar_gate};
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
+                           int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
+    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, false);
+}
+
+kda_status gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
+                           int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
+    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, true);
 }
 
 static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
@@ -149,11 +163,11 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
     return out;
 }
 
-kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
-                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
-                         kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
-                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                                 const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                                 int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                                 kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream, bool scalar_gate) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -180,7 +194,8 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const char *nn[] = {"q", "k", "v", "log_alpha", "beta", "o"};
     for (int i = 0; i < 6; ++i) {
         if (!need[i] && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", nn[i]);
-        const bool scalar = i == 4;  // beta is read element by element
+        // beta and a scalar gate are read element by element
+        const bool scalar = i == 4 || (i == 3 && scalar_gate);
         if (need[i] && (scalar ? !aligned4(need[i]) : !aligned16(need[i])))
             return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", nn[i], scalar ? 4 : 16);
     }
@@ -205,7 +220,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     size_t bq, bv, bg, bb, bs, bo, bc;
     if (!bytes_of(bq, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, esz) ||
         !bytes_of(bv, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, esz) ||
-        !bytes_of(bg, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, 4) ||
+        !bytes_of(bg, {(uint64_t)B, (uint64_t)T, (uint64_t)H, scalar_gate ? 1u : (uint64_t)Dk}, 4) ||
         !bytes_of(bb, {(uint64_t)B, (uint64_t)T, (uint64_t)H}, 4) ||
         !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
         !bytes_of(bo, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, 4))
@@ -233,7 +248,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.init_state = init_state; a.cu_seqlens = cu_seqlens;
     a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.C = chunk_size; a.T = T;
-    a.bf16 = bf16; a.o = o; a.final_state = final_state;
+    a.bf16 = bf16; a.scalar_gate = scalar_gate; a.o = o; a.final_state = final_state;
     a.workspace = static_cast<char *>(workspace);
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
@@ -241,6 +256,24 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     hipError_t e = kda::launch_prefill(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                         kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
+                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, false);
+}
+
+kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                         kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
+                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -12,6 +12,10 @@
 //   S   = S' + k u^T                              == (I - b k k^T) S' + b k v^T
 //   o   = S^T q = r + (k . q) u
 //
+// The Gated DeltaNet step (one scalar gate per head, the recurrence the same
+// page compares KDA against) is the same kernel with that gate read once per
+// (n, h) and applied to every row.
+//
 // One workgroup of min(512, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
 // (one float4) of RPT rows spaced RG apart, so each wave reads and writes whole
 // contiguous rows (coalesced 16-byte accesses).  Reductions: butterfly
@@ -24,7 +28,9 @@ namespace kda {
 
 constexpr int kDecodeThreads = 512;
 
-template <int DK, int DV, bool kBf16>
+// SG: one scalar gate per (n, h) (log_alpha [N, H]) instead of one per key
+// channel (log_alpha [N, H, Dk]).
+template <int DK, int DV, bool kBf16, bool SG>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
                    const void *__restrict__ v, const float *__restrict__ log_alpha,
@@ -56,11 +62,11 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(v, unit * DV + 4 * cg + e);
-    const float *gp = log_alpha + unit * DK;
     for (int c = t; c < DK; c += blockDim.x) {
         s_k[c] = load_in<kBf16>(k, unit * DK + c);
         s_q[c] = load_in<kBf16>(q, unit * DK + c);
-        s_a[c] = fast_exp2(gp[c] * kLog2e);  // exp(-inf) -> 0
+        const float g = SG ? log_alpha[unit] : log_alpha[unit * DK + c];
+        s_a[c] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
     }
     __syncthreads();
 
@@ -115,8 +121,12 @@ template <int DK, int DV, bool kBf16>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     constexpr int NT = (DK * DV / 4 < kDecodeThreads) ? DK * DV / 4 : kDecodeThreads;
     const dim3 grid(static_cast<unsigned>(a.N * a.H));
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16>), grid, dim3(NT), 0, stream, a.q, a.k,
-                       a.v, a.log_alpha, a.beta, a.state, a.o);
+    if (a.scalar_gate)
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, true>), grid, dim3(NT), 0, stream, a.q,
+                           a.k, a.v, a.log_alpha, a.beta, a.state, a.o);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, false>), grid, dim3(NT), 0, stream, a.q,
+                           a.k, a.v, a.log_alpha, a.beta, a.state, a.o);
     return hipGetLastError();
 }
 

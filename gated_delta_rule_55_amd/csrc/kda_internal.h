@@ -14,6 +14,7 @@ struct DecodeArgs {
     float *state, *o;
     int32_t N, H, Dk, Dv;
     bool bf16;
+    bool scalar_gate;  // log_alpha [N, H] (GDN) instead of [N, H, Dk] (KDA)
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -64,6 +65,7 @@ struct PrefillArgs {
     int32_t B, H, Dk, Dv, N, C;
     int64_t T;
     bool bf16;
+    bool scalar_gate;           // log_alpha [B, T, H] (GDN) instead of [B, T, H, Dk] (KDA)
     float *o, *final_state;     // final_state nullable
     char *workspace;
     int64_t n_slots;            // chunk slots in the workspace

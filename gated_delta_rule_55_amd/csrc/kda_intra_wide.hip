@@ -120,6 +120,9 @@ struct WideRaw {
     float beta[4];
 };
 
+// SG (scalar gate, GDN): one log_alpha per (token, head), broadcast to every
+// channel; otherwise one per key channel.
+template <bool SG>
 __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, int nvalid, int h, int w, int t16,
                                            int kg, WideRaw &r) {
     const int H = p.H;
@@ -134,20 +137,27 @@ __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, i
         const uint2 k0 = *reinterpret_cast<const uint2 *>(kb), k1 = *reinterpret_cast<const uint2 *>(kb + 16);
         const uint2 q0 = *reinterpret_cast<const uint2 *>(qb), q1 = *reinterpret_cast<const uint2 *>(qb + 16);
         const uint2 v0 = *reinterpret_cast<const uint2 *>(vb), v1 = *reinterpret_cast<const uint2 *>(vb + 16);
-        const f32x4 l0 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off);
-        const f32x4 l1 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off + 16);
         r.k[t][0] = k0.x; r.k[t][1] = k0.y; r.k[t][2] = k1.x; r.k[t][3] = k1.y;
         r.q[t][0] = q0.x; r.q[t][1] = q0.y; r.q[t][2] = q1.x; r.q[t][3] = q1.y;
         r.v[t][0] = v0.x; r.v[t][1] = v0.y; r.v[t][2] = v1.x; r.v[t][3] = v1.y;
+        if constexpr (SG) {
+            const float g = p.log_alpha[row];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            r.la[t][e] = l0[e];
-            r.la[t][4 + e] = l1[e];
+            for (int e = 0; e < 8; ++e) r.la[t][e] = g;
+        } else {
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off);
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(p.log_alpha + off + 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r.la[t][e] = l0[e];
+                r.la[t][4 + e] = l1[e];
+            }
         }
         r.beta[t] = p.beta[row];
     }
 }
 
+template <bool SG>
 __global__ void __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 intra_wide_kernel(IntraParams p, int64_t n_items) {
     constexpr int C = kWC, NT16 = 4, PARTS = 2, MS = kAS;
@@ -172,7 +182,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
     WideRaw raw;
     {
         const int tid = threadIdx.x;
-        fetch_item(p, tok0, nvalid, static_cast<int>(h0), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
+        fetch_item<SG>(p, tok0, nvalid, static_cast<int>(h0), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
     }
     for (;;) {
         // Lane-dependent addresses and masks are recomputed per item: hoisted out
@@ -601,26 +611,33 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         item = next;
         tok0 = tok0_n;
         nvalid = nvalid_n;
-        fetch_item(p, tok0, nvalid, static_cast<int>(h_n), w, t16, kg, raw);
+        fetch_item<SG>(p, tok0, nvalid, static_cast<int>(h_n), w, t16, kg, raw);
     }
 }
 
 }  // namespace
 
-hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
-    if (n_items <= 0) return hipSuccess;
+template <bool SG>
+static hipError_t launch_intra_wide_t(const IntraParams &p, int64_t n_items, hipStream_t stream) {
     static thread_local int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_wide_kernel, kIntraThreads, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_wide_kernel<SG>, kIntraThreads, 0) !=
+                hipSuccess ||
             nb <= 0)
             nb = 1;
         per_cu = nb;
     }
     const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
-    hipLaunchKernelGGL(intra_wide_kernel, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream, p,
-                       n_items);
+    hipLaunchKernelGGL(intra_wide_kernel<SG>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
+                       p, n_items);
     return hipGetLastError();
+}
+
+hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    return p.g_ch == 0 ? launch_intra_wide_t<true>(p, n_items, stream)
+                       : launch_intra_wide_t<false>(p, n_items, stream);
 }
 
 }  // namespace kda

@@ -24,6 +24,10 @@ struct IntraParams {
     char *ws;
     size_t pkg_bytes;
     PackageLayout L;
+    // log_alpha element of (token-head row r, key channel c) is
+    // log_alpha[r * g_row + c * g_ch]: (Dk, 1) per-channel gates (KDA),
+    // (1, 0) one scalar gate per token and head (GDN)
+    int32_t g_row, g_ch;
 };
 
 struct StateParams {

@@ -111,7 +111,7 @@ struct IntraInputs {
 #pragma unroll
         for (int u = 0; u < TPS; ++u) {
             const int i = seg * TPS + u;
-            g[u] = (i < nvalid) ? p.log_alpha[((tok0 + i) * H + h) * DK + cc] : 0.f;
+            g[u] = (i < nvalid) ? p.log_alpha[((tok0 + i) * H + h) * p.g_row + cc * p.g_ch] : 0.f;
         }
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -909,7 +909,8 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     }
     if (a.n_slots > 0) {
         IntraParams ip{a.q, a.k, a.v, a.log_alpha, a.beta, a.cu_seqlens, a.chunk_offsets,
-                       a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
+                       a.T, a.H, a.N, a.workspace, a.pkg_bytes, L,
+                       a.scalar_gate ? 1 : DK, a.scalar_gate ? 0 : 1};
         // persistent: a few workgroups per compute unit walk the (chunk, head)
         // items, each loading the next item's inputs while computing one
         const int64_t n_items = a.n_slots * a.H;

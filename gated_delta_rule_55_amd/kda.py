@@ -40,6 +40,10 @@ def load():
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, fp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = lib.kda_chunk_fwd.argtypes
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
+    lib.gdn_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -80,9 +84,23 @@ def workspace_size(B, T, H, Dk, Dv, n_seqs=0, dtype=torch.bfloat16, chunk_size=6
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk_size=64,
               out=None, final_state=None, output_final_state=True, workspace=None, stream=None):
-    """Chunked prefill.  q, k [B,T,H,Dk]; v [B,T,H,Dv]; log_alpha [B,T,H,Dk] fp32;
+    """KDA chunked prefill.  q, k [B,T,H,Dk]; v [B,T,H,Dv]; log_alpha [B,T,H,Dk] fp32;
     beta [B,T,H] fp32; init_state [N,H,Dk,Dv] fp32 or None; cu_seqlens int32 [N+1]
     (device) or None.  Returns (o [B,T,H,Dv] fp32, final_state [N,H,Dk,Dv] or None)."""
+    return _chunk_fwd(load().kda_chunk_fwd, q, k, v, log_alpha, beta, init_state, cu_seqlens,
+                      chunk_size, out, final_state, output_final_state, workspace, stream)
+
+
+def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk_size=64,
+                  out=None, final_state=None, output_final_state=True, workspace=None, stream=None):
+    """Gated DeltaNet chunked prefill: as ``chunk_fwd`` with log_alpha [B,T,H] fp32
+    (one scalar gate per token and head)."""
+    return _chunk_fwd(load().gdn_chunk_fwd, q, k, v, log_alpha, beta, init_state, cu_seqlens,
+                      chunk_size, out, final_state, output_final_state, workspace, stream)
+
+
+def _chunk_fwd(fn, q, k, v, log_alpha, beta, init_state, cu_seqlens, chunk_size, out,
+               final_state, output_final_state, workspace, stream):
     lib = load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -97,22 +115,29 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk_
     ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, code, chunk_size))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    _check(lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs, code,
-                             chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+              _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs, code,
+              chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, final_state
 
 
 def decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
-    """One step per (n, h); state [N,H,Dk,Dv] fp32 is updated in place.
-    Returns o [N,H,Dv] fp32."""
-    lib = load()
+    """One KDA step per (n, h); log_alpha [N,H,Dk]; state [N,H,Dk,Dv] fp32 is
+    updated in place.  Returns o [N,H,Dv] fp32."""
+    return _decode(load().kda_decode_step, q, k, v, log_alpha, beta, state, out, stream)
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
+    """One Gated DeltaNet step per (n, h): as ``decode_step`` with log_alpha [N,H]."""
+    return _decode(load().gdn_decode_step, q, k, v, log_alpha, beta, state, out, stream)
+
+
+def _decode(fn, q, k, v, log_alpha, beta, state, out, stream):
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
-    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                               _ptr(state), N, H, Dk, Dv, _dtype_code(q), _ptr(out),
-                               _stream(stream)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+              _ptr(state), N, H, Dk, Dv, _dtype_code(q), _ptr(out), _stream(stream)))
     return out

@@ -18,6 +18,8 @@ the device):
   channel (channel-wise decay in [0, 1], section "Kimi Delta Attention (KDA)").
 * beta = sigmoid(x), x ~ N(0, 1), fp32, one value per (token, head).
 * initial states ~ N(0, 0.02^2) in fp32 where the workload has one.
+* gate="scalar" (Gated DeltaNet): log_alpha = -softplus(x + shift) with one
+  x ~ N(0, 1) per (token, head) instead of per key channel.
 * varlen: lengths uniform on [1, 16384], redrawn while a multiple of 64;
   a Bernoulli(0.05) draw per packed token marks a state reset, which sets
   log_alpha = -inf (alpha = 0) on every head and channel of that token.
@@ -98,7 +100,7 @@ def varlen_lengths(n: int, max_len: int, chunk: int, seed: int) -> list:
 def make_prefill(name: str = "prefill", device="cpu", seed: int = 0, *, T: Optional[int] = None,
                  H: Optional[int] = None, dtype: Optional[str] = None, shift: Optional[float] = None,
                  lengths: Optional[list] = None, init: Optional[str] = None,
-                 reset_p: Optional[float] = None) -> dict:
+                 reset_p: Optional[float] = None, gate: str = "channel") -> dict:
     """Inputs of a prefill workload; keyword overrides give scaled-down variants.
 
     Returns a dict with q, k, v, log_alpha, beta, init_state (or None),
@@ -128,7 +130,8 @@ def make_prefill(name: str = "prefill", device="cpu", seed: int = 0, *, T: Optio
     q = _unit_rows((B, T, H, w.Dk), g, device, dt)
     k = _unit_rows((B, T, H, w.Dk), g, device, dt)
     v = torch.randn((B, T, H, w.Dv), generator=g, device=device, dtype=torch.float32).to(dt)
-    x = torch.randn((B, T, H, w.Dk), generator=g, device=device, dtype=torch.float32)
+    gshape = (B, T, H) if gate == "scalar" else (B, T, H, w.Dk)
+    x = torch.randn(gshape, generator=g, device=device, dtype=torch.float32)
     log_alpha = -F.softplus(x + shift)
     del x
     beta = torch.sigmoid(torch.randn((B, T, H), generator=g, device=device, dtype=torch.float32))
@@ -143,9 +146,17 @@ def make_prefill(name: str = "prefill", device="cpu", seed: int = 0, *, T: Optio
                 chunk=w.chunk, workload=w, T=T, N=N, H=H)
 
 
+def scalar_log_alpha(shape, shift: float, device="cpu", seed: int = 0) -> torch.Tensor:
+    """Gated DeltaNet gates of any shape: -softplus(x + shift), x ~ N(0, 1), fp32,
+    from a generator of their own seeded with ``seed``."""
+    g = _gen(device, seed)
+    return -F.softplus(torch.randn(shape, generator=g, device=device, dtype=torch.float32) + shift)
+
+
 def make_decode(name: str = "decode", device="cpu", seed: int = 0, *, N: Optional[int] = None,
                 H: Optional[int] = None, steps: Optional[int] = None,
-                dtype: Optional[str] = None, D: Optional[int] = None) -> dict:
+                dtype: Optional[str] = None, D: Optional[int] = None,
+                gate: str = "channel") -> dict:
     """Initial state [N, H, Dk, Dv] and per-step inputs of the decode workload.
 
     Returns a dict with ``state`` and lists q, k, v, log_alpha, beta (one
@@ -165,7 +176,7 @@ def make_decode(name: str = "decode", device="cpu", seed: int = 0, *, N: Optiona
         out["q"].append(_unit_rows((N, H, Dk), g, device, dt))
         out["k"].append(_unit_rows((N, H, Dk), g, device, dt))
         out["v"].append(torch.randn((N, H, Dv), generator=g, device=device).to(dt))
-        x = torch.randn((N, H, Dk), generator=g, device=device)
+        x = torch.randn((N, H) if gate == "scalar" else (N, H, Dk), generator=g, device=device)
         out["log_alpha"].append(-F.softplus(x + w.shift))
         out["beta"].append(torch.sigmoid(torch.randn((N, H), generator=g, device=device)))
     return out

@@ -135,6 +135,40 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream);
 
+/*
+ * Gated DeltaNet (GDN): the scalar-gate recurrence the same page sets KDA
+ * against (bullet on channel-wise decay in the KDA section: GDN's forget gate
+ * alpha_t is one head-wise scalar; list of related work: GDN is DeltaNet with
+ * a scalar forget gate):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) alpha_t S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * i.e. KDA with Diag(alpha_t) = alpha_t I.  The two entry points below run the
+ * KDA kernels with that gate read once per (token, head) and applied to every
+ * key channel; everything not stated here (layouts of q, k, v, beta, states,
+ * o, workspace, cu_seqlens, chunk sizes, dtypes, ownership, errors,
+ * determinism, preconditions) is exactly as for kda_chunk_fwd and
+ * kda_decode_step.
+ *
+ * gdn_chunk_fwd -- chunked prefill; log_alpha is [B, T, H] fp32 (one log gate
+ * <= 0 per token and head, 4-byte aligned; -inf resets the state).  The
+ * workspace is kda_chunk_fwd_workspace_size() bytes for the same sizes.
+ */
+kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                         kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_decode_step -- one GDN token for each of N independent sequences, the
+ * state updated in place; log_alpha is [N, H] fp32 (4-byte aligned).
+ */
+kda_status gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                           const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
+                           int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream);
+
 /* Static name of a status code ("KDA_OK", ...). */
 const char *kda_status_string(kda_status status);
 

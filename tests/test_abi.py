@@ -20,7 +20,7 @@ FAKE = 0x10000000  # never dereferenced: every call below fails validation first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:kda|gdn)_[a-z_0-9]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +34,8 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
-            "kda_status_string", "kda_last_error", "kda_version"} <= set(names)
+            "kda_status_string", "kda_last_error", "kda_version",
+            "gdn_chunk_fwd", "gdn_decode_step"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
 
@@ -63,17 +64,17 @@ def test_workspace_size(lib):
         assert ws(*bad) == 0, bad
 
 
-def _chunk(lib, **kw):
+def _chunk(lib, fn="kda_chunk_fwd", **kw):
     a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, log_alpha=FAKE + 0x3000000,
              beta=FAKE + 0x4000000, init_state=None, cu_seqlens=None, B=1, T=64, H=1, Dk=16,
              Dv=16, n_seqs=0, dtype=BF16, chunk=16, o=FAKE + 0x5000000, final_state=None,
              ws=FAKE + 0x6000000, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     p = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.kda_chunk_fwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
-                             p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"],
-                             a["Dk"], a["Dv"], a["n_seqs"], a["dtype"], a["chunk"], p(a["o"]),
-                             p(a["final_state"]), p(a["ws"]), a["ws_bytes"], a["stream"])
+    return getattr(lib, fn)(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
+                            p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"],
+                            a["Dk"], a["Dv"], a["n_seqs"], a["dtype"], a["chunk"], p(a["o"]),
+                            p(a["final_state"]), p(a["ws"]), a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -98,8 +99,9 @@ def _chunk(lib, **kw):
     (dict(n_seqs=3), INVALID),                         # n_seqs without cu_seqlens
     (dict(final_state=FAKE + 0x5000000), INVALID),     # final_state aliases o
 ])
-def test_chunk_fwd_rejects(lib, kw, code):
-    assert _chunk(lib, **kw) == code
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "gdn_chunk_fwd"])
+def test_chunk_fwd_rejects(lib, fn, kw, code):
+    assert _chunk(lib, fn, **kw) == code
     assert lib.kda_last_error()  # a detail message is set
 
 
@@ -107,15 +109,15 @@ def test_chunk_fwd_partial_alias_of_init_state_rejected(lib):
     assert _chunk(lib, init_state=FAKE + 0x7000000, final_state=FAKE + 0x7000100) == INVALID
 
 
-def _decode(lib, **kw):
+def _decode(lib, fn="kda_decode_step", **kw):
     a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, log_alpha=FAKE + 0x3000000,
              beta=FAKE + 0x4000000, state=FAKE + 0x5000000, N=4, H=2, Dk=128, Dv=128,
              dtype=BF16, o=FAKE + 0x6000000, stream=None)
     a.update(kw)
     p = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.kda_decode_step(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
-                               p(a["state"]), a["N"], a["H"], a["Dk"], a["Dv"], a["dtype"],
-                               p(a["o"]), a["stream"])
+    return getattr(lib, fn)(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
+                            p(a["state"]), a["N"], a["H"], a["Dk"], a["Dv"], a["dtype"],
+                            p(a["o"]), a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -130,8 +132,9 @@ def _decode(lib, **kw):
     (dict(o=FAKE + 0x5000000), INVALID),   # o aliases the state
     (dict(state=FAKE + 0x1000000), INVALID),  # state aliases k
 ])
-def test_decode_rejects(lib, kw, code):
-    assert _decode(lib, **kw) == code
+@pytest.mark.parametrize("fn", ["kda_decode_step", "gdn_decode_step"])
+def test_decode_rejects(lib, fn, kw, code):
+    assert _decode(lib, fn, **kw) == code
 
 
 def test_beta_and_cu_seqlens_need_only_natural_alignment(lib):
@@ -145,3 +148,28 @@ def test_beta_and_cu_seqlens_need_only_natural_alignment(lib):
 def test_empty_decode_is_a_no_op(lib):
     # N = 0: nothing to do, no pointer is touched and no HIP call is made
     assert _decode(lib, N=0, q=None, k=None, v=None, state=None, o=None) == OK
+
+
+def test_gdn_gate_layout_and_alignment(lib):
+    """GDN gates are [B, T, H] / [N, H] fp32 read one by one: 4-byte alignment
+    suffices (the calls below then fail a later check on purpose, so no kernel
+    is launched), 2-byte does not, and the gate's extent is T*H (or N*H)
+    elements, not T*H*Dk."""
+    assert _chunk(lib, "gdn_chunk_fwd", log_alpha=FAKE + 0x3000004, ws=None) == WORKSPACE
+    assert _chunk(lib, "gdn_chunk_fwd", log_alpha=FAKE + 0x3000002) == INVALID
+    assert _chunk(lib, "kda_chunk_fwd", log_alpha=FAKE + 0x3000004) == INVALID
+    # o right after a [64, 1] gate: overlaps a KDA gate [64, 1, 16], not a GDN one
+    assert _chunk(lib, "kda_chunk_fwd", o=FAKE + 0x3000000 + 256, ws=None) == WORKSPACE
+    assert _chunk(lib, "kda_chunk_fwd", o=FAKE + 0x3000000 + 256) == INVALID
+    assert b"o overlaps log_alpha" in lib.kda_last_error()
+    # decode: accepted alignment, then the o/state alias is what is reported
+    assert _decode(lib, "gdn_decode_step", log_alpha=FAKE + 0x3000004, o=FAKE + 0x5000000) == INVALID
+    assert b"o overlaps state" in lib.kda_last_error()
+    assert _decode(lib, "kda_decode_step", log_alpha=FAKE + 0x3000004) == INVALID
+    assert b"log_alpha is not 16-byte aligned" in lib.kda_last_error()
+    # gdn decode: state right after an [N, H] gate (4 x 2 floats) is no overlap,
+    # so the o/state alias is reported instead
+    assert _decode(lib, "gdn_decode_step", state=FAKE + 0x3000000 + 32, o=FAKE + 0x3000000 + 32) == INVALID
+    assert b"o overlaps state" in lib.kda_last_error()
+    assert _decode(lib, "kda_decode_step", state=FAKE + 0x3000000 + 32) == INVALID
+    assert b"state overlaps log_alpha" in lib.kda_last_error()
