@@ -19,10 +19,15 @@ scalar-gate recurrence the same page sets KDA against (one head-wise
 ``log_alpha`` of shape [B, T, H] (prefill) or [N, H] (decode).  Its C update
 shares no arithmetic with the KDA one.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_pins_gdn.py`` against closed forms, special cases, exact
-rational arithmetic and explicit-matrix brute force; none is "parity
-unpinned".
+``layer_forward`` and ``layer_decode_step`` (``layer.py``) add the KDA
+layer's prologue (L2Norm of q and k, the -softplus decay gate, the sigmoid
+beta) and epilogue (RMSNorm and the sigmoid output gate) around ``forward`` /
+``decode_step``.
+
+Every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_pins_gdn.py`` and ``tests/test_oracle_pins_layer.py``
+against closed forms, special cases, invariants, exact rational arithmetic and
+explicit-matrix brute force; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -158,3 +163,6 @@ def _decode(scalar_gate, q, k, v, log_alpha, beta, state):
     if rc != 0:
         raise ValueError(f"{'gdn' if scalar_gate else 'kda'}_oracle_decode_step failed with code {rc}")
     return o, st
+
+
+from .layer import layer_decode_step, layer_forward  # noqa: E402  (the layer around the operator)
