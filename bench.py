@@ -13,7 +13,8 @@ workload on the host cores (cpu_baseline).
 After the timed KDA steps, the Gated DeltaNet (scalar-gate) variant is timed
 on the same tensors with one log gate per (token, head) -- gdn_chunk_fwd over
 the 1M-token workload and 64 gdn_decode_step calls -- and reported in the
-"gdn" object of the same JSON line.
+"gdn" object of the same JSON line; then the KDA layer (fused prologue and
+epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -59,6 +60,15 @@ def prefill_alg_flops(T, H, Dk, Dv, C):
     return T * H * (6 * Dk * Dv + C * (3 * Dk + 2 * Dv) + C * C / 3)
 
 
+def layer_alg_bytes(T, H, Dk, Dv, N, decode=False):
+    """The KDA layer's algorithmic bytes: bf16 q, k, v, x_alpha, x_beta and output
+    gate read, fp32 output written, the state written (decode: read and written);
+    the RMSNorm weight is negligible."""
+    per = 2 * (2 * Dk + Dv) + 2 * Dk + 2 + 2 * Dv + 4 * Dv
+    state = N * H * Dk * Dv * 4
+    return T * H * per + state * (2 if decode else 1)
+
+
 def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
     """State read and written once, plus the token's q, k, v, log_alpha, beta, o
     (gate_per_head: Dk for KDA, 1 for GDN)."""
@@ -92,18 +102,23 @@ def measured_traffic(key):
 
 # Kernels of each C-ABI launch on the 1M-token prefill / 256x32-state decode
 # workloads (rocprofv3 names, shortened).  The state pass is one kernel for
-# both prefill variants: its last dispatch in a bench run is the GDN one, and
-# its traffic is the same for both (the package does not depend on the gate).
-KDA_INTRA = "kda::intra_wide_kernel<false>"
-GDN_INTRA = "kda::intra_wide_kernel<true>"
+# every prefill variant: its last dispatch in a bench run is the layer's, and
+# its traffic is the same for all (the package does not depend on the gate).
+KDA_INTRA = "kda::intra_wide_kernel<0>"
+GDN_INTRA = "kda::intra_wide_kernel<1>"
 STATE = "kda::state_kernel<64, 128, 128, true>"
-KDA_DECODE = "kda::decode_step_kernel<128, 128, true, false>"
-GDN_DECODE = "kda::decode_step_kernel<128, 128, true, true>"
+KDA_DECODE = "kda::decode_step_kernel<128, 128, true, 0>"
+GDN_DECODE = "kda::decode_step_kernel<128, 128, true, 1>"
+LAYER_INTRA = "kda::intra_wide_kernel<2>"
+LAYER_EPILOGUE = "kda::layer_epilogue_kernel"
+LAYER_DECODE = "kda::decode_step_kernel<128, 128, true, 2>"
 LAUNCH_KERNELS = {
     "kda_chunk_fwd": (KDA_INTRA, STATE),
     "kda_decode_step": (KDA_DECODE,),
     "gdn_chunk_fwd": (GDN_INTRA, STATE),
     "gdn_decode_step": (GDN_DECODE,),
+    "kda_layer_chunk_fwd": (LAYER_INTRA, STATE, LAYER_EPILOGUE),
+    "kda_layer_decode_step": (LAYER_DECODE,),
 }
 
 
@@ -354,6 +369,31 @@ def main():
 
     warm(gdn_prefill, gdn_decode)
     g_pre_ms, g_dec_ms = timed(gdn_prefill, gdn_decode)
+    del gdn_la, gdn_dla
+
+    # ---- the KDA layer: raw bf16 projections in, prologue and epilogue fused ----
+    lg = torch.Generator(device=dev)
+    lg.manual_seed(3)
+    bfn = lambda shape, shift=0.0: (torch.randn(shape, generator=lg, device=dev) + shift).to(torch.bfloat16)
+    l_xa = bfn((1, T, H, Dk), w.shift)
+    l_xb = bfn((1, T, H))
+    l_g = bfn((1, T, H, Dv))
+    l_w = 0.5 + torch.rand((Dv,), generator=lg, device=dev)
+    ld_xa = bfn((dsteps, dw.N, dw.H, dw.Dk), dw.shift)
+    ld_xb = bfn((dsteps, dw.N, dw.H))
+    ld_g = bfn((dsteps, dw.N, dw.H, dw.Dv))
+    lstate = state0.clone()
+
+    def layer_prefill():
+        kda.layer_chunk_fwd(pin["q"], pin["k"], pin["v"], l_xa, l_xb, l_g, l_w, 1e-6, 1e-5,
+                            out=o, final_state=fs, workspace=ws)
+
+    def layer_decode(t):
+        kda.layer_decode_step(din["q"][t], din["k"][t], din["v"][t], ld_xa[t], ld_xb[t], ld_g[t], l_w,
+                              lstate, 1e-6, 1e-5, out=od)
+
+    warm(layer_prefill, layer_decode)
+    l_pre_ms, l_dec_ms = timed(layer_prefill, layer_decode)
 
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
@@ -371,6 +411,13 @@ def main():
     g_t_dec = sum(g_dec_ms) / len(g_dec_ms) / 1e3
     g_pb = prefill_alg_bytes(T, H, Dk, Dv, N, gate_per_head=1)
     g_db = decode_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv, gate_per_head=1)
+
+    l_pre_ms.sort()
+    l_dec_sorted = sorted(l_dec_ms)
+    l_t_pre = sum(l_pre_ms) / len(l_pre_ms) / 1e3
+    l_t_dec = sum(l_dec_ms) / len(l_dec_ms) / 1e3
+    l_pb = layer_alg_bytes(T, H, Dk, Dv, N)
+    l_db = layer_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv, dw.N, decode=True)  # one token per sequence
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128, T=1M) + decode step HBM GB/s, 1 MI355X",
@@ -408,7 +455,7 @@ def main():
             "alg_bytes_per_step": db,
         },
         "roofline": {
-            "kernel": "kda_chunk_fwd (intra_wide_kernel<false> + state_kernel<64,128,128,bf16>)",
+            "kernel": "kda_chunk_fwd (intra_wide_kernel<0> + state_kernel<64,128,128,bf16>)",
             "bound": "hbm",
             "achieved": pb / t_pre / 1e9,
             "peak": HBM_PEAK / 1e9,
@@ -417,7 +464,7 @@ def main():
             "traffic": measured_traffic("kda_chunk_fwd"),
         },
         "decode_roofline": {
-            "kernel": "decode_step_kernel<128,128,bf16,false>",
+            "kernel": "decode_step_kernel<128,128,bf16,0>",
             "bound": "hbm",
             "achieved": dec_gbs,
             "peak": HBM_PEAK / 1e9,
@@ -437,7 +484,7 @@ def main():
             "hbm_frac_algorithmic": g_pb / g_t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / g_t_pre / BF16_PEAK,
             "alg_bytes": g_pb, "alg_flops": pf,
-            "roofline": {"kernel": "gdn_chunk_fwd (intra_wide_kernel<true> + state_kernel)",
+            "roofline": {"kernel": "gdn_chunk_fwd (intra_wide_kernel<1> + state_kernel)",
                          "bound": "hbm", "achieved": g_pb / g_t_pre / 1e9,
                          "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                          "frac": g_pb / g_t_pre / HBM_PEAK,
@@ -450,6 +497,33 @@ def main():
             "hbm_frac": g_db / g_t_dec / HBM_PEAK,
             "alg_bytes_per_step": g_db,
             "traffic": measured_traffic("gdn_decode_step"),
+        },
+    }
+
+    result["layer"] = {
+        "workload": "KDA layer (kda_layer_chunk_fwd / kda_layer_decode_step): bf16 q, k, v as "
+                    "above taken as raw projections, x_alpha ~ N(0,1)+3, x_beta, output gate ~ "
+                    "N(0,1) bf16, RMSNorm weight U[0.5,1.5]; prologue (L2Norm, -softplus, sigmoid) "
+                    "and epilogue (RMSNorm x weight x sigmoid gate) fused",
+        "prefill": {
+            "ms_mean": l_t_pre * 1e3, "ms_median": l_pre_ms[len(l_pre_ms) // 2],
+            "tokens_per_s": T / l_t_pre,
+            "hbm_frac_algorithmic": l_pb / l_t_pre / HBM_PEAK,
+            "alg_bytes": l_pb,
+            "roofline": {"kernel": "kda_layer_chunk_fwd (intra_wide_kernel<2> + state_kernel + "
+                                   "layer_epilogue_kernel)",
+                         "bound": "hbm", "achieved": l_pb / l_t_pre / 1e9,
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": l_pb / l_t_pre / HBM_PEAK,
+                         "traffic": measured_traffic("kda_layer_chunk_fwd")},
+        },
+        "decode": {
+            "us_per_step_mean": l_t_dec * 1e6,
+            "us_per_step_median": l_dec_sorted[len(l_dec_sorted) // 2] * 1e3,
+            "GB_per_s": l_db / l_t_dec / 1e9,
+            "hbm_frac": l_db / l_t_dec / HBM_PEAK,
+            "alg_bytes_per_step": l_db,
+            "traffic": measured_traffic("kda_layer_decode_step"),
         },
     }
 

@@ -24,8 +24,6 @@ bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
 };
@@ -52,6 +50,26 @@ bool bytes_of(size_t &out, std::initializer_list<uint64_t> dims, size_t elem) {
     return true;
 }
 
+// One device buffer the call reads: its bytes and the alignment its loads need.
+struct Input {
+    const void *p;
+    const char *name;
+    size_t bytes;
+    unsigned align;
+    bool required;
+};
+
+bool aligned(const void *p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The KDA layer's extra arguments (gate mode 2).
+struct LayerIn {
+    const void *x_alpha, *x_beta, *out_gate;
+    const float *norm_weight;
+    float l2_eps, norm_eps;
+};
+
+bool eps_ok(float e) { return e >= 0.f && e <= 3.0e38f; }  // rejects NaN, inf and negatives
+
 }  // namespace
 
 extern "C" {
@@ -74,44 +92,75 @@ int kda_version(void) { return KDA_VERSION; }
 static kda_status decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                               const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                               int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream,
-                              bool scalar_gate) {
+                              int gate_mode, const LayerIn *L) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
+    if (gate_mode == 2 && in_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "the layer entry points take bf16 inputs");
     if (!supported_dim(Dk) || !supported_dim(Dv))
         return fail(KDA_ERR_UNSUPPORTED, "Dk=%d Dv=%d: each must be 16, 32, 64 or 128", Dk, Dv);
     if (N < 0 || H < 1) return fail(KDA_ERR_INVALID_ARG, "N=%d H=%d: need N >= 0, H >= 1", N, H);
     if ((int64_t)N * H > 0x7fffffff)
         return fail(KDA_ERR_INVALID_ARG, "N*H=%lld exceeds the grid limit", (long long)N * H);
+    if (gate_mode == 2 && (!eps_ok(L->l2_eps) || !eps_ok(L->norm_eps)))
+        return fail(KDA_ERR_INVALID_ARG, "l2_eps and norm_eps must be finite and >= 0");
     if (N == 0) return KDA_OK;
-    const void *ptrs[] = {q, k, v, log_alpha, beta, state, o};
-    const char *names[] = {"q", "k", "v", "log_alpha", "beta", "state", "o"};
-    for (int i = 0; i < 7; ++i) {
-        if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", names[i]);
-        // beta and a scalar gate are read element by element
-        const bool scalar = i == 4 || (i == 3 && scalar_gate);
-        if (scalar ? !aligned4(ptrs[i]) : !aligned16(ptrs[i]))
-            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", names[i], scalar ? 4 : 16);
-    }
     const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
-    size_t bq, bv, bg, bb, bs, bo;
+    size_t bq, bv, bg, bb, bs, bo, bxa, bxb, bog;
     if (!bytes_of(bq, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk}, esz) ||
         !bytes_of(bv, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, esz) ||
-        !bytes_of(bg, {(uint64_t)N, (uint64_t)H, scalar_gate ? 1u : (uint64_t)Dk}, 4) ||
+        !bytes_of(bg, {(uint64_t)N, (uint64_t)H, gate_mode == 1 ? 1u : (uint64_t)Dk}, 4) ||
         !bytes_of(bb, {(uint64_t)N, (uint64_t)H}, 4) ||
         !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
-        !bytes_of(bo, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, 4))
+        !bytes_of(bo, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, 4) ||
+        !bytes_of(bxa, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk}, 2) ||
+        !bytes_of(bxb, {(uint64_t)N, (uint64_t)H}, 2) ||
+        !bytes_of(bog, {(uint64_t)N, (uint64_t)H, (uint64_t)Dv}, 2))
         return fail(KDA_ERR_INVALID_ARG, "tensor sizes overflow size_t");
+    Input in[8];
+    int n_in = 0;
+    in[n_in++] = {q, "q", bq, 16, true};
+    in[n_in++] = {k, "k", bq, 16, true};
+    in[n_in++] = {v, "v", bv, 16, true};
+    if (gate_mode == 2) {
+        in[n_in++] = {L->x_alpha, "x_alpha", bxa, 2, true};
+        in[n_in++] = {L->x_beta, "x_beta", bxb, 2, true};
+        in[n_in++] = {L->out_gate, "out_gate", bog, 2, true};
+        in[n_in++] = {L->norm_weight, "norm_weight", (size_t)Dv * 4, 16, true};
+    } else {
+        // a per-channel gate is read in 16-byte vectors; a scalar gate and beta one by one
+        in[n_in++] = {log_alpha, "log_alpha", bg, gate_mode == 1 ? 4u : 16u, true};
+        in[n_in++] = {beta, "beta", bb, 4, true};
+    }
+    for (int i = 0; i < n_in; ++i) {
+        if (!in[i].p) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", in[i].name);
+        if (!aligned(in[i].p, in[i].align))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %u-byte aligned", in[i].name, in[i].align);
+    }
+    if (!state) return fail(KDA_ERR_INVALID_ARG, "state is NULL");
+    if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARG, "state is not 16-byte aligned");
+    if (!o) return fail(KDA_ERR_INVALID_ARG, "o is NULL");
+    if (!aligned16(o)) return fail(KDA_ERR_INVALID_ARG, "o is not 16-byte aligned");
     const Range ro = span(o, bo), rs = span(state, bs);
-    const Range ins[] = {span(q, bq), span(k, bq), span(v, bv), span(log_alpha, bg), span(beta, bb)};
-    const char *in_names[] = {"q", "k", "v", "log_alpha", "beta"};
-    for (int i = 0; i < 5; ++i) {
-        if (overlap(ro, ins[i])) return fail(KDA_ERR_INVALID_ARG, "o overlaps %s", in_names[i]);
-        if (overlap(rs, ins[i])) return fail(KDA_ERR_INVALID_ARG, "state overlaps %s", in_names[i]);
+    for (int i = 0; i < n_in; ++i) {
+        const Range ri = span(in[i].p, in[i].bytes);
+        if (overlap(ro, ri)) return fail(KDA_ERR_INVALID_ARG, "o overlaps %s", in[i].name);
+        if (overlap(rs, ri)) return fail(KDA_ERR_INVALID_ARG, "state overlaps %s", in[i].name);
     }
     if (overlap(ro, rs)) return fail(KDA_ERR_INVALID_ARG, "o overlaps state");
 
-    kda::DecodeArgs a{q, k, v, log_alpha, beta, state, o, N, H, Dk, Dv, in_dtype == KDA_BF16, scalar_gate};
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.state = state; a.o = o;
+    a.N = N; a.H = H; a.Dk = Dk; a.Dv = Dv; a.bf16 = in_dtype == KDA_BF16; a.gate_mode = gate_mode;
+    if (gate_mode == 2) {
+        a.x_alpha = static_cast<const uint16_t *>(L->x_alpha);
+        a.x_beta = static_cast<const uint16_t *>(L->x_beta);
+        a.out_gate = static_cast<const uint16_t *>(L->out_gate);
+        a.norm_weight = L->norm_weight;
+        a.l2_eps = L->l2_eps;
+        a.norm_eps = L->norm_eps;
+    }
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
@@ -120,13 +169,13 @@ static kda_status decode_impl(const void *q, const void *k, const void *v, const
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                            const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
-    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, false);
+    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, 0, nullptr);
 }
 
 kda_status gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                            const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
-    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, true);
+    return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, 1, nullptr);
 }
 
 static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
@@ -167,7 +216,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                                  const float *beta, const float *init_state, const int32_t *cu_seqlens,
                                  int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                                  kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
-                                 void *workspace, size_t ws_bytes, hipStream_t stream, bool scalar_gate) {
+                                 void *workspace, size_t ws_bytes, hipStream_t stream, int gate_mode,
+                                 const LayerIn *L) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -178,6 +228,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: must be 16, 32 or 64", chunk_size);
     chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
+    if (gate_mode == 2 && (in_dtype != KDA_BF16 || Dk != 128 || chunk_size != 64))
+        return fail(KDA_ERR_UNSUPPORTED, "the layer prefill runs bf16 inputs at Dk = Dv = 128 in 64-token chunks");
     if (B < 1 || T < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARG, "B=%d T=%lld H=%d: need B >= 1, T >= 0, H >= 1", B,
                     (long long)T, H);
@@ -189,24 +241,50 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     const int32_t N = varlen ? n_seqs : B;
     if ((int64_t)N * H > 0x7fffffff || T > ((int64_t)1 << 40))
         return fail(KDA_ERR_INVALID_ARG, "sizes exceed the supported range");
+    if (gate_mode == 2 && (!eps_ok(L->l2_eps) || !eps_ok(L->norm_eps)))
+        return fail(KDA_ERR_INVALID_ARG, "l2_eps and norm_eps must be finite and >= 0");
     if (N == 0) return KDA_OK;
-    const void *need[] = {q, k, v, log_alpha, beta, o};
-    const char *nn[] = {"q", "k", "v", "log_alpha", "beta", "o"};
-    for (int i = 0; i < 6; ++i) {
-        if (!need[i] && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", nn[i]);
-        // beta and a scalar gate are read element by element
-        const bool scalar = i == 4 || (i == 3 && scalar_gate);
-        if (need[i] && (scalar ? !aligned4(need[i]) : !aligned16(need[i])))
-            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", nn[i], scalar ? 4 : 16);
-    }
-    const void *opt[] = {init_state, cu_seqlens, final_state};
-    const char *on[] = {"init_state", "cu_seqlens", "final_state"};
-    for (int i = 0; i < 3; ++i) {
-        const bool scalar = i == 1;  // cu_seqlens: int32 offsets
-        if (opt[i] && (scalar ? !aligned4(opt[i]) : !aligned16(opt[i])))
-            return fail(KDA_ERR_INVALID_ARG, "%s is not %d-byte aligned", on[i], scalar ? 4 : 16);
-    }
     const bool bf16 = in_dtype == KDA_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    size_t bq, bv, bg, bb, bs, bo, bc, bxa, bxb, bog;
+    if (!bytes_of(bq, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, esz) ||
+        !bytes_of(bv, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, esz) ||
+        !bytes_of(bg, {(uint64_t)B, (uint64_t)T, (uint64_t)H, gate_mode == 1 ? 1u : (uint64_t)Dk}, 4) ||
+        !bytes_of(bb, {(uint64_t)B, (uint64_t)T, (uint64_t)H}, 4) ||
+        !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
+        !bytes_of(bo, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, 4) ||
+        !bytes_of(bxa, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, 2) ||
+        !bytes_of(bxb, {(uint64_t)B, (uint64_t)T, (uint64_t)H}, 2) ||
+        !bytes_of(bog, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, 2))
+        return fail(KDA_ERR_INVALID_ARG, "tensor sizes overflow size_t");
+    bc = varlen ? ((size_t)N + 1) * 4 : 0;
+    // inputs in checking order; init_state stays last (final_state may alias it)
+    Input in[10];
+    int n_in = 0;
+    in[n_in++] = {q, "q", bq, 16, true};
+    in[n_in++] = {k, "k", bq, 16, true};
+    in[n_in++] = {v, "v", bv, 16, true};
+    if (gate_mode == 2) {
+        in[n_in++] = {L->x_alpha, "x_alpha", bxa, 16, true};
+        in[n_in++] = {L->x_beta, "x_beta", bxb, 2, true};
+        in[n_in++] = {L->out_gate, "out_gate", bog, 16, true};
+        in[n_in++] = {L->norm_weight, "norm_weight", (size_t)Dv * 4, 16, true};
+    } else {
+        // a per-channel gate is read in 16-byte vectors; a scalar gate and beta one by one
+        in[n_in++] = {log_alpha, "log_alpha", bg, gate_mode == 1 ? 4u : 16u, true};
+        in[n_in++] = {beta, "beta", bb, 4, true};
+    }
+    in[n_in++] = {cu_seqlens, "cu_seqlens", bc, 4, false};
+    in[n_in++] = {init_state, "init_state", init_state ? bs : 0, 16, false};
+    for (int i = 0; i < n_in; ++i) {
+        if (in[i].required && !in[i].p && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", in[i].name);
+        if (in[i].p && !aligned(in[i].p, in[i].align))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %u-byte aligned", in[i].name, in[i].align);
+    }
+    if (!o && T > 0) return fail(KDA_ERR_INVALID_ARG, "o is NULL");
+    if (o && !aligned16(o)) return fail(KDA_ERR_INVALID_ARG, "o is not 16-byte aligned");
+    if (final_state && !aligned16(final_state))
+        return fail(KDA_ERR_INVALID_ARG, "final_state is not 16-byte aligned");
     size_t need_ws = 0, pkg = 0;
     int64_t slots = 0;
     if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots))
@@ -216,30 +294,18 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                     workspace, need_ws);
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    const size_t esz = bf16 ? 2 : 4;
-    size_t bq, bv, bg, bb, bs, bo, bc;
-    if (!bytes_of(bq, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, esz) ||
-        !bytes_of(bv, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, esz) ||
-        !bytes_of(bg, {(uint64_t)B, (uint64_t)T, (uint64_t)H, scalar_gate ? 1u : (uint64_t)Dk}, 4) ||
-        !bytes_of(bb, {(uint64_t)B, (uint64_t)T, (uint64_t)H}, 4) ||
-        !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
-        !bytes_of(bo, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dv}, 4))
-        return fail(KDA_ERR_INVALID_ARG, "tensor sizes overflow size_t");
-    bc = varlen ? ((size_t)N + 1) * 4 : 0;
     const Range ro = span(o, bo), rws = span(workspace, need_ws);
-    const Range rin[] = {span(q, bq), span(k, bq), span(v, bv), span(log_alpha, bg),
-                         span(beta, bb), span(init_state, init_state ? bs : 0),
-                         span(cu_seqlens, bc)};
-    const char *in_n[] = {"q", "k", "v", "log_alpha", "beta", "init_state", "cu_seqlens"};
     const Range rfs = span(final_state, final_state ? bs : 0);
-    for (int i = 0; i < 7; ++i) {
-        if (overlap(ro, rin[i])) return fail(KDA_ERR_INVALID_ARG, "o overlaps %s", in_n[i]);
-        if (overlap(rws, rin[i])) return fail(KDA_ERR_INVALID_ARG, "workspace overlaps %s", in_n[i]);
+    const Range rinit = span(init_state, init_state ? bs : 0);
+    for (int i = 0; i < n_in; ++i) {
+        const Range ri = span(in[i].p, in[i].bytes);
+        if (overlap(ro, ri)) return fail(KDA_ERR_INVALID_ARG, "o overlaps %s", in[i].name);
+        if (overlap(rws, ri)) return fail(KDA_ERR_INVALID_ARG, "workspace overlaps %s", in[i].name);
         // final_state may alias init_state exactly (continuing a sequence), nothing else
-        if (i != 5 && overlap(rfs, rin[i]))
-            return fail(KDA_ERR_INVALID_ARG, "final_state overlaps %s", in_n[i]);
+        if (in[i].p != init_state && overlap(rfs, ri))
+            return fail(KDA_ERR_INVALID_ARG, "final_state overlaps %s", in[i].name);
     }
-    if (final_state && init_state && overlap(rfs, rin[5]) && final_state != init_state)
+    if (final_state && init_state && overlap(rfs, rinit) && final_state != init_state)
         return fail(KDA_ERR_INVALID_ARG, "final_state partially overlaps init_state");
     if (overlap(ro, rws) || overlap(ro, rfs) || overlap(rws, rfs))
         return fail(KDA_ERR_INVALID_ARG, "o, final_state and workspace must not overlap");
@@ -248,7 +314,15 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.init_state = init_state; a.cu_seqlens = cu_seqlens;
     a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.N = N; a.C = chunk_size; a.T = T;
-    a.bf16 = bf16; a.scalar_gate = scalar_gate; a.o = o; a.final_state = final_state;
+    a.bf16 = bf16; a.gate_mode = gate_mode; a.o = o; a.final_state = final_state;
+    if (gate_mode == 2) {
+        a.x_alpha = static_cast<const uint16_t *>(L->x_alpha);
+        a.x_beta = static_cast<const uint16_t *>(L->x_beta);
+        a.out_gate = static_cast<const uint16_t *>(L->out_gate);
+        a.norm_weight = L->norm_weight;
+        a.l2_eps = L->l2_eps;
+        a.norm_eps = L->norm_eps;
+    }
     a.workspace = static_cast<char *>(workspace);
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
@@ -264,7 +338,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                          void *workspace, size_t ws_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
-                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, false);
+                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, 0, nullptr);
 }
 
 kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -273,7 +347,26 @@ kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                          void *workspace, size_t ws_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
-                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, true);
+                          in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, 1, nullptr);
+}
+
+kda_status kda_layer_chunk_fwd(const void *q, const void *k, const void *v, const void *x_alpha,
+                               const void *x_beta, const void *out_gate, const float *norm_weight,
+                               float l2_eps, float norm_eps, const float *init_state,
+                               const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t Dk,
+                               int32_t Dv, int32_t n_seqs, float *o, float *final_state, void *workspace,
+                               size_t ws_bytes, hipStream_t stream) {
+    const LayerIn L{x_alpha, x_beta, out_gate, norm_weight, l2_eps, norm_eps};
+    return chunk_fwd_impl(q, k, v, nullptr, nullptr, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
+                          KDA_BF16, 64, o, final_state, workspace, ws_bytes, stream, 2, &L);
+}
+
+kda_status kda_layer_decode_step(const void *q, const void *k, const void *v, const void *x_alpha,
+                                 const void *x_beta, const void *out_gate, const float *norm_weight,
+                                 float l2_eps, float norm_eps, float *state, int32_t N, int32_t H,
+                                 int32_t Dk, int32_t Dv, float *o, hipStream_t stream) {
+    const LayerIn L{x_alpha, x_beta, out_gate, norm_weight, l2_eps, norm_eps};
+    return decode_impl(q, k, v, nullptr, nullptr, state, N, H, Dk, Dv, KDA_BF16, o, stream, 2, &L);
 }
 
 }  // extern "C"

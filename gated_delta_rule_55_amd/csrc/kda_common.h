@@ -13,6 +13,7 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Raw bfloat16 bits -> fp32 (exact).
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -30,5 +31,13 @@ __device__ __forceinline__ float load_in(const void *p, int64_t i) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// -softplus(x) = -(max(x, 0) + log(1 + e^-|x|)), natural log; +inf -> -inf, -inf -> 0
+__device__ __forceinline__ float neg_softplus(float x) {
+    return -(fmaxf(x, 0.f) + kLn2 * __log2f(1.f + fast_exp2(-fabsf(x) * kLog2e)));
+}
+
+// 1 / (1 + e^-x); -inf -> 0, +inf -> 1
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
 
 }  // namespace kda

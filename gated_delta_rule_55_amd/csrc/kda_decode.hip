@@ -28,55 +28,87 @@ namespace kda {
 
 constexpr int kDecodeThreads = 512;
 
-// SG: one scalar gate per (n, h) (log_alpha [N, H]) instead of one per key
-// channel (log_alpha [N, H, Dk]).
-template <int DK, int DV, bool kBf16, bool SG>
-__global__ void __launch_bounds__(kDecodeThreads)
-decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
-                   const void *__restrict__ v, const float *__restrict__ log_alpha,
-                   const float *__restrict__ beta, float *__restrict__ state,
-                   float *__restrict__ o) {
+// Gate modes: 0 KDA (log_alpha [N, H, Dk]); 1 Gated DeltaNet (one log_alpha per
+// (n, h), [N, H]); 2 KDA layer: q and k arrive unnormalised and are divided by
+// sqrt(|x|^2 + l2_eps), alpha = exp(-softplus(x_alpha)), beta = sigmoid(x_beta)
+// from bf16 projections, and the output is o / sqrt(mean o^2 + norm_eps) * w *
+// sigmoid(g) (the KDA-layer item of the page's model-architecture list).
+template <int DK, int DV, bool kBf16, int GM>
+__global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs a) {
     constexpr int CG = DV / 4;                                  // float4 column groups
     constexpr int NT = (DK * DV / 4 < kDecodeThreads) ? DK * DV / 4 : kDecodeThreads;  // threads
     constexpr int RG = NT / CG;                                 // row groups
     constexpr int RPT = DK / RG;                                // rows per thread
     constexpr int NW = (NT + kWave - 1) / kWave;                // waves holding rows
+    constexpr int NWK = (DK + kWave - 1) / kWave;               // waves holding a key channel
     static_assert(CG <= kWave && kWave % CG == 0, "column groups must tile a wave");
     static_assert(RG * RPT == DK, "rows must tile the state");
+    static_assert(NT >= DK, "one thread per key channel");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ f32x4 s_red[NW][CG][2];
     __shared__ float s_kq[NW][CG];
+    __shared__ float s_nrm[NWK][2];
 
     const int t = threadIdx.x;
     const int64_t unit = blockIdx.x;  // n * H + h
     const int cg = t % CG;
     const int rg = t / CG;
-    f32x4 *S = reinterpret_cast<f32x4 *>(state + unit * DK * DV);
+    const int w = t / kWave, lane = t % kWave;
+    f32x4 *S = reinterpret_cast<f32x4 *>(a.state + unit * DK * DV);
 
     // the state stream is issued first; the token's vectors load under it
     f32x4 sv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
-    const float b = beta[unit];
+    const float b = GM == 2 ? sigmoid_f(bf16_bits_to_f32(a.x_beta[unit])) : a.beta[unit];
     f32x4 vv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(v, unit * DV + 4 * cg + e);
-    for (int c = t; c < DK; c += blockDim.x) {
-        s_k[c] = load_in<kBf16>(k, unit * DK + c);
-        s_q[c] = load_in<kBf16>(q, unit * DK + c);
-        const float g = SG ? log_alpha[unit] : log_alpha[unit * DK + c];
-        s_a[c] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
+    for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(a.v, unit * DV + 4 * cg + e);
+    float kk = 0.f, qq = 0.f;
+    if (t < DK) {
+        const float kc = load_in<kBf16>(a.k, unit * DK + t), qc = load_in<kBf16>(a.q, unit * DK + t);
+        s_k[t] = kc;
+        s_q[t] = qc;
+        kk = kc * kc;
+        qq = qc * qc;
+        float g;
+        if constexpr (GM == 2) g = neg_softplus(bf16_bits_to_f32(a.x_alpha[unit * DK + t]));
+        else if constexpr (GM == 1) g = a.log_alpha[unit];
+        else g = a.log_alpha[unit * DK + t];
+        s_a[t] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
+    }
+    if constexpr (GM == 2) {
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
+        if (lane == 0 && w < NWK) {
+            s_nrm[w][0] = kk;
+            s_nrm[w][1] = qq;
+        }
     }
     __syncthreads();
+    float rk = 1.f, rq = 1.f;  // 1 / |k|, 1 / |q| (gate mode 2)
+    if constexpr (GM == 2) {
+        float nk = 0.f, nq = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NWK; ++ww) {
+            nk += s_nrm[ww][0];
+            nq += s_nrm[ww][1];
+        }
+        rk = 1.f / sqrtf(nk + a.l2_eps);
+        rq = 1.f / sqrtf(nq + a.l2_eps);
+    }
 
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
-        const float a = s_a[row], kr = s_k[row], qr = s_q[row];
-        sv[i] *= a;
+        const float al = s_a[row], kr = s_k[row] * rk, qr = s_q[row] * rq;
+        sv[i] *= al;
         p += sv[i] * kr;
         r += sv[i] * qr;
         kq += kr * qr;
@@ -92,7 +124,6 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
         }
         kq += __shfl_xor(kq, off);
     }
-    const int w = t / kWave, lane = t % kWave;
     if (lane < CG) {
         s_red[w][lane][0] = p;
         s_red[w][lane][1] = r;
@@ -112,21 +143,41 @@ decode_step_kernel(const void *__restrict__ q, const void *__restrict__ k,
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
-        __builtin_nontemporal_store(sv[i] + s_k[row] * u, &S[row * CG + cg]);
+        __builtin_nontemporal_store(sv[i] + (s_k[row] * rk) * u, &S[row * CG + cg]);
     }
-    if (rg == 0) reinterpret_cast<f32x4 *>(o + unit * DV)[cg] = r + kq * u;
+    if (rg == 0) {
+        f32x4 ot = r + kq * u;
+        if constexpr (GM == 2) {
+            // RMSNorm over the DV columns held by lanes 0 .. CG-1 of wave 0
+            float ss = ot[0] * ot[0] + ot[1] * ot[1] + ot[2] * ot[2] + ot[3] * ot[3];
+#pragma unroll
+            for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off);
+            const float sc = 1.f / sqrtf(ss / DV + a.norm_eps);
+            const f32x4 wv = reinterpret_cast<const f32x4 *>(a.norm_weight)[cg];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ot[e] = ot[e] * sc * wv[e] * sigmoid_f(bf16_bits_to_f32(a.out_gate[unit * DV + 4 * cg + e]));
+        }
+        reinterpret_cast<f32x4 *>(a.o + unit * DV)[cg] = ot;
+    }
 }
 
 template <int DK, int DV, bool kBf16>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     constexpr int NT = (DK * DV / 4 < kDecodeThreads) ? DK * DV / 4 : kDecodeThreads;
     const dim3 grid(static_cast<unsigned>(a.N * a.H));
-    if (a.scalar_gate)
-        hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, true>), grid, dim3(NT), 0, stream, a.q,
-                           a.k, a.v, a.log_alpha, a.beta, a.state, a.o);
-    else
-        hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, false>), grid, dim3(NT), 0, stream, a.q,
-                           a.k, a.v, a.log_alpha, a.beta, a.state, a.o);
+    switch (a.gate_mode) {
+        case 0: hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 0>), grid, dim3(NT), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 1>), grid, dim3(NT), 0, stream, a); break;
+        case 2:
+            if constexpr (kBf16) {
+                hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 2>), grid, dim3(NT), 0, stream, a);
+                break;
+            } else {
+                return hipErrorInvalidValue;  // the layer's projections are bf16
+            }
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

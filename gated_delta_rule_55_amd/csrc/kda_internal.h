@@ -14,7 +14,12 @@ struct DecodeArgs {
     float *state, *o;
     int32_t N, H, Dk, Dv;
     bool bf16;
-    bool scalar_gate;  // log_alpha [N, H] (GDN) instead of [N, H, Dk] (KDA)
+    int32_t gate_mode;  // 0 KDA, 1 GDN (log_alpha [N, H]), 2 KDA layer (below)
+    // gate mode 2: q, k unnormalised; bf16 x_alpha [N, H, Dk], x_beta [N, H],
+    // output gate [N, H, Dv]; RMSNorm weight [Dv]
+    const uint16_t *x_alpha, *x_beta, *out_gate;
+    const float *norm_weight;
+    float l2_eps, norm_eps;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -65,7 +70,12 @@ struct PrefillArgs {
     int32_t B, H, Dk, Dv, N, C;
     int64_t T;
     bool bf16;
-    bool scalar_gate;           // log_alpha [B, T, H] (GDN) instead of [B, T, H, Dk] (KDA)
+    int32_t gate_mode;          // 0 KDA, 1 GDN (log_alpha [B, T, H]), 2 KDA layer (below)
+    // gate mode 2: q, k unnormalised; bf16 x_alpha [B, T, H, Dk], x_beta [B, T, H],
+    // output gate [B, T, H, Dv]; RMSNorm weight [Dv]
+    const uint16_t *x_alpha, *x_beta, *out_gate;
+    const float *norm_weight;
+    float l2_eps, norm_eps;
     float *o, *final_state;     // final_state nullable
     char *workspace;
     int64_t n_slots;            // chunk slots in the workspace
@@ -80,6 +90,11 @@ inline int64_t prefill_slots(int32_t B, int64_t T, int32_t N, int32_t C, bool va
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// o <- o / sqrt(mean_j o_j^2 + eps) * w * sigmoid(g) over each row of Dv = 128
+// values, in place (the KDA layer's epilogue), rows = B * T * H.
+hipError_t launch_layer_epilogue(float *o, const uint16_t *g, const float *w, int64_t rows, float eps,
+                                 hipStream_t stream);
 
 // Chunk size the kernels use for a requested one (the fp32 path at d = 128 is
 // limited to 32 tokens by LDS capacity).  Results do not depend on it beyond

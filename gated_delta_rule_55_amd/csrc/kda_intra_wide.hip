@@ -116,13 +116,21 @@ __device__ __forceinline__ f32x4 gram_bf16x3(const float (&x)[8], const bf16x8 &
 // zeroed when the item is unpacked, so no wait sits between the loads.
 struct WideRaw {
     uint32_t k[4][4], q[4][4], v[4][4];
-    float la[4][8];
+    float la[4][8];     // log_alpha (gate modes 0 and 1)
     float beta[4];
+    uint32_t xa[4][4];  // gate mode 2: x_alpha, bf16 bits
+    uint16_t xb[4];     // gate mode 2: x_beta, bf16 bits
 };
 
-// SG (scalar gate, GDN): one log_alpha per (token, head), broadcast to every
-// channel; otherwise one per key channel.
-template <bool SG>
+// Gate modes of the kernel:
+//   0  KDA: log_alpha [.., Dk] fp32 per key channel, beta fp32
+//   1  Gated DeltaNet: one log_alpha per (token, head), broadcast to every channel
+//   2  KDA layer: q and k arrive unnormalised and are L2-normalised here; the
+//      decay gate log_alpha = -softplus(x_alpha) and beta = sigmoid(x_beta) are
+//      formed from bf16 projections (the KDA-layer item of the page's
+//      model-architecture list: L2Norm on q/k, low-rank channel-wise decay gate)
+
+template <int GM>
 __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, int nvalid, int h, int w, int t16,
                                            int kg, WideRaw &r) {
     const int H = p.H;
@@ -140,7 +148,12 @@ __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, i
         r.k[t][0] = k0.x; r.k[t][1] = k0.y; r.k[t][2] = k1.x; r.k[t][3] = k1.y;
         r.q[t][0] = q0.x; r.q[t][1] = q0.y; r.q[t][2] = q1.x; r.q[t][3] = q1.y;
         r.v[t][0] = v0.x; r.v[t][1] = v0.y; r.v[t][2] = v1.x; r.v[t][3] = v1.y;
-        if constexpr (SG) {
+        if constexpr (GM == 2) {
+            const uint16_t *xab = p.x_alpha + off;
+            const uint2 a0 = *reinterpret_cast<const uint2 *>(xab), a1 = *reinterpret_cast<const uint2 *>(xab + 16);
+            r.xa[t][0] = a0.x; r.xa[t][1] = a0.y; r.xa[t][2] = a1.x; r.xa[t][3] = a1.y;
+            r.xb[t] = p.x_beta[row];
+        } else if constexpr (GM == 1) {
             const float g = p.log_alpha[row];
 #pragma unroll
             for (int e = 0; e < 8; ++e) r.la[t][e] = g;
@@ -153,17 +166,20 @@ __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, i
                 r.la[t][4 + e] = l1[e];
             }
         }
-        r.beta[t] = p.beta[row];
+        if constexpr (GM != 2) r.beta[t] = p.beta[row];
     }
 }
 
-template <bool SG>
+
+
+template <int GM>
 __global__ void __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 intra_wide_kernel(IntraParams p, int64_t n_items) {
     constexpr int C = kWC, NT16 = 4, PARTS = 2, MS = kAS;
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
     __shared__ float sBeta[C];
     __shared__ uint64_t sRst[4];
+    __shared__ float sNrm[GM == 2 ? 4 : 1][2][GM == 2 ? C : 1];  // per-wave sums of k^2, q^2 per token
 
     float(*sA)[kAS] = reinterpret_cast<float(*)[kAS]>(smem);
     float(*sP)[kAS] = reinterpret_cast<float(*)[kAS]>(smem + kWC * kAS * 4);
@@ -182,7 +198,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
     WideRaw raw;
     {
         const int tid = threadIdx.x;
-        fetch_item<SG>(p, tok0, nvalid, static_cast<int>(h0), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
+        fetch_item<GM>(p, tok0, nvalid, static_cast<int>(h0), tid >> 6, tid & 15, (tid & 63) >> 4, raw);
     }
     for (;;) {
         // Lane-dependent addresses and masks are recomputed per item: hoisted out
@@ -208,12 +224,44 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                 qr[t][x] = raw.q[t][x] & m;
                 vr[t][x] = raw.v[t][x] & m;
             }
+            if constexpr (GM == 2) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) G[t][e] = ok ? raw.la[t][e] : 0.f;
-            if (w == 0 && kg == 0) sBeta[i] = ok ? raw.beta[t] : 0.f;
+                for (int e = 0; e < 8; ++e) G[t][e] = ok ? neg_softplus(bf_at(raw.xa[t], e)) : 0.f;
+                const float xbv = __builtin_bit_cast(float, static_cast<uint32_t>(raw.xb[t]) << 16);
+                if (w == 0 && kg == 0) sBeta[i] = ok ? sigmoid_f(xbv) : 0.f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) G[t][e] = ok ? raw.la[t][e] : 0.f;
+                if (w == 0 && kg == 0) sBeta[i] = ok ? raw.beta[t] : 0.f;
+            }
         }
-        auto Kf = [&](int t, int e) { return bf_at(kr[t], e); };
-        auto Qf = [&](int t, int e) { return bf_at(qr[t], e); };
+        if constexpr (GM == 2) {
+            // this wave's share of |k|^2 and |q|^2 per token: 8 channels per lane,
+            // summed over the four lane groups of the wave, then across waves in LDS
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sk += bf_at(kr[t], e) * bf_at(kr[t], e);
+                    sq += bf_at(qr[t], e) * bf_at(qr[t], e);
+                }
+                sk += __shfl_xor(sk, 16);
+                sq += __shfl_xor(sq, 16);
+                sk += __shfl_xor(sk, 32);
+                sq += __shfl_xor(sq, 32);
+                if (kg == 0) {
+                    sNrm[w][0][16 * t + t16] = sk;
+                    sNrm[w][1][16 * t + t16] = sq;
+                }
+            }
+        }
+        // gate mode 2: 1 / |k|, 1 / |q| of this lane's four tokens, applied at every
+        // use in fp32 (rounding the normalised vectors back to bf16 would cost
+        // ~1e-2 of the output's RMS); 1 otherwise
+        float nk[4] = {1.f, 1.f, 1.f, 1.f}, nq[4] = {1.f, 1.f, 1.f, 1.f};
+        auto Kf = [&](int t, int e) { return bf_at(kr[t], e) * nk[t]; };
+        auto Qf = [&](int t, int e) { return bf_at(qr[t], e) * nq[t]; };
 
         // ---- resets: tokens whose log_alpha is -inf on all channels
         {
@@ -229,6 +277,19 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             if (lane == 0) sRst[w] = mine;
         }
         __syncthreads();  // also: every wave is done with the previous item's LDS
+        if constexpr (GM == 2) {
+            // 1 / sqrt(|x|^2 + eps) per token; padding rows are zeros already and
+            // keep a zero scale whatever eps is
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = 16 * t + t16;
+                const bool ok = i < nvalid;
+                nk[t] = ok ? 1.f / sqrtf(sNrm[0][0][i] + sNrm[1][0][i] + sNrm[2][0][i] + sNrm[3][0][i] + p.l2_eps)
+                           : 0.f;
+                nq[t] = ok ? 1.f / sqrtf(sNrm[0][1][i] + sNrm[1][1][i] + sNrm[2][1][i] + sNrm[3][1][i] + p.l2_eps)
+                           : 0.f;
+            }
+        }
         const uint64_t rst = sRst[0] & sRst[1] & sRst[2] & sRst[3];
         const int first_rst = rst ? __builtin_ctzll(rst) : C;  // tokens before it see the incoming state
         const int last_rst = rst ? 63 - __builtin_clzll(rst) : -1;
@@ -611,33 +672,37 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         item = next;
         tok0 = tok0_n;
         nvalid = nvalid_n;
-        fetch_item<SG>(p, tok0, nvalid, static_cast<int>(h_n), w, t16, kg, raw);
+        fetch_item<GM>(p, tok0, nvalid, static_cast<int>(h_n), w, t16, kg, raw);
     }
 }
 
 }  // namespace
 
-template <bool SG>
+template <int GM>
 static hipError_t launch_intra_wide_t(const IntraParams &p, int64_t n_items, hipStream_t stream) {
     static thread_local int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_wide_kernel<SG>, kIntraThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, intra_wide_kernel<GM>, kIntraThreads, 0) !=
                 hipSuccess ||
             nb <= 0)
             nb = 1;
         per_cu = nb;
     }
     const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
-    hipLaunchKernelGGL(intra_wide_kernel<SG>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
+    hipLaunchKernelGGL(intra_wide_kernel<GM>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
                        p, n_items);
     return hipGetLastError();
 }
 
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
     if (n_items <= 0) return hipSuccess;
-    return p.g_ch == 0 ? launch_intra_wide_t<true>(p, n_items, stream)
-                       : launch_intra_wide_t<false>(p, n_items, stream);
+    switch (p.gate_mode) {
+        case 0: return launch_intra_wide_t<0>(p, n_items, stream);
+        case 1: return launch_intra_wide_t<1>(p, n_items, stream);
+        case 2: return launch_intra_wide_t<2>(p, n_items, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace kda

@@ -28,6 +28,10 @@ struct IntraParams {
     // log_alpha[r * g_row + c * g_ch]: (Dk, 1) per-channel gates (KDA),
     // (1, 0) one scalar gate per token and head (GDN)
     int32_t g_row, g_ch;
+    // 0 KDA, 1 GDN, 2 KDA layer (raw q, k; bf16 x_alpha [.., Dk], x_beta [..])
+    int32_t gate_mode;
+    const uint16_t *x_alpha, *x_beta;
+    float l2_eps;
 };
 
 struct StateParams {

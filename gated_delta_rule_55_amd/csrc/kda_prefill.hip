@@ -910,7 +910,8 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     if (a.n_slots > 0) {
         IntraParams ip{a.q, a.k, a.v, a.log_alpha, a.beta, a.cu_seqlens, a.chunk_offsets,
                        a.T, a.H, a.N, a.workspace, a.pkg_bytes, L,
-                       a.scalar_gate ? 1 : DK, a.scalar_gate ? 0 : 1};
+                       a.gate_mode == 1 ? 1 : DK, a.gate_mode == 1 ? 0 : 1,
+                       a.gate_mode, a.x_alpha, a.x_beta, a.l2_eps};
         // persistent: a few workgroups per compute unit walk the (chunk, head)
         // items, each loading the next item's inputs while computing one
         const int64_t n_items = a.n_slots * a.H;
@@ -918,6 +919,7 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
             const hipError_t e = launch_intra_wide(ip, n_items, stream);
             if (e != hipSuccess) return e;
         } else {
+        if (a.gate_mode == 2) return hipErrorInvalidValue;  // the layer runs on the wide kernel only
         static thread_local int per_cu = 0;  // resident workgroups per CU for this instantiation
         if (per_cu == 0) {
             int nb = 0;
@@ -934,6 +936,12 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state,
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
     hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
+    if (a.gate_mode == 2 && a.T > 0) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_layer_epilogue(a.o, a.out_gate, a.norm_weight, static_cast<int64_t>(a.B) * a.T * a.H,
+                                     a.norm_eps, stream);
+    }
     return hipGetLastError();
 }
 

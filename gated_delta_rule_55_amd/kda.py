@@ -44,6 +44,13 @@ def load():
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = lib.kda_decode_step.argtypes
     lib.gdn_decode_step.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.kda_layer_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, fp, f32, f32, fp, ip, i32, i64, i32, i32,
+                                        i32, i32, fp, fp, vp, sz, vp]
+    lib.kda_layer_chunk_fwd.restype = ctypes.c_int
+    lib.kda_layer_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, fp, f32, f32, fp, i32, i32, i32, i32,
+                                          fp, vp]
+    lib.kda_layer_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -140,4 +147,47 @@ def _decode(fn, q, k, v, log_alpha, beta, state, out, stream):
         out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
               _ptr(state), N, H, Dk, Dv, _dtype_code(q), _ptr(out), _stream(stream)))
+    return out
+
+
+def layer_chunk_fwd(q, k, v, x_alpha, x_beta, out_gate, norm_weight, l2_eps=1e-6, norm_eps=1e-5,
+                    init_state=None, cu_seqlens=None, out=None, final_state=None,
+                    output_final_state=True, workspace=None, stream=None):
+    """The KDA layer's prefill: L2Norm(q, k), log_alpha = -softplus(x_alpha),
+    beta = sigmoid(x_beta), the recurrence, then RMSNorm(o) * norm_weight *
+    sigmoid(out_gate).  q, k, x_alpha [B,T,H,128], v, out_gate [B,T,H,128],
+    x_beta [B,T,H], all bf16; norm_weight [128] fp32.  Returns (out fp32, final_state)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = B if cu_seqlens is None else n_seqs
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, KDA_BF16, 64))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.kda_layer_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(x_alpha), _ptr(x_beta),
+                                   _ptr(out_gate), _ptr(norm_weight), float(l2_eps), float(norm_eps),
+                                   _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs,
+                                   _ptr(out), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, final_state
+
+
+def layer_decode_step(q, k, v, x_alpha, x_beta, out_gate, norm_weight, state, l2_eps=1e-6,
+                      norm_eps=1e-5, out=None, stream=None):
+    """One KDA-layer token per (n, h); bf16 q, k, x_alpha [N,H,Dk], v, out_gate
+    [N,H,Dv], x_beta [N,H]; state [N,H,Dk,Dv] fp32 updated in place.  Returns out fp32."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
+    _check(load().kda_layer_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(x_alpha), _ptr(x_beta),
+                                        _ptr(out_gate), _ptr(norm_weight), float(l2_eps),
+                                        float(norm_eps), _ptr(state), N, H, Dk, Dv, _ptr(out),
+                                        _stream(stream)))
     return out

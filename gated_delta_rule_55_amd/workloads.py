@@ -20,6 +20,11 @@ the device):
 * initial states ~ N(0, 0.02^2) in fp32 where the workload has one.
 * gate="scalar" (Gated DeltaNet): log_alpha = -softplus(x + shift) with one
   x ~ N(0, 1) per (token, head) instead of per key channel.
+* KDA layer (make_layer_prefill / make_layer_decode): the layer's raw bf16
+  projections instead -- q, k ~ 3 N(0, 1) unnormalised, v ~ N(0, 1),
+  x_alpha ~ N(0, 1) + shift (so -softplus(x_alpha) has the workload's gate
+  law), x_beta ~ N(0, 1), output gate ~ N(0, 1) -- plus an RMSNorm weight
+  ~ U[0.5, 1.5] [Dv] fp32; resets set x_alpha = +inf.
 * varlen: lengths uniform on [1, 16384], redrawn while a multiple of 64;
   a Bernoulli(0.05) draw per packed token marks a state reset, which sets
   log_alpha = -inf (alpha = 0) on every head and channel of that token.
@@ -179,4 +184,79 @@ def make_decode(name: str = "decode", device="cpu", seed: int = 0, *, N: Optiona
         x = torch.randn((N, H) if gate == "scalar" else (N, H, Dk), generator=g, device=device)
         out["log_alpha"].append(-F.softplus(x + w.shift))
         out["beta"].append(torch.sigmoid(torch.randn((N, H), generator=g, device=device)))
+    return out
+
+
+def _bf16_normal(shape, g, device, scale=1.0, shift=0.0):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return (scale * x + shift).to(torch.bfloat16)
+
+
+def make_layer_prefill(name: str = "prefill", device="cpu", seed: int = 0, *, T: Optional[int] = None,
+                       H: Optional[int] = None, shift: Optional[float] = None,
+                       lengths: Optional[list] = None, init: Optional[str] = None,
+                       reset_p: Optional[float] = None) -> dict:
+    """Raw bf16 projections of the KDA layer for a prefill workload's shapes
+    (d = 128).  Returns q, k, v, x_alpha, x_beta, out_gate, norm_weight,
+    init_state, cu_seqlens, T, N, H."""
+    w = WORKLOADS[name]
+    H = w.H if H is None else H
+    shift = w.shift if shift is None else shift
+    init = w.init if init is None else init
+    reset_p = w.reset_p if reset_p is None else reset_p
+    cu = None
+    if w.varlen or lengths is not None:
+        if lengths is None:
+            lengths = varlen_lengths(w.varlen, w.max_len, w.chunk, seed)
+        offs = [0]
+        for L in lengths:
+            offs.append(offs[-1] + int(L))
+        T = offs[-1]
+        cu = torch.tensor(offs, dtype=torch.int32, device=device)
+        N = len(lengths)
+    else:
+        T = w.T if T is None else T
+        N = w.B
+    B = 1 if cu is not None else w.B
+    g = _gen(device, seed)
+    q = _bf16_normal((B, T, H, w.Dk), g, device, scale=3.0)
+    k = _bf16_normal((B, T, H, w.Dk), g, device, scale=3.0)
+    v = _bf16_normal((B, T, H, w.Dv), g, device)
+    x_alpha = _bf16_normal((B, T, H, w.Dk), g, device, shift=shift)
+    x_beta = _bf16_normal((B, T, H), g, device)
+    out_gate = _bf16_normal((B, T, H, w.Dv), g, device)
+    norm_weight = 0.5 + torch.rand((w.Dv,), generator=g, device=device, dtype=torch.float32)
+    s0 = None
+    if init == "normal":
+        s0 = STATE_STD * torch.randn((N, H, w.Dk, w.Dv), generator=g, device=device,
+                                     dtype=torch.float32)
+    if reset_p > 0.0:
+        mask = torch.rand((T,), generator=g, device=device) < reset_p
+        x_alpha[:, mask] = float("inf")
+    return dict(q=q, k=k, v=v, x_alpha=x_alpha, x_beta=x_beta, out_gate=out_gate,
+                norm_weight=norm_weight, init_state=s0, cu_seqlens=cu, T=T, N=N, H=H, workload=w)
+
+
+def make_layer_decode(name: str = "decode", device="cpu", seed: int = 0, *, N: Optional[int] = None,
+                      H: Optional[int] = None, steps: Optional[int] = None,
+                      D: Optional[int] = None) -> dict:
+    """Initial state and per-step raw bf16 projections of the KDA layer for the
+    decode workload's shapes."""
+    w = WORKLOADS[name]
+    N = w.N if N is None else N
+    H = w.H if H is None else H
+    steps = w.steps if steps is None else steps
+    Dk = Dv = (w.Dk if D is None else D)
+    g = _gen(device, seed)
+    state = STATE_STD * torch.randn((N, H, Dk, Dv), generator=g, device=device, dtype=torch.float32)
+    norm_weight = 0.5 + torch.rand((Dv,), generator=g, device=device, dtype=torch.float32)
+    out = dict(state=state, norm_weight=norm_weight, q=[], k=[], v=[], x_alpha=[], x_beta=[],
+               out_gate=[], N=N, H=H, steps=steps, workload=w)
+    for _ in range(steps):
+        out["q"].append(_bf16_normal((N, H, Dk), g, device, scale=3.0))
+        out["k"].append(_bf16_normal((N, H, Dk), g, device, scale=3.0))
+        out["v"].append(_bf16_normal((N, H, Dv), g, device))
+        out["x_alpha"].append(_bf16_normal((N, H, Dk), g, device, shift=w.shift))
+        out["x_beta"].append(_bf16_normal((N, H), g, device))
+        out["out_gate"].append(_bf16_normal((N, H, Dv), g, device))
     return out

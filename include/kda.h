@@ -169,6 +169,61 @@ kda_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream);
 
+/*
+ * The KDA layer around the operator (the KDA-layer item of the page's
+ * model-architecture list: L2Norm on q/k, a low-rank channel-wise decay gate,
+ * a sigmoid output gate with RMSNorm), fused into the operator's kernels.  The
+ * caller passes the raw bf16 projections; per (token, head) the library forms
+ *
+ *     q = q_raw / sqrt(|q_raw|^2 + l2_eps),  k likewise       (L2Norm)
+ *     log_alpha = -softplus(x_alpha) = -log(1 + exp(x_alpha))  (decay gate)
+ *     beta = sigmoid(x_beta)
+ *
+ * runs the KDA recurrence and readout o_t = S_t^T q_t, and returns
+ *
+ *     out = o / sqrt(mean_j o_j^2 + norm_eps) * norm_weight * sigmoid(out_gate)
+ *
+ * (RMSNorm over the head's Dv values, then the output gate).  The low-rank
+ * projection producing x_alpha (and any bias) is the caller's GEMM; the page
+ * does not name the gate's activation, -softplus is the one taken.  x_alpha =
+ * +inf on every channel of a token resets the state.  The norms are formed in
+ * fp32 and 1/|q|, 1/|k| are applied to the bf16 inputs at every use, so the
+ * normalised vectors are never rounded.  l2_eps = 0 with an all-zero q or k row, or
+ * norm_eps = 0 with an all-zero output row, gives NaN, as the formulas do.
+ *
+ *   q, k        [B, T, H, Dk] bf16   unnormalised queries / keys
+ *   v           [B, T, H, Dv] bf16
+ *   x_alpha     [B, T, H, Dk] bf16   decay-gate pre-activation (16-byte aligned)
+ *   x_beta      [B, T, H]     bf16   beta pre-activation (2-byte aligned)
+ *   out_gate    [B, T, H, Dv] bf16   output-gate pre-activation (16-byte aligned)
+ *   norm_weight [Dv]          fp32   RMSNorm weight shared by all heads
+ *   l2_eps, norm_eps                 finite, >= 0 (else KDA_ERR_INVALID_ARG)
+ *   o           [B, T, H, Dv] fp32   the layer's output before its output projection
+ *
+ * kda_layer_chunk_fwd -- prefill at Dk = Dv = 128 with 64-token chunks (other
+ * sizes return KDA_ERR_UNSUPPORTED).  init_state, cu_seqlens, n_seqs,
+ * final_state, workspace (kda_chunk_fwd_workspace_size(B, T, H, 128, 128,
+ * n_seqs, KDA_BF16, 64) bytes), stream and every convention not stated here
+ * are as for kda_chunk_fwd.
+ */
+kda_status kda_layer_chunk_fwd(const void *q, const void *k, const void *v, const void *x_alpha,
+                               const void *x_beta, const void *out_gate, const float *norm_weight,
+                               float l2_eps, float norm_eps, const float *init_state,
+                               const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t Dk,
+                               int32_t Dv, int32_t n_seqs, float *o, float *final_state, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_layer_decode_step -- one layer token for each of N sequences, the state
+ * updated in place; shapes as above without T ([N, H, ...]; x_beta [N, H],
+ * 2-byte aligned), Dk, Dv in {16, 32, 64, 128}, everything else as for
+ * kda_decode_step.
+ */
+kda_status kda_layer_decode_step(const void *q, const void *k, const void *v, const void *x_alpha,
+                                 const void *x_beta, const void *out_gate, const float *norm_weight,
+                                 float l2_eps, float norm_eps, float *state, int32_t N, int32_t H,
+                                 int32_t Dk, int32_t Dv, float *o, hipStream_t stream);
+
 /* Static name of a status code ("KDA_OK", ...). */
 const char *kda_status_string(kda_status status);
 

@@ -35,7 +35,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
             "kda_status_string", "kda_last_error", "kda_version",
-            "gdn_chunk_fwd", "gdn_decode_step"} <= set(names)
+            "gdn_chunk_fwd", "gdn_decode_step", "kda_layer_chunk_fwd",
+            "kda_layer_decode_step"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
 
@@ -173,3 +174,51 @@ def test_gdn_gate_layout_and_alignment(lib):
     assert b"o overlaps state" in lib.kda_last_error()
     assert _decode(lib, "kda_decode_step", state=FAKE + 0x3000000 + 32) == INVALID
     assert b"state overlaps log_alpha" in lib.kda_last_error()
+
+
+def _layer_chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, xa=FAKE + 0x3000000, xb=FAKE + 0x4000000,
+             g=FAKE + 0x5000000, w=FAKE + 0x6000000, l2=1e-6, ne=1e-5, init_state=None, cu_seqlens=None,
+             B=1, T=64, H=1, Dk=128, Dv=128, n_seqs=0, o=FAKE + 0x7000000, final_state=None,
+             ws=FAKE + 0x8000000, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_layer_chunk_fwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["xa"]), p(a["xb"]), p(a["g"]),
+                                   p(a["w"]), ctypes.c_float(a["l2"]), ctypes.c_float(a["ne"]),
+                                   p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"], a["Dk"],
+                                   a["Dv"], a["n_seqs"], p(a["o"]), p(a["final_state"]), p(a["ws"]),
+                                   a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Dk=64, Dv=64), UNSUPPORTED, b"128"),
+    (dict(l2=-1.0), INVALID, b"eps"),
+    (dict(ne=float("nan")), INVALID, b"eps"),
+    (dict(ne=float("inf")), INVALID, b"eps"),
+    (dict(xa=None), INVALID, b"x_alpha is NULL"),
+    (dict(w=None), INVALID, b"norm_weight is NULL"),
+    (dict(xa=FAKE + 0x3000008), INVALID, b"x_alpha is not 16-byte aligned"),
+    (dict(xb=FAKE + 0x4000001), INVALID, b"x_beta is not 2-byte aligned"),
+    (dict(g=FAKE + 0x5000004), INVALID, b"out_gate is not 16-byte aligned"),
+    (dict(o=FAKE + 0x5000000), INVALID, b"o overlaps out_gate"),
+    (dict(ws=None), WORKSPACE, b"workspace"),
+    (dict(xb=FAKE + 0x4000002, ws=None), WORKSPACE, b"workspace"),  # x_beta: 2-byte alignment suffices
+])
+def test_layer_chunk_rejects(lib, kw, code, msg):
+    assert _layer_chunk(lib, **kw) == code
+    assert msg in lib.kda_last_error()
+
+
+def test_layer_decode_rejects(lib):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(N=4, Dk=128, l2=1e-6, xb=FAKE + 0x4000000, o=FAKE + 0x7000000):
+        return lib.kda_layer_decode_step(p(FAKE), p(FAKE + 0x1000000), p(FAKE + 0x2000000),
+                                         p(FAKE + 0x3000000), p(xb), p(FAKE + 0x5000000),
+                                         p(FAKE + 0x6000000), ctypes.c_float(l2), ctypes.c_float(1e-5),
+                                         p(FAKE + 0x8000000), N, 2, Dk, 128, p(o), None)
+    assert call(Dk=8) == UNSUPPORTED
+    assert call(l2=-0.5) == INVALID
+    assert call(xb=FAKE + 0x4000001) == INVALID and b"x_beta" in lib.kda_last_error()
+    assert call(o=FAKE + 0x8000000) == INVALID and b"o overlaps state" in lib.kda_last_error()
+    assert call(N=0) == OK
