@@ -7,7 +7,9 @@ workload (256 sequences x 32 heads, 128x128 fp32 states).  Inputs are seeded
 synthetic tensors already resident in HBM; outputs and workspaces are
 preallocated.  `value` is prefill tokens/s; the decode step's HBM GB/s is
 reported next to it.  Times come from HIP events on the stream the kernels run
-on.  The fp64 CPU oracle is timed on a bounded sample of the same prefill
+on: W warm-up passes (default 3), then K timed ones (default 10), each prefill
+preceded by a 512 MiB write that flushes L2 and the MALL; reported times are
+medians (means beside them).  The fp64 CPU oracle is timed on a bounded sample of the same prefill
 workload on the host cores (cpu_baseline).
 
 After the timed KDA steps, the Gated DeltaNet (scalar-gate) variant is timed
@@ -40,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12        # MI355X HBM3E bytes/s
 COPY_BYTES = 1 << 31     # size of the calibration copy (read once, written once)
+FLUSH_BYTES = 1 << 29    # cache flush written before each timed prefill (> the 256 MB MALL)
 BF16_PEAK = 2.5e15       # MI355X dense bf16/fp16 matrix flop/s
 
 
@@ -232,6 +235,17 @@ def measured_mfma_busy(launch):
     return {k: kern[k]["mfma_busy_pct"] for k in names if "mfma_busy_pct" in kern.get(k, {})}
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, heads, T_sample, threads):
     import oracle
     sl = lambda x: x[:, :T_sample, heads].detach().to("cpu").double().numpy()
@@ -245,8 +259,8 @@ def cpu_baseline(inp, heads, T_sample, threads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
@@ -330,10 +344,15 @@ def main():
                 decode_fn(t)
         torch.cuda.synchronize()
 
+    # written before each timed prefill so that no input starts in L2 or the
+    # 256 MB MALL (outside the timed region)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
     def timed(prefill_fn, decode_fn):
         """K timed passes: per-call prefill ms and per-step decode ms (HIP events)."""
         pre, dec = [], []
         for _ in range(args.steps):
+            flush.zero_()
             e0, e1 = ev(), ev()
             e0.record(stream)
             prefill_fn()
@@ -397,8 +416,9 @@ def main():
 
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
-    t_pre = sum(pre_ms) / len(pre_ms) / 1e3
-    t_dec = sum(dec_ms) / len(dec_ms) / 1e3
+    # medians of the timed calls and steps (means reported beside them)
+    t_pre = pre_ms[len(pre_ms) // 2] / 1e3
+    t_dec = dec_sorted[len(dec_sorted) // 2] / 1e3
     tok_s = T / t_pre
     pb = prefill_alg_bytes(T, H, Dk, Dv, N)
     pf = prefill_alg_flops(T, H, Dk, Dv, C)
@@ -407,15 +427,15 @@ def main():
 
     g_pre_ms.sort()
     g_dec_sorted = sorted(g_dec_ms)
-    g_t_pre = sum(g_pre_ms) / len(g_pre_ms) / 1e3
-    g_t_dec = sum(g_dec_ms) / len(g_dec_ms) / 1e3
+    g_t_pre = g_pre_ms[len(g_pre_ms) // 2] / 1e3
+    g_t_dec = g_dec_sorted[len(g_dec_sorted) // 2] / 1e3
     g_pb = prefill_alg_bytes(T, H, Dk, Dv, N, gate_per_head=1)
     g_db = decode_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv, gate_per_head=1)
 
     l_pre_ms.sort()
     l_dec_sorted = sorted(l_dec_ms)
-    l_t_pre = sum(l_pre_ms) / len(l_pre_ms) / 1e3
-    l_t_dec = sum(l_dec_ms) / len(l_dec_ms) / 1e3
+    l_t_pre = l_pre_ms[len(l_pre_ms) // 2] / 1e3
+    l_t_dec = l_dec_sorted[len(l_dec_sorted) // 2] / 1e3
     l_pb = layer_alg_bytes(T, H, Dk, Dv, N)
     l_db = layer_alg_bytes(dw.N, dw.H, dw.Dk, dw.Dv, dw.N, decode=True)  # one token per sequence
 
@@ -440,7 +460,7 @@ def main():
             "decode_states": dw.N * dw.H, "decode_steps": dsteps,
         },
         "prefill": {
-            "ms_mean": t_pre * 1e3, "ms_median": pre_ms[len(pre_ms) // 2],
+            "ms_mean": sum(pre_ms) / len(pre_ms), "ms_median": t_pre * 1e3,
             "tokens_per_s": tok_s,
             "hbm_frac_algorithmic": pb / t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / t_pre / BF16_PEAK,
@@ -448,8 +468,8 @@ def main():
             "alg_bytes": pb, "alg_flops": pf,
         },
         "decode": {
-            "us_per_step_mean": t_dec * 1e6,
-            "us_per_step_median": dec_sorted[len(dec_sorted) // 2] * 1e3,
+            "us_per_step_mean": sum(dec_ms) / len(dec_ms) * 1e3,
+            "us_per_step_median": t_dec * 1e6,
             "GB_per_s": dec_gbs,
             "hbm_frac": db / t_dec / HBM_PEAK,
             "alg_bytes_per_step": db,
@@ -479,7 +499,7 @@ def main():
                     "same q/k/v/beta tensors: gdn_chunk_fwd over the 1M-token prefill, then 64 "
                     "gdn_decode_step calls on 256 seqs x 32 heads",
         "prefill": {
-            "ms_mean": g_t_pre * 1e3, "ms_median": g_pre_ms[len(g_pre_ms) // 2],
+            "ms_mean": sum(g_pre_ms) / len(g_pre_ms), "ms_median": g_t_pre * 1e3,
             "tokens_per_s": T / g_t_pre,
             "hbm_frac_algorithmic": g_pb / g_t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / g_t_pre / BF16_PEAK,
@@ -491,8 +511,8 @@ def main():
                          "traffic": measured_traffic("gdn_chunk_fwd")},
         },
         "decode": {
-            "us_per_step_mean": g_t_dec * 1e6,
-            "us_per_step_median": g_dec_sorted[len(g_dec_sorted) // 2] * 1e3,
+            "us_per_step_mean": sum(g_dec_ms) / len(g_dec_ms) * 1e3,
+            "us_per_step_median": g_t_dec * 1e6,
             "GB_per_s": g_db / g_t_dec / 1e9,
             "hbm_frac": g_db / g_t_dec / HBM_PEAK,
             "alg_bytes_per_step": g_db,
@@ -506,7 +526,7 @@ def main():
                     "N(0,1) bf16, RMSNorm weight U[0.5,1.5]; prologue (L2Norm, -softplus, sigmoid) "
                     "and epilogue (RMSNorm x weight x sigmoid gate) fused",
         "prefill": {
-            "ms_mean": l_t_pre * 1e3, "ms_median": l_pre_ms[len(l_pre_ms) // 2],
+            "ms_mean": sum(l_pre_ms) / len(l_pre_ms), "ms_median": l_t_pre * 1e3,
             "tokens_per_s": T / l_t_pre,
             "hbm_frac_algorithmic": l_pb / l_t_pre / HBM_PEAK,
             "alg_bytes": l_pb,
@@ -518,8 +538,8 @@ def main():
                          "traffic": measured_traffic("kda_layer_chunk_fwd")},
         },
         "decode": {
-            "us_per_step_mean": l_t_dec * 1e6,
-            "us_per_step_median": l_dec_sorted[len(l_dec_sorted) // 2] * 1e3,
+            "us_per_step_mean": sum(l_dec_ms) / len(l_dec_ms) * 1e3,
+            "us_per_step_median": l_t_dec * 1e6,
             "GB_per_s": l_db / l_t_dec / 1e9,
             "hbm_frac": l_db / l_t_dec / HBM_PEAK,
             "alg_bytes_per_step": l_db,
@@ -532,6 +552,8 @@ def main():
         heads = list(range(16))
         T_s = 262144
         dt = cpu_baseline(pin, heads, T_s, threads)
+        T_1 = 65536
+        dt1 = cpu_baseline(pin, [0], T_1, 1)
         # the metric's unit is tokens/s at H=32: token-heads/s divided by 32
         result["cpu_baseline"] = {
             "value": T_s * len(heads) / dt / H,
@@ -540,6 +562,11 @@ def main():
             "kind": "oracle",
             "sample": f"fp64 token loop on heads 0-15 x first {T_s} tokens of the long "
                       f"prefill workload ({dt:.1f} s wall), scaled to H=32 tokens/s",
+            "value_1_thread": T_1 / dt1 / H,
+            "sample_1_thread": f"head 0 x first {T_1} tokens on one thread ({dt1:.1f} s wall), "
+                               f"scaled to H=32 tokens/s",
+            "host_cpu": host_cpu_model(),
+            "host_threads": os.cpu_count(),
         }
     print(json.dumps(result))
 
