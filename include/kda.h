@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 100 /* 1.0.0 */
+#define KDA_VERSION 110 /* 1.1.0: adds the gdn_* and kda_layer_* entry points */
 
 typedef enum {
     KDA_OK = 0,

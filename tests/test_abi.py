@@ -42,7 +42,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 100
+    assert lib.kda_version() == 110
     for code, name in [(0, b"KDA_OK"), (1, b"KDA_ERR_INVALID_ARG"), (2, b"KDA_ERR_UNSUPPORTED"),
                        (3, b"KDA_ERR_WORKSPACE"), (4, b"KDA_ERR_HIP")]:
         assert lib.kda_status_string(code) == name

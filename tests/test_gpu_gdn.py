@@ -162,3 +162,15 @@ def test_gdn_abi_rejects_misaligned_and_null():
     la = torch.zeros(2 * 2 + 1, device="cuda")[1:].view(2, 2)
     kda.gdn_decode_step(inp["q"][0], inp["k"][0], inp["v"][0], la, inp["beta"][0], state)
     torch.cuda.synchronize()
+
+
+def test_gdn_empty_inputs():
+    """T = 0 keeps the initial state; N = 0 decode is a no-op."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=17, T=0, H=2, gate="scalar")
+    o, fs = _gpu(inp)
+    assert o.numel() == 0 and torch.equal(fs, inp["init_state"])
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((0, 2, 128, 128), device="cuda")
+    out = kda.gdn_decode_step(z, z, z, torch.empty((0, 2), device="cuda"), torch.empty((0, 2), device="cuda"), st)
+    torch.cuda.synchronize()
+    assert out.numel() == 0

@@ -135,3 +135,24 @@ def test_layer_decode_workload_sampled_units():
             assert_parity(sl(o), o_ref, TAU[torch.bfloat16], f"layer decode workload out step {t}")
     torch.cuda.synchronize()
     assert_parity(sl(state), st, TAU[torch.bfloat16], "layer decode workload states")
+
+
+def test_layer_empty_and_zero_length_sequences():
+    """T = 0 keeps the initial state; zero-length sequences inside a varlen
+    batch keep theirs; N = 0 decode is a no-op."""
+    inp = workloads.make_layer_prefill("prefill", "cuda", seed=26, T=0, H=2)
+    o, fs = _gpu(inp)
+    assert o.numel() == 0 and torch.equal(fs, inp["init_state"])
+    inp = workloads.make_layer_prefill("varlen", "cuda", seed=27, H=2, lengths=[0, 70, 0, 5, 0])
+    g = torch.Generator(device="cuda").manual_seed(28)
+    inp["init_state"] = 0.02 * torch.randn((5, 2, 128, 128), device="cuda", generator=g)
+    o, fs = _gpu(inp)
+    for n in (0, 2, 4):
+        assert torch.equal(fs[n], inp["init_state"][n])
+    _check(inp, o, fs, label="layer varlen with empty sequences")
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((0, 2, 128, 128), device="cuda")
+    out = kda.layer_decode_step(z, z, z, z, torch.empty((0, 2), dtype=torch.bfloat16, device="cuda"), z,
+                                inp["norm_weight"], st)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
