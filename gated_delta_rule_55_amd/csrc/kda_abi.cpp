@@ -199,7 +199,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
                                     int32_t n_seqs, kda_dtype in_dtype, int32_t chunk_size) {
     if (chunk_size == 0) chunk_size = 64;
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
-    if (!supported_dim(Dk) || !supported_dim(Dv) || Dk != Dv) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return 0;
     if (B < 1 || T < 0 || H < 1 || n_seqs < 0) return 0;
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return 0;
     chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
@@ -223,7 +223,6 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
     if (!supported_dim(Dk) || !supported_dim(Dv))
         return fail(KDA_ERR_UNSUPPORTED, "Dk=%d Dv=%d: each must be 16, 32, 64 or 128", Dk, Dv);
-    if (Dk != Dv) return fail(KDA_ERR_UNSUPPORTED, "prefill needs Dk == Dv (got %d, %d)", Dk, Dv);
     if (chunk_size == 0) chunk_size = 64;
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: must be 16, 32 or 64", chunk_size);

@@ -153,7 +153,8 @@ __device__ __forceinline__ float touch_next_item(const IntraParams &p, int64_t i
         if (l < LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.q) + row * DK) + l * 32;
         else if (l < 2 * LK) src = reinterpret_cast<const float *>(static_cast<const In *>(p.k) + row * DK) + (l - LK) * 32;
         else if (l < 2 * LK + LV) src = reinterpret_cast<const float *>(static_cast<const In *>(p.v) + row * DV) + (l - 2 * LK) * 32;
-        else src = p.log_alpha + row * DK + (l - 2 * LK - LV) * 32;
+        else  // the gate row: Dk values (KDA) or one value (g_ch = 0, scalar gate)
+            src = p.log_alpha + row * p.g_row + (p.g_ch ? (l - 2 * LK - LV) * 32 : 0);
         acc += *src;
     }
     return acc;

@@ -945,17 +945,29 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int C, int DK, bool BF>
+static hipError_t dispatch_dv(const PrefillArgs &a, hipStream_t s) {
+    // the fp32 path holds q, k, v and the decay in fp32 in LDS: 64-token chunks
+    // with d_k or d_v = 128 do not fit (prefill_effective_chunk maps them to 32)
+    switch (a.Dv) {
+        case 16: return launch_t<C, DK, 16, BF>(a, s);
+        case 32: return launch_t<C, DK, 32, BF>(a, s);
+        case 64: return launch_t<C, DK, 64, BF>(a, s);
+        case 128:
+            if constexpr (BF || C <= 32) return launch_t<C, DK, 128, BF>(a, s);
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int C, bool BF>
 static hipError_t dispatch_d(const PrefillArgs &a, hipStream_t s) {
-    if (a.Dk != a.Dv) return hipErrorInvalidValue;
     switch (a.Dk) {
-        case 16: return launch_t<C, 16, 16, BF>(a, s);
-        case 32: return launch_t<C, 32, 32, BF>(a, s);
-        case 64: return launch_t<C, 64, 64, BF>(a, s);
+        case 16: return dispatch_dv<C, 16, BF>(a, s);
+        case 32: return dispatch_dv<C, 32, BF>(a, s);
+        case 64: return dispatch_dv<C, 64, BF>(a, s);
         case 128:
-            // the fp32 path holds q, k, v in fp32 in LDS; 64-token chunks at
-            // d = 128 do not fit (prefill_effective_chunk maps them to 32)
-            if constexpr (BF || C <= 32) return launch_t<C, 128, 128, BF>(a, s);
+            if constexpr (BF || C <= 32) return dispatch_dv<C, 128, BF>(a, s);
             else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }

@@ -63,8 +63,9 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, aliasing   */
-    KDA_ERR_UNSUPPORTED = 2, /* Dk/Dv outside {16,32,64,128} (prefill: Dk != Dv),
-                                chunk size, dtype                             */
+    KDA_ERR_UNSUPPORTED = 2, /* Dk/Dv outside {16,32,64,128}, chunk size,
+                                dtype; the layer prefill: sizes other than
+                                Dk = Dv = 128                                 */
     KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
     KDA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError)      */
 } kda_status;
@@ -93,7 +94,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
  *   beta        [B, T, H]     fp32               write strength
  *   init_state  [N, H, Dk, Dv] fp32, nullable    incoming state (NULL: zeros)
  *   cu_seqlens  [N + 1] int32, nullable          packed sequence offsets (device)
- *   B, T, H, Dk, Dv                              sizes; Dk == Dv in {16, 32, 64, 128}
+ *   B, T, H, Dk, Dv                              sizes; Dk, Dv each in {16, 32, 64, 128}
  *   n_seqs      N when cu_seqlens is given (then B must be 1), else ignored (N = B)
  *   in_dtype    KDA_BF16 or KDA_F32
  *   chunk_size  16, 32 or 64 (0 selects 64); results do not depend on it

@@ -59,8 +59,11 @@ def test_workspace_size(lib):
     assert ws(1, 4097, 1, 16, 16, 0, F32, 16) == ws(1, 4112, 1, 16, 16, 0, F32, 16)
     assert ws(1, 1000, 2, 64, 64, 5, BF16, 64) > ws(1, 1000, 2, 64, 64, 0, BF16, 64)
     assert ws(3, 100, 2, 32, 32, 0, BF16, 32) == 3 * ws(1, 100, 2, 32, 32, 0, BF16, 32)
+    # d_k and d_v are independent: the package grows with each
+    assert ws(1, 64, 1, 16, 32, 0, BF16, 16) > ws(1, 64, 1, 16, 16, 0, BF16, 16)
+    assert ws(1, 64, 1, 32, 16, 0, BF16, 16) > ws(1, 64, 1, 16, 16, 0, BF16, 16)
     for bad in [(1, 64, 1, 16, 16, 0, BF16, 48), (1, 64, 1, 24, 24, 0, BF16, 16),
-                (1, 64, 1, 16, 32, 0, BF16, 16), (0, 64, 1, 16, 16, 0, BF16, 16),
+                (1, 64, 1, 16, 24, 0, BF16, 16), (0, 64, 1, 16, 16, 0, BF16, 16),
                 (1, -1, 1, 16, 16, 0, BF16, 16), (1, 64, 1, 16, 16, 0, 7, 16)]:
         assert ws(*bad) == 0, bad
 
@@ -81,7 +84,7 @@ def _chunk(lib, fn="kda_chunk_fwd", **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), UNSUPPORTED),
     (dict(Dk=24, Dv=24), UNSUPPORTED),
-    (dict(Dk=16, Dv=32), UNSUPPORTED),
+    (dict(Dk=16, Dv=24), UNSUPPORTED),
     (dict(chunk=48), UNSUPPORTED),
     (dict(B=0), INVALID),
     (dict(T=-1), INVALID),

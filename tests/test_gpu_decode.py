@@ -85,3 +85,25 @@ def test_decode_workload_sampled_units():
     worst = max(worst, e)
     assert_parity(state[ns, hs], st[:, 0], TAU[torch.bfloat16], "final state (48 units)")
     assert worst < 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 128), (128, 16), (64, 32), (32, 64)])
+def test_decode_unequal_dims(dtype, Dk, Dv):
+    """d_k != d_v: the first Dk key channels (q, k re-normalised) and Dv value columns."""
+    log(f"decode Dk={Dk} Dv={Dv} {dtype}")
+    inp = workloads.make_decode("decode", "cuda", seed=Dk + Dv, N=3, H=2, steps=4, dtype=dtype)
+    nrm = lambda x: (x[..., :Dk].float() / torch.linalg.vector_norm(x[..., :Dk].float(), dim=-1, keepdim=True)).to(x.dtype)
+    q = [nrm(x) for x in inp["q"]]
+    k = [nrm(x) for x in inp["k"]]
+    v = [x[..., :Dv].contiguous() for x in inp["v"]]
+    la = [x[..., :Dk].contiguous() for x in inp["log_alpha"]]
+    state = inp["state"][:, :, :Dk, :Dv].contiguous()
+    st = host64(state)
+    tau = TAU[torch.bfloat16 if dtype == "bf16" else torch.float32]
+    for t in range(4):
+        o = kda.decode_step(q[t], k[t], v[t], la[t], inp["beta"][t], state)
+        torch.cuda.synchronize()
+        o_ref, st = oracle.decode_step(q[t], k[t], v[t], la[t], inp["beta"][t], st)
+        assert assert_parity(o, o_ref, tau, f"decode Dk={Dk} Dv={Dv} o step {t}") < 1e-5
+    assert assert_parity(state, st, tau, f"decode Dk={Dk} Dv={Dv} state") < 1e-5

@@ -234,3 +234,26 @@ def test_dense_batch_with_resets(D, dtype):
     o, fs = _gpu(inp)
     tau = TAU[torch.bfloat16 if dtype == "bf16" else torch.float32]
     _check(inp, o, fs, tau, label=f"dense batch D={D} {dtype}")
+
+
+def _shrink2(inp, Dk, Dv):
+    """Keeps the first Dk key channels (re-normalising q, k) and Dv value columns."""
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name][..., :Dk].float()
+        out[name] = (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(inp[name].dtype)
+    out["v"] = inp["v"][..., :Dv].contiguous()
+    out["log_alpha"] = inp["log_alpha"][..., :Dk].contiguous()
+    if inp["init_state"] is not None:
+        out["init_state"] = inp["init_state"][:, :, :Dk, :Dv].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 32), (32, 16), (64, 128), (128, 64), (16, 128), (128, 16)])
+def test_unequal_key_and_value_dims(dtype, Dk, Dv):
+    """d_k != d_v: T = 157 (ragged), 3 heads, random initial state, 64-token chunks."""
+    log(f"prefill Dk={Dk} Dv={Dv} {dtype}")
+    inp = _shrink2(workloads.make_prefill("prefill", "cuda", seed=Dk + 3 * Dv, T=157, H=3, dtype=dtype), Dk, Dv)
+    o, fs = _gpu(inp, chunk=64)
+    _check(inp, o, fs, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32], label=f"Dk={Dk} Dv={Dv} {dtype}")
