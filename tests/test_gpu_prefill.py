@@ -257,3 +257,15 @@ def test_unequal_key_and_value_dims(dtype, Dk, Dv):
     inp = _shrink2(workloads.make_prefill("prefill", "cuda", seed=Dk + 3 * Dv, T=157, H=3, dtype=dtype), Dk, Dv)
     o, fs = _gpu(inp, chunk=64)
     _check(inp, o, fs, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32], label=f"Dk={Dk} Dv={Dv} {dtype}")
+
+
+def test_slow_decay_gate_variant():
+    """The harder precision case: log_alpha = logsigmoid(N(0,1) + 2) per channel
+    (mean alpha ~ 0.85, long memory) on the 4096-token workload, every output."""
+    log("prefill 4096x32 slow decay")
+    inp = workloads.make_prefill("prefill", "cuda", seed=31)
+    g = torch.Generator(device="cuda").manual_seed(32)
+    x = torch.randn(inp["log_alpha"].shape, device="cuda", generator=g)
+    inp["log_alpha"] = torch.nn.functional.logsigmoid(x + 2.0)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label="slow decay 4096x32")

@@ -285,3 +285,29 @@ def test_bad_arguments_raise():
     q, k, v, la, be, s0 = _rand_inputs(rng, 4, 1, 2, 2)
     with pytest.raises(ValueError):
         oracle.forward(q, k, v, la, be, None, cu_seqlens=np.array([0, 3], np.int32))  # cu[-1] != T
+
+
+def test_dplr_identity():
+    """(I - b k k^T) Diag(a) = Diag(a) - (b k)(a * k)^T, the diagonal-plus-low-rank
+    form of the transition (KDA section: DPLR with a = b = k): the recurrence
+    written as S <- Diag(a) S - (b k)((a * k)^T S) + b k v^T, with explicit
+    vectors, matches the oracle (this fixes the order decay-then-erase)."""
+    rng = np.random.default_rng(14)
+    T, H, Dk, Dv = 11, 2, 5, 4
+    q, k, v, la, be, s0 = _rand_inputs(rng, T, H, Dk, Dv)
+    o, fs = oracle.forward(q, k, v, la, be, s0)
+    for h in range(H):
+        S = s0[0, h].copy()
+        for t in range(T):
+            a = np.exp(la[0, t, h])
+            kk, b = k[0, t, h], be[0, t, h]
+            S = a[:, None] * S - np.outer(b * kk, (a * kk) @ S) + b * np.outer(kk, v[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], S.T @ q[0, t, h], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(fs[0, h], S, rtol=0, atol=1e-13)
+    # the erase after the decay is not the same operator: (I - b k k^T) then Diag(a) differs
+    a = np.exp(la[0, 0, 0])
+    kk, b = k[0, 0, 0], be[0, 0, 0]
+    M1 = (np.eye(Dk) - b * np.outer(kk, kk)) @ np.diag(a)
+    M2 = np.diag(a) @ (np.eye(Dk) - b * np.outer(kk, kk))
+    assert np.max(np.abs(M1 - M2)) > 1e-3
+    np.testing.assert_allclose(M1, np.diag(a) - np.outer(b * kk, a * kk), rtol=0, atol=1e-15)
