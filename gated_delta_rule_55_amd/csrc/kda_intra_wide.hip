@@ -180,6 +180,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
     __shared__ float sBeta[C];
     __shared__ uint64_t sRst[4];
     __shared__ float sNrm[GM == 2 ? 4 : 1][2][GM == 2 ? C : 1];  // per-wave sums of k^2, q^2 per token
+    __shared__ float sGs[GM == 1 ? C : 1];  // scalar gate: cumulative log2-decay per token
 
     float(*sA)[kAS] = reinterpret_cast<float(*)[kAS]>(smem);
     float(*sP)[kAS] = reinterpret_cast<float(*)[kAS]>(smem + kWC * kAS * 4);
@@ -312,6 +313,13 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             }
         }
 
+        if constexpr (GM == 1) {
+            if (w == 0 && kg == 0) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sGs[16 * t + t16] = G[t][0];
+            }
+        }
+
         // ---- this wave's share of the Gram tiles A' (k k) and P (q k), factored
         //      exponents.  Tile matrix tm (A tiles 0..9, P tiles 10..19) belongs to
         //      wave tm % 4; the other waves leave their shares in LDS for it.
@@ -321,6 +329,26 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             if (owner == w) fin[tm >> 2] = v;
             else red[(tm * 3 + ((w - owner + 3) & 3)) * 64 + lane] = v;
         };
+        // Scalar gate (GDN): the decay e^{G_i - G_j} is one number per token pair,
+        // so the tiles are plain K K^T and Q K^T on the bf16 inputs (exact
+        // products, fp32 sums) and the decay is applied per element when the
+        // shares are summed.
+        auto bits8 = [](const uint32_t (&u)[4]) {
+            typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+            return __builtin_bit_cast(bf16x8, u32x4_t{u[0], u[1], u[2], u[3]});
+        };
+        if constexpr (GM == 1) {
+            static_for<0, 4>([&](auto Jc) {
+                constexpr int J = decltype(Jc)::value;
+                const bf16x8 kj = bits8(kr[J]);
+                static_for<J, 4>([&](auto Ic) {
+                    constexpr int I = decltype(Ic)::value;
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, mfma_bf16(bits8(kr[I]), kj, z));
+                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, mfma_bf16(bits8(qr[I]), kj, z));
+                });
+            });
+        } else
         static_for<0, 4>([&](auto Jc) {
             constexpr int J = decltype(Jc)::value;
             float gm[8];  // G at token 16 J + 15
@@ -426,7 +454,9 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                     const int i = 16 * I + 4 * kg + r;
                     bool keep = tm < 10 ? j < i : j <= i;
                     if constexpr (kMasked) keep = keep && (rst & tokens_between(j, i)) == 0;  // no reset in (j, i]
-                    dst[i][j] = keep ? (tm < 10 ? sBeta[i] : 1.f) * fin[k][r] : 0.f;
+                    float val = (tm < 10 ? sBeta[i] : 1.f) * fin[k][r];
+                    if constexpr (GM == 1) val *= fast_exp2(sGs[i] - sGs[j]);  // i >= j: at most 1
+                    dst[i][j] = keep ? val : 0.f;
                 }
             }
         };

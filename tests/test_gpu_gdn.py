@@ -82,16 +82,25 @@ def test_gdn_varlen_with_resets():
     _check(inp, o, fs, TAU[torch.bfloat16], label="gdn varlen")
 
 
-def test_gdn_equals_kda_with_broadcast_gate():
-    """The scalar gate broadcast over key channels through kda_chunk_fwd gives
-    bit-identical results (both paths feed the same values to the same kernels)."""
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (32, "f32")])
+def test_gdn_agrees_with_kda_on_the_broadcast_gate(D, dtype):
+    """The scalar gate broadcast over key channels through kda_chunk_fwd: the same
+    function, computed by the channel-wise path (the d = 128 bf16 scalar-gate
+    path forms its Gram tiles differently, so the two agree to rounding; the
+    general kernel reads the same values either way, so there they are equal)."""
     inp = workloads.make_prefill("varlen", "cuda", seed=16, H=4, lengths=[300, 1, 129],
-                                 gate="scalar")
+                                 gate="scalar", dtype=dtype)
+    if D != 128:
+        inp = _shrink(inp, D)
     o, fs = _gpu(inp)
-    la_b = inp["log_alpha"][..., None].expand(*inp["log_alpha"].shape, 128).contiguous()
+    la_b = inp["log_alpha"][..., None].expand(*inp["log_alpha"].shape, D).contiguous()
     ok, fk = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], la_b, inp["beta"], None, inp["cu_seqlens"], 64)
     torch.cuda.synchronize()
-    assert torch.equal(o, ok) and torch.equal(fs, fk)
+    if D == 128 and dtype == "bf16":
+        assert_parity(o, host64(ok), 3e-3, "gdn vs kda broadcast o")
+        assert_parity(fs, host64(fk), 3e-3, "gdn vs kda broadcast final state")
+    else:
+        assert torch.equal(o, ok) and torch.equal(fs, fk)
 
 
 @pytest.mark.timeout(600)
