@@ -269,3 +269,23 @@ def test_slow_decay_gate_variant():
     inp["log_alpha"] = torch.nn.functional.logsigmoid(x + 2.0)
     o, fs = _gpu(inp)
     _check(inp, o, fs, TAU[torch.bfloat16], label="slow decay 4096x32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_token_values(dtype):
+    """Tokens with beta = 0 (no write), alpha = 1 on every channel (no decay),
+    k = 0 (nothing erased or written), q = 0 (zero readout), v = 0, and a reset
+    on a chunk's first token, mixed into a ragged 3-head sequence."""
+    log(f"degenerate values {dtype}")
+    inp = workloads.make_prefill("prefill", "cuda", seed=41, T=300, H=3, dtype=dtype)
+    if dtype == "f32":
+        inp = _shrink(inp, 64)
+    inp["beta"][0, 10:20] = 0.0
+    inp["log_alpha"][0, 30:45] = 0.0
+    inp["k"][0, 50:53] = 0
+    inp["q"][0, 60:70, 1] = 0
+    inp["v"][0, 80:90, 2] = 0
+    inp["log_alpha"][0, 128] = float("-inf")
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32], label=f"degenerate {dtype}")
+    assert torch.all(o[0, 60:70, 1] == 0)
