@@ -166,6 +166,23 @@ def _last_dispatch_counters(d, counter):
     return last
 
 
+def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir):
+    """The rocprofv3 runs (each counter in its own run; <repo> is the repository root and
+    each run's output is the directory given here) and this summary's command line."""
+    prof = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/{d} -o run -- " \
+           "python3 <repo>/bench.py {a}"
+    bench_args = "--steps 1 --warmup 0 --no-cpu-baseline"
+    cmds = [prof.format(c="FETCH_SIZE", d=fetch_dir, a=bench_args),
+            prof.format(c="WRITE_SIZE", d=write_dir, a=bench_args),
+            prof.format(c="FETCH_SIZE", d=copy_fetch_dir, a="--only copy --steps 2"),
+            prof.format(c="WRITE_SIZE", d=copy_write_dir, a="--only copy --steps 2")]
+    if mfma_dir:
+        cmds.append(prof.format(c="MfmaUtil", d=mfma_dir, a=bench_args))
+    dirs = [fetch_dir, write_dir, copy_fetch_dir, copy_write_dir] + ([mfma_dir] if mfma_dir else [])
+    cmds.append("python bench.py --summarize-counters " + " ".join(dirs))
+    return cmds
+
+
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None):
     fetch = _last_dispatch_counters(fetch_dir, "FETCH_SIZE")
     write = _last_dispatch_counters(write_dir, "WRITE_SIZE")
@@ -194,19 +211,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfm
             launches[launch] = {"kernels": list(names),
                                 "hbm_bytes": sum(kernels[n]["hbm_bytes"] for n in names)}
     rec = {"source_digest": source_digest(),
-           "commands": [
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
-               "gpurun_out/prof/pmc_bench_FETCH_SIZE -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 0 "
-               "--no-cpu-baseline   (likewise WRITE_SIZE)",
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $GRAFT_REPO_ROOT/"
-               "gpurun_out/prof/pmc_copy_FETCH_SIZE -o run -- python3 $GRAFT_REPO_ROOT/bench.py --only copy --steps 2"
-               "   (likewise WRITE_SIZE)",
-               "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc MfmaUtil --output-format csv -d $GRAFT_REPO_ROOT/"
-               "gpurun_out/prof/pmc_bench_MfmaUtil -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 0 "
-               "--no-cpu-baseline",
-               "python bench.py --summarize-counters gpurun_out/prof/pmc_bench_FETCH_SIZE gpurun_out/prof/"
-               "pmc_bench_WRITE_SIZE gpurun_out/prof/pmc_copy_FETCH_SIZE gpurun_out/prof/pmc_copy_WRITE_SIZE "
-               "gpurun_out/prof/pmc_bench_MfmaUtil"],
+           "commands": _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir),
            "note": "per-launch bytes of the last dispatch of each kernel; each counter scaled by what it reads "
                    "for a plain device copy of copy_bytes (read once, written once)",
            "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": _short(copy_name),
