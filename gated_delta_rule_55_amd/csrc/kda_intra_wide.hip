@@ -117,9 +117,9 @@ __device__ __forceinline__ f32x4 gram_bf16x3(const float (&x)[8], const bf16x8 &
 struct WideRaw {
     uint32_t k[4][4], q[4][4], v[4][4];
     float la[4][8];     // log_alpha (gate modes 0 and 1)
-    float beta[4];
+    float beta;         // beta of token l (lane l; gate modes 0 and 1)
     uint32_t xa[4][4];  // gate mode 2: x_alpha, bf16 bits
-    uint16_t xb[4];     // gate mode 2: x_beta, bf16 bits
+    uint16_t xb;        // gate mode 2: x_beta of token l, bf16 bits
 };
 
 // Gate modes of the kernel:
@@ -130,29 +130,55 @@ struct WideRaw {
 //      formed from bf16 projections (the KDA-layer item of the page's
 //      model-architecture list: L2Norm on q/k, low-rank channel-wise decay gate)
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Each 16-bit input arrives as one 16-byte load per lane of 8 consecutive
+// channels, at 16 (kg & 1) + 8 (kg >> 1) within the wave's 32 (so the four
+// lanes of a token cover them once).  Swapping halves with the lane 16 away
+// (rows of 16 lanes: even rows keep their first half and take the odd
+// neighbour's first half as their second; odd rows take the even neighbour's
+// second half as their first) leaves lane l with channels 4 (l / 16) + 0..3
+// and 16 + 4 (l / 16) + 0..3, the layout above.
+__device__ __forceinline__ int64_t load16_channel(int kg) { return 16 * (kg & 1) + 8 * (kg >> 1); }
+__device__ __forceinline__ void halves_to_layout(uint32_t (&u)[4]) {
+    const auto a = __builtin_amdgcn_permlane16_swap(u[0], u[2], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(u[1], u[3], false, false);
+    u[0] = a[0];
+    u[2] = a[1];
+    u[1] = b[0];
+    u[3] = b[1];
+}
+__device__ __forceinline__ void put4(uint32_t (&d)[4], const u32x4 &x) {
+    d[0] = x[0];
+    d[1] = x[1];
+    d[2] = x[2];
+    d[3] = x[3];
+}
+
+// Loads one work item's inputs (raw 16-bit words still in load order: the
+// unpack puts them in the register layout once they have arrived).  Lane l
+// also loads the beta of token l.
 template <int GM>
 __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, int nvalid, int h, int w, int t16,
                                            int kg, WideRaw &r) {
     const int H = p.H;
+    {
+        const int l = 16 * kg + t16;
+        const int64_t row = (tok0 + (l < nvalid ? l : nvalid - 1)) * H + h;
+        if constexpr (GM == 2) r.xb = p.x_beta[row];
+        else r.beta = p.beta[row];
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int i = 16 * t + t16;
         const int64_t row = (tok0 + (i < nvalid ? i : nvalid - 1)) * H + h;
         const int64_t off = row * kWD + 32 * w + 4 * kg;
-        const uint16_t *kb = static_cast<const uint16_t *>(p.k) + off;
-        const uint16_t *qb = static_cast<const uint16_t *>(p.q) + off;
-        const uint16_t *vb = static_cast<const uint16_t *>(p.v) + off;
-        const uint2 k0 = *reinterpret_cast<const uint2 *>(kb), k1 = *reinterpret_cast<const uint2 *>(kb + 16);
-        const uint2 q0 = *reinterpret_cast<const uint2 *>(qb), q1 = *reinterpret_cast<const uint2 *>(qb + 16);
-        const uint2 v0 = *reinterpret_cast<const uint2 *>(vb), v1 = *reinterpret_cast<const uint2 *>(vb + 16);
-        r.k[t][0] = k0.x; r.k[t][1] = k0.y; r.k[t][2] = k1.x; r.k[t][3] = k1.y;
-        r.q[t][0] = q0.x; r.q[t][1] = q0.y; r.q[t][2] = q1.x; r.q[t][3] = q1.y;
-        r.v[t][0] = v0.x; r.v[t][1] = v0.y; r.v[t][2] = v1.x; r.v[t][3] = v1.y;
+        const int64_t off16 = row * kWD + 32 * w + load16_channel(kg);
+        put4(r.k[t], *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.k) + off16));
+        put4(r.q[t], *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.q) + off16));
+        put4(r.v[t], *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.v) + off16));
         if constexpr (GM == 2) {
-            const uint16_t *xab = p.x_alpha + off;
-            const uint2 a0 = *reinterpret_cast<const uint2 *>(xab), a1 = *reinterpret_cast<const uint2 *>(xab + 16);
-            r.xa[t][0] = a0.x; r.xa[t][1] = a0.y; r.xa[t][2] = a1.x; r.xa[t][3] = a1.y;
-            r.xb[t] = p.x_beta[row];
+            put4(r.xa[t], *reinterpret_cast<const u32x4 *>(p.x_alpha + off16));
         } else if constexpr (GM == 1) {
             const float g = p.log_alpha[row];
 #pragma unroll
@@ -166,11 +192,8 @@ __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, i
                 r.la[t][4 + e] = l1[e];
             }
         }
-        if constexpr (GM != 2) r.beta[t] = p.beta[row];
     }
 }
-
-
 
 template <int GM>
 __global__ void __launch_bounds__(kIntraThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -219,6 +242,10 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             const int i = 16 * t + t16;
             const bool ok = i < nvalid;
             const uint32_t m = ok ? 0xffffffffu : 0u;
+            halves_to_layout(raw.k[t]);
+            halves_to_layout(raw.q[t]);
+            halves_to_layout(raw.v[t]);
+            if constexpr (GM == 2) halves_to_layout(raw.xa[t]);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 kr[t][x] = raw.k[t][x] & m;
@@ -228,13 +255,17 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             if constexpr (GM == 2) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) G[t][e] = ok ? neg_softplus(bf_at(raw.xa[t], e)) : 0.f;
-                const float xbv = __builtin_bit_cast(float, static_cast<uint32_t>(raw.xb[t]) << 16);
-                if (w == 0 && kg == 0) sBeta[i] = ok ? sigmoid_f(xbv) : 0.f;
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) G[t][e] = ok ? raw.la[t][e] : 0.f;
-                if (w == 0 && kg == 0) sBeta[i] = ok ? raw.beta[t] : 0.f;
             }
+        }
+        if (w == 0) {  // beta of token l from lane l
+            const bool ok = lane < nvalid;
+            if constexpr (GM == 2)
+                sBeta[lane] = ok ? sigmoid_f(__builtin_bit_cast(float, static_cast<uint32_t>(raw.xb) << 16)) : 0.f;
+            else
+                sBeta[lane] = ok ? raw.beta : 0.f;
         }
         if constexpr (GM == 2) {
             // this wave's share of |k|^2 and |q|^2 per token: 8 channels per lane,
