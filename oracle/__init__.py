@@ -19,13 +19,18 @@ scalar-gate recurrence the same page sets KDA against (one head-wise
 ``log_alpha`` of shape [B, T, H] (prefill) or [N, H] (decode).  Its C update
 shares no arithmetic with the KDA one.
 
+``backward`` differentiates the KDA token loop in reverse mode, one token at
+a time (the gradients with respect to q, k, v, log_alpha, beta and the initial
+state, given those of o and of the final state).
+
 ``layer_forward`` and ``layer_decode_step`` (``layer.py``) add the KDA
 layer's prologue (L2Norm of q and k, the -softplus decay gate, the sigmoid
 beta) and epilogue (RMSNorm and the sigmoid output gate) around ``forward`` /
 ``decode_step``.
 
 Every function here is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_oracle_pins_gdn.py`` and ``tests/test_oracle_pins_layer.py``
+``tests/test_oracle_pins_gdn.py``, ``tests/test_oracle_pins_layer.py`` and
+``tests/test_oracle_pins_bwd.py`` (finite differences of ``forward``)
 against closed forms, special cases, invariants, exact rational arithmetic and
 explicit-matrix brute force; none is "parity unpinned".
 """
@@ -72,6 +77,10 @@ def _load():
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.gdn_oracle_decode_step.argtypes = lib.kda_oracle_decode_step.argtypes
         lib.gdn_oracle_decode_step.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+            i64, i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -136,6 +145,47 @@ def _forward(scalar_gate, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_th
     if rc != 0:
         raise ValueError(f"{'gdn' if scalar_gate else 'kda'}_oracle_forward failed with code {rc}")
     return o, fs
+
+
+def backward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, d_o=None, d_final_state=None,
+             n_threads=None):
+    """Gradients of ``forward`` in fp64, by reverse mode over the token loop.
+
+    d_o: [B, T, H, Dv] (required); d_final_state: [N, H, Dk, Dv] or None (zero).
+    Returns (dq, dk, dv, dlog_alpha, dbeta, d_init_state) as fp64 numpy arrays;
+    dlog_alpha is 0 where log_alpha is -inf.
+    """
+    q, k, v, la, be, do = (_f64(a) for a in (q, k, v, log_alpha, beta, d_o))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    assert k.shape == q.shape and la.shape == q.shape
+    assert v.shape == (B, T, H, Dv) and be.shape == (B, T, H) and do.shape == v.shape
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens), dtype=np.int32)
+        N = cu.size - 1
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        cu, N, cu_p = None, B, None
+    s0 = None if init_state is None else _f64(init_state)
+    dsf = None if d_final_state is None else _f64(d_final_state)
+    for a in (s0, dsf):
+        if a is not None:
+            assert a.shape == (N, H, Dk, Dv)
+    dq = np.zeros((B, T, H, Dk))
+    dk = np.zeros((B, T, H, Dk))
+    dv = np.zeros((B, T, H, Dv))
+    dla = np.zeros((B, T, H, Dk))
+    dbeta = np.zeros((B, T, H))
+    ds0 = np.zeros((N, H, Dk, Dv))
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    rc = _load().kda_oracle_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0), cu_p, B, T, H, Dk, Dv, N,
+        _ptr(do), _ptr(dsf), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(dbeta), _ptr(ds0), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_backward failed with code {rc}")
+    return dq, dk, dv, dla, dbeta, ds0
 
 
 def decode_step(q, k, v, log_alpha, beta, state):

@@ -42,6 +42,23 @@
  *
  * and log_alpha laid out [B, T, H] (prefill) or [N, H] (decode).  It shares no
  * arithmetic with token_update, so the two can be checked against each other.
+ *
+ * kda_oracle_backward is reverse-mode differentiation of the KDA token loop
+ * above, one token at a time in reverse order (the gradients the training
+ * workload of the pages needs: of q, k, v, log_alpha, beta and the initial
+ * state, given the gradients of o and of the final state).  Written out for
+ * one token, with S' = Diag(alpha) S_prev, p = S'^T k, u = beta (v - p),
+ * S = S' + k u^T and o = S^T q, and dS the gradient of the loss with respect
+ * to S from everything after the token:
+ *
+ *     dS += q do^T            dq = S do
+ *     du  = dS^T k            dk = dS u + S' dp,   dp = -beta du
+ *     dv  = beta du           dbeta = du . (v - p)
+ *     dS' = dS + k dp^T       dlog_alpha_c = alpha_c sum_j S_prev[c][j] dS'[c][j]
+ *     dS_prev = Diag(alpha) dS'
+ *
+ * (dlog_alpha is 0 where log_alpha = -inf: alpha = 0 there.)  The states the
+ * reverse sweep needs are recomputed from checkpoints every 64 tokens.
  */
 #include <math.h>
 #include <pthread.h>
@@ -283,4 +300,207 @@ int gdn_oracle_decode_step(const double *q, const double *k, const double *v,
                          beta[u], e, o + (size_t)u * (size_t)Dv);
     free(e);
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward (reverse mode) of the KDA token loop.                            */
+/* ------------------------------------------------------------------------- */
+#define BWD_SEG 64
+
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *beta, *init_state, *d_o, *d_final;
+    const int32_t *cu_seqlens;
+    int64_t B, T, H, Dk, Dv, N;
+    double *dq, *dk, *dv, *dlog_alpha, *dbeta, *d_init;
+    int64_t next_unit;
+    pthread_mutex_t lock;
+} bwd_job;
+
+/* Reverse step of one token.  S_prev: state before the token, S: after it,
+ * dS: in = gradient with respect to S from later tokens and the final state;
+ * out = gradient with respect to S_prev.  Scratch: Sd (Dk*Dv), p, u, du, dp (Dv). */
+static void token_backward(int64_t Dk, int64_t Dv, const double *S_prev, const double *S,
+                           const double *q, const double *k, const double *v,
+                           const double *log_alpha, double beta, const double *d_o,
+                           double *dS, double *Sd, double *p, double *u, double *du, double *dp,
+                           double *dq, double *dk, double *dv, double *dla, double *dbeta)
+{
+    /* the forward quantities of the token: S' (Sd), p, u */
+    for (int64_t c = 0; c < Dk; ++c) {
+        const double a = exp(log_alpha[c]);
+        for (int64_t j = 0; j < Dv; ++j) Sd[c * Dv + j] = a * S_prev[c * Dv + j];
+    }
+    for (int64_t j = 0; j < Dv; ++j) p[j] = 0.0;
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < Dv; ++j) p[j] += Sd[c * Dv + j] * k[c];
+    for (int64_t j = 0; j < Dv; ++j) u[j] = beta * (v[j] - p[j]);
+
+    /* readout o = S^T q */
+    for (int64_t c = 0; c < Dk; ++c)
+        for (int64_t j = 0; j < Dv; ++j) dS[c * Dv + j] += q[c] * d_o[j];
+    for (int64_t c = 0; c < Dk; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dv; ++j) acc += S[c * Dv + j] * d_o[j];
+        dq[c] = acc;
+    }
+    /* S = S' + k u^T */
+    for (int64_t j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) acc += dS[c * Dv + j] * k[c];
+        du[j] = acc;
+    }
+    for (int64_t c = 0; c < Dk; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dv; ++j) acc += dS[c * Dv + j] * u[j];
+        dk[c] = acc;
+    }
+    /* u = beta (v - p) */
+    double db = 0.0;
+    for (int64_t j = 0; j < Dv; ++j) {
+        db += du[j] * (v[j] - p[j]);
+        dv[j] = beta * du[j];
+        dp[j] = -beta * du[j];
+    }
+    *dbeta = db;
+    /* p = S'^T k: dS' = dS + k dp^T, dk += S' dp */
+    for (int64_t c = 0; c < Dk; ++c) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dv; ++j) acc += Sd[c * Dv + j] * dp[j];
+        dk[c] += acc;
+        for (int64_t j = 0; j < Dv; ++j) dS[c * Dv + j] += k[c] * dp[j];
+    }
+    /* S' = Diag(alpha) S_prev */
+    for (int64_t c = 0; c < Dk; ++c) {
+        const double a = exp(log_alpha[c]);
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dv; ++j) acc += S_prev[c * Dv + j] * dS[c * Dv + j];
+        dla[c] = a * acc;
+        for (int64_t j = 0; j < Dv; ++j) dS[c * Dv + j] *= a;
+    }
+}
+
+static int run_bwd_unit(const bwd_job *J, int64_t n, int64_t h, double *ckpt, double *seg,
+                        double *dS, double *scratch)
+{
+    const int64_t Dk = J->Dk, Dv = J->Dv, H = J->H, DD = Dk * Dv;
+    int64_t b, t0, t1;
+    if (J->cu_seqlens) { b = 0; t0 = J->cu_seqlens[n]; t1 = J->cu_seqlens[n + 1]; }
+    else               { b = n; t0 = 0;               t1 = J->T; }
+    const int64_t L = t1 - t0, nseg = (L + BWD_SEG - 1) / BWD_SEG;
+    const size_t sidx = (size_t)(n * H + h) * (size_t)DD;
+    double *Sd = scratch, *p = Sd + DD, *o_t = p + Dv, *u = o_t + Dv, *du = u + Dv, *dp = du + Dv;
+
+    /* forward: checkpoint the state at the start of every segment */
+    double *S = seg;  /* running state (seg[0]) */
+    if (J->init_state) memcpy(S, J->init_state + sidx, sizeof(double) * (size_t)DD);
+    else               memset(S, 0, sizeof(double) * (size_t)DD);
+    for (int64_t t = t0; t < t1; ++t) {
+        if ((t - t0) % BWD_SEG == 0)
+            memcpy(ckpt + (size_t)((t - t0) / BWD_SEG) * (size_t)DD, S, sizeof(double) * (size_t)DD);
+        const size_t row = (size_t)((b * J->T + t) * H + h);
+        token_update(S, Dk, Dv, J->q + row * (size_t)Dk, J->k + row * (size_t)Dk, J->v + row * (size_t)Dv,
+                     J->log_alpha + row * (size_t)Dk, J->beta[row], p, o_t);
+    }
+    /* reverse sweep */
+    if (J->d_final) memcpy(dS, J->d_final + sidx, sizeof(double) * (size_t)DD);
+    else            memset(dS, 0, sizeof(double) * (size_t)DD);
+    for (int64_t m = nseg - 1; m >= 0; --m) {
+        const int64_t s0 = t0 + m * BWD_SEG, s1 = (s0 + BWD_SEG < t1) ? s0 + BWD_SEG : t1;
+        /* seg[i] = state before token s0 + i; seg[s1 - s0] = state after the last */
+        memcpy(seg, ckpt + (size_t)m * (size_t)DD, sizeof(double) * (size_t)DD);
+        for (int64_t t = s0; t < s1; ++t) {
+            double *nxt = seg + (size_t)(t - s0 + 1) * (size_t)DD;
+            memcpy(nxt, seg + (size_t)(t - s0) * (size_t)DD, sizeof(double) * (size_t)DD);
+            const size_t row = (size_t)((b * J->T + t) * H + h);
+            token_update(nxt, Dk, Dv, J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
+                         J->v + row * (size_t)Dv, J->log_alpha + row * (size_t)Dk, J->beta[row], p, o_t);
+        }
+        for (int64_t t = s1 - 1; t >= s0; --t) {
+            const size_t row = (size_t)((b * J->T + t) * H + h);
+            token_backward(Dk, Dv, seg + (size_t)(t - s0) * (size_t)DD, seg + (size_t)(t - s0 + 1) * (size_t)DD,
+                           J->q + row * (size_t)Dk, J->k + row * (size_t)Dk, J->v + row * (size_t)Dv,
+                           J->log_alpha + row * (size_t)Dk, J->beta[row], J->d_o + row * (size_t)Dv,
+                           dS, Sd, p, u, du, dp,
+                           J->dq + row * (size_t)Dk, J->dk + row * (size_t)Dk, J->dv + row * (size_t)Dv,
+                           J->dlog_alpha + row * (size_t)Dk, J->dbeta + row);
+        }
+    }
+    if (J->d_init) memcpy(J->d_init + sidx, dS, sizeof(double) * (size_t)DD);
+    return 0;
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job *J = (bwd_job *)arg;
+    const int64_t DD = J->Dk * J->Dv;
+    int64_t maxL = J->T;  /* the longest sequence bounds the checkpoints */
+    const int64_t nck = (maxL + BWD_SEG - 1) / BWD_SEG + 1;
+    double *ckpt = (double *)malloc(sizeof(double) * (size_t)(nck * DD));
+    double *seg = (double *)malloc(sizeof(double) * (size_t)((BWD_SEG + 1) * DD));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)DD);
+    double *scratch = (double *)malloc(sizeof(double) * (size_t)(DD + 5 * J->Dv));
+    if (!ckpt || !seg || !dS || !scratch) { free(ckpt); free(seg); free(dS); free(scratch); return (void *)1; }
+    const int64_t units = J->N * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t un = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (un >= units) break;
+        run_bwd_unit(J, un / J->H, un % J->H, ckpt, seg, dS, scratch);
+    }
+    free(ckpt); free(seg); free(dS); free(scratch);
+    return NULL;
+}
+
+/*
+ * kda_oracle_backward: gradients of the KDA forward (kda_oracle_forward, same
+ * layouts and cu_seqlens rules) given d_o [B, T, H, Dv] and d_final
+ * [N, H, Dk, Dv] (NULL: zero).  Writes dq, dk, dlog_alpha [B, T, H, Dk],
+ * dv [B, T, H, Dv], dbeta [B, T, H] and d_init [N, H, Dk, Dv] (NULL: not
+ * written).  Tokens of no sequence are left untouched.  Threads and return
+ * codes as in kda_oracle_forward.
+ */
+int kda_oracle_backward(const double *q, const double *k, const double *v,
+                        const double *log_alpha, const double *beta,
+                        const double *init_state, const int32_t *cu_seqlens,
+                        int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t n_seqs,
+                        const double *d_o, const double *d_final,
+                        double *dq, double *dk, double *dv, double *dlog_alpha, double *dbeta,
+                        double *d_init, int n_threads)
+{
+    if (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk || !dv || !dlog_alpha || !dbeta) return -1;
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    bwd_job J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta;
+    J.init_state = init_state; J.d_o = d_o; J.d_final = d_final; J.cu_seqlens = cu_seqlens;
+    J.B = B; J.T = T; J.H = H; J.Dk = Dk; J.Dv = Dv;
+    J.dq = dq; J.dk = dk; J.dv = dv; J.dlog_alpha = dlog_alpha; J.dbeta = dbeta; J.d_init = d_init;
+    if (cu_seqlens) {
+        if (B != 1 || n_seqs < 1) return -1;
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != T) return -1;
+        for (int64_t n = 0; n < n_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+        J.N = n_seqs;
+    } else {
+        J.N = B;
+    }
+    pthread_mutex_init(&J.lock, NULL);
+    if (n_threads < 1) n_threads = 1;
+    if ((int64_t)n_threads > J.N * H) n_threads = (int)(J.N * H);
+    int rc = 0, started = 0;
+    pthread_t *tid = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!tid) rc = -2;
+    for (int i = 0; i < n_threads && rc == 0; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0) rc = -2;
+        else ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret) rc = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return rc;
 }
