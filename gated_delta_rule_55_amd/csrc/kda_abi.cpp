@@ -360,6 +360,139 @@ kda_status kda_layer_chunk_fwd(const void *q, const void *k, const void *v, cons
                           KDA_BF16, 64, o, final_state, workspace, ws_bytes, stream, 2, &L);
 }
 
+// Backward workspace: the forward's (packages, varlen plan), then the state
+// entering and the state gradient leaving every chunk, then the gradient
+// kernel's per-workgroup scratch; sections 256-byte aligned.
+static bool bwd_workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t D, int32_t N, bool varlen, bool bf16,
+                                int32_t C, size_t &out, size_t &fwd, size_t &pkg, int64_t &slots, size_t &states) {
+    if (!workspace_bytes(B, T, H, D, D, N, varlen, bf16, C, fwd, pkg, slots)) return false;
+    fwd = kda::align256(fwd);
+    states = 4;
+    if (!mul_ok(states, (uint64_t)slots) || !mul_ok(states, (uint64_t)H) || !mul_ok(states, (uint64_t)D) ||
+        !mul_ok(states, (uint64_t)D))
+        return false;
+    states = kda::align256(states);
+    const size_t scratch = (size_t)kda::kBwdMaxGroups * kda::kBwdScratchMats * (size_t)C * (size_t)D * 4;
+    if (states > (SIZE_MAX - fwd - scratch) / 2) return false;
+    out = fwd + 2 * states + scratch;
+    return true;
+}
+
+size_t kda_chunk_bwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                                    kda_dtype in_dtype, int32_t chunk_size) {
+    if (chunk_size == 0) chunk_size = 64;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
+    if (!supported_dim(Dk) || Dk != Dv) return 0;
+    if (B < 1 || T < 0 || H < 1 || n_seqs < 0) return 0;
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return 0;
+    chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
+    const bool varlen = n_seqs > 0 && B == 1;
+    size_t out = 0, fwd = 0, pkg = 0, states = 0;
+    int64_t slots = 0;
+    if (!bwd_workspace_bytes(B, T, H, Dk, varlen ? n_seqs : B, varlen, in_dtype == KDA_BF16, chunk_size, out, fwd,
+                             pkg, slots, states))
+        return 0;
+    return out;
+}
+
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
+                         const float *init_state, const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H,
+                         int32_t Dk, int32_t Dv, int32_t n_seqs, kda_dtype in_dtype, int32_t chunk_size,
+                         const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv,
+                         float *dlog_alpha, float *dbeta, float *d_init_state, void *workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+    g_err[0] = '\0';
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
+    if (!supported_dim(Dk) || Dk != Dv)
+        return fail(KDA_ERR_UNSUPPORTED, "Dk=%d Dv=%d: the backward needs Dk = Dv in {16, 32, 64, 128}", Dk, Dv);
+    if (chunk_size == 0) chunk_size = 64;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: must be 16, 32 or 64", chunk_size);
+    chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
+    if (B < 1 || T < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARG, "B=%d T=%lld H=%d: need B >= 1, T >= 0, H >= 1", B, (long long)T, H);
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen && B != 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens given but B=%d != 1", B);
+    if (varlen && n_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens given but n_seqs=%d", n_seqs);
+    if (!varlen && n_seqs != 0 && n_seqs != B)
+        return fail(KDA_ERR_INVALID_ARG, "n_seqs=%d without cu_seqlens (must be 0 or B)", n_seqs);
+    const int32_t N = varlen ? n_seqs : B;
+    if ((int64_t)N * H > 0x7fffffff || T > ((int64_t)1 << 40))
+        return fail(KDA_ERR_INVALID_ARG, "sizes exceed the supported range");
+    if (N == 0) return KDA_OK;
+    const bool bf16 = in_dtype == KDA_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    size_t bq, bg, bb, bs, bf;
+    if (!bytes_of(bq, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, esz) ||
+        !bytes_of(bg, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, 4) ||
+        !bytes_of(bb, {(uint64_t)B, (uint64_t)T, (uint64_t)H}, 4) ||
+        !bytes_of(bs, {(uint64_t)N, (uint64_t)H, (uint64_t)Dk, (uint64_t)Dv}, 4) ||
+        !bytes_of(bf, {(uint64_t)B, (uint64_t)T, (uint64_t)H, (uint64_t)Dk}, 4))
+        return fail(KDA_ERR_INVALID_ARG, "tensor sizes overflow size_t");
+    const size_t bc = varlen ? ((size_t)N + 1) * 4 : 0;
+    // Dk = Dv: q, k, v share a size, and so do the fp32 [B, T, H, D] tensors
+    const Input in[] = {
+        {q, "q", bq, 16, true},           {k, "k", bq, 16, true},
+        {v, "v", bq, 16, true},           {log_alpha, "log_alpha", bg, 16, true},
+        {beta, "beta", bb, 4, true},      {d_o, "d_o", bf, 16, true},
+        {cu_seqlens, "cu_seqlens", bc, 4, false},
+        {init_state, "init_state", init_state ? bs : 0, 16, false},
+        {d_final_state, "d_final_state", d_final_state ? bs : 0, 16, false},
+    };
+    const Input out[] = {
+        {dq, "dq", bf, 16, true},         {dk, "dk", bf, 16, true},
+        {dv, "dv", bf, 16, true},         {dlog_alpha, "dlog_alpha", bf, 16, true},
+        {dbeta, "dbeta", bb, 4, true},    {d_init_state, "d_init_state", d_init_state ? bs : 0, 16, false},
+    };
+    for (const Input &x : in) {
+        if (x.required && !x.p && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", x.name);
+        if (x.p && !aligned(x.p, x.align)) return fail(KDA_ERR_INVALID_ARG, "%s is not %u-byte aligned", x.name, x.align);
+    }
+    for (const Input &x : out) {
+        if (x.required && !x.p && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", x.name);
+        if (x.p && !aligned(x.p, x.align)) return fail(KDA_ERR_INVALID_ARG, "%s is not %u-byte aligned", x.name, x.align);
+    }
+    size_t need_ws = 0, fwd = 0, pkg = 0, states = 0;
+    int64_t slots = 0;
+    if (!bwd_workspace_bytes(B, T, H, Dk, N, varlen, bf16, chunk_size, need_ws, fwd, pkg, slots, states))
+        return fail(KDA_ERR_INVALID_ARG, "workspace size overflows size_t");
+    if (!workspace || ws_bytes < need_ws)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu needed", ws_bytes, workspace, need_ws);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    const Range rws = span(workspace, need_ws);
+    for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+        const Range ro = span(out[i].p, out[i].bytes);
+        if (overlap(ro, rws)) return fail(KDA_ERR_INVALID_ARG, "%s overlaps the workspace", out[i].name);
+        for (const Input &x : in)
+            if (overlap(ro, span(x.p, x.bytes))) return fail(KDA_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, x.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlap(ro, span(out[j].p, out[j].bytes)))
+                return fail(KDA_ERR_INVALID_ARG, "%s overlaps %s", out[i].name, out[j].name);
+    }
+    for (const Input &x : in)
+        if (overlap(rws, span(x.p, x.bytes))) return fail(KDA_ERR_INVALID_ARG, "workspace overlaps %s", x.name);
+
+    kda::BackwardArgs a{};
+    kda::PrefillArgs &f = a.fwd;
+    f.q = q; f.k = k; f.v = v; f.log_alpha = log_alpha; f.beta = beta;
+    f.init_state = init_state; f.cu_seqlens = cu_seqlens;
+    f.B = B; f.H = H; f.Dk = Dk; f.Dv = Dv; f.N = N; f.C = chunk_size; f.T = T;
+    f.bf16 = bf16; f.gate_mode = 0;
+    f.workspace = static_cast<char *>(workspace);
+    f.n_slots = slots; f.pkg_bytes = pkg;
+    f.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(f.workspace + pkg * (size_t)slots * (size_t)H) : nullptr;
+    a.d_o = d_o; a.d_final_state = d_final_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.d_init_state = d_init_state;
+    a.chunk_states = reinterpret_cast<float *>(f.workspace + fwd);
+    a.chunk_dstates = reinterpret_cast<float *>(f.workspace + fwd + states);
+    a.scratch = reinterpret_cast<float *>(f.workspace + fwd + 2 * states);
+    hipError_t e = kda::launch_backward(a, stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
 kda_status kda_layer_decode_step(const void *q, const void *k, const void *v, const void *x_alpha,
                                  const void *x_beta, const void *out_gate, const float *norm_weight,
                                  float l2_eps, float norm_eps, float *state, int32_t N, int32_t H,

@@ -1,0 +1,577 @@
+// kda_backward.hip -- chunked backward of the KDA prefill on gfx950.
+//
+// Gradients of the recurrence of the section "Kimi Delta Attention (KDA)" on
+// the page "Kimi Linear 高效注意力架构" (the training workload the page names),
+// taken through the same chunked form the forward uses.  Per chunk, with incoming state S0,
+// outgoing state S1 and the forward's quantities (G, Gamma, A = Diag(beta) Abar,
+// T = (I + A)^-1, P, W, U' as in kda_prefill.hip):
+//
+//   R = V - (K*Gamma) S0,  X = Diag(beta) R,  U = T X
+//   O = (Q*Gamma) S0 + P U,  S1 = Diag(Gamma_C) S0 + Kt^T U
+//
+// Given dO and dS1, reverse mode gives
+//
+//   dS0  = Diag(Gamma_C) dS1 + Q'^T dO - W^T (Kt dS1)          (state pass)
+//   dU   = P^T dO + Kt dS1,   dX = T^T dU,   dR = Diag(beta) dX = dV
+//   dT   = dU X^T,   dA = -T^T dT T^T (strictly lower),   dAbar = Diag(beta) dA
+//   dP   = dO U^T (lower),   d(Q*Gamma) = dO S0^T,   d(K*Gamma) = -dR S0^T,
+//   dKt  = U dS1^T,   dGamma_C = rowsum(S0 * dS1)
+//   dbeta_i = sum_v R_iv dX_iv + sum_j dA_ij Abar_ij
+//
+// and the decayed Gram products (e_ijc = exp(G_ic - G_jc), i >= j)
+//
+//   dq_i += sum_j dP_ij e_ij k_j,   dk_j += sum_i dP_ij e_ij q_i,
+//   dk_i += sum_j dAbar_ij e_ij k_j,   dk_j += sum_i dAbar_ij e_ij k_i,
+//
+// each pair term f contributing +f to dG_i and -f to dG_j; dlog_alpha is the
+// reverse cumulative sum of dG over the chunk (0 at -inf gates and resets).
+//
+// Passes: the forward's intra-chunk packages and a state pass that saves the
+// state entering every chunk (kda_prefill.hip), then bwd_state_kernel walks
+// each (sequence, head, 16-column slab) backwards writing dS1 of every chunk
+// and dS0 of the sequence, then intra_bwd_kernel computes every gradient of
+// one (chunk, head) at a time.  All arithmetic after the package is fp32
+// (fp32 matrix cores, exact exponentials of every decay pair).
+#include <algorithm>
+#include <type_traits>
+
+#include "kda_prefill.h"
+
+namespace kda {
+namespace {
+
+constexpr int kBwdThreads = 256;
+
+// acc += A B for one 16x16 output tile on the fp32 matrix cores, K a multiple
+// of 4: a(r, k) is element (r, k) of the tile's 16 rows of A, b(k, n) element
+// (k, n) of its 16 columns of B.  Lane l supplies row / column l % 16 at
+// k = 4 s + l / 16 of step s; the accumulator holds C[4 (l / 16) + r][l % 16].
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ void mm_f32(f32x4 &acc, FA &&a, FB &&b, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(r, k + kk), b(k + kk, r), acc, 0, 0, 0);
+}
+
+// sum over the 16 lanes of each row group (lanes 16 g .. 16 g + 15)
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+// -----------------------------------------------------------------------------
+// state pass, backwards: one workgroup per (sequence, head, 16-column slab)
+// -----------------------------------------------------------------------------
+template <int C, int D, bool BF>
+__global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p) {
+    using F = Cfg<C, D, D, BF>;
+    using Op = typename F::Op;
+    constexpr int NT16 = C / 16, NTK = D / 16, KSK = F::DKP / 32, KSC = F::CP / 32, NRT = 2 * NT16;
+    constexpr int GS = D + 1, SS = 17;
+    __shared__ float sW[C][GS], sQ[C][GS], sKt[C][GS];
+    __shared__ float sdO[C][SS], sdS[D][SS], sX[C][SS];
+    __shared__ float sGL[D];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
+    const int H = p.H;
+    int64_t tok_base, L, slot_base;
+    if (p.cu_seqlens) {
+        tok_base = p.cu_seqlens[n];
+        L = p.cu_seqlens[n + 1] - tok_base;
+        slot_base = p.chunk_offsets[n];
+    } else {
+        tok_base = static_cast<int64_t>(n) * p.T;
+        L = p.T;
+        slot_base = static_cast<int64_t>(n) * ((p.T + C - 1) / C);
+    }
+    const int64_t nchunks = (L + C - 1) / C;
+    const int col = 16 * ct + l16;
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
+
+    // dS slab: wave w owns the 16-channel tiles tk = w, w + 4, ...
+    constexpr int SPW = (NTK + 3) / 4;
+    f32x4 dS[SPW];
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl) {
+        const int tk = w + 4 * sl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dS[sl][r] = (tk < NTK && p.d_final) ? p.d_final[sbase + static_cast<size_t>(16 * tk + 4 * kg + r) * D + col]
+                                                : 0.f;
+    }
+
+    for (int64_t c = nchunks - 1; c >= 0; --c) {
+        const int64_t slot = slot_base + c;
+        const int nvalid = static_cast<int>(L - c * C < C ? L - c * C : C);
+        const char *pkg = p.ws + (static_cast<size_t>(slot) * H + h) * p.pkg_bytes;
+        // dS1 of this chunk: to the chunk-state buffer and to LDS
+        float *cds = p.chunk_dstates + (static_cast<size_t>(slot) * H + h) * D * D;
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * tk + 4 * kg + r;
+                    cds[static_cast<size_t>(row) * D + col] = dS[sl][r];
+                    sdS[row][l16] = dS[sl][r];
+                }
+            }
+        }
+        // the package's W, Q' and Kt as [token][channel] fp32, Gamma_C, the dO slab
+        const Op *wqp = reinterpret_cast<const Op *>(pkg + p.L.wq);
+        for (int b = w; b < NRT * KSK; b += 4) {
+            const int rt = b / KSK, ks = b % KSK;
+            const Op *src = wqp + (static_cast<size_t>(b) * 64 + lane) * 8;
+            const int i = 16 * (rt % NT16) + l16;
+            float(*dst)[GS] = rt < NT16 ? sW : sQ;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ch = 32 * ks + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4);
+                if (ch < D) dst[i][ch] = static_cast<float>(src[e]);
+            }
+        }
+        const Op *ktp = reinterpret_cast<const Op *>(pkg + p.L.kt);
+        for (int b = w; b < NTK * KSC; b += 4) {
+            const int tk = b / KSC, ks = b % KSC;
+            const Op *src = ktp + (static_cast<size_t>(b) * 64 + lane) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 32 * ks + 8 * kg + e;
+                if (i < C) sKt[i][16 * tk + l16] = static_cast<float>(src[e]);
+            }
+        }
+        for (int x = tid; x < D; x += kBwdThreads) sGL[x] = reinterpret_cast<const float *>(pkg + p.L.gl)[x];
+        for (int x = tid; x < C * 16; x += kBwdThreads) {
+            const int i = x / 16, j = x % 16;
+            sdO[i][j] = i < nvalid ? p.d_o[((tok_base + c * C + i) * H + h) * D + 16 * ct + j] : 0.f;
+        }
+        __syncthreads();
+        // X = Kt dS1 (C x 16), one 16-token tile per wave
+        if (w < NT16) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<D>(acc, [&](int r, int k) { return sKt[16 * w + r][k]; }, [&](int k, int nn) { return sdS[k][nn]; },
+                      lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sX[16 * w + 4 * kg + r][l16] = acc[r];
+        }
+        __syncthreads();
+        // dS0 = Diag(Gamma_C) dS1 + Q'^T dO - W^T X
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = sGL[16 * tk + 4 * kg + r] * dS[sl][r];
+                mm_f32<C>(acc, [&](int r, int k) { return sQ[k][16 * tk + r]; }, [&](int k, int nn) { return sdO[k][nn]; },
+                          lane);
+                mm_f32<C>(acc, [&](int r, int k) { return -sW[k][16 * tk + r]; }, [&](int k, int nn) { return sX[k][nn]; },
+                          lane);
+                dS[sl] = acc;
+            }
+        }
+        __syncthreads();  // LDS is refilled by the next (earlier) chunk
+    }
+    if (p.d_init) {
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p.d_init[sbase + static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] = dS[sl][r];
+            }
+        }
+    }
+}
+
+// -----------------------------------------------------------------------------
+// gradients of one (chunk, head) at a time; persistent workgroups
+// -----------------------------------------------------------------------------
+// Per-workgroup fp32 [C][D] scratch matrices in the workspace.
+enum Scratch { kKG, kQG, kKT, kR, kU, kDU, kDR, kDQ, kDK, kDG, kNumScratch };
+static_assert(kNumScratch == kBwdScratchMats, "scratch matrices per workgroup");
+
+template <int C, int D, bool BF>
+__global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p, int64_t n_items) {
+    using In = std::conditional_t<BF, uint16_t, float>;
+    // The cumulative decay G is held in fp64 on the fp32-input path: every decay
+    // factor is e^(G_i - G_j), and G_i, G_j of a chunk reach |G| ~ 10^2, so their
+    // fp32 roundings would put ~|G| 2^-24 into each factor (and the reverse sum
+    // of dG cancels); the difference is formed in fp64, the exponential in fp32.
+    using GT = std::conditional_t<BF, float, double>;
+    constexpr int GS = D + 1, MS = C + 1, NTI = C / 16, NTD = D / 16, NBI = C / 4;
+    constexpr int NBLK = NBI * (NBI + 1) / 2;
+    static_assert(NBLK <= kBwdThreads, "one 4x4 block of the Gram matrices per thread");
+    __shared__ GT sG[C][GS];
+    __shared__ In sK[C][GS], sQ[C][GS];
+    __shared__ float sM[4][C][MS];  // Abar; P -> dT -> dAbar; T; Y -> dP
+    __shared__ float sBeta[C];
+    __shared__ int sCnt[C], sNotRst[C];
+    __shared__ float sGC[D], sdGL[D];
+    __shared__ float sPart[C][NTD], sPart2[C][NTI], sPart3[NTI][D];
+    __shared__ int sFirst, sLast;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int H = p.H;
+    float *scr = p.scratch + static_cast<size_t>(blockIdx.x) * kNumScratch * C * D;
+    auto S_ = [&](int m) { return scr + static_cast<size_t>(m) * C * D; };
+    float *KG = S_(kKG), *QG = S_(kQG), *KT = S_(kKT), *R = S_(kR), *U = S_(kU), *DU = S_(kDU), *DR = S_(kDR);
+    float *DQ = S_(kDQ), *DK = S_(kDK), *DG = S_(kDG);
+    auto toF = [](In x) {
+        if constexpr (BF) return bf16_bits_to_f32(x);
+        else return x;
+    };
+
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        int64_t slot, hh;
+        divmod_nonneg(item, H, slot, hh);
+        const int h = static_cast<int>(hh);
+        int64_t tok0;
+        int nvalid;
+        if (!locate_chunk(slot, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) break;
+        const float *S0 = p.chunk_states + (static_cast<size_t>(slot) * H + h) * D * D;
+        const float *dS1 = p.chunk_dstates + (static_cast<size_t>(slot) * H + h) * D * D;
+        auto row_of = [&](int i) { return (tok0 + i) * H + h; };
+        auto dO_at = [&](int i, int col) { return i < nvalid ? p.d_o[row_of(i) * D + col] : 0.f; };
+
+        // ---- inputs, resets, cumulative decay (natural-log units)
+        for (int x = tid; x < C * D; x += kBwdThreads) {
+            const int i = x / D, c = x % D;
+            const bool ok = i < nvalid;
+            const int64_t o = row_of(ok ? i : 0) * D + c;
+            sK[i][c] = ok ? static_cast<const In *>(p.k)[o] : In(0);
+            sQ[i][c] = ok ? static_cast<const In *>(p.q)[o] : In(0);
+            sG[i][c] = ok ? static_cast<GT>(p.log_alpha[o]) : GT(0);
+        }
+        for (int i = tid; i < C; i += kBwdThreads) {
+            sBeta[i] = i < nvalid ? p.beta[row_of(i)] : 0.f;
+            sNotRst[i] = i < nvalid ? 0 : 1;
+        }
+        for (int x = tid; x < C * 4 * MS; x += kBwdThreads) (&sM[0][0][0])[x] = 0.f;
+        __syncthreads();
+        for (int x = tid; x < C * D; x += kBwdThreads) {
+            const int i = x / D, c = x % D;
+            if (i < nvalid && sG[i][c] != static_cast<GT>(kNegInf)) sNotRst[i] = 1;
+        }
+        __syncthreads();
+        for (int c = tid; c < D; c += kBwdThreads) {
+            GT acc = 0;
+            for (int i = 0; i < C; ++i) {
+                const GT g = sNotRst[i] ? (sG[i][c] > GT(kGFloor) ? sG[i][c] : GT(kGFloor)) : GT(0);
+                acc += g;
+                sG[i][c] = acc;
+            }
+        }
+        if (tid == 0) {
+            int cnt = 0, first = C, last = -1;
+            for (int i = 0; i < C; ++i) {
+                if (!sNotRst[i]) {
+                    ++cnt;
+                    if (first == C) first = i;
+                    last = i;
+                }
+                sCnt[i] = cnt;
+            }
+            sFirst = first;
+            sLast = last;
+        }
+        __syncthreads();
+        const int first_rst = sFirst, last_rst = sLast;
+
+        // ---- K*Gamma, Q*Gamma, Kt (scratch); Gamma_C
+        for (int x = tid; x < C * D; x += kBwdThreads) {
+            const int i = x / D, c = x % D;
+            const GT G = sG[i][c];
+            const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
+            const float eg = i < first_rst ? __expf(static_cast<float>(G)) : 0.f;
+            KG[x] = kv * eg;
+            QG[x] = qv * eg;
+            KT[x] = i >= last_rst ? kv * __expf(static_cast<float>(sG[C - 1][c] - G)) : 0.f;
+        }
+        for (int c = tid; c < D; c += kBwdThreads)
+            sGC[c] = last_rst >= 0 ? 0.f : __expf(static_cast<float>(sG[C - 1][c]));
+
+        // ---- Abar (strictly lower) and P (lower), exact decay per term
+        if (tid < NBLK) {
+            int bi = 0, bj = tid;
+            while (bj > bi) { bj -= bi + 1; ++bi; }
+            float a[4][4] = {}, pp[4][4] = {};
+            for (int c = 0; c < D; ++c) {
+                GT gi[4], gj[4];
+                float ki[4], kj[4], qi[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    gi[x] = sG[4 * bi + x][c];
+                    gj[x] = sG[4 * bj + x][c];
+                    ki[x] = toF(sK[4 * bi + x][c]);
+                    kj[x] = toF(sK[4 * bj + x][c]);
+                    qi[x] = toF(sQ[4 * bi + x][c]);
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        const float e = __expf(fminf(static_cast<float>(gi[x] - gj[y]), 0.f)) * kj[y];
+                        a[x][y] += ki[x] * e;
+                        pp[x][y] += qi[x] * e;
+                    }
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int i = 4 * bi + x, j = 4 * bj + y;
+                    const bool nores = sCnt[i] == sCnt[j];
+                    sM[0][i][j] = (j < i && nores) ? a[x][y] : 0.f;
+                    sM[1][i][j] = (j <= i && nores) ? pp[x][y] : 0.f;
+                }
+        }
+        __syncthreads();
+
+        // ---- T = (I + Diag(beta) Abar)^-1, one column per thread (forward
+        //      substitution; the column is built in place in LDS)
+        if (tid < C) {
+            const int j = tid;
+            for (int i = 0; i < C; ++i) {
+                float acc = 0.f;
+                for (int m = j; m < i; ++m) acc += sM[0][i][m] * sM[2][m][j];
+                sM[2][i][j] = i < j ? 0.f : (i == j ? 1.f : -sBeta[i] * acc);
+            }
+        }
+        __syncthreads();  // also: K*Gamma, Kt written
+
+        // ---- R = V - (K*Gamma) S0
+        for (int t = w; t < NTI * NTD; t += 4) {
+            const int ti = t / NTD, td = t % NTD;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<D>(acc, [&](int r, int k) { return KG[(16 * ti + r) * D + k]; },
+                      [&](int k, int nn) { return S0[static_cast<size_t>(k) * D + 16 * td + nn]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
+                const float vv = i < nvalid ? toF(static_cast<const In *>(p.v)[row_of(i) * D + cc]) : 0.f;
+                R[i * D + cc] = vv - acc[r];
+            }
+        }
+        __syncthreads();
+        // ---- U = T Diag(beta) R;  dU = P^T dO + Kt dS1
+        for (int t = w; t < NTI * NTD; t += 4) {
+            const int ti = t / NTD, td = t % NTD;
+            f32x4 u = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<C>(u, [&](int r, int k) { return sM[2][16 * ti + r][k]; },
+                      [&](int k, int nn) { return sBeta[k] * R[k * D + 16 * td + nn]; }, lane);
+            mm_f32<C>(du, [&](int r, int k) { return sM[1][k][16 * ti + r]; },
+                      [&](int k, int nn) { return dO_at(k, 16 * td + nn); }, lane);
+            mm_f32<D>(du, [&](int r, int k) { return KT[(16 * ti + r) * D + k]; },
+                      [&](int k, int nn) { return dS1[static_cast<size_t>(k) * D + 16 * td + nn]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
+                U[i * D + cc] = u[r];
+                DU[i * D + cc] = du[r];
+            }
+        }
+        __syncthreads();
+        // ---- dX = T^T dU;  dR = dV = Diag(beta) dX;  dbeta (value part)
+        for (int t = w; t < NTI * NTD; t += 4) {
+            const int ti = t / NTD, td = t % NTD;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<C>(acc, [&](int r, int k) { return sM[2][k][16 * ti + r]; },
+                      [&](int k, int nn) { return DU[k * D + 16 * td + nn]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
+                const float dr = sBeta[i] * acc[r];
+                DR[i * D + cc] = dr;
+                if (i < nvalid) p.dv[row_of(i) * D + cc] = dr;
+                const float part = sum16(R[i * D + cc] * acc[r]);
+                if (l16 == 0) sPart[i][td] = part;
+            }
+        }
+        // ---- dT = dU X^T (into P's buffer: P is no longer needed)
+        for (int t = w; t < NTI * NTI; t += 4) {
+            const int ti = t / NTI, tj = t % NTI;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<D>(acc, [&](int r, int k) { return DU[(16 * ti + r) * D + k]; },
+                      [&](int k, int nn) { return sBeta[16 * tj + nn] * R[(16 * tj + nn) * D + k]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sM[3][16 * ti + 4 * kg + r][16 * tj + l16] = acc[r];
+        }
+        __syncthreads();
+        // Y = dT T^T  (dT in sM[3] for now, Y into sM[1])
+        for (int t = w; t < NTI * NTI; t += 4) {
+            const int ti = t / NTI, tj = t % NTI;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<C>(acc, [&](int r, int k) { return sM[3][16 * ti + r][k]; },
+                      [&](int k, int nn) { return sM[2][16 * tj + nn][k]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sM[1][16 * ti + 4 * kg + r][16 * tj + l16] = acc[r];
+        }
+        __syncthreads();
+        // dA = -T^T Y (strictly lower, no reset in (j, i]) into sM[3]; dbeta (gate
+        // part) = sum_j dA_ij Abar_ij; then dAbar = Diag(beta) dA in place
+        for (int t = w; t < NTI * NTI; t += 4) {
+            const int ti = t / NTI, tj = t % NTI;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<C>(acc, [&](int r, int k) { return sM[2][k][16 * ti + r]; },
+                      [&](int k, int nn) { return sM[1][k][16 * tj + nn]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, j = 16 * tj + l16;
+                const float da = (j < i && sCnt[i] == sCnt[j]) ? -acc[r] : 0.f;
+                const float part = sum16(da * sM[0][i][j]);
+                if (l16 == 0) sPart2[i][tj] = part;
+                sM[3][i][j] = sBeta[i] * da;
+            }
+        }
+        __syncthreads();
+        // ---- dP = dO U^T (lower, no reset in (j, i]) into sM[1]
+        for (int t = w; t < NTI * NTI; t += 4) {
+            const int ti = t / NTI, tj = t % NTI;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mm_f32<D>(acc, [&](int r, int k) { return dO_at(16 * ti + r, k); },
+                      [&](int k, int nn) { return U[(16 * tj + nn) * D + k]; }, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, j = 16 * tj + l16;
+                sM[1][i][j] = (j <= i && sCnt[i] == sCnt[j]) ? acc[r] : 0.f;
+            }
+        }
+        // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
+        //      their Gamma terms
+        for (int t = w; t < NTI * NTD; t += 4) {
+            const int ti = t / NTD, tc = t % NTD;
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
+            mm_f32<D>(aq, [&](int r, int k) { return dO_at(16 * ti + r, k); },
+                      [&](int k, int nn) { return S0[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
+            mm_f32<D>(ak, [&](int r, int k) { return DR[(16 * ti + r) * D + k]; },
+                      [&](int k, int nn) { return S0[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
+            mm_f32<D>(at, [&](int r, int k) { return U[(16 * ti + r) * D + k]; },
+                      [&](int k, int nn) { return dS1[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
+            float colsum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * kg + r, c = 16 * tc + l16;
+                const float qg = QG[i * D + c], kgm = KG[i * D + c], ktv = KT[i * D + c];
+                const float eg = i < first_rst ? __expf(static_cast<float>(sG[i][c])) : 0.f;
+                const float et = i >= last_rst ? __expf(static_cast<float>(sG[C - 1][c] - sG[i][c])) : 0.f;
+                DQ[i * D + c] = aq[r] * eg;
+                DK[i * D + c] = -ak[r] * eg + at[r] * et;
+                DG[i * D + c] = aq[r] * qg - ak[r] * kgm - at[r] * ktv;
+                colsum += at[r] * ktv;
+            }
+            colsum += __shfl_xor(colsum, 16);
+            colsum += __shfl_xor(colsum, 32);
+            if (kg == 0) sPart3[ti][16 * tc + l16] = colsum;
+        }
+        __syncthreads();
+        // dG of the chunk's last token: dKt terms and dGamma_C = rowsum(S0 * dS1)
+        for (int c = tid; c < D; c += kBwdThreads) {
+            float s = 0.f;
+            for (int v = 0; v < D; ++v) s += S0[static_cast<size_t>(c) * D + v] * dS1[static_cast<size_t>(c) * D + v];
+            float acc = s * sGC[c];
+            for (int ti = 0; ti < NTI; ++ti) acc += sPart3[ti][c];
+            sdGL[c] = acc;
+        }
+        // ---- the decayed Gram products, exact decay per term; dq, dk out
+        for (int x = tid; x < C * D; x += kBwdThreads) {
+            const int i = x / D, c = x % D;
+            const GT Gi = sG[i][c];
+            float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
+            for (int j = 0; j <= i; ++j) {
+                const float e = __expf(static_cast<float>(Gi - sG[j][c])) * toF(sK[j][c]);
+                rowP += sM[1][i][j] * e;
+                rowA += sM[3][i][j] * e;
+            }
+            for (int m = i; m < C; ++m) {
+                const float e = __expf(static_cast<float>(sG[m][c] - Gi));
+                colP += sM[1][m][i] * e * toF(sQ[m][c]);
+                colA += sM[3][m][i] * e * toF(sK[m][c]);
+            }
+            const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
+            if (i < nvalid) {
+                p.dq[row_of(i) * D + c] = DQ[x] + rowP;
+                p.dk[row_of(i) * D + c] = DK[x] + rowA + colP + colA;
+            }
+            DG[x] += qv * rowP + kv * rowA - kv * (colP + colA);
+        }
+        __syncthreads();
+        // ---- dlog_alpha = reverse cumulative sum of dG; dbeta
+        for (int c = tid; c < D; c += kBwdThreads) {
+            GT acc = sdGL[c];
+            for (int i = C - 1; i >= 0; --i) {
+                acc += DG[i * D + c];
+                if (i < nvalid) {
+                    const int64_t o = row_of(i) * D + c;
+                    p.dlog_alpha[o] = (sNotRst[i] && p.log_alpha[o] != kNegInf) ? static_cast<float>(acc) : 0.f;
+                }
+            }
+        }
+        for (int i = tid; i < nvalid; i += kBwdThreads) {
+            float s = 0.f;
+            for (int td = 0; td < NTD; ++td) s += sPart[i][td];
+            for (int tj = 0; tj < NTI; ++tj) s += sPart2[i][tj];
+            p.dbeta[row_of(i)] = s;
+        }
+        __syncthreads();  // LDS and scratch are reused by the next item
+    }
+}
+
+template <int C, int D, bool BF>
+hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t stream) {
+    PrefillArgs f = a.fwd;
+    f.o = nullptr;
+    f.final_state = nullptr;
+    hipError_t e = launch_forward_states<C, D, D, BF>(f, a.chunk_states, stream);
+    if (e != hipSuccess) return e;
+    const PackageLayout L = package_layout(C, D, D, BF);
+    BwdStateParams sp{f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N, f.workspace, f.pkg_bytes, L,
+                      a.d_o, a.d_final_state, a.chunk_dstates, a.d_init_state};
+    hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n_items = f.n_slots * f.H;
+    if (n_items <= 0) return hipSuccess;
+    const int64_t grid = std::min<int64_t>(n_items, std::min<int64_t>(kBwdMaxGroups, device_cu_count()));
+    BwdIntraParams ip{f.q, f.k, f.v, f.log_alpha, f.beta, f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N,
+                      a.d_o, a.chunk_states, a.chunk_dstates, a.scratch,
+                      a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta};
+    hipLaunchKernelGGL((intra_bwd_kernel<C, D, BF>), dim3(static_cast<unsigned>(grid)), dim3(kBwdThreads), 0, stream,
+                       ip, n_items);
+    return hipGetLastError();
+}
+
+template <int C, bool BF>
+hipError_t dispatch_bwd_d(const BackwardArgs &a, hipStream_t s) {
+    switch (a.fwd.Dk) {
+        case 16: return launch_bwd_t<C, 16, BF>(a, s);
+        case 32: return launch_bwd_t<C, 32, BF>(a, s);
+        case 64: return launch_bwd_t<C, 64, BF>(a, s);
+        case 128:
+            if constexpr (BF || C <= 32) return launch_bwd_t<C, 128, BF>(a, s);
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream) {
+    if (a.fwd.N == 0) return hipSuccess;
+    const bool bf = a.fwd.bf16;
+    switch (a.fwd.C) {
+        case 16: return bf ? dispatch_bwd_d<16, true>(a, stream) : dispatch_bwd_d<16, false>(a, stream);
+        case 32: return bf ? dispatch_bwd_d<32, true>(a, stream) : dispatch_bwd_d<32, false>(a, stream);
+        case 64: return bf ? dispatch_bwd_d<64, true>(a, stream) : dispatch_bwd_d<64, false>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kda

@@ -96,6 +96,23 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_layer_epilogue(float *o, const uint16_t *g, const float *w, int64_t rows, float eps,
                                  hipStream_t stream);
 
+// Backward of the prefill: fwd describes the forward call (its o and
+// final_state are unused; its workspace holds the packages and, for varlen,
+// the chunk plan).  chunk_states / chunk_dstates: [slots, H, Dk, Dv] fp32, the
+// state entering each chunk and the gradient with respect to the state leaving
+// it; scratch: kBwdMaxGroups * kBwdScratchMats * C * Dk fp32.
+struct BackwardArgs {
+    PrefillArgs fwd;
+    const float *d_o, *d_final_state;  // d_final_state nullable (zero)
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta;
+    float *d_init_state;               // nullable
+    float *chunk_states, *chunk_dstates, *scratch;
+};
+constexpr int kBwdMaxGroups = 1024;    // persistent workgroups of the gradient kernel
+constexpr int kBwdScratchMats = 10;    // fp32 [C][D] scratch matrices per workgroup
+
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
+
 // Chunk size the kernels use for a requested one (the fp32 path at d = 128 is
 // limited to 32 tokens by LDS capacity).  Results do not depend on it beyond
 // rounding.

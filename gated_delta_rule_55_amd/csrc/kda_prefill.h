@@ -38,11 +38,35 @@ struct StateParams {
     const float *init_state;
     const int32_t *cu_seqlens, *chunk_offsets;
     float *o, *final_state;
+    float *chunk_states;  // saving variant: the state entering each chunk, [slots, H, Dk, Dv]
     int64_t T;
     int32_t H, N;
     const char *ws;
     size_t pkg_bytes;
     PackageLayout L;
+};
+
+struct BwdStateParams {
+    const int32_t *cu_seqlens, *chunk_offsets;
+    int64_t T;
+    int32_t H, N;
+    const char *ws;
+    size_t pkg_bytes;
+    PackageLayout L;
+    const float *d_o, *d_final;  // d_final nullable
+    float *chunk_dstates;
+    float *d_init;               // nullable
+};
+
+struct BwdIntraParams {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    const int32_t *cu_seqlens, *chunk_offsets;
+    int64_t T;
+    int32_t H, N;
+    const float *d_o, *chunk_states, *chunk_dstates;
+    float *scratch;
+    float *dq, *dk, *dv, *dlog_alpha, *dbeta;
 };
 
 template <int C, int DK, int DV, bool BF>
@@ -177,5 +201,12 @@ inline int device_cu_count() {
 // Launches the register-resident intra-chunk kernel for 64-token chunks at
 // d_k = d_v = 128 with bf16 inputs (kda_intra_wide.hip).
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream);
+
+// The forward's intra-chunk pass (packages in a.workspace) followed by the
+// state pass in its saving variant: the state entering every chunk is written
+// to chunk_states [slots, H, DK, DV] fp32 and no output is produced
+// (kda_prefill.hip; instantiated for the shapes the backward supports).
+template <int C, int DK, int DV, bool BF>
+hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipStream_t stream);
 
 }  // namespace kda

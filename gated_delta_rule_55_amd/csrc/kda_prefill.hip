@@ -709,7 +709,9 @@ struct StateFrags {
     }
 };
 
-template <int C, int DK, int DV, bool BF>
+// SAVE: the saving variant (the backward's forward pass) writes the state
+// entering each chunk to p.chunk_states and stores no output.
+template <int C, int DK, int DV, bool BF, bool SAVE = false>
 __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     using F = Cfg<C, DK, DV, BF>;
     using Op = typename F::Op;
@@ -784,6 +786,17 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
         constexpr bool kPartial = decltype(partial_tag)::value;
         const int64_t rem = L - c * C;
         const int nvalid = static_cast<int>(rem < C ? rem : C);
+        if constexpr (SAVE) {
+            float *cs = p.chunk_states + (static_cast<size_t>(slot_base + c) * H + h) * DK * DV;
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+                const int tk = w + 4 * sl;
+                if (tk < NTK) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) cs[static_cast<size_t>(16 * tk + 4 * kg + r) * DV + col] = S[sl][r];
+                }
+            }
+        }
         __syncthreads();  // sS holds this chunk's incoming state
 
         // (a) [W; Q'] S0 for this wave's row tiles; U = U' - W S0, O = O_intra + Q' S0
@@ -814,7 +827,7 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
                     sU[0][l16][j] = hi;
                     if constexpr (BF) sU[1][l16][j] = static_cast<Op>(u[r] - static_cast<float>(hi));
                 }
-            } else {
+            } else if constexpr (!SAVE) {
                 const int I = rt - NT16;
                 const f32x4 ov = f.uo[rw] + acc;
                 float *orow = p.o + ((tok_base + c * C + 16 * I + 4 * kg) * H + h) * DV + col;
@@ -900,8 +913,9 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
 // -----------------------------------------------------------------------------
 // launch
 // -----------------------------------------------------------------------------
+// The intra-chunk pass: every (chunk, head) package into a.workspace.
 template <int C, int DK, int DV, bool BF>
-static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
+static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream) {
     const PackageLayout L = package_layout(C, DK, DV, BF);
     if (a.cu_seqlens) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, C,
@@ -933,8 +947,15 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
                            stream, ip, n_items);
         }
     }
-    StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state,
-                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
+    return hipSuccess;
+}
+
+template <int C, int DK, int DV, bool BF>
+static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
+    const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream);
+    if (ei != hipSuccess) return ei;
+    StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state, nullptr,
+                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
     hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
     if (a.gate_mode == 2 && a.T > 0) {
         const hipError_t e = hipGetLastError();
@@ -944,6 +965,26 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     }
     return hipGetLastError();
 }
+
+template <int C, int DK, int DV, bool BF>
+hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipStream_t stream) {
+    const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream);
+    if (ei != hipSuccess) return ei;
+    StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, nullptr, nullptr, chunk_states,
+                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
+    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF, true>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
+    return hipGetLastError();
+}
+// the shapes the backward supports: d_k = d_v, the chunk the forward uses
+#define KDA_FWD_STATES(C, D, BF) \
+    template hipError_t launch_forward_states<C, D, D, BF>(const PrefillArgs &, float *, hipStream_t);
+KDA_FWD_STATES(16, 16, true) KDA_FWD_STATES(16, 32, true) KDA_FWD_STATES(16, 64, true) KDA_FWD_STATES(16, 128, true)
+KDA_FWD_STATES(32, 16, true) KDA_FWD_STATES(32, 32, true) KDA_FWD_STATES(32, 64, true) KDA_FWD_STATES(32, 128, true)
+KDA_FWD_STATES(64, 16, true) KDA_FWD_STATES(64, 32, true) KDA_FWD_STATES(64, 64, true) KDA_FWD_STATES(64, 128, true)
+KDA_FWD_STATES(16, 16, false) KDA_FWD_STATES(16, 32, false) KDA_FWD_STATES(16, 64, false) KDA_FWD_STATES(16, 128, false)
+KDA_FWD_STATES(32, 16, false) KDA_FWD_STATES(32, 32, false) KDA_FWD_STATES(32, 64, false) KDA_FWD_STATES(32, 128, false)
+KDA_FWD_STATES(64, 16, false) KDA_FWD_STATES(64, 32, false) KDA_FWD_STATES(64, 64, false)
+#undef KDA_FWD_STATES
 
 template <int C, int DK, bool BF>
 static hipError_t dispatch_dv(const PrefillArgs &a, hipStream_t s) {

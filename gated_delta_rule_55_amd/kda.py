@@ -51,6 +51,11 @@ def load():
     lib.kda_layer_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, fp, f32, f32, fp, i32, i32, i32, i32,
                                           fp, vp]
     lib.kda_layer_decode_step.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = lib.kda_chunk_fwd_workspace_size.argtypes
+    lib.kda_chunk_bwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32, ctypes.c_int, i32,
+                                  fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -127,6 +132,43 @@ def _chunk_fwd(fn, q, k, v, log_alpha, beta, init_state, cu_seqlens, chunk_size,
               chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, final_state
+
+
+def bwd_workspace_size(B, T, H, D, n_seqs=0, dtype=torch.bfloat16, chunk_size=64) -> int:
+    """Bytes of workspace ``chunk_bwd`` needs (0 for unsupported sizes)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_chunk_bwd_workspace_size(B, T, H, D, D, n_seqs, code, chunk_size))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, cu_seqlens=None, d_final_state=None,
+              chunk_size=64, grads=None, output_d_init_state=True, workspace=None, stream=None):
+    """Gradients of ``chunk_fwd``: given d_o [B,T,H,Dv] fp32 (and optionally
+    d_final_state [N,H,Dk,Dv]), returns (dq, dk, dv, dlog_alpha, dbeta,
+    d_init_state) in fp32, d_init_state None unless requested.  Dk must equal Dv.
+    ``grads`` may supply the six output tensors."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = B if cu_seqlens is None else n_seqs
+    dev = q.device
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        grads = (torch.empty((B, T, H, Dk), **f32), torch.empty((B, T, H, Dk), **f32),
+                 torch.empty((B, T, H, Dv), **f32), torch.empty((B, T, H, Dk), **f32),
+                 torch.empty((B, T, H), **f32),
+                 torch.empty((N, H, Dk, Dv), **f32) if output_d_init_state else None)
+    dq, dk, dv, dla, dbeta, ds0 = grads
+    code = _dtype_code(q)
+    ws_bytes = int(lib.kda_chunk_bwd_workspace_size(B, T, H, Dk, Dv, n_seqs, code, chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(init_state),
+                             _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs, code, chunk_size, _ptr(d_o),
+                             _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(dbeta),
+                             _ptr(ds0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
+    return dq, dk, dv, dla, dbeta, ds0
 
 
 def decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):

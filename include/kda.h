@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 110 /* 1.1.0: adds the gdn_* and kda_layer_* entry points */
+#define KDA_VERSION 120 /* 1.2.0: adds kda_chunk_bwd (1.1.0: the gdn_* and kda_layer_* entry points) */
 
 typedef enum {
     KDA_OK = 0,
@@ -116,6 +116,45 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                          kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_bwd_workspace_size -- bytes of device workspace kda_chunk_bwd
+ * needs (host only, pure; 0 for invalid or unsupported arguments).  It holds
+ * the forward's packages, the state entering every chunk and the gradient of
+ * the state leaving it ([chunks, H, Dk, Dv] fp32 each), and a fixed scratch of
+ * 1024 x 10 x C x Dk fp32.
+ */
+size_t kda_chunk_bwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv,
+                                    int32_t n_seqs, kda_dtype in_dtype, int32_t chunk_size);
+
+/*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd (the training workload of the
+ * page "Kimi Linear 高效注意力架构"; the recurrence of its section "Kimi Delta
+ * Attention (KDA)", differentiated through the same chunked form).
+ *
+ *   q .. chunk_size     the forward's inputs, as in kda_chunk_fwd (the forward
+ *                       is recomputed; its outputs are not needed)
+ *   d_o           [B, T, H, Dv] fp32     gradient of the loss w.r.t. o
+ *   d_final_state [N, H, Dk, Dv] fp32, nullable (zero)   w.r.t. final_state
+ *   dq, dk        [B, T, H, Dk] fp32 out
+ *   dv            [B, T, H, Dv] fp32 out
+ *   dlog_alpha    [B, T, H, Dk] fp32 out (0 where log_alpha is -inf)
+ *   dbeta         [B, T, H]     fp32 out
+ *   d_init_state  [N, H, Dk, Dv] fp32 out, nullable      w.r.t. init_state
+ *   workspace     at least kda_chunk_bwd_workspace_size() bytes, 256-byte aligned
+ *
+ * Dk must equal Dv (KDA_ERR_UNSUPPORTED otherwise).  Outputs must not overlap
+ * each other, any input or the workspace; all pointers 16-byte aligned except
+ * beta, dbeta and cu_seqlens (4).  Arithmetic after the forward's packages is
+ * fp32; the result is bitwise deterministic.
+ */
+kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                         const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                         int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                         kda_dtype in_dtype, int32_t chunk_size, const float *d_o,
+                         const float *d_final_state, float *dq, float *dk, float *dv, float *dlog_alpha,
+                         float *dbeta, float *d_init_state, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * kda_decode_step -- one token for each of N independent sequences, the state

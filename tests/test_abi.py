@@ -36,13 +36,13 @@ def test_every_declared_function_is_exported(lib):
     assert {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size",
             "kda_status_string", "kda_last_error", "kda_version",
             "gdn_chunk_fwd", "gdn_decode_step", "kda_layer_chunk_fwd",
-            "kda_layer_decode_step"} <= set(names)
+            "kda_layer_decode_step", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 110
+    assert lib.kda_version() == 120
     for code, name in [(0, b"KDA_OK"), (1, b"KDA_ERR_INVALID_ARG"), (2, b"KDA_ERR_UNSUPPORTED"),
                        (3, b"KDA_ERR_WORKSPACE"), (4, b"KDA_ERR_HIP")]:
         assert lib.kda_status_string(code) == name
@@ -225,3 +225,55 @@ def test_layer_decode_rejects(lib):
     assert call(xb=FAKE + 0x4000001) == INVALID and b"x_beta" in lib.kda_last_error()
     assert call(o=FAKE + 0x8000000) == INVALID and b"o overlaps state" in lib.kda_last_error()
     assert call(N=0) == OK
+
+
+def test_bwd_workspace_size(lib):
+    fws, bws = lib.kda_chunk_fwd_workspace_size, lib.kda_chunk_bwd_workspace_size
+    # the forward's packages, two fp32 states per (chunk, head), a fixed scratch
+    a = bws(1, 4096, 32, 128, 128, 0, BF16, 64)
+    b = bws(1, 8192, 32, 128, 128, 0, BF16, 64)
+    states = 2 * 64 * 32 * 128 * 128 * 4  # 64 more chunks of 32 heads
+    assert b - a == (fws(1, 8192, 32, 128, 128, 0, BF16, 64) - fws(1, 4096, 32, 128, 128, 0, BF16, 64)) + states
+    assert a > fws(1, 4096, 32, 128, 128, 0, BF16, 64) + 2 * 64 * 32 * 128 * 128 * 4
+    for bad in [(1, 64, 1, 16, 32, 0, BF16, 16), (1, 64, 1, 24, 24, 0, BF16, 16), (1, 64, 1, 16, 16, 0, BF16, 48),
+                (0, 64, 1, 16, 16, 0, BF16, 16), (1, 64, 1, 16, 16, 0, 7, 16)]:
+        assert bws(*bad) == 0, bad
+
+
+def _bwd(lib, **kw):
+    base = FAKE
+    a = dict(q=base, k=base + 0x1000000, v=base + 0x2000000, log_alpha=base + 0x3000000,
+             beta=base + 0x4000000, init_state=None, cu_seqlens=None, B=1, T=64, H=1, Dk=16, Dv=16,
+             n_seqs=0, dtype=BF16, chunk=16, d_o=base + 0x5000000, d_final=None, dq=base + 0x6000000,
+             dk=base + 0x7000000, dv=base + 0x8000000, dla=base + 0x9000000, dbeta=base + 0xa000000,
+             ds0=None, ws=base + 0x10000000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_bwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
+                             p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"], a["Dk"], a["Dv"],
+                             a["n_seqs"], a["dtype"], a["chunk"], p(a["d_o"]), p(a["d_final"]), p(a["dq"]),
+                             p(a["dk"]), p(a["dv"]), p(a["dla"]), p(a["dbeta"]), p(a["ds0"]), p(a["ws"]),
+                             a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Dk=16, Dv=32), UNSUPPORTED, b"Dk = Dv"),
+    (dict(Dk=24, Dv=24), UNSUPPORTED, b"Dk = Dv"),
+    (dict(dtype=5), UNSUPPORTED, b"in_dtype"),
+    (dict(chunk=48), UNSUPPORTED, b"chunk_size"),
+    (dict(H=0), INVALID, b"H=0"),
+    (dict(d_o=None), INVALID, b"d_o is NULL"),
+    (dict(dq=None), INVALID, b"dq is NULL"),
+    (dict(dbeta=FAKE + 0xa000002), INVALID, b"dbeta is not 4-byte aligned"),
+    (dict(dk=FAKE + 0x7000008), INVALID, b"dk is not 16-byte aligned"),
+    (dict(dq=FAKE + 0x5000000), INVALID, b"dq overlaps d_o"),
+    (dict(dv=FAKE + 0x6000000), INVALID, b"dv overlaps dq"),
+    (dict(ds0=FAKE + 0x3000000), INVALID, b"d_init_state overlaps log_alpha"),
+    (dict(ws=FAKE + 0x9000000), INVALID, b"overlaps the workspace"),
+    (dict(ws=None), WORKSPACE, b"workspace"),
+    (dict(ws_bytes=1024), WORKSPACE, b"workspace"),
+    (dict(ws=FAKE + 0x10000010), INVALID, b"256-byte"),
+])
+def test_chunk_bwd_rejects(lib, kw, code, msg):
+    assert _bwd(lib, **kw) == code
+    assert msg in lib.kda_last_error()

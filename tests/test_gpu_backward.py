@@ -1,0 +1,114 @@
+"""kda_chunk_bwd on the GPU, through the C-ABI, against the fp64 backward oracle
+(reverse mode over the token loop, pinned by finite differences of the forward
+oracle), at the operator's parity bar applied to every gradient:
+max|gpu - oracle| <= tau * RMS(oracle), tau = 2e-2 for bf16 inputs and 1e-4
+for fp32 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_55_amd import kda, workloads
+from kda_testlib import TAU, assert_parity, log, oracle_threads
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_init_state")
+
+
+def _shrink(inp, D):
+    """Keeps the first D channels (q and k re-normalised) for smaller head dims."""
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name][..., :D].float()
+        out[name] = (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(inp[name].dtype)
+    out["v"] = inp["v"][..., :D].contiguous()
+    out["log_alpha"] = inp["log_alpha"][..., :D].contiguous()
+    if inp["init_state"] is not None:
+        out["init_state"] = inp["init_state"][:, :, :D, :D].contiguous()
+    return out
+
+
+def _cotangents(inp, seed, with_final=True):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    B, T, H, D = inp["v"].shape
+    d_o = torch.randn((B, T, H, D), device="cuda", generator=g)
+    dsf = torch.randn((inp["N"], H, inp["q"].shape[-1], D), device="cuda", generator=g) if with_final else None
+    return d_o, dsf
+
+
+def _run(inp, d_o, dsf, chunk):
+    names = ("q", "k", "v", "log_alpha", "beta")
+    grads = kda.chunk_bwd(*(inp[n] for n in names), d_o, inp["init_state"], inp["cu_seqlens"], dsf, chunk)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _check(inp, grads, d_o, dsf, tau, heads=None, label=""):
+    hs = (lambda x: x) if heads is None else (lambda x: x[:, :, heads])
+    sel = lambda x: None if x is None else (x if heads is None else x[:, heads])
+    ref = oracle.backward(*(hs(inp[n]) for n in ("q", "k", "v", "log_alpha", "beta")), sel(inp["init_state"]),
+                          inp["cu_seqlens"], hs(d_o), sel(dsf), n_threads=oracle_threads())
+    for name, got, r in zip(NAMES, grads, ref):
+        if got is None:
+            continue
+        got = got if heads is None else (got[:, heads] if name == "d_init_state" else got[:, :, heads])
+        assert_parity(got, r, tau, f"{label} {name}")
+
+
+@pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("bf16", 64, 32), ("bf16", 32, 16),
+                                        ("f32", 16, 16), ("f32", 64, 64), ("f32", 128, 32)])
+def test_bwd_ragged_small(dtype, D, C):
+    """T = 157 (no multiple of any chunk size), 2 heads, random initial and final-state gradients."""
+    log(f"bwd ragged dtype={dtype} D={D} C={C}")
+    inp = workloads.make_prefill("prefill", "cuda", seed=400 + D + C, T=157, H=2, dtype=dtype)
+    if D != 128:
+        inp = _shrink(inp, D)
+    d_o, dsf = _cotangents(inp, 401 + D)
+    grads = _run(inp, d_o, dsf, C)
+    _check(inp, grads, d_o, dsf, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32],
+           label=f"bwd {dtype} D={D} C={C}")
+
+
+def test_bwd_tiny_fp32_single_chunk():
+    """The 64-token, d = 16, C = 16 fp32 case without a final-state gradient."""
+    inp = workloads.make_prefill("tiny", "cuda", seed=0)
+    d_o, _ = _cotangents(inp, 3, with_final=False)
+    grads = _run(inp, d_o, None, 16)
+    _check(inp, grads, d_o, None, TAU[torch.float32], label="bwd tiny")
+
+
+def test_bwd_varlen_with_resets():
+    """Packed sequences (one empty, several partial chunks) with their own initial
+    states; one head resets inside a chunk, one channel gate is -inf."""
+    lens = [1, 64, 65, 130, 7, 0, 200, 33]
+    inp = workloads.make_prefill("varlen", "cuda", seed=31, H=3, lengths=lens)
+    g = torch.Generator(device="cuda").manual_seed(32)
+    inp["init_state"] = 0.02 * torch.randn((len(lens), 3, 128, 128), device="cuda", generator=g)
+    inp["log_alpha"][0, 100, 1] = float("-inf")
+    inp["log_alpha"][0, 300, 2, 5] = float("-inf")
+    d_o, dsf = _cotangents(inp, 33)
+    grads = _run(inp, d_o, dsf, 64)
+    _check(inp, grads, d_o, dsf, TAU[torch.bfloat16], label="bwd varlen")
+    dla = grads[3]
+    assert torch.all(dla[0, 100, 1] == 0) and dla[0, 300, 2, 5] == 0
+
+
+def test_bwd_prefill_workload_sampled_heads():
+    """T = 4096, H = 32, d = 128, bf16, random initial state: every gradient of
+    four heads (heads are independent, so the oracle runs on those alone)."""
+    log("bwd prefill workload 4096x32, heads 0 9 22 31")
+    inp = workloads.make_prefill("prefill", "cuda", seed=5)
+    d_o, dsf = _cotangents(inp, 6)
+    grads = _run(inp, d_o, dsf, 64)
+    for x in grads:
+        assert torch.isfinite(x).all()
+    _check(inp, grads, d_o, dsf, TAU[torch.bfloat16], heads=[0, 9, 22, 31], label="bwd prefill")
+
+
+def test_bwd_empty_sequence_passes_the_state_gradient():
+    inp = workloads.make_prefill("prefill", "cuda", seed=7, T=0, H=2)
+    d_o = torch.empty((1, 0, 2, 128), device="cuda")
+    dsf = torch.randn((1, 2, 128, 128), device="cuda")
+    grads = _run(inp, d_o, dsf, 64)
+    assert torch.equal(grads[5], dsf)
