@@ -16,7 +16,9 @@ After the timed KDA steps, the Gated DeltaNet (scalar-gate) variant is timed
 on the same tensors with one log gate per (token, head) -- gdn_chunk_fwd over
 the 1M-token workload and 64 gdn_decode_step calls -- and reported in the
 "gdn" object of the same JSON line; then the KDA layer (fused prologue and
-epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object.
+epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object;
+then the backward (kda_chunk_bwd) over the first 262,144 tokens of the same
+prefill inputs in the "backward" object.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -70,6 +72,14 @@ def layer_alg_bytes(T, H, Dk, Dv, N, decode=False):
     per = 2 * (2 * Dk + Dv) + 2 * Dk + 2 + 2 * Dv + 4 * Dv
     state = N * H * Dk * Dv * 4
     return T * H * per + state * (2 if decode else 1)
+
+
+def backward_alg_bytes(T, H, Dk, Dv, in_bytes=2):
+    """kda_chunk_bwd, per token and head: q, k, v (in_bytes each element),
+    log_alpha, beta and d_o read; dq, dk, dv, dlog_alpha, dbeta written (fp32)."""
+    read = in_bytes * (2 * Dk + Dv) + 4 * Dk + 4 + 4 * Dv
+    write = 4 * (3 * Dk + Dv) + 4
+    return T * H * (read + write)
 
 
 def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
@@ -261,6 +271,30 @@ def cpu_baseline(inp, heads, T_sample, threads):
     return dt
 
 
+def backward_leg(torch, kda, pin, dev, C):
+    """kda_chunk_bwd over the first 262,144 tokens of the long prefill inputs
+    (its workspace holds two fp32 states per (chunk, head), so the full 1M
+    tokens would not fit beside the forward's buffers), with d_o ~ N(0, 1) and
+    preallocated gradients and workspace.  Returns (call, T_B)."""
+    T, H, Dk, Dv = pin["T"], pin["H"], pin["q"].shape[-1], pin["v"].shape[-1]
+    T_B = min(T, 1 << 18)
+    bq, bk, bv, bla, bbeta = (pin[n][:, :T_B] for n in ("q", "k", "v", "log_alpha", "beta"))
+    bgen = torch.Generator(device=dev)
+    bgen.manual_seed(4)
+    b_do = torch.randn((1, T_B, H, Dv), generator=bgen, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    b_grads = (torch.empty((1, T_B, H, Dk), **f32), torch.empty((1, T_B, H, Dk), **f32),
+               torch.empty((1, T_B, H, Dv), **f32), torch.empty((1, T_B, H, Dk), **f32),
+               torch.empty((1, T_B, H), **f32), None)
+    b_ws = torch.empty(kda.bwd_workspace_size(1, T_B, H, Dk, 0, torch.bfloat16, C), dtype=torch.uint8,
+                       device=dev)
+
+    def backward():
+        kda.chunk_bwd(bq, bk, bv, bla, bbeta, b_do, None, None, None, C, grads=b_grads, workspace=b_ws)
+
+    return backward, T_B
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,7 +303,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
                     help="run one part only (for profilers); prints no JSON line")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
@@ -330,6 +364,12 @@ def main():
         kda.decode_step(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t],
                         din["beta"][t], state, out=od)
 
+    if args.only == "backward":
+        backward, _ = backward_leg(torch, kda, pin, dev, C)
+        for _ in range(args.warmup + args.steps):
+            backward()
+        torch.cuda.synchronize()
+        return
     if args.only:
         for _ in range(args.warmup + args.steps):
             if args.only == "prefill":
@@ -418,6 +458,23 @@ def main():
 
     warm(layer_prefill, layer_decode)
     l_pre_ms, l_dec_ms = timed(layer_prefill, layer_decode)
+    del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g
+
+    # ---- the backward (kda_chunk_bwd) over the first T_B tokens of the same inputs
+    backward, T_B = backward_leg(torch, kda, pin, dev, C)
+    for _ in range(args.warmup):
+        backward()
+    torch.cuda.synchronize()
+    b_ms = []
+    for _ in range(args.steps):
+        flush.zero_()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        backward()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b_ms.append(e0.elapsed_time(e1))
+    del backward
 
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
@@ -550,6 +607,25 @@ def main():
             "alg_bytes_per_step": l_db,
             "traffic": measured_traffic("kda_layer_decode_step"),
         },
+    }
+
+    b_ms.sort()
+    b_t = b_ms[len(b_ms) // 2] / 1e3
+    b_bytes = backward_alg_bytes(T_B, H, Dk, Dv)
+    result["backward"] = {
+        "workload": f"kda_chunk_bwd over the first {T_B} tokens of the long prefill workload (H=32, "
+                    f"d=128, chunk 64, bf16 q/k/v, fp32 gates), d_o ~ N(0,1) fp32, no initial or "
+                    f"final state: gradients of q, k, v, log_alpha and beta (fp32)",
+        "T": T_B,
+        "ms_mean": sum(b_ms) / len(b_ms), "ms_median": b_t * 1e3,
+        "tokens_per_s": T_B / b_t,
+        "alg_bytes": b_bytes,
+        "hbm_frac_algorithmic": b_bytes / b_t / HBM_PEAK,
+        "roofline": {"kernel": "kda_chunk_bwd (forward packages and saved states, bwd_state_kernel, "
+                               "intra_bwd_kernel)",
+                     "bound": "hbm", "achieved": b_bytes / b_t / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": b_bytes / b_t / HBM_PEAK,
+                     "traffic": measured_traffic("kda_chunk_bwd")},
     }
 
     if not args.no_cpu_baseline:

@@ -46,11 +46,23 @@ constexpr int kBwdThreads = 256;
 // of 4: a(r, k) is element (r, k) of the tile's 16 rows of A, b(k, n) element
 // (k, n) of its 16 columns of B.  Lane l supplies row / column l % 16 at
 // k = 4 s + l / 16 of step s; the accumulator holds C[4 (l / 16) + r][l % 16].
+// The operands of up to 16 steps are loaded as one batch before their
+// products, so a batch costs one memory round trip.
 template <int K, typename FA, typename FB>
 __device__ __forceinline__ void mm_f32(f32x4 &acc, FA &&a, FB &&b, int lane) {
     const int r = lane & 15, kk = lane >> 4;
-#pragma unroll 8
-    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(r, k + kk), b(k + kk, r), acc, 0, 0, 0);
+    constexpr int BATCH = K / 4 < 16 ? K / 4 : 16;
+    static_assert(K % (4 * BATCH) == 0, "K is a multiple of the batch");
+    for (int k0 = 0; k0 < K; k0 += 4 * BATCH) {
+        float av[BATCH], bv[BATCH];
+#pragma unroll
+        for (int s = 0; s < BATCH; ++s) {
+            av[s] = a(r, k0 + 4 * s + kk);
+            bv[s] = b(k0 + 4 * s + kk, r);
+        }
+#pragma unroll
+        for (int s = 0; s < BATCH; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+    }
 }
 
 // sum over the 16 lanes of each row group (lanes 16 g .. 16 g + 15)
@@ -65,11 +77,112 @@ __device__ __forceinline__ float sum16(float x) {
 // -----------------------------------------------------------------------------
 // state pass, backwards: one workgroup per (sequence, head, 16-column slab)
 // -----------------------------------------------------------------------------
+// 8 package operand values of one lane (fp16 on the 16-bit path, fp32 otherwise)
+template <bool BF>
+struct Raw8;
+template <>
+struct Raw8<true> {
+    f16x8 v;
+    __device__ __forceinline__ void load(const void *p) { v = *reinterpret_cast<const f16x8 *>(p); }
+    __device__ __forceinline__ float at(int e) const { return static_cast<float>(v[e]); }
+};
+template <>
+struct Raw8<false> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const void *p) {
+        a = reinterpret_cast<const f32x4 *>(p)[0];
+        b = reinterpret_cast<const f32x4 *>(p)[1];
+    }
+    __device__ __forceinline__ float at(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+// One chunk's operands of the backward state pass as this thread loads them:
+// its blocks of the package's W / Q' and Kt fragments, its share of Gamma_C
+// and of the dO slab.  The next (earlier) chunk's are loaded while one computes.
 template <int C, int D, bool BF>
-__global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p) {
+struct BwdFrags {
     using F = Cfg<C, D, D, BF>;
     using Op = typename F::Op;
-    constexpr int NT16 = C / 16, NTK = D / 16, KSK = F::DKP / 32, KSC = F::CP / 32, NRT = 2 * NT16;
+    static constexpr int NT16 = C / 16, NTK = D / 16, KSK = F::DKP / 32, KSC = F::CP / 32, NRT = 2 * NT16;
+    static constexpr int WQB = (NRT * KSK + 3) / 4, KTB = (NTK * KSC + 3) / 4;
+    static constexpr int DOE = (C * 16 + kBwdThreads - 1) / kBwdThreads, GLE = (D + kBwdThreads - 1) / kBwdThreads;
+    Raw8<BF> wq[WQB], kt[KTB];
+    float dO[DOE], gl[GLE];
+
+    __device__ __forceinline__ void load(const BwdStateParams &p, const char *pkg, int64_t row0, int nvalid, int ct,
+                                         int h, int tid) {
+        const int lane = tid & 63, w = tid >> 6;
+        const Op *wqp = reinterpret_cast<const Op *>(pkg + p.L.wq);
+#pragma unroll
+        for (int j = 0; j < WQB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NRT * KSK) wq[j].load(wqp + (static_cast<size_t>(b) * 64 + lane) * 8);
+        }
+        const Op *ktp = reinterpret_cast<const Op *>(pkg + p.L.kt);
+#pragma unroll
+        for (int j = 0; j < KTB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NTK * KSC) kt[j].load(ktp + (static_cast<size_t>(b) * 64 + lane) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < GLE; ++j) {
+            const int x = tid + kBwdThreads * j;
+            gl[j] = x < D ? reinterpret_cast<const float *>(pkg + p.L.gl)[x] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < DOE; ++j) {
+            const int x = tid + kBwdThreads * j, i = x / 16, jj = x % 16;
+            dO[j] = (x < C * 16 && i < nvalid) ? p.d_o[((row0 + i) * p.H + h) * D + 16 * ct + jj] : 0.f;
+        }
+    }
+
+    // scatter into the [token][channel] fp32 LDS copies
+    template <int GS, int SS>
+    __device__ __forceinline__ void store(float (*sW)[GS], float (*sQ)[GS], float (*sKt)[GS], float *sGL,
+                                          float (*sdO)[SS], int tid) const {
+        const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < WQB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NRT * KSK) {
+                const int rt = b / KSK, ks = b % KSK, i = 16 * (rt % NT16) + l16;
+                float(*dst)[GS] = rt < NT16 ? sW : sQ;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ch = 32 * ks + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4);
+                    if (ch < D) dst[i][ch] = wq[j].at(e);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KTB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NTK * KSC) {
+                const int tk = b / KSC, ks = b % KSC;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 32 * ks + 8 * kg + e;
+                    if (i < C) sKt[i][16 * tk + l16] = kt[j].at(e);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GLE; ++j) {
+            const int x = tid + kBwdThreads * j;
+            if (x < D) sGL[x] = gl[j];
+        }
+#pragma unroll
+        for (int j = 0; j < DOE; ++j) {
+            const int x = tid + kBwdThreads * j;
+            if (x < C * 16) sdO[x / 16][x % 16] = dO[j];
+        }
+    }
+};
+
+template <int C, int D, bool BF>
+__global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p) {
+    using Frags = BwdFrags<C, D, BF>;
+    constexpr int NT16 = C / 16, NTK = D / 16;
     constexpr int GS = D + 1, SS = 17;
     __shared__ float sW[C][GS], sQ[C][GS], sKt[C][GS];
     __shared__ float sdO[C][SS], sdS[D][SS], sX[C][SS];
@@ -92,6 +205,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
     const int64_t nchunks = (L + C - 1) / C;
     const int col = 16 * ct + l16;
     const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
+    auto pkg_of = [&](int64_t c) { return p.ws + (static_cast<size_t>(slot_base + c) * H + h) * p.pkg_bytes; };
+    auto nvalid_of = [&](int64_t c) { return static_cast<int>(L - c * C < C ? L - c * C : C); };
 
     // dS slab: wave w owns the 16-channel tiles tk = w, w + 4, ...
     constexpr int SPW = (NTK + 3) / 4;
@@ -105,12 +220,11 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
                                                 : 0.f;
     }
 
+    Frags cur, nxt;
+    if (nchunks > 0) cur.load(p, pkg_of(nchunks - 1), tok_base + (nchunks - 1) * C, nvalid_of(nchunks - 1), ct, h, tid);
     for (int64_t c = nchunks - 1; c >= 0; --c) {
-        const int64_t slot = slot_base + c;
-        const int nvalid = static_cast<int>(L - c * C < C ? L - c * C : C);
-        const char *pkg = p.ws + (static_cast<size_t>(slot) * H + h) * p.pkg_bytes;
         // dS1 of this chunk: to the chunk-state buffer and to LDS
-        float *cds = p.chunk_dstates + (static_cast<size_t>(slot) * H + h) * D * D;
+        float *cds = p.chunk_dstates + (static_cast<size_t>(slot_base + c) * H + h) * D * D;
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
@@ -123,34 +237,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
                 }
             }
         }
-        // the package's W, Q' and Kt as [token][channel] fp32, Gamma_C, the dO slab
-        const Op *wqp = reinterpret_cast<const Op *>(pkg + p.L.wq);
-        for (int b = w; b < NRT * KSK; b += 4) {
-            const int rt = b / KSK, ks = b % KSK;
-            const Op *src = wqp + (static_cast<size_t>(b) * 64 + lane) * 8;
-            const int i = 16 * (rt % NT16) + l16;
-            float(*dst)[GS] = rt < NT16 ? sW : sQ;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ch = 32 * ks + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4);
-                if (ch < D) dst[i][ch] = static_cast<float>(src[e]);
-            }
-        }
-        const Op *ktp = reinterpret_cast<const Op *>(pkg + p.L.kt);
-        for (int b = w; b < NTK * KSC; b += 4) {
-            const int tk = b / KSC, ks = b % KSC;
-            const Op *src = ktp + (static_cast<size_t>(b) * 64 + lane) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = 32 * ks + 8 * kg + e;
-                if (i < C) sKt[i][16 * tk + l16] = static_cast<float>(src[e]);
-            }
-        }
-        for (int x = tid; x < D; x += kBwdThreads) sGL[x] = reinterpret_cast<const float *>(pkg + p.L.gl)[x];
-        for (int x = tid; x < C * 16; x += kBwdThreads) {
-            const int i = x / 16, j = x % 16;
-            sdO[i][j] = i < nvalid ? p.d_o[((tok_base + c * C + i) * H + h) * D + 16 * ct + j] : 0.f;
-        }
+        cur.template store<GS, SS>(sW, sQ, sKt, sGL, sdO, tid);
+        if (c > 0) nxt.load(p, pkg_of(c - 1), tok_base + (c - 1) * C, nvalid_of(c - 1), ct, h, tid);
         __syncthreads();
         // X = Kt dS1 (C x 16), one 16-token tile per wave
         if (w < NT16) {
@@ -177,6 +265,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
             }
         }
         __syncthreads();  // LDS is refilled by the next (earlier) chunk
+        cur = nxt;
     }
     if (p.d_init) {
 #pragma unroll
@@ -197,8 +286,11 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
 enum Scratch { kKG, kQG, kKT, kR, kU, kDU, kDR, kDQ, kDK, kDG, kNumScratch };
 static_assert(kNumScratch == kBwdScratchMats, "scratch matrices per workgroup");
 
+constexpr int kBwdIntraThreads = 512;  // 8 waves: two per SIMD hide the products' memory latency
+constexpr int kIW = kBwdIntraThreads / 64;
+
 template <int C, int D, bool BF>
-__global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p, int64_t n_items) {
+__global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraParams p, int64_t n_items) {
     using In = std::conditional_t<BF, uint16_t, float>;
     // The cumulative decay G is held in fp64 on the fp32-input path: every decay
     // factor is e^(G_i - G_j), and G_i, G_j of a chunk reach |G| ~ 10^2, so their
@@ -207,7 +299,7 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
     using GT = std::conditional_t<BF, float, double>;
     constexpr int GS = D + 1, MS = C + 1, NTI = C / 16, NTD = D / 16, NBI = C / 4;
     constexpr int NBLK = NBI * (NBI + 1) / 2;
-    static_assert(NBLK <= kBwdThreads, "one 4x4 block of the Gram matrices per thread");
+    static_assert(NBLK <= kBwdIntraThreads, "one 4x4 block of the Gram matrices per thread");
     __shared__ GT sG[C][GS];
     __shared__ In sK[C][GS], sQ[C][GS];
     __shared__ float sM[4][C][MS];  // Abar; P -> dT -> dAbar; T; Y -> dP
@@ -217,8 +309,6 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
     __shared__ float sPart[C][NTD], sPart2[C][NTI], sPart3[NTI][D];
     __shared__ int sFirst, sLast;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l16 = lane & 15, kg = lane >> 4;
     const int H = p.H;
     float *scr = p.scratch + static_cast<size_t>(blockIdx.x) * kNumScratch * C * D;
     auto S_ = [&](int m) { return scr + static_cast<size_t>(m) * C * D; };
@@ -230,6 +320,12 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
     };
 
     for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        // lane-dependent addresses are recomputed per item: hoisted out of the
+        // loop they would be held in registers across all of it
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l16 = lane & 15, kg = lane >> 4;
         int64_t slot, hh;
         divmod_nonneg(item, H, slot, hh);
         const int h = static_cast<int>(hh);
@@ -242,7 +338,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         auto dO_at = [&](int i, int col) { return i < nvalid ? p.d_o[row_of(i) * D + col] : 0.f; };
 
         // ---- inputs, resets, cumulative decay (natural-log units)
-        for (int x = tid; x < C * D; x += kBwdThreads) {
+#pragma unroll
+        for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
             const bool ok = i < nvalid;
             const int64_t o = row_of(ok ? i : 0) * D + c;
@@ -250,18 +347,18 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
             sQ[i][c] = ok ? static_cast<const In *>(p.q)[o] : In(0);
             sG[i][c] = ok ? static_cast<GT>(p.log_alpha[o]) : GT(0);
         }
-        for (int i = tid; i < C; i += kBwdThreads) {
+        for (int i = tid; i < C; i += kBwdIntraThreads) {
             sBeta[i] = i < nvalid ? p.beta[row_of(i)] : 0.f;
             sNotRst[i] = i < nvalid ? 0 : 1;
         }
-        for (int x = tid; x < C * 4 * MS; x += kBwdThreads) (&sM[0][0][0])[x] = 0.f;
+        for (int x = tid; x < C * 4 * MS; x += kBwdIntraThreads) (&sM[0][0][0])[x] = 0.f;
         __syncthreads();
-        for (int x = tid; x < C * D; x += kBwdThreads) {
+        for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
             if (i < nvalid && sG[i][c] != static_cast<GT>(kNegInf)) sNotRst[i] = 1;
         }
         __syncthreads();
-        for (int c = tid; c < D; c += kBwdThreads) {
+        for (int c = tid; c < D; c += kBwdIntraThreads) {
             GT acc = 0;
             for (int i = 0; i < C; ++i) {
                 const GT g = sNotRst[i] ? (sG[i][c] > GT(kGFloor) ? sG[i][c] : GT(kGFloor)) : GT(0);
@@ -286,7 +383,7 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         const int first_rst = sFirst, last_rst = sLast;
 
         // ---- K*Gamma, Q*Gamma, Kt (scratch); Gamma_C
-        for (int x = tid; x < C * D; x += kBwdThreads) {
+        for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
             const GT G = sG[i][c];
             const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
@@ -295,7 +392,7 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
             QG[x] = qv * eg;
             KT[x] = i >= last_rst ? kv * __expf(static_cast<float>(sG[C - 1][c] - G)) : 0.f;
         }
-        for (int c = tid; c < D; c += kBwdThreads)
+        for (int c = tid; c < D; c += kBwdIntraThreads)
             sGC[c] = last_rst >= 0 ? 0.f : __expf(static_cast<float>(sG[C - 1][c]));
 
         // ---- Abar (strictly lower) and P (lower), exact decay per term
@@ -303,6 +400,7 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
             int bi = 0, bj = tid;
             while (bj > bi) { bj -= bi + 1; ++bi; }
             float a[4][4] = {}, pp[4][4] = {};
+#pragma unroll 2
             for (int c = 0; c < D; ++c) {
                 GT gi[4], gj[4];
                 float ki[4], kj[4], qi[4];
@@ -335,20 +433,53 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
 
-        // ---- T = (I + Diag(beta) Abar)^-1, one column per thread (forward
-        //      substitution; the column is built in place in LDS)
-        if (tid < C) {
-            const int j = tid;
-            for (int i = 0; i < C; ++i) {
-                float acc = 0.f;
-                for (int m = j; m < i; ++m) acc += sM[0][i][m] * sM[2][m][j];
-                sM[2][i][j] = i < j ? 0.f : (i == j ? 1.f : -sBeta[i] * acc);
-            }
+        // ---- T = (I + A)^-1 with A = Diag(beta) Abar, in place in sM[2]: the
+        //      16x16 diagonal blocks by forward substitution (one wave each, one
+        //      column per lane), then T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on
+        //      the fp32 matrix cores, one block row at a time
+        for (int x = tid; x < C * C; x += kBwdIntraThreads) {
+            const int i = x / C, j = x % C;
+            sM[2][i][j] = sBeta[i] * sM[0][i][j];
         }
-        __syncthreads();  // also: K*Gamma, Kt written
+        __syncthreads();
+        if (w < NTI && lane < 16) {
+            const int base = 16 * w, col = lane;
+            float tv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float val = (i == col) ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) val -= sM[2][base + i][base + j] * tv[j];
+                tv[i] = val;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sM[2][base + i][base + col] = i >= col ? tv[i] : 0.f;
+        }
+        __syncthreads();
+        for (int I = 1; I < NTI; ++I) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            const int J = w;
+            if (J < I) {
+                f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K)
+                    mm_f32<16>(xv, [&](int r, int k) { return sM[2][16 * I + r][16 * K + k]; },
+                               [&](int k, int nn) { return sM[2][16 * K + k][16 * J + nn]; }, lane);
+                // y = T_II xv: xv's rows come back through LDS-free lane exchange
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[2][16 * I + l16][16 * I + 4 * kg + r], xv[r], y, 0, 0, 0);
+            }
+            __syncthreads();
+            if (J < I) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sM[2][16 * I + 4 * kg + r][16 * J + l16] = -y[r];
+            }
+            __syncthreads();
+        }  // also: K*Gamma, Kt written
 
         // ---- R = V - (K*Gamma) S0
-        for (int t = w; t < NTI * NTD; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<D>(acc, [&](int r, int k) { return KG[(16 * ti + r) * D + k]; },
@@ -362,7 +493,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
         // ---- U = T Diag(beta) R;  dU = P^T dO + Kt dS1
-        for (int t = w; t < NTI * NTD; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 u = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
             mm_f32<C>(u, [&](int r, int k) { return sM[2][16 * ti + r][k]; },
@@ -380,7 +512,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
         // ---- dX = T^T dU;  dR = dV = Diag(beta) dX;  dbeta (value part)
-        for (int t = w; t < NTI * NTD; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<C>(acc, [&](int r, int k) { return sM[2][k][16 * ti + r]; },
@@ -396,7 +529,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
             }
         }
         // ---- dT = dU X^T (into P's buffer: P is no longer needed)
-        for (int t = w; t < NTI * NTI; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<D>(acc, [&](int r, int k) { return DU[(16 * ti + r) * D + k]; },
@@ -406,7 +540,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
         // Y = dT T^T  (dT in sM[3] for now, Y into sM[1])
-        for (int t = w; t < NTI * NTI; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<C>(acc, [&](int r, int k) { return sM[3][16 * ti + r][k]; },
@@ -417,7 +552,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         __syncthreads();
         // dA = -T^T Y (strictly lower, no reset in (j, i]) into sM[3]; dbeta (gate
         // part) = sum_j dA_ij Abar_ij; then dAbar = Diag(beta) dA in place
-        for (int t = w; t < NTI * NTI; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<C>(acc, [&](int r, int k) { return sM[2][k][16 * ti + r]; },
@@ -433,7 +569,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
         // ---- dP = dO U^T (lower, no reset in (j, i]) into sM[1]
-        for (int t = w; t < NTI * NTI; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mm_f32<D>(acc, [&](int r, int k) { return dO_at(16 * ti + r, k); },
@@ -446,7 +583,8 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
         //      their Gamma terms
-        for (int t = w; t < NTI * NTD; t += 4) {
+        #pragma unroll 1
+        for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, tc = t % NTD;
             f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
             mm_f32<D>(aq, [&](int r, int k) { return dO_at(16 * ti + r, k); },
@@ -472,16 +610,22 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
             if (kg == 0) sPart3[ti][16 * tc + l16] = colsum;
         }
         __syncthreads();
-        // dG of the chunk's last token: dKt terms and dGamma_C = rowsum(S0 * dS1)
-        for (int c = tid; c < D; c += kBwdThreads) {
+        // dG of the chunk's last token: dKt terms and dGamma_C = rowsum(S0 * dS1),
+        // one wave per row (coalesced), rows c = w, w + 8, ...
+        for (int c = w; c < D; c += kIW) {
             float s = 0.f;
-            for (int v = 0; v < D; ++v) s += S0[static_cast<size_t>(c) * D + v] * dS1[static_cast<size_t>(c) * D + v];
-            float acc = s * sGC[c];
-            for (int ti = 0; ti < NTI; ++ti) acc += sPart3[ti][c];
-            sdGL[c] = acc;
+#pragma unroll
+            for (int v = lane; v < D; v += 64) s += S0[static_cast<size_t>(c) * D + v] * dS1[static_cast<size_t>(c) * D + v];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+            if (lane == 0) {
+                float acc = s * sGC[c];
+                for (int ti = 0; ti < NTI; ++ti) acc += sPart3[ti][c];
+                sdGL[c] = acc;
+            }
         }
         // ---- the decayed Gram products, exact decay per term; dq, dk out
-        for (int x = tid; x < C * D; x += kBwdThreads) {
+        for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
             const GT Gi = sG[i][c];
             float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
@@ -504,17 +648,26 @@ __global__ void __launch_bounds__(kBwdThreads) intra_bwd_kernel(BwdIntraParams p
         }
         __syncthreads();
         // ---- dlog_alpha = reverse cumulative sum of dG; dbeta
-        for (int c = tid; c < D; c += kBwdThreads) {
+        for (int c = tid; c < D; c += kBwdIntraThreads) {
             GT acc = sdGL[c];
-            for (int i = C - 1; i >= 0; --i) {
-                acc += DG[i * D + c];
-                if (i < nvalid) {
-                    const int64_t o = row_of(i) * D + c;
-                    p.dlog_alpha[o] = (sNotRst[i] && p.log_alpha[o] != kNegInf) ? static_cast<float>(acc) : 0.f;
+            for (int i0 = C - 16; i0 >= 0; i0 -= 16) {  // 16 rows of the column per batch of loads
+                float dgc[16], la[16];
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int i = i0 + x;
+                    dgc[x] = DG[i * D + c];
+                    la[x] = i < nvalid ? p.log_alpha[row_of(i) * D + c] : 0.f;
+                }
+#pragma unroll
+                for (int x = 15; x >= 0; --x) {
+                    const int i = i0 + x;
+                    acc += dgc[x];
+                    if (i < nvalid)
+                        p.dlog_alpha[row_of(i) * D + c] = (sNotRst[i] && la[x] != kNegInf) ? static_cast<float>(acc) : 0.f;
                 }
             }
         }
-        for (int i = tid; i < nvalid; i += kBwdThreads) {
+        for (int i = tid; i < nvalid; i += kBwdIntraThreads) {
             float s = 0.f;
             for (int td = 0; td < NTD; ++td) s += sPart[i][td];
             for (int tj = 0; tj < NTI; ++tj) s += sPart2[i][tj];
@@ -543,7 +696,7 @@ hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t stream) {
     BwdIntraParams ip{f.q, f.k, f.v, f.log_alpha, f.beta, f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N,
                       a.d_o, a.chunk_states, a.chunk_dstates, a.scratch,
                       a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta};
-    hipLaunchKernelGGL((intra_bwd_kernel<C, D, BF>), dim3(static_cast<unsigned>(grid)), dim3(kBwdThreads), 0, stream,
+    hipLaunchKernelGGL((intra_bwd_kernel<C, D, BF>), dim3(static_cast<unsigned>(grid)), dim3(kBwdIntraThreads), 0, stream,
                        ip, n_items);
     return hipGetLastError();
 }
