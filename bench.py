@@ -119,7 +119,7 @@ def measured_traffic(key):
 # its traffic is the same for all (the package does not depend on the gate).
 KDA_INTRA = "kda::intra_wide_kernel<0>"
 GDN_INTRA = "kda::intra_wide_kernel<1>"
-STATE = "kda::state_kernel<64, 128, 128, true>"
+STATE = "kda::state_kernel<64, 128, 128, true, false>"
 KDA_DECODE = "kda::decode_step_kernel<128, 128, true, 0>"
 GDN_DECODE = "kda::decode_step_kernel<128, 128, true, 1>"
 LAYER_INTRA = "kda::intra_wide_kernel<2>"
@@ -181,7 +181,7 @@ def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma
     each run's output is the directory given here) and this summary's command line."""
     prof = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/{d} -o run -- " \
            "python3 <repo>/bench.py {a}"
-    bench_args = "--steps 1 --warmup 0 --no-cpu-baseline"
+    bench_args = "--steps 1 --warmup 0 --no-cpu-baseline --no-backward"
     cmds = [prof.format(c="FETCH_SIZE", d=fetch_dir, a=bench_args),
             prof.format(c="WRITE_SIZE", d=write_dir, a=bench_args),
             prof.format(c="FETCH_SIZE", d=copy_fetch_dir, a="--only copy --steps 2"),
@@ -301,6 +301,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (the forward profiles use this: the backward's own "
+                         "forward pass runs the same kernels at another size)")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
@@ -461,20 +464,21 @@ def main():
     del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g
 
     # ---- the backward (kda_chunk_bwd) over the first T_B tokens of the same inputs
-    backward, T_B = backward_leg(torch, kda, pin, dev, C)
-    for _ in range(args.warmup):
-        backward()
-    torch.cuda.synchronize()
     b_ms = []
-    for _ in range(args.steps):
-        flush.zero_()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        backward()
-        e1.record(stream)
+    if not args.no_backward:
+        backward, T_B = backward_leg(torch, kda, pin, dev, C)
+        for _ in range(args.warmup):
+            backward()
         torch.cuda.synchronize()
-        b_ms.append(e0.elapsed_time(e1))
-    del backward
+        for _ in range(args.steps):
+            flush.zero_()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            backward()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            b_ms.append(e0.elapsed_time(e1))
+        del backward
 
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
@@ -609,24 +613,25 @@ def main():
         },
     }
 
-    b_ms.sort()
-    b_t = b_ms[len(b_ms) // 2] / 1e3
-    b_bytes = backward_alg_bytes(T_B, H, Dk, Dv)
-    result["backward"] = {
-        "workload": f"kda_chunk_bwd over the first {T_B} tokens of the long prefill workload (H=32, "
-                    f"d=128, chunk 64, bf16 q/k/v, fp32 gates), d_o ~ N(0,1) fp32, no initial or "
-                    f"final state: gradients of q, k, v, log_alpha and beta (fp32)",
-        "T": T_B,
-        "ms_mean": sum(b_ms) / len(b_ms), "ms_median": b_t * 1e3,
-        "tokens_per_s": T_B / b_t,
-        "alg_bytes": b_bytes,
-        "hbm_frac_algorithmic": b_bytes / b_t / HBM_PEAK,
-        "roofline": {"kernel": "kda_chunk_bwd (forward packages and saved states, bwd_state_kernel, "
-                               "intra_bwd_kernel)",
-                     "bound": "hbm", "achieved": b_bytes / b_t / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": b_bytes / b_t / HBM_PEAK,
-                     "traffic": measured_traffic("kda_chunk_bwd")},
-    }
+    if b_ms:
+        b_ms.sort()
+        b_t = b_ms[len(b_ms) // 2] / 1e3
+        b_bytes = backward_alg_bytes(T_B, H, Dk, Dv)
+        result["backward"] = {
+            "workload": f"kda_chunk_bwd over the first {T_B} tokens of the long prefill workload (H=32, "
+                        f"d=128, chunk 64, bf16 q/k/v, fp32 gates), d_o ~ N(0,1) fp32, no initial or "
+                        f"final state: gradients of q, k, v, log_alpha and beta (fp32)",
+            "T": T_B,
+            "ms_mean": sum(b_ms) / len(b_ms), "ms_median": b_t * 1e3,
+            "tokens_per_s": T_B / b_t,
+            "alg_bytes": b_bytes,
+            "hbm_frac_algorithmic": b_bytes / b_t / HBM_PEAK,
+            "roofline": {"kernel": "kda_chunk_bwd (forward packages and saved states, bwd_state_kernel, "
+                                   "intra_bwd_kernel)",
+                         "bound": "hbm", "achieved": b_bytes / b_t / 1e9, "peak": HBM_PEAK / 1e9,
+                         "unit": "GB/s", "frac": b_bytes / b_t / HBM_PEAK,
+                         "traffic": measured_traffic("kda_chunk_bwd")},
+        }
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
