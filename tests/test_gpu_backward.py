@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from gated_delta_rule_55_amd import kda, workloads
-from kda_testlib import TAU, assert_parity, log, oracle_threads
+from kda_testlib import TAU, assert_parity, host64, log, oracle_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,56 @@ def test_bwd_empty_sequence_passes_the_state_gradient():
     dsf = torch.randn((1, 2, 128, 128), device="cuda")
     grads = _run(inp, d_o, dsf, 64)
     assert torch.equal(grads[5], dsf)
+
+
+def test_bwd_dense_batch_determinism_and_chunk_invariance():
+    """B = 3 sequences of 150 tokens (a partial chunk each) with initial states:
+    parity, bitwise-identical repeated calls, and C = 16 / 32 / 64 agreeing."""
+    g = torch.Generator(device="cuda").manual_seed(41)
+    B, T, H, D = 3, 150, 2, 64
+    nrm = lambda x: (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(torch.bfloat16)
+    inp = dict(q=nrm(torch.randn((B, T, H, D), device="cuda", generator=g)),
+               k=nrm(torch.randn((B, T, H, D), device="cuda", generator=g)),
+               v=torch.randn((B, T, H, D), device="cuda", generator=g).to(torch.bfloat16),
+               log_alpha=-torch.nn.functional.softplus(torch.randn((B, T, H, D), device="cuda", generator=g) + 1),
+               beta=torch.sigmoid(torch.randn((B, T, H), device="cuda", generator=g)),
+               init_state=0.05 * torch.randn((B, H, D, D), device="cuda", generator=g), cu_seqlens=None, N=B)
+    inp["log_alpha"][1, 70] = float("-inf")  # a reset in sequence 1
+    d_o, dsf = _cotangents(inp, 42)
+    ga = _run(inp, d_o, dsf, 64)
+    gb = _run(inp, d_o, dsf, 64)
+    for x, y in zip(ga, gb):
+        assert torch.equal(x, y)
+    _check(inp, ga, d_o, dsf, TAU[torch.bfloat16], label="bwd batch C=64")
+    for C in (16, 32):
+        gc = _run(inp, d_o, dsf, C)
+        for name, x, y in zip(NAMES, gc, ga):
+            assert_parity(x, host64(y), TAU[torch.bfloat16], f"bwd batch C={C} vs C=64 {name}")
+
+
+def test_bwd_state_gradient_chains_across_a_split():
+    """The backward of [0, T1) fed the state gradient that the backward of [T1, T)
+    returns (started from the forward's state at T1) equals the backward of [0, T):
+    the gradient analogue of split/resume."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=43, T=300, H=2, dtype="f32")
+    inp = _shrink(inp, 32)
+    g = torch.Generator(device="cuda").manual_seed(44)
+    inp["init_state"] = 0.05 * torch.randn((1, 2, 32, 32), device="cuda", generator=g)
+    d_o, dsf = _cotangents(inp, 45)
+    full = _run(inp, d_o, dsf, 32)
+    T1 = 130
+    cut = lambda x, a, b: x[:, a:b].contiguous()
+    names = ("q", "k", "v", "log_alpha", "beta")
+    first = {n: cut(inp[n], 0, T1) for n in names}
+    second = {n: cut(inp[n], T1, 300) for n in names}
+    _, s_mid = kda.chunk_fwd(*(first[n] for n in names), inp["init_state"], None, 32)
+    torch.cuda.synchronize()
+    second.update(init_state=s_mid, cu_seqlens=None, N=1)
+    first.update(init_state=inp["init_state"], cu_seqlens=None, N=1)
+    g2 = _run(second, cut(d_o, T1, 300), dsf, 32)
+    g1 = _run(first, cut(d_o, 0, T1), g2[5], 32)
+    tau = TAU[torch.float32]
+    for i, name in enumerate(NAMES[:5]):
+        whole = host64(full[i])
+        assert_parity(torch.cat([g1[i], g2[i]], dim=1), whole, tau, f"bwd split {name}")
+    assert_parity(g1[5], host64(full[5]), tau, "bwd split d_init_state")
