@@ -65,6 +65,32 @@ __device__ __forceinline__ void mm_f32(f32x4 &acc, FA &&a, FB &&b, int lane) {
     }
 }
 
+// The same product with the operands read 4 k at a time: a4(r, k0) returns
+// A[r][k0 .. k0 + 3] and b4(k0, n) B[k0 .. k0 + 3][n] (a 16-byte load where the
+// operand is contiguous in k).  Step (t, j) gives lane l the k = 16 t + 4 (l / 16) + j,
+// the same for both operands, so the steps still cover every k once.  K is a
+// multiple of 16.
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ void mm_f32_v(f32x4 &acc, FA &&a4, FB &&b4, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+    constexpr int NT = K / 16, BATCH = NT < 4 ? NT : 4;
+    static_assert(K % 16 == 0 && NT % BATCH == 0, "K is a multiple of 16 and of the batch");
+    for (int t0 = 0; t0 < NT; t0 += BATCH) {
+        f32x4 av[BATCH], bv[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            av[b] = a4(r, 16 * (t0 + b) + 4 * kk);
+            bv[b] = b4(16 * (t0 + b) + 4 * kk, r);
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[b][j], bv[b][j], acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
 // sum over the 16 lanes of each row group (lanes 16 g .. 16 g + 15)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1);
@@ -336,6 +362,9 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         const float *dS1 = p.chunk_dstates + (static_cast<size_t>(slot) * H + h) * D * D;
         auto row_of = [&](int i) { return (tok0 + i) * H + h; };
         auto dO_at = [&](int i, int col) { return i < nvalid ? p.d_o[row_of(i) * D + col] : 0.f; };
+        auto dO4 = [&](int i, int col) {
+            return i < nvalid ? ld4(p.d_o + row_of(i) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        };
 
         // ---- inputs, resets, cumulative decay (natural-log units)
 #pragma unroll
@@ -482,8 +511,11 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32<D>(acc, [&](int r, int k) { return KG[(16 * ti + r) * D + k]; },
-                      [&](int k, int nn) { return S0[static_cast<size_t>(k) * D + 16 * td + nn]; }, lane);
+            mm_f32_v<D>(acc, [&](int r, int k0) { return ld4(KG + (16 * ti + r) * D + k0); },
+                        [&](int k0, int nn) {
+                            const float *b = S0 + static_cast<size_t>(k0) * D + 16 * td + nn;
+                            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
+                        }, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
@@ -501,8 +533,11 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                       [&](int k, int nn) { return sBeta[k] * R[k * D + 16 * td + nn]; }, lane);
             mm_f32<C>(du, [&](int r, int k) { return sM[1][k][16 * ti + r]; },
                       [&](int k, int nn) { return dO_at(k, 16 * td + nn); }, lane);
-            mm_f32<D>(du, [&](int r, int k) { return KT[(16 * ti + r) * D + k]; },
-                      [&](int k, int nn) { return dS1[static_cast<size_t>(k) * D + 16 * td + nn]; }, lane);
+            mm_f32_v<D>(du, [&](int r, int k0) { return ld4(KT + (16 * ti + r) * D + k0); },
+                        [&](int k0, int nn) {
+                            const float *b = dS1 + static_cast<size_t>(k0) * D + 16 * td + nn;
+                            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
+                        }, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
@@ -533,8 +568,8 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32<D>(acc, [&](int r, int k) { return DU[(16 * ti + r) * D + k]; },
-                      [&](int k, int nn) { return sBeta[16 * tj + nn] * R[(16 * tj + nn) * D + k]; }, lane);
+            mm_f32_v<D>(acc, [&](int r, int k0) { return ld4(DU + (16 * ti + r) * D + k0); },
+                        [&](int k0, int nn) { return sBeta[16 * tj + nn] * ld4(R + (16 * tj + nn) * D + k0); }, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sM[3][16 * ti + 4 * kg + r][16 * tj + l16] = acc[r];
         }
@@ -573,8 +608,8 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32<D>(acc, [&](int r, int k) { return dO_at(16 * ti + r, k); },
-                      [&](int k, int nn) { return U[(16 * tj + nn) * D + k]; }, lane);
+            mm_f32_v<D>(acc, [&](int r, int k0) { return dO4(16 * ti + r, k0); },
+                        [&](int k0, int nn) { return ld4(U + (16 * tj + nn) * D + k0); }, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, j = 16 * tj + l16;
@@ -587,12 +622,12 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, tc = t % NTD;
             f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
-            mm_f32<D>(aq, [&](int r, int k) { return dO_at(16 * ti + r, k); },
-                      [&](int k, int nn) { return S0[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
-            mm_f32<D>(ak, [&](int r, int k) { return DR[(16 * ti + r) * D + k]; },
-                      [&](int k, int nn) { return S0[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
-            mm_f32<D>(at, [&](int r, int k) { return U[(16 * ti + r) * D + k]; },
-                      [&](int k, int nn) { return dS1[static_cast<size_t>(16 * tc + nn) * D + k]; }, lane);
+            mm_f32_v<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); },
+                        [&](int k0, int nn) { return ld4(S0 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
+            mm_f32_v<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); },
+                        [&](int k0, int nn) { return ld4(S0 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
+            mm_f32_v<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); },
+                        [&](int k0, int nn) { return ld4(dS1 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
             float colsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
