@@ -157,13 +157,14 @@ __device__ __forceinline__ void put4(uint32_t (&d)[4], const u32x4 &x) {
 
 // Loads one work item's inputs (raw 16-bit words still in load order: the
 // unpack puts them in the register layout once they have arrived).  Lane l
-// also loads the beta of token l.
+// of wave 0 also loads the beta of token l; the other waves, which do not use
+// it, all read token 0's (one cache line instead of one per token).
 template <int GM>
 __device__ __forceinline__ void fetch_item(const IntraParams &p, int64_t tok0, int nvalid, int h, int w, int t16,
                                            int kg, WideRaw &r) {
     const int H = p.H;
     {
-        const int l = 16 * kg + t16;
+        const int l = w == 0 ? 16 * kg + t16 : 0;
         const int64_t row = (tok0 + (l < nvalid ? l : nvalid - 1)) * H + h;
         if constexpr (GM == 2) r.xb = p.x_beta[row];
         else r.beta = p.beta[row];
