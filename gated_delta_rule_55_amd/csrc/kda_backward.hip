@@ -91,6 +91,41 @@ __device__ __forceinline__ void mm_f32_v(f32x4 &acc, FA &&a4, FB &&b4, int lane)
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// One lane's share of an operand over a whole contraction of K, in the order
+// of mm_f32_v: v[t][j] is its value at k = 16 t + 4 (lane / 16) + j, and
+// f4(k0, n) as mm_f32_v's b4.  Loaded once, it serves every output tile that
+// shares the operand.
+template <int K>
+struct Frag {
+    f32x4 v[K / 16];
+};
+
+template <int K, typename F4>
+__device__ __forceinline__ Frag<K> frag_of(F4 &&f4, int lane) {
+    Frag<K> f;
+    const int r = lane & 15, kk = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < K / 16; ++t) f.v[t] = f4(16 * t + 4 * kk, r);
+    return f;
+}
+
+// mm_f32_v with B given as a preloaded fragment
+template <int K, typename FA>
+__device__ __forceinline__ void mm_f32_vb(f32x4 &acc, FA &&a4, const Frag<K> &bf, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+    constexpr int NT = K / 16, BATCH = NT < 4 ? NT : 4;
+#pragma unroll
+    for (int t0 = 0; t0 < NT; t0 += BATCH) {
+        f32x4 av[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) av[b] = a4(r, 16 * (t0 + b) + 4 * kk);
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[b][j], bf.v[t0 + b][j], acc, 0, 0, 0);
+    }
+}
+
 // sum over the 16 lanes of each row group (lanes 16 g .. 16 g + 15)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1);
@@ -507,15 +542,18 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         }  // also: K*Gamma, Kt written
 
         // ---- R = V - (K*Gamma) S0
-        #pragma unroll 1
+                // (the column tile of every tile a wave takes, t = w + 8 m, is w % NTD: NTD
+        //  divides 8, so each wave loads its right-hand operand once per product)
+        static_assert(kIW % NTD == 0 && kIW % NTI == 0, "column tiles divide the waves");
+        const Frag<D> bS0 = frag_of<D>([&](int k0, int nn) {
+            const float *b = S0 + static_cast<size_t>(k0) * D + 16 * (w % NTD) + nn;
+            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
+        }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_v<D>(acc, [&](int r, int k0) { return ld4(KG + (16 * ti + r) * D + k0); },
-                        [&](int k0, int nn) {
-                            const float *b = S0 + static_cast<size_t>(k0) * D + 16 * td + nn;
-                            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
-                        }, lane);
+            mm_f32_vb<D>(acc, [&](int r, int k0) { return ld4(KG + (16 * ti + r) * D + k0); }, bS0, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
@@ -525,19 +563,33 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         }
         __syncthreads();
         // ---- U = T Diag(beta) R;  dU = P^T dO + Kt dS1
-        #pragma unroll 1
+                {
+            const int tdw = w % NTD;
+            const Frag<C> bX = frag_of<C>([&](int k0, int nn) {
+                const float *b = R + k0 * D + 16 * tdw + nn;
+                return f32x4{sBeta[k0] * b[0], sBeta[k0 + 1] * b[D], sBeta[k0 + 2] * b[2 * D], sBeta[k0 + 3] * b[3 * D]};
+            }, lane);
+            const Frag<C> bO = frag_of<C>([&](int k0, int nn) {
+                return f32x4{dO_at(k0, 16 * tdw + nn), dO_at(k0 + 1, 16 * tdw + nn), dO_at(k0 + 2, 16 * tdw + nn),
+                             dO_at(k0 + 3, 16 * tdw + nn)};
+            }, lane);
+            const Frag<D> bS1 = frag_of<D>([&](int k0, int nn) {
+                const float *b = dS1 + static_cast<size_t>(k0) * D + 16 * tdw + nn;
+                return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
+            }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 u = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-            mm_f32<C>(u, [&](int r, int k) { return sM[2][16 * ti + r][k]; },
-                      [&](int k, int nn) { return sBeta[k] * R[k * D + 16 * td + nn]; }, lane);
-            mm_f32<C>(du, [&](int r, int k) { return sM[1][k][16 * ti + r]; },
-                      [&](int k, int nn) { return dO_at(k, 16 * td + nn); }, lane);
-            mm_f32_v<D>(du, [&](int r, int k0) { return ld4(KT + (16 * ti + r) * D + k0); },
-                        [&](int k0, int nn) {
-                            const float *b = dS1 + static_cast<size_t>(k0) * D + 16 * td + nn;
-                            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
-                        }, lane);
+            mm_f32_vb<C>(u, [&](int r, int k0) {
+                const float *a = &sM[2][16 * ti + r][k0];
+                return f32x4{a[0], a[1], a[2], a[3]};
+            }, bX, lane);
+            mm_f32_vb<C>(du, [&](int r, int k0) {
+                return f32x4{sM[1][k0][16 * ti + r], sM[1][k0 + 1][16 * ti + r], sM[1][k0 + 2][16 * ti + r],
+                             sM[1][k0 + 3][16 * ti + r]};
+            }, bO, lane);
+            mm_f32_vb<D>(du, [&](int r, int k0) { return ld4(KT + (16 * ti + r) * D + k0); }, bS1, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
@@ -545,14 +597,21 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                 DU[i * D + cc] = du[r];
             }
         }
+        }
         __syncthreads();
         // ---- dX = T^T dU;  dR = dV = Diag(beta) dX;  dbeta (value part)
-        #pragma unroll 1
+                const Frag<C> bDU = frag_of<C>([&](int k0, int nn) {
+            const float *b = DU + k0 * D + 16 * (w % NTD) + nn;
+            return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
+        }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, td = t % NTD;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32<C>(acc, [&](int r, int k) { return sM[2][k][16 * ti + r]; },
-                      [&](int k, int nn) { return DU[k * D + 16 * td + nn]; }, lane);
+            mm_f32_vb<C>(acc, [&](int r, int k0) {
+                return f32x4{sM[2][k0][16 * ti + r], sM[2][k0 + 1][16 * ti + r], sM[2][k0 + 2][16 * ti + r],
+                             sM[2][k0 + 3][16 * ti + r]};
+            }, bDU, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
@@ -564,12 +623,15 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             }
         }
         // ---- dT = dU X^T (into P's buffer: P is no longer needed)
-        #pragma unroll 1
+                const Frag<D> bXT = frag_of<D>([&](int k0, int nn) {
+            const int j = 16 * (w % NTI) + nn;
+            return sBeta[j] * ld4(R + j * D + k0);
+        }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_v<D>(acc, [&](int r, int k0) { return ld4(DU + (16 * ti + r) * D + k0); },
-                        [&](int k0, int nn) { return sBeta[16 * tj + nn] * ld4(R + (16 * tj + nn) * D + k0); }, lane);
+            mm_f32_vb<D>(acc, [&](int r, int k0) { return ld4(DU + (16 * ti + r) * D + k0); }, bXT, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sM[3][16 * ti + 4 * kg + r][16 * tj + l16] = acc[r];
         }
@@ -604,12 +666,12 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         }
         __syncthreads();
         // ---- dP = dO U^T (lower, no reset in (j, i]) into sM[1]
-        #pragma unroll 1
+                const Frag<D> bUT = frag_of<D>([&](int k0, int nn) { return ld4(U + (16 * (w % NTI) + nn) * D + k0); }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTI; t += kIW) {
             const int ti = t / NTI, tj = t % NTI;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_v<D>(acc, [&](int r, int k0) { return dO4(16 * ti + r, k0); },
-                        [&](int k0, int nn) { return ld4(U + (16 * tj + nn) * D + k0); }, lane);
+            mm_f32_vb<D>(acc, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bUT, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * ti + 4 * kg + r, j = 16 * tj + l16;
@@ -618,16 +680,19 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         }
         // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
         //      their Gamma terms
-        #pragma unroll 1
+                const Frag<D> bS0T = frag_of<D>([&](int k0, int nn) {
+            return ld4(S0 + static_cast<size_t>(16 * (w % NTD) + nn) * D + k0);
+        }, lane);
+        const Frag<D> bS1T = frag_of<D>([&](int k0, int nn) {
+            return ld4(dS1 + static_cast<size_t>(16 * (w % NTD) + nn) * D + k0);
+        }, lane);
+#pragma unroll 1
         for (int t = w; t < NTI * NTD; t += kIW) {
             const int ti = t / NTD, tc = t % NTD;
             f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
-            mm_f32_v<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); },
-                        [&](int k0, int nn) { return ld4(S0 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
-            mm_f32_v<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); },
-                        [&](int k0, int nn) { return ld4(S0 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
-            mm_f32_v<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); },
-                        [&](int k0, int nn) { return ld4(dS1 + static_cast<size_t>(16 * tc + nn) * D + k0); }, lane);
+            mm_f32_vb<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bS0T, lane);
+            mm_f32_vb<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); }, bS0T, lane);
+            mm_f32_vb<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); }, bS1T, lane);
             float colsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
