@@ -464,7 +464,7 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             int bi = 0, bj = tid;
             while (bj > bi) { bj -= bi + 1; ++bi; }
             float a[4][4] = {}, pp[4][4] = {};
-#pragma unroll 2
+#pragma unroll 4
             for (int c = 0; c < D; ++c) {
                 GT gi[4], gj[4];
                 float ki[4], kj[4], qi[4];
@@ -729,11 +729,13 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             const int i = x / D, c = x % D;
             const GT Gi = sG[i][c];
             float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
+#pragma unroll 4
             for (int j = 0; j <= i; ++j) {
                 const float e = __expf(static_cast<float>(Gi - sG[j][c])) * toF(sK[j][c]);
                 rowP += sM[1][i][j] * e;
                 rowA += sM[3][i][j] * e;
             }
+#pragma unroll 4
             for (int m = i; m < C; ++m) {
                 const float e = __expf(static_cast<float>(sG[m][c] - Gi));
                 colP += sM[1][m][i] * e * toF(sQ[m][c]);
