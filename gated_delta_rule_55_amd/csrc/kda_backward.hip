@@ -459,41 +459,66 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int c = tid; c < D; c += kBwdIntraThreads)
             sGC[c] = last_rst >= 0 ? 0.f : __expf(static_cast<float>(sG[C - 1][c]));
 
-        // ---- Abar (strictly lower) and P (lower), exact decay per term
-        if (tid < NBLK) {
-            int bi = 0, bj = tid;
+        // ---- Abar (strictly lower) and P (lower), exact decay per term: one 4x4
+        //      block per thread, its channels split in two halves (threads t and
+        //      t + NBLK); the second half's sums reach the first through LDS (over
+        //      sM[2] and sM[3], not yet in use) and are added in a fixed order
+        {
+            constexpr int NH = 2 * NBLK <= kBwdIntraThreads ? 2 : 1, CH = D / NH;
+            static_assert(NBLK * 32 <= 2 * C * MS, "the partial sums fit in two C x C buffers");
+            float(*part)[32] = reinterpret_cast<float(*)[32]>(&sM[2][0][0]);
+            const int blk = tid % NBLK, half = tid / NBLK;
+            int bi = 0, bj = blk;
             while (bj > bi) { bj -= bi + 1; ++bi; }
             float a[4][4] = {}, pp[4][4] = {};
+            if (tid < NH * NBLK) {
 #pragma unroll 4
-            for (int c = 0; c < D; ++c) {
-                GT gi[4], gj[4];
-                float ki[4], kj[4], qi[4];
+                for (int c = half * CH; c < (half + 1) * CH; ++c) {
+                    GT gi[4], gj[4];
+                    float ki[4], kj[4], qi[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    gi[x] = sG[4 * bi + x][c];
-                    gj[x] = sG[4 * bj + x][c];
-                    ki[x] = toF(sK[4 * bi + x][c]);
-                    kj[x] = toF(sK[4 * bj + x][c]);
-                    qi[x] = toF(sQ[4 * bi + x][c]);
+                    for (int x = 0; x < 4; ++x) {
+                        gi[x] = sG[4 * bi + x][c];
+                        gj[x] = sG[4 * bj + x][c];
+                        ki[x] = toF(sK[4 * bi + x][c]);
+                        kj[x] = toF(sK[4 * bj + x][c]);
+                        qi[x] = toF(sQ[4 * bi + x][c]);
+                    }
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) {
+                            const float e = __expf(fminf(static_cast<float>(gi[x] - gj[y]), 0.f)) * kj[y];
+                            a[x][y] += ki[x] * e;
+                            pp[x][y] += qi[x] * e;
+                        }
                 }
+                if (half == 1) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) {
+                            part[blk][4 * x + y] = a[x][y];
+                            part[blk][16 + 4 * x + y] = pp[x][y];
+                        }
+                }
+            }
+            __syncthreads();
+            if (tid < NBLK) {
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
                     for (int y = 0; y < 4; ++y) {
-                        const float e = __expf(fminf(static_cast<float>(gi[x] - gj[y]), 0.f)) * kj[y];
-                        a[x][y] += ki[x] * e;
-                        pp[x][y] += qi[x] * e;
+                        if constexpr (NH == 2) {
+                            a[x][y] += part[blk][4 * x + y];
+                            pp[x][y] += part[blk][16 + 4 * x + y];
+                        }
+                        const int i = 4 * bi + x, j = 4 * bj + y;
+                        const bool nores = sCnt[i] == sCnt[j];
+                        sM[0][i][j] = (j < i && nores) ? a[x][y] : 0.f;
+                        sM[1][i][j] = (j <= i && nores) ? pp[x][y] : 0.f;
                     }
             }
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int i = 4 * bi + x, j = 4 * bj + y;
-                    const bool nores = sCnt[i] == sCnt[j];
-                    sM[0][i][j] = (j < i && nores) ? a[x][y] : 0.f;
-                    sM[1][i][j] = (j <= i && nores) ? pp[x][y] : 0.f;
-                }
         }
         __syncthreads();
 
