@@ -113,7 +113,7 @@ __device__ __forceinline__ Frag<K> frag_of(F4 &&f4, int lane) {
 template <int K, typename FA>
 __device__ __forceinline__ void mm_f32_vb(f32x4 &acc, FA &&a4, const Frag<K> &bf, int lane) {
     const int r = lane & 15, kk = lane >> 4;
-    constexpr int NT = K / 16, BATCH = NT < 4 ? NT : 4;
+    constexpr int NT = K / 16, BATCH = NT;  // the whole left-hand fragment in one batch
 #pragma unroll
     for (int t0 = 0; t0 < NT; t0 += BATCH) {
         f32x4 av[BATCH];
