@@ -749,19 +749,95 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                 sdGL[c] = acc;
             }
         }
-        // ---- the decayed Gram products, exact decay per term; dq, dk out
+        // ---- the decay-weighted products of the blocks below the diagonal, on the
+        //      fp32 matrix cores.  For 16-token blocks I > J and the reference m =
+        //      the last token of J, e^{G_i - G_j} = e^{G_i - G_m} e^{G_m - G_j}
+        //      with both factors <= 1, so (dM = dP with X = Q, dM = dAbar with X = K)
+        //        row sums of block I    += e^{G_I - G_m} * (dM_IJ (e^{G_m - G_J} * K_J))
+        //        column sums of block J += e^{G_m - G_J} * (dM_IJ^T (e^{G_I - G_m} * X_I)).
+        //      A wave owns a 16-channel column tile for every token, so it adds its
+        //      sums into DQ, DK and DG alone and in a fixed order.
+        for (int td = w; td < NTD; td += kIW) {
+            const int c = 16 * td + l16;  // this lane's channel
+            f32x4 rP[NTI], rA[NTI];
+#pragma unroll
+            for (int I = 0; I < NTI; ++I) rP[I] = rA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int J = 0; J + 1 < NTI; ++J) {
+                const int m = 16 * J + 15;
+                const GT Gm = sG[m][c];
+                f32x4 cP = {0.f, 0.f, 0.f, 0.f}, cA = cP;  // block J's column sums: complete after the I loop
+                float ys[4];  // e^{G_m - G_j} k_j at j = 16 J + 4 s + lane / 16
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int j = 16 * J + 4 * s4 + kg;
+                    ys[s4] = __expf(static_cast<float>(Gm - sG[j][c])) * toF(sK[j][c]);
+                }
+#pragma unroll
+                for (int I = J + 1; I < NTI; ++I) {
+                    f32x4 zp = {0.f, 0.f, 0.f, 0.f}, za = zp, wp = zp, wa = zp;
+                    float xq[4], xk[4];  // e^{G_i - G_m} q_i, k_i at i = 16 I + 4 s + lane / 16
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int i = 16 * I + 4 * s4 + kg;
+                        const float f = __expf(static_cast<float>(sG[i][c] - Gm));
+                        xq[s4] = f * toF(sQ[i][c]);
+                        xk[s4] = f * toF(sK[i][c]);
+                    }
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        zp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], zp, 0,
+                                                                  0, 0);
+                        za = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], za, 0,
+                                                                  0, 0);
+                        wp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + 4 * s4 + kg][16 * J + l16], xq[s4], wp, 0,
+                                                                  0, 0);
+                        wa = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + 4 * s4 + kg][16 * J + l16], xk[s4], wa, 0,
+                                                                  0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float ei = __expf(static_cast<float>(sG[16 * I + 4 * kg + r][c] - Gm));
+                        const float ej = __expf(static_cast<float>(Gm - sG[16 * J + 4 * kg + r][c]));
+                        rP[I][r] += ei * zp[r];
+                        rA[I][r] += ei * za[r];
+                        cP[r] += ej * wp[r];
+                        cA[r] += ej * wa[r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * J + 4 * kg + r;
+                    DK[j * D + c] += cP[r] + cA[r];
+                    DG[j * D + c] -= toF(sK[j][c]) * (cP[r] + cA[r]);
+                }
+            }
+#pragma unroll
+            for (int I = 1; I < NTI; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * kg + r;
+                    const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
+                    DQ[i * D + c] += rP[I][r];
+                    DK[i * D + c] += rA[I][r];
+                    DG[i * D + c] += qv * rP[I][r] + kv * rA[I][r];
+                }
+        }
+        __syncthreads();
+        // ---- the diagonal blocks' decay-weighted products, exact decay per term;
+        //      dq, dk out
         for (int x = tid; x < C * D; x += kBwdIntraThreads) {
-            const int i = x / D, c = x % D;
+            const int i = x / D, c = x % D, i0 = i & ~15;
             const GT Gi = sG[i][c];
             float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
 #pragma unroll 4
-            for (int j = 0; j <= i; ++j) {
+            for (int j = i0; j <= i; ++j) {
                 const float e = __expf(static_cast<float>(Gi - sG[j][c])) * toF(sK[j][c]);
                 rowP += sM[1][i][j] * e;
                 rowA += sM[3][i][j] * e;
             }
 #pragma unroll 4
-            for (int m = i; m < C; ++m) {
+            for (int m = i; m < i0 + 16; ++m) {
                 const float e = __expf(static_cast<float>(sG[m][c] - Gi));
                 colP += sM[1][m][i] * e * toF(sQ[m][c]);
                 colA += sM[3][m][i] * e * toF(sK[m][c]);
