@@ -459,21 +459,51 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         for (int c = tid; c < D; c += kBwdIntraThreads)
             sGC[c] = last_rst >= 0 ? 0.f : __expf(static_cast<float>(sG[C - 1][c]));
 
-        // ---- Abar (strictly lower) and P (lower), exact decay per term: one 4x4
-        //      block per thread, its channels split in two halves (threads t and
-        //      t + NBLK); the second half's sums reach the first through LDS (over
-        //      sM[2] and sM[3], not yet in use) and are added in a fixed order
+        // ---- Abar (strictly lower) and P (lower).  Blocks below the diagonal on
+        //      the fp32 matrix cores, one 16x16 block pair per wave: with m = the
+        //      last token of block J, Abar_IJ = (e^{G_I - G_m} * K_I)(e^{G_m - G_J} * K_J)^T
+        //      and P_IJ the same with Q_I, both factors <= 1.  The diagonal blocks'
+        //      pairs with the exact exponential per term: one 4x4 sub-block per
+        //      thread, its channels in four quarters whose sums meet in LDS (over
+        //      sM[2] and sM[3], not yet in use) and are added in a fixed order.
         {
-            constexpr int NH = 2 * NBLK <= kBwdIntraThreads ? 2 : 1, CH = D / NH;
-            static_assert(NBLK * 32 <= 2 * C * MS, "the partial sums fit in two C x C buffers");
-            float(*part)[32] = reinterpret_cast<float(*)[32]>(&sM[2][0][0]);
-            const int blk = tid % NBLK, half = tid / NBLK;
-            int bi = 0, bj = blk;
-            while (bj > bi) { bj -= bi + 1; ++bi; }
-            float a[4][4] = {}, pp[4][4] = {};
-            if (tid < NH * NBLK) {
+            constexpr int NPAIR = NTI * (NTI - 1) / 2;
+            for (int pr = w; pr < NPAIR; pr += kIW) {
+                int I = 1, J = pr;
+                while (J >= I) { J -= I; ++I; }
+                const int m = 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
+                f32x4 acA = {0.f, 0.f, 0.f, 0.f}, acP = acA;
 #pragma unroll 4
-                for (int c = half * CH; c < (half + 1) * CH; ++c) {
+                for (int s4 = 0; s4 < D / 4; ++s4) {
+                    const int c = 4 * s4 + kg;
+                    const GT Gm = sG[m][c];
+                    const float fa = __expf(static_cast<float>(sG[i][c] - Gm));
+                    const float fb = __expf(static_cast<float>(Gm - sG[j][c])) * toF(sK[j][c]);
+                    acA = __builtin_amdgcn_mfma_f32_16x16x4f32(fa * toF(sK[i][c]), fb, acA, 0, 0, 0);
+                    acP = __builtin_amdgcn_mfma_f32_16x16x4f32(fa * toF(sQ[i][c]), fb, acP, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ii = 16 * I + 4 * kg + r;
+                    const bool nores = sCnt[ii] == sCnt[j];
+                    sM[0][ii][j] = nores ? acA[r] : 0.f;
+                    sM[1][ii][j] = nores ? acP[r] : 0.f;
+                }
+            }
+            constexpr int NSB = NTI * 10;
+            constexpr int NQ = (4 * NSB <= kBwdIntraThreads && 3 * NSB * 32 <= 2 * C * MS) ? 4
+                             : (2 * NSB <= kBwdIntraThreads && NSB * 32 <= 2 * C * MS) ? 2 : 1;
+            constexpr int CQ = D / NQ, NP = NQ > 1 ? NQ - 1 : 1;
+            static_assert(NSB * NP * 32 <= 2 * C * MS, "the partial sums fit in two C x C buffers");
+            float(*part)[NP][32] = reinterpret_cast<float(*)[NP][32]>(&sM[2][0][0]);
+            const int sb = tid % NSB, qt = tid / NSB;
+            int li = 0, lj = sb % 10;  // sub-block (li, lj), li >= lj, of diagonal block sb / 10
+            while (lj > li) { lj -= li + 1; ++li; }
+            const int bi = 4 * (sb / 10) + li, bj = 4 * (sb / 10) + lj;
+            float a[4][4] = {}, pp[4][4] = {};
+            if (tid < NQ * NSB) {
+#pragma unroll 4
+                for (int c = qt * CQ; c < (qt + 1) * CQ; ++c) {
                     GT gi[4], gj[4];
                     float ki[4], kj[4], qi[4];
 #pragma unroll
@@ -493,25 +523,26 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                             pp[x][y] += qi[x] * e;
                         }
                 }
-                if (half == 1) {
+                if (qt > 0) {
 #pragma unroll
                     for (int x = 0; x < 4; ++x)
 #pragma unroll
                         for (int y = 0; y < 4; ++y) {
-                            part[blk][4 * x + y] = a[x][y];
-                            part[blk][16 + 4 * x + y] = pp[x][y];
+                            part[sb][qt - 1][4 * x + y] = a[x][y];
+                            part[sb][qt - 1][16 + 4 * x + y] = pp[x][y];
                         }
                 }
             }
             __syncthreads();
-            if (tid < NBLK) {
+            if (tid < NSB) {
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
                     for (int y = 0; y < 4; ++y) {
-                        if constexpr (NH == 2) {
-                            a[x][y] += part[blk][4 * x + y];
-                            pp[x][y] += part[blk][16 + 4 * x + y];
+#pragma unroll
+                        for (int q = 1; q < NQ; ++q) {
+                            a[x][y] += part[sb][q - 1][4 * x + y];
+                            pp[x][y] += part[sb][q - 1][16 + 4 * x + y];
                         }
                         const int i = 4 * bi + x, j = 4 * bj + y;
                         const bool nores = sCnt[i] == sCnt[j];
