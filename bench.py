@@ -633,6 +633,23 @@ def main():
                          "traffic": measured_traffic("kda_chunk_bwd")},
         }
 
+    if b_ms and not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        heads, T_s = list(range(16)), 16384
+        sl = lambda x: x[:, :T_s, heads].detach().to("cpu").double().numpy()
+        args_b = [sl(pin[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
+        d_o_s = np.random.default_rng(4).standard_normal(args_b[2].shape)
+        t0 = time.perf_counter()
+        oracle.backward(*args_b, d_o=d_o_s, n_threads=threads)
+        dtb = time.perf_counter() - t0
+        result["backward"]["cpu_baseline"] = {
+            "value": T_s * len(heads) / dtb / H, "unit": "tokens/s", "cores": min(threads, len(heads)),
+            "kind": "oracle",
+            "sample": f"fp64 reverse-mode token loop on heads 0-15 x first {T_s} tokens of the long prefill "
+                      f"workload ({dtb:.1f} s wall), scaled to H=32 tokens/s"}
+
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         heads = list(range(16))
