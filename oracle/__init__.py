@@ -19,6 +19,11 @@ scalar-gate recurrence the same page sets KDA against (one head-wise
 ``log_alpha`` of shape [B, T, H] (prefill) or [N, H] (decode).  Its C update
 shares no arithmetic with the KDA one.
 
+``dplr_forward`` runs the general diagonal-plus-low-rank recurrence that the
+page contrasts KDA with (KDA ties both low-rank vectors to the key), read with
+free per-token vectors a_t, b_t and an unscaled write:
+``S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T``, ``o_t = S_t^T q_t``.
+
 ``backward`` differentiates the KDA token loop in reverse mode, one token at
 a time (the gradients with respect to q, k, v, log_alpha, beta and the initial
 state, given those of o and of the final state).
@@ -30,7 +35,8 @@ beta) and epilogue (RMSNorm and the sigmoid output gate) around ``forward`` /
 
 Every function here is pinned by ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_pins_gdn.py``, ``tests/test_oracle_pins_layer.py`` and
-``tests/test_oracle_pins_bwd.py`` (finite differences of ``forward``)
+``tests/test_oracle_pins_bwd.py`` (finite differences of ``forward``) and
+``tests/test_oracle_pins_dplr.py``
 against closed forms, special cases, invariants, exact rational arithmetic and
 explicit-matrix brute force; none is "parity unpinned".
 """
@@ -73,6 +79,10 @@ def _load():
         lib.kda_oracle_forward.restype = ctypes.c_int
         lib.gdn_oracle_forward.argtypes = lib.kda_oracle_forward.argtypes
         lib.gdn_oracle_forward.restype = ctypes.c_int
+        lib.dplr_oracle_forward.argtypes = [
+            dp, dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+            i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
+        lib.dplr_oracle_forward.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.gdn_oracle_decode_step.argtypes = lib.kda_oracle_decode_step.argtypes
@@ -144,6 +154,39 @@ def _forward(scalar_gate, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_th
             cu_p, B, T, H, Dk, Dv, N, _ptr(o), _ptr(fs), int(n_threads))
     if rc != 0:
         raise ValueError(f"{'gdn' if scalar_gate else 'kda'}_oracle_forward failed with code {rc}")
+    return o, fs
+
+
+def dplr_forward(q, k, v, a, b, log_alpha, init_state=None, cu_seqlens=None, n_threads=None):
+    """Runs the DPLR recurrence token by token in fp64.
+
+    q, k, a, b, log_alpha: [B, T, H, Dk]; v: [B, T, H, Dv]; init_state:
+    [N, H, Dk, Dv] or None (zeros); cu_seqlens: int [N+1] or None.
+    Returns (o [B, T, H, Dv], final_state [N, H, Dk, Dv]) as fp64 numpy arrays.
+    """
+    q, k, v, a, b, la = (_f64(x) for x in (q, k, v, a, b, log_alpha))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    assert k.shape == q.shape and a.shape == q.shape and b.shape == q.shape and la.shape == q.shape
+    assert v.shape == (B, T, H, Dv)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens), dtype=np.int32)
+        N = cu.size - 1
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        cu, N, cu_p = None, B, None
+    s0 = None if init_state is None else _f64(init_state)
+    if s0 is not None:
+        assert s0.shape == (N, H, Dk, Dv)
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    fs = np.zeros((N, H, Dk, Dv), dtype=np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    rc = _load().dplr_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(la), _ptr(s0),
+                                     cu_p, B, T, H, Dk, Dv, N, _ptr(o), _ptr(fs), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"dplr_oracle_forward failed with code {rc}")
     return o, fs
 
 

@@ -43,6 +43,18 @@
  * and log_alpha laid out [B, T, H] (prefill) or [N, H] (decode).  It shares no
  * arithmetic with token_update, so the two can be checked against each other.
  *
+ * The general diagonal-plus-low-rank (DPLR) transition that the same section
+ * contrasts KDA with (its bullet on the hardware-efficient chunked algorithm:
+ * KDA ties both low-rank vectors to the key; the related-work list: GLA and
+ * RWKV7 use the general form), read with two free per-token vectors a_t and
+ * b_t and an unscaled write, is computed by dplr_token_update:
+ *
+ *     S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
+ *
+ * KDA is the case a_t = -beta_t k_t, b_t = alpha_t * k_t with v_t scaled by
+ * beta_t.  Both terms of the transition act on S_{t-1} as it was before the
+ * token: e = b^T S_{t-1} first, then S = Diag(alpha) S_{t-1} + a e + k v^T.
+ *
  * kda_oracle_backward is reverse-mode differentiation of the KDA token loop
  * above, one token at a time in reverse order (the gradients the training
  * workload of the pages needs: of q, k, v, log_alpha, beta and the initial
@@ -68,9 +80,10 @@
 
 typedef struct {
     const double *q, *k, *v, *log_alpha, *beta, *init_state;
+    const double *a, *b;    /* DPLR low-rank vectors [B, T, H, Dk] (mode 2 only) */
     const int32_t *cu_seqlens;
     int64_t B, T, H, Dk, Dv, N;
-    int scalar_gate;        /* 0: KDA, log_alpha [.., Dk]; 1: GDN, log_alpha [..] */
+    int scalar_gate;        /* 0: KDA, log_alpha [.., Dk]; 1: GDN, log_alpha [..]; 2: DPLR */
     double *o, *final_state;
     int64_t next_unit;      /* work counter, guarded by lock */
     pthread_mutex_t lock;
@@ -128,6 +141,31 @@ static void gdn_token_update(double *S, int64_t Dk, int64_t Dv,
     }
 }
 
+/* One token of the DPLR recurrence.  e (caller scratch, length Dv) is
+ * b^T S_{t-1}, taken before S changes; then every row c of the state becomes
+ * alpha_c S_{t-1}[c] + a_c e + k_c v^T; then the readout. */
+static void dplr_token_update(double *S, int64_t Dk, int64_t Dv,
+                              const double *q, const double *k, const double *v,
+                              const double *a, const double *b, const double *log_alpha,
+                              double *e, double *o_t)
+{
+    for (int64_t j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) acc += b[c] * S[c * Dv + j];
+        e[j] = acc;
+    }
+    for (int64_t c = 0; c < Dk; ++c) {
+        const double al = exp(log_alpha[c]);
+        for (int64_t j = 0; j < Dv; ++j)
+            S[c * Dv + j] = al * S[c * Dv + j] + a[c] * e[j] + k[c] * v[j];
+    }
+    for (int64_t j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < Dk; ++c) acc += q[c] * S[c * Dv + j];
+        o_t[j] = acc;
+    }
+}
+
 /* Runs the whole token loop of one (sequence n, head h) unit. */
 static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, double *p)
 {
@@ -142,7 +180,13 @@ static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, doubl
 
     for (int64_t t = t0; t < t1; ++t) {
         const size_t row = (size_t)((b * J->T + t) * H + h);
-        if (J->scalar_gate)
+        if (J->scalar_gate == 2)
+            dplr_token_update(S, Dk, Dv,
+                              J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
+                              J->v + row * (size_t)Dv, J->a + row * (size_t)Dk,
+                              J->b + row * (size_t)Dk, J->log_alpha + row * (size_t)Dk,
+                              p, J->o + row * (size_t)Dv);
+        else if (J->scalar_gate)
             gdn_token_update(S, Dk, Dv,
                              J->q + row * (size_t)Dk, J->k + row * (size_t)Dk,
                              J->v + row * (size_t)Dv, J->log_alpha[row],
@@ -189,14 +233,16 @@ static int forward_impl(const double *q, const double *k, const double *v,
                         const double *init_state, const int32_t *cu_seqlens,
                         int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                         int64_t n_seqs, double *o, double *final_state, int n_threads,
-                        int scalar_gate)
+                        int scalar_gate, const double *a, const double *b)
 {
-    if (!q || !k || !v || !log_alpha || !beta || !o) return -1;
+    if (!q || !k || !v || !log_alpha || !o) return -1;
+    if (scalar_gate == 2 ? (!a || !b) : !beta) return -1;
     if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return -1;
     oracle_job J;
     memset(&J, 0, sizeof(J));
     J.scalar_gate = scalar_gate;
     J.q = q; J.k = k; J.v = v; J.log_alpha = log_alpha; J.beta = beta;
+    J.a = a; J.b = b;
     J.init_state = init_state; J.cu_seqlens = cu_seqlens;
     J.B = B; J.T = T; J.H = H; J.Dk = Dk; J.Dv = Dv;
     J.o = o; J.final_state = final_state;
@@ -237,7 +283,7 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
                        int64_t n_seqs, double *o, double *final_state, int n_threads)
 {
     return forward_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv,
-                        n_seqs, o, final_state, n_threads, 0);
+                        n_seqs, o, final_state, n_threads, 0, NULL, NULL);
 }
 
 /*
@@ -252,7 +298,22 @@ int gdn_oracle_forward(const double *q, const double *k, const double *v,
                        int64_t n_seqs, double *o, double *final_state, int n_threads)
 {
     return forward_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv,
-                        n_seqs, o, final_state, n_threads, 1);
+                        n_seqs, o, final_state, n_threads, 1, NULL, NULL);
+}
+
+/*
+ * dplr_oracle_forward: the DPLR recurrence over every (sequence, head) unit,
+ * with a, b [B, T, H, Dk] beside q and k and no beta.  Everything else
+ * (layouts, cu_seqlens, threads, return codes) is as in kda_oracle_forward.
+ */
+int dplr_oracle_forward(const double *q, const double *k, const double *v,
+                        const double *a, const double *b, const double *log_alpha,
+                        const double *init_state, const int32_t *cu_seqlens,
+                        int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                        int64_t n_seqs, double *o, double *final_state, int n_threads)
+{
+    return forward_impl(q, k, v, log_alpha, NULL, init_state, cu_seqlens, B, T, H, Dk, Dv,
+                        n_seqs, o, final_state, n_threads, 2, a, b);
 }
 
 /*
