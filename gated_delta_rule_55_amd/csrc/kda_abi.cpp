@@ -180,8 +180,9 @@ kda_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
 
 static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                             bool varlen, bool bf16, int32_t C, size_t &out, size_t &pkg,
-                            int64_t &slots) {
-    const kda::PackageLayout L = kda::package_layout(C, Dk, Dv, bf16);
+                            int64_t &slots, bool dplr = false) {
+    const kda::PackageLayout L = dplr ? kda::dplr_package_layout(C, Dk, Dv, bf16)
+                                      : kda::package_layout(C, Dk, Dv, bf16);
     pkg = L.bytes;
     slots = kda::prefill_slots(B, T, N, C, varlen);
     size_t total = pkg;
@@ -217,7 +218,7 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                                  int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                                  kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                                  void *workspace, size_t ws_bytes, hipStream_t stream, int gate_mode,
-                                 const LayerIn *L) {
+                                 const LayerIn *L, const void *lr_a = nullptr, const void *lr_b = nullptr) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -227,6 +228,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: must be 16, 32 or 64", chunk_size);
     chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
+    if (gate_mode == 3 && Dk != Dv)
+        return fail(KDA_ERR_UNSUPPORTED, "the DPLR prefill needs Dk == Dv (got %d, %d)", Dk, Dv);
     if (gate_mode == 2 && (in_dtype != KDA_BF16 || Dk != 128 || chunk_size != 64))
         return fail(KDA_ERR_UNSUPPORTED, "the layer prefill runs bf16 inputs at Dk = Dv = 128 in 64-token chunks");
     if (B < 1 || T < 0 || H < 1)
@@ -268,6 +271,10 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         in[n_in++] = {L->x_beta, "x_beta", bxb, 2, true};
         in[n_in++] = {L->out_gate, "out_gate", bog, 16, true};
         in[n_in++] = {L->norm_weight, "norm_weight", (size_t)Dv * 4, 16, true};
+    } else if (gate_mode == 3) {
+        in[n_in++] = {lr_a, "a", bq, 16, true};
+        in[n_in++] = {lr_b, "b", bq, 16, true};
+        in[n_in++] = {log_alpha, "log_alpha", bg, 16u, true};
     } else {
         // a per-channel gate is read in 16-byte vectors; a scalar gate and beta one by one
         in[n_in++] = {log_alpha, "log_alpha", bg, gate_mode == 1 ? 4u : 16u, true};
@@ -286,7 +293,7 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         return fail(KDA_ERR_INVALID_ARG, "final_state is not 16-byte aligned");
     size_t need_ws = 0, pkg = 0;
     int64_t slots = 0;
-    if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots))
+    if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots, gate_mode == 3))
         return fail(KDA_ERR_INVALID_ARG, "workspace size overflows size_t");
     if (T > 0 && (!workspace || ws_bytes < need_ws))
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu needed", ws_bytes,
@@ -326,7 +333,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
                              : nullptr;
-    hipError_t e = kda::launch_prefill(a, stream);
+    a.lr_a = lr_a; a.lr_b = lr_b;
+    hipError_t e = gate_mode == 3 ? kda::launch_dplr(a, stream) : kda::launch_prefill(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
 }
@@ -338,6 +346,32 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          void *workspace, size_t ws_bytes, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
                           in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, 0, nullptr);
+}
+
+size_t kda_dplr_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs,
+                                         kda_dtype in_dtype, int32_t chunk_size) {
+    if (chunk_size == 0) chunk_size = 64;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return 0;
+    if (!supported_dim(D)) return 0;
+    if (B < 1 || T < 0 || H < 1 || n_seqs < 0) return 0;
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return 0;
+    chunk_size = kda::prefill_effective_chunk(chunk_size, D, D, in_dtype == KDA_BF16);
+    const bool varlen = n_seqs > 0 && B == 1;
+    size_t out = 0, pkg = 0;
+    int64_t slots = 0;
+    if (!workspace_bytes(B, T, H, D, D, varlen ? n_seqs : B, varlen, in_dtype == KDA_BF16, chunk_size, out, pkg,
+                         slots, true))
+        return 0;
+    return out;
+}
+
+kda_status kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                              const float *log_alpha, const float *init_state, const int32_t *cu_seqlens,
+                              int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs, kda_dtype in_dtype,
+                              int32_t chunk_size, float *o, float *final_state, void *workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, nullptr, init_state, cu_seqlens, B, T, H, D, D, n_seqs, in_dtype,
+                          chunk_size, o, final_state, workspace, ws_bytes, stream, 3, nullptr, a, b);
 }
 
 kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -63,6 +63,25 @@ __host__ __device__ inline PackageLayout package_layout(int C, int Dk, int Dv, b
     return L;
 }
 
+// The DPLR form's package (kda_dplr.hip): WQ, UP, OI and GL as above with W
+// stored negated and UP holding U' = T Abk V; KT holds 2 CP tokens, the
+// decayed low-rank vectors A-tilde (k-steps 0 .. CP/32 - 1) then the decayed
+// keys K-tilde.
+__host__ __device__ inline PackageLayout dplr_package_layout(int C, int Dk, int Dv, bool bf16) {
+    const size_t osz = bf16 ? 2 : 4;
+    const size_t dkp = Dk < 32 ? 32 : Dk;
+    const size_t cp = C < 32 ? 32 : C;
+    PackageLayout L;
+    size_t off = 0;
+    L.wq = off; off += align256(2 * (size_t)C * dkp * osz);
+    L.kt = off; off += align256((size_t)Dk * 2 * cp * osz);
+    L.up = off; off += align256((size_t)C * Dv * 4);
+    L.oi = off; off += align256((size_t)C * Dv * 4);
+    L.gl = off; off += align256((size_t)Dk * 4);
+    L.bytes = off;
+    return L;
+}
+
 struct PrefillArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta, *init_state;
@@ -70,7 +89,8 @@ struct PrefillArgs {
     int32_t B, H, Dk, Dv, N, C;
     int64_t T;
     bool bf16;
-    int32_t gate_mode;          // 0 KDA, 1 GDN (log_alpha [B, T, H]), 2 KDA layer (below)
+    int32_t gate_mode;          // 0 KDA, 1 GDN (log_alpha [B, T, H]), 2 KDA layer (below), 3 DPLR
+    const void *lr_a, *lr_b;    // gate mode 3: low-rank vectors a, b [B, T, H, Dk] in_dtype (no beta)
     // gate mode 2: q, k unnormalised; bf16 x_alpha [B, T, H, Dk], x_beta [B, T, H],
     // output gate [B, T, H, Dv]; RMSNorm weight [Dv]
     const uint16_t *x_alpha, *x_beta, *out_gate;
@@ -90,6 +110,9 @@ inline int64_t prefill_slots(int32_t B, int64_t T, int32_t N, int32_t C, bool va
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// The DPLR form's prefill (gate mode 3; Dk = Dv, packages of dplr_package_layout).
+hipError_t launch_dplr(const PrefillArgs &a, hipStream_t stream);
 
 // o <- o / sqrt(mean_j o_j^2 + eps) * w * sigmoid(g) over each row of Dv = 128
 // values, in place (the KDA layer's epilogue), rows = B * T * H.

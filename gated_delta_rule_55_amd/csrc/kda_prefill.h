@@ -44,6 +44,7 @@ struct StateParams {
     const char *ws;
     size_t pkg_bytes;
     PackageLayout L;
+    const void *v;        // DPLR state pass only: the values [.., H, Dv] of the input
 };
 
 struct BwdStateParams {
@@ -208,5 +209,13 @@ hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t 
 // (kda_prefill.hip; instantiated for the shapes the backward supports).
 template <int C, int DK, int DV, bool BF>
 hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipStream_t stream);
+
+// chunk_offsets[n] = sum_{m<n} ceil(len_m / C) for varlen batches, on the device
+hipError_t launch_plan(const int32_t *cu_seqlens, int32_t N, int C, int32_t *chunk_offsets, hipStream_t stream);
+
+// The DPLR form's state pass over packages already in sp.ws (kda_prefill.hip;
+// d_k = d_v = D).
+template <int C, int D, bool BF>
+hipError_t launch_dplr_state(const StateParams &sp, hipStream_t stream);
 
 }  // namespace kda

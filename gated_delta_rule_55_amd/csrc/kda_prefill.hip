@@ -73,6 +73,11 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t *__restrict__ c
     if (t == 255) off[N] = run;
 }
 
+hipError_t launch_plan(const int32_t *cu_seqlens, int32_t N, int C, int32_t *chunk_offsets, hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, C, chunk_offsets);
+    return hipGetLastError();
+}
+
 // -----------------------------------------------------------------------------
 // intra-chunk package
 // -----------------------------------------------------------------------------
@@ -666,16 +671,38 @@ __device__ __forceinline__ void unpack8(const Vec8<false> &x, float (&o)[8]) {
 
 // The part of one chunk's package a wave of the state pass consumes, held in
 // registers so the next chunk's loads are in flight while this one computes.
-template <int C, int DK, int DV, bool BF>
+// LR2: the DPLR form (kda_dplr.hip), whose state update adds a second
+// low-rank term: the Kt section holds 2 CP tokens, [A-tilde; K-tilde], and the
+// chunk's values V (read from the input) follow U in the contraction.
+template <int C, int DK, int DV, bool BF, bool LR2 = false>
 struct StateFrags {
     using F = Cfg<C, DK, DV, BF>;
     static constexpr int NTK = DK / 16, SPW = (NTK + 3) / 4;
     static constexpr int NRT = 2 * F::NT16, RPW = (NRT + 3) / 4;
     static constexpr int KSK = F::DKP / 32, KSC = F::CP / 32, PARTS = BF ? 2 : 1;  // U hi/lo
+    static constexpr int KSC2 = LR2 ? 2 * KSC : KSC;
     Vec8<BF> wq[RPW][KSK];
     f32x4 uo[RPW];
-    Vec8<BF> kt[SPW][KSC];
+    Vec8<BF> kt[SPW][KSC2];
     f32x4 gl[SPW];
+    f32x4 vx[LR2 ? RPW : 1];  // LR2: V rows 16 rt + 4 (lane / 16) + r, column 16 ct + lane % 16
+
+    // LR2: this wave's V values of chunk c (zero past the sequence's L tokens)
+    __device__ __forceinline__ void load_v(const StateParams &p, int64_t tok_base, int64_t L, int64_t c, int h,
+                                           int w, int lane, int ct) {
+        using In = typename F::In;
+#pragma unroll
+        for (int rw = 0; rw < RPW; ++rw) {
+            const int rt = w + 4 * rw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t j = c * C + 16 * rt + 4 * (lane >> 4) + r;
+                const bool ok = rt < F::NT16 && j < L;
+                const int64_t off = ((tok_base + (ok ? j : 0)) * p.H + h) * DV + 16 * ct + (lane & 15);
+                vx[rw][r] = ok ? in_to_f32<BF>(static_cast<const In *>(p.v)[off]) : 0.f;
+            }
+        }
+    }
 
     __device__ __forceinline__ void load(const char *pkg, const PackageLayout &L, int w, int lane,
                                          int ct) {
@@ -701,8 +728,8 @@ struct StateFrags {
             const int tk = w + 4 * sl;
             if (NTK % 4 == 0 || tk < NTK) {
 #pragma unroll
-                for (int ks = 0; ks < KSC; ++ks)
-                    kt[sl][ks] = ld_vec8<BF>(ktp + ((static_cast<size_t>(tk) * KSC + ks) * 64 + lane) * 8);
+                for (int ks = 0; ks < KSC2; ++ks)
+                    kt[sl][ks] = ld_vec8<BF>(ktp + ((static_cast<size_t>(tk) * KSC2 + ks) * 64 + lane) * 8);
                 gl[sl] = *reinterpret_cast<const f32x4 *>(glp + 16 * tk + 4 * (lane >> 4));
             }
         }
@@ -710,17 +737,18 @@ struct StateFrags {
 };
 
 // SAVE: the saving variant (the backward's forward pass) writes the state
-// entering each chunk to p.chunk_states and stores no output.
-template <int C, int DK, int DV, bool BF, bool SAVE = false>
-__global__ void __launch_bounds__(256) state_kernel(StateParams p) {
+// entering each chunk to p.chunk_states and stores no output.  LR2: the DPLR
+// form (see StateFrags).
+template <int C, int DK, int DV, bool BF, bool SAVE, bool LR2>
+__device__ __forceinline__ void state_body(const StateParams &p) {
     using F = Cfg<C, DK, DV, BF>;
     using Op = typename F::Op;
-    using Frags = StateFrags<C, DK, DV, BF>;
+    using Frags = StateFrags<C, DK, DV, BF, LR2>;
     constexpr int NT16 = F::NT16, CP = F::CP, DKP = F::DKP;
     constexpr int NTK = Frags::NTK, SPW = Frags::SPW, NRT = Frags::NRT, RPW = Frags::RPW;
-    constexpr int KSK = Frags::KSK, KSC = Frags::KSC, PARTS = Frags::PARTS;
+    constexpr int KSK = Frags::KSK, KSC = Frags::KSC2, PARTS = Frags::PARTS;
     constexpr int SSS = DKP + 8;                 // LDS strides (elements)
-    constexpr int SUS = CP + 8;
+    constexpr int SUS = (LR2 ? 2 * CP : CP) + 8;
 
     __shared__ __align__(16) Op sS[16][SSS];          // state slab as a B operand [col][channel]
     __shared__ __align__(16) Op sU[PARTS][16][SUS];   // U (hi, lo) as a B operand [col][token]
@@ -826,6 +854,12 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
                     const Op hi = static_cast<Op>(u[r]);
                     sU[0][l16][j] = hi;
                     if constexpr (BF) sU[1][l16][j] = static_cast<Op>(u[r] - static_cast<float>(hi));
+                    if constexpr (LR2) {
+                        const float x = f.vx[rw][r];
+                        const Op xh = static_cast<Op>(x);
+                        sU[0][l16][CP + j] = xh;
+                        if constexpr (BF) sU[1][l16][CP + j] = static_cast<Op>(x - static_cast<float>(xh));
+                    }
                 }
             } else if constexpr (!SAVE) {
                 const int I = rt - NT16;
@@ -876,20 +910,24 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     using Part = std::true_type;
     const int64_t nfull = L / C;  // chunks with C valid tokens
     Frags f0, f1, f2;
-    if (nchunks > 0) f0.load(pkg_of(0), p.L, w, lane, ct);
-    if (nchunks > 1) f1.load(pkg_of(1), p.L, w, lane, ct);
+    auto load = [&](Frags &f, int64_t cc) {
+        f.load(pkg_of(cc), p.L, w, lane, ct);
+        if constexpr (LR2) f.load_v(p, tok_base, L, cc, h, w, lane, ct);
+    };
+    if (nchunks > 0) load(f0, 0);
+    if (nchunks > 1) load(f1, 1);
     int64_t c = 0;
     for (; c + 4 < nfull; c += 3) {  // chunks c .. c + 2 are full; c + 3 and c + 4 exist
-        f2.load(pkg_of(c + 2), p.L, w, lane, ct);
+        load(f2, c + 2);
         step(f0, c, Full{});
-        f0.load(pkg_of(c + 3), p.L, w, lane, ct);
+        load(f0, c + 3);
         step(f1, c + 1, Full{});
-        f1.load(pkg_of(c + 4), p.L, w, lane, ct);
+        load(f1, c + 4);
         step(f2, c + 2, Full{});
     }
     // tail: f0 holds chunk c and f1 chunk c + 1 (when it exists)
     for (; c < nchunks; ++c) {
-        if (c + 2 < nchunks) f2.load(pkg_of(c + 2), p.L, w, lane, ct);
+        if (c + 2 < nchunks) load(f2, c + 2);
         if (c < nfull) step(f0, c, Full{});
         else step(f0, c, Part{});
         f0 = f1;
@@ -908,6 +946,16 @@ __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
             }
         }
     }
+}
+
+template <int C, int DK, int DV, bool BF, bool SAVE = false>
+__global__ void __launch_bounds__(256) state_kernel(StateParams p) {
+    state_body<C, DK, DV, BF, SAVE, false>(p);
+}
+
+template <int C, int DK, int DV, bool BF>
+__global__ void __launch_bounds__(256) dplr_state_kernel(StateParams p) {
+    state_body<C, DK, DV, BF, false, true>(p);
 }
 
 // -----------------------------------------------------------------------------
@@ -975,6 +1023,20 @@ hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipS
     hipLaunchKernelGGL((state_kernel<C, DK, DV, BF, true>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
+template <int C, int D, bool BF>
+hipError_t launch_dplr_state(const StateParams &sp, hipStream_t stream) {
+    hipLaunchKernelGGL((dplr_state_kernel<C, D, D, BF>), dim3(sp.N, sp.H, D / 16), dim3(256), 0, stream, sp);
+    return hipGetLastError();
+}
+#define KDA_DPLR_STATE(C, D) \
+    template hipError_t launch_dplr_state<C, D, true>(const StateParams &, hipStream_t); \
+    template hipError_t launch_dplr_state<C, D, false>(const StateParams &, hipStream_t);
+KDA_DPLR_STATE(16, 16) KDA_DPLR_STATE(16, 32) KDA_DPLR_STATE(16, 64) KDA_DPLR_STATE(16, 128)
+KDA_DPLR_STATE(32, 16) KDA_DPLR_STATE(32, 32) KDA_DPLR_STATE(32, 64) KDA_DPLR_STATE(32, 128)
+KDA_DPLR_STATE(64, 16) KDA_DPLR_STATE(64, 32) KDA_DPLR_STATE(64, 64)
+template hipError_t launch_dplr_state<64, 128, true>(const StateParams &, hipStream_t);
+#undef KDA_DPLR_STATE
+
 // the shapes the backward supports: d_k = d_v, the chunk the forward uses
 #define KDA_FWD_STATES(C, D, BF) \
     template hipError_t launch_forward_states<C, D, D, BF>(const PrefillArgs &, float *, hipStream_t);

@@ -56,6 +56,11 @@ def load():
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32, ctypes.c_int, i32,
                                   fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_dplr_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int, i32]
+    lib.kda_dplr_chunk_fwd_workspace_size.restype = sz
+    lib.kda_dplr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, ip, i32, i64, i32, i32, i32, ctypes.c_int, i32,
+                                       fp, fp, vp, sz, vp]
+    lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -131,6 +136,38 @@ def _chunk_fwd(fn, q, k, v, log_alpha, beta, init_state, cu_seqlens, chunk_size,
               _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs, code,
               chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, final_state
+
+
+def dplr_workspace_size(B, T, H, D, n_seqs=0, dtype=torch.bfloat16, chunk_size=64) -> int:
+    """Bytes of workspace ``dplr_chunk_fwd`` needs (0 for unsupported sizes)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_dplr_chunk_fwd_workspace_size(B, T, H, D, n_seqs, code, chunk_size))
+
+
+def dplr_chunk_fwd(q, k, v, a, b, log_alpha, init_state=None, cu_seqlens=None, chunk_size=64,
+                   out=None, final_state=None, output_final_state=True, workspace=None, stream=None):
+    """Chunked prefill of the general DPLR recurrence
+    S_t = (Diag(exp(log_alpha_t)) + a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+    q, k, v, a, b [B,T,H,D] (one dtype); log_alpha [B,T,H,D] fp32; the rest as
+    ``chunk_fwd``.  Returns (o [B,T,H,D] fp32, final_state [N,H,D,D] or None)."""
+    lib = load()
+    B, T, H, D = q.shape
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = B if cu_seqlens is None else n_seqs
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    code = _dtype_code(q)
+    ws_bytes = int(lib.kda_dplr_chunk_fwd_workspace_size(B, T, H, D, n_seqs, code, chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.kda_dplr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
+                                  _ptr(init_state), _ptr(cu_seqlens), B, T, H, D, n_seqs, code, chunk_size,
+                                  _ptr(out), _ptr(final_state), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, final_state
 
 

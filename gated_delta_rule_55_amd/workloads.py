@@ -151,6 +151,22 @@ def make_prefill(name: str = "prefill", device="cpu", seed: int = 0, *, T: Optio
                 chunk=w.chunk, workload=w, T=T, N=N, H=H)
 
 
+def dplr_vectors(inp: dict, seed: int = 0, gate_b: bool = True):
+    """Low-rank vectors (a, b) of the general DPLR transition Diag(alpha) + a b^T
+    for a prefill workload's inputs: a = -beta * u, b = alpha * u' (or u' alone
+    when ``gate_b`` is False), u the workload's unit key rows and u' unit rows
+    of u + 0.5 N(0, 1), both in the workload's dtype.  With u' = u this is the
+    KDA transition; u' != u makes a and b independent vectors."""
+    k = inp["k"]
+    g = _gen(k.device, seed)
+    u = k.float()
+    u2 = u + 0.5 * torch.randn(u.shape, generator=g, device=k.device, dtype=torch.float32)
+    u2 = u2 / torch.linalg.vector_norm(u2, dim=-1, keepdim=True)
+    a = (-inp["beta"][..., None] * u).to(k.dtype)
+    b = (torch.exp(inp["log_alpha"]) * u2 if gate_b else u2).to(k.dtype)
+    return a, b
+
+
 def scalar_log_alpha(shape, shift: float, device="cpu", seed: int = 0) -> torch.Tensor:
     """Gated DeltaNet gates of any shape: -softplus(x + shift), x ~ N(0, 1), fp32,
     from a generator of their own seeded with ``seed``."""

@@ -58,7 +58,8 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 120 /* 1.2.0: adds kda_chunk_bwd (1.1.0: the gdn_* and kda_layer_* entry points) */
+#define KDA_VERSION 130 /* 1.3.0: adds kda_dplr_chunk_fwd (1.2.0: kda_chunk_bwd; 1.1.0: the gdn_* and
+                            kda_layer_* entry points) */
 
 typedef enum {
     KDA_OK = 0,
@@ -200,6 +201,40 @@ kda_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                          kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The general diagonal-plus-low-rank (DPLR) transition that the same section
+ * contrasts KDA with (its bullet on the hardware-efficient chunked algorithm:
+ * KDA ties both low-rank vectors to the key, which removes work; the
+ * related-work list places GLA and RWKV7 on the general form), read with two
+ * free per-token vectors a_t, b_t and an unscaled write:
+ *
+ *     S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ *
+ * (KDA is a_t = -beta_t k_t, b_t = alpha_t * k_t with v_t scaled by beta_t).
+ *
+ * kda_dplr_chunk_fwd_workspace_size -- bytes of device workspace
+ * kda_dplr_chunk_fwd needs (host only, pure; 0 for invalid arguments).
+ *
+ * kda_dplr_chunk_fwd -- chunked prefill of that recurrence; d_k = d_v = D.
+ *   q, k, a, b  [B, T, H, D] in_dtype, 16-byte aligned
+ *   v           [B, T, H, D] in_dtype
+ *   log_alpha   [B, T, H, D] fp32 (<= 0; a token whose log_alpha is -inf on
+ *               every channel keeps only the low-rank and write terms)
+ *   everything else (init_state, cu_seqlens, B, T, H, n_seqs, in_dtype,
+ *   chunk_size, o, final_state, workspace, stream, ownership, aliasing rules,
+ *   errors) as for kda_chunk_fwd with Dk = Dv = D; there is no beta.
+ * The arithmetic of the intra-chunk pass is fp32 on every path; the state
+ * pass uses the precision scheme of kda_chunk_fwd.
+ */
+size_t kda_dplr_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs,
+                                         kda_dtype in_dtype, int32_t chunk_size);
+
+kda_status kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const void *a, const void *b,
+                              const float *log_alpha, const float *init_state, const int32_t *cu_seqlens,
+                              int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs, kda_dtype in_dtype,
+                              int32_t chunk_size, float *o, float *final_state, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * gdn_decode_step -- one GDN token for each of N independent sequences, the

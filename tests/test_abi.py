@@ -42,7 +42,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 120
+    assert lib.kda_version() == 130
     for code, name in [(0, b"KDA_OK"), (1, b"KDA_ERR_INVALID_ARG"), (2, b"KDA_ERR_UNSUPPORTED"),
                        (3, b"KDA_ERR_WORKSPACE"), (4, b"KDA_ERR_HIP")]:
         assert lib.kda_status_string(code) == name
@@ -276,4 +276,51 @@ def _bwd(lib, **kw):
 ])
 def test_chunk_bwd_rejects(lib, kw, code, msg):
     assert _bwd(lib, **kw) == code
+    assert msg in lib.kda_last_error()
+
+
+def test_dplr_workspace_size(lib):
+    ws = lib.kda_dplr_chunk_fwd_workspace_size
+    kda_ws = lib.kda_chunk_fwd_workspace_size
+    per = ws(1, 4096, 32, 128, 0, BF16, 64) // (64 * 32)
+    assert per * 64 * 32 == ws(1, 4096, 32, 128, 0, BF16, 64)
+    # W and Q' (fp16), [A-tilde; K-tilde] (fp16, 2 x 64 tokens), U', O_intra, Gamma_last
+    assert per >= 2 * 64 * 128 * 2 + 128 * 128 * 2 + 2 * 64 * 128 * 4 + 128 * 4
+    assert ws(1, 4096, 32, 128, 0, BF16, 64) > kda_ws(1, 4096, 32, 128, 128, 0, BF16, 64)
+    assert ws(1, 4096, 32, 128, 0, BF16, 0) == ws(1, 4096, 32, 128, 0, BF16, 64)
+    assert ws(1, 1000, 2, 64, 5, BF16, 64) > ws(1, 1000, 2, 64, 0, BF16, 64)
+    for bad in [(1, 64, 1, 16, 0, BF16, 48), (1, 64, 1, 24, 0, BF16, 16), (0, 64, 1, 16, 0, BF16, 16),
+                (1, -1, 1, 16, 0, BF16, 16), (1, 64, 1, 16, 0, 7, 16)]:
+        assert ws(*bad) == 0, bad
+
+
+def _dplr(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, a=FAKE + 0x3000000, b=FAKE + 0x4000000,
+             log_alpha=FAKE + 0x5000000, init_state=None, cu_seqlens=None, B=1, T=64, H=1, D=16, n_seqs=0,
+             dtype=BF16, chunk=16, o=FAKE + 0x6000000, final_state=None, ws=FAKE + 0x8000000,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_dplr_chunk_fwd(p(a["q"]), p(a["k"]), p(a["v"]), p(a["a"]), p(a["b"]), p(a["log_alpha"]),
+                                  p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"], a["D"],
+                                  a["n_seqs"], a["dtype"], a["chunk"], p(a["o"]), p(a["final_state"]),
+                                  p(a["ws"]), a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=24), UNSUPPORTED, b"Dk=24"),
+    (dict(dtype=5), UNSUPPORTED, b"in_dtype"),
+    (dict(chunk=48), UNSUPPORTED, b"chunk_size"),
+    (dict(H=0), INVALID, b"H=0"),
+    (dict(a=None), INVALID, b"a is NULL"),
+    (dict(b=None), INVALID, b"b is NULL"),
+    (dict(log_alpha=None), INVALID, b"log_alpha is NULL"),
+    (dict(b=FAKE + 0x4000008), INVALID, b"b is not 16-byte aligned"),
+    (dict(o=FAKE + 0x3000000), INVALID, b"o overlaps a"),
+    (dict(ws=FAKE + 0x4000000), INVALID, b"workspace overlaps b"),
+    (dict(ws=None), WORKSPACE, b"workspace"),
+    (dict(ws_bytes=1024), WORKSPACE, b"workspace"),
+])
+def test_dplr_chunk_fwd_rejects(lib, kw, code, msg):
+    assert _dplr(lib, **kw) == code
     assert msg in lib.kda_last_error()

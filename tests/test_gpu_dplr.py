@@ -1,0 +1,128 @@
+"""kda_dplr_chunk_fwd (the general diagonal-plus-low-rank recurrence) on the GPU,
+through the C-ABI, against the fp64 DPLR oracle at the operator's parity bar:
+max|gpu - oracle| <= tau * RMS(oracle) for o and for the final state, tau = 2e-2
+for bf16 inputs and 1e-4 for fp32 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_55_amd import kda, workloads
+from kda_testlib import TAU, assert_parity, host64, log, oracle_threads
+
+pytestmark = pytest.mark.gpu
+
+
+def _shrink(inp, D):
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name][..., :D].float()
+        out[name] = (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(inp[name].dtype)
+    out["v"] = inp["v"][..., :D].contiguous()
+    out["log_alpha"] = inp["log_alpha"][..., :D].contiguous()
+    if inp["init_state"] is not None:
+        out["init_state"] = inp["init_state"][:, :, :D, :D].contiguous()
+    return out
+
+
+def _run(inp, a, b, chunk):
+    o, fs = kda.dplr_chunk_fwd(inp["q"], inp["k"], inp["v"], a, b, inp["log_alpha"], inp["init_state"],
+                               inp["cu_seqlens"], chunk)
+    torch.cuda.synchronize()
+    return o, fs
+
+
+def _check(inp, a, b, o, fs, tau, heads=None, label=""):
+    hs = (lambda x: x) if heads is None else (lambda x: x[:, :, heads])
+    s0 = inp["init_state"]
+    s0 = None if s0 is None else (s0 if heads is None else s0[:, heads])
+    ro, rfs = oracle.dplr_forward(hs(inp["q"]), hs(inp["k"]), hs(inp["v"]), hs(a), hs(b), hs(inp["log_alpha"]),
+                                  s0, inp["cu_seqlens"], n_threads=oracle_threads())
+    assert_parity(hs(o), ro, tau, f"{label} o")
+    assert_parity(fs if heads is None else fs[:, heads], rfs, tau, f"{label} final_state")
+
+
+@pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("bf16", 64, 32), ("bf16", 32, 16),
+                                        ("f32", 16, 16), ("f32", 64, 64), ("f32", 128, 32)])
+def test_dplr_ragged_small(dtype, D, C):
+    """T = 157 (no multiple of any chunk size), 2 heads, random initial state."""
+    log(f"dplr ragged dtype={dtype} D={D} C={C}")
+    inp = workloads.make_prefill("prefill", "cuda", seed=500 + D + C, T=157, H=2, dtype=dtype)
+    if D != 128:
+        inp = _shrink(inp, D)
+    a, b = workloads.dplr_vectors(inp, seed=501 + D)
+    o, fs = _run(inp, a, b, C)
+    _check(inp, a, b, o, fs, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32],
+           label=f"dplr {dtype} D={D} C={C}")
+
+
+def test_dplr_tiny_fp32_single_chunk():
+    inp = workloads.make_prefill("tiny", "cuda", seed=0)
+    a, b = workloads.dplr_vectors(inp, seed=1, gate_b=False)
+    o, fs = _run(inp, a, b, 16)
+    _check(inp, a, b, o, fs, TAU[torch.float32], label="dplr tiny")
+
+
+def test_dplr_varlen_with_resets():
+    """Packed sequences (one empty, several partial chunks) with their own initial
+    states; head 1 has a token whose gate is -inf on every channel (its low-rank
+    term still reads the state: b is not gated here), head 2 one -inf channel."""
+    lens = [1, 64, 65, 130, 7, 0, 200, 33]
+    log("dplr varlen with resets")
+    inp = workloads.make_prefill("varlen", "cuda", seed=51, H=3, lengths=lens)
+    g = torch.Generator(device="cuda").manual_seed(52)
+    inp["init_state"] = 0.02 * torch.randn((len(lens), 3, 128, 128), device="cuda", generator=g)
+    inp["log_alpha"][0, 100, 1] = float("-inf")
+    inp["log_alpha"][0, 300, 2, 5] = float("-inf")
+    a, b = workloads.dplr_vectors(inp, seed=53, gate_b=False)
+    o, fs = _run(inp, a, b, 64)
+    _check(inp, a, b, o, fs, TAU[torch.bfloat16], label="dplr varlen")
+
+
+def test_dplr_prefill_workload_sampled_heads():
+    """T = 4096, H = 32, d = 128, bf16, random initial state: o and final state of
+    four heads (heads are independent, so the oracle runs on those alone)."""
+    log("dplr prefill workload 4096x32, heads 0 9 22 31")
+    inp = workloads.make_prefill("prefill", "cuda", seed=55)
+    a, b = workloads.dplr_vectors(inp, seed=56)
+    o, fs = _run(inp, a, b, 64)
+    assert torch.isfinite(o).all() and torch.isfinite(fs).all()
+    _check(inp, a, b, o, fs, TAU[torch.bfloat16], heads=[0, 9, 22, 31], label="dplr prefill")
+
+
+def test_dplr_kda_special_case_matches_kda():
+    """a = -beta k, b = alpha * k, v -> beta v is KDA: the DPLR path agrees with
+    kda_chunk_fwd on the same inputs (fp32, d = 64, with resets)."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=57, T=300, H=2, dtype="f32")
+    inp = _shrink(inp, 64)
+    inp["log_alpha"][0, 77] = float("-inf")
+    g = torch.Generator(device="cuda").manual_seed(58)
+    inp["init_state"] = 0.05 * torch.randn((1, 2, 64, 64), device="cuda", generator=g)
+    beta = inp["beta"][..., None]
+    a = -beta * inp["k"]
+    b = torch.exp(inp["log_alpha"]) * inp["k"]
+    o, fs = kda.dplr_chunk_fwd(inp["q"], inp["k"], (beta * inp["v"]).contiguous(), a, b, inp["log_alpha"],
+                               inp["init_state"], None, 64)
+    ko, kfs = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["init_state"], None, 64)
+    torch.cuda.synchronize()
+    tau = TAU[torch.float32]
+    assert_parity(o, host64(ko), 2 * tau, "dplr as kda o")
+    assert_parity(fs, host64(kfs), 2 * tau, "dplr as kda final_state")
+
+
+def test_dplr_empty_and_determinism_and_chunk_invariance():
+    inp = workloads.make_prefill("prefill", "cuda", seed=59, T=0, H=2)
+    a, b = workloads.dplr_vectors(inp, seed=60)
+    inp["init_state"] = torch.randn((1, 2, 128, 128), device="cuda")
+    o, fs = _run(inp, a, b, 64)
+    assert torch.equal(fs, inp["init_state"])
+    inp = workloads.make_prefill("prefill", "cuda", seed=61, T=150, H=2)
+    inp = _shrink(inp, 64)
+    a, b = workloads.dplr_vectors(inp, seed=62)
+    oa, fa = _run(inp, a, b, 64)
+    ob, fb = _run(inp, a, b, 64)
+    assert torch.equal(oa, ob) and torch.equal(fa, fb)
+    for C in (16, 32):
+        oc, fc = _run(inp, a, b, C)
+        assert_parity(oc, host64(oa), TAU[torch.bfloat16], f"dplr C={C} vs C=64 o")
+        assert_parity(fc, host64(fa), TAU[torch.bfloat16], f"dplr C={C} vs C=64 final_state")
