@@ -42,7 +42,8 @@
 namespace kda {
 namespace {
 
-constexpr int kDplrThreads = 256;  // 4 waves
+constexpr int kDplrThreads = 512;  // 8 waves
+constexpr int kDplrWaves = kDplrThreads / 64;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 struct DplrIntraParams {
@@ -60,6 +61,19 @@ template <bool BF>
 __device__ __forceinline__ float ld_in(const void *p, int64_t i) {
     if constexpr (BF) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
     else return static_cast<const float *>(p)[i];
+}
+
+// Elements i .. i + 3 of an input (i a multiple of 4): one 8-byte (bf16) or
+// 16-byte (fp32) load.
+template <bool BF>
+__device__ __forceinline__ f32x4 ld_in4(const void *p, int64_t i) {
+    if constexpr (BF) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + i);
+    }
 }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -82,15 +96,15 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     using Op = typename F::Op;
     constexpr int NTI = C / 16, NTD = D / 16, CP = F::CP, DKP = F::DKP;
     constexpr int KSC2 = 2 * (CP / 32), KSK = DKP / 32;
-    constexpr int GS = D + 1, MS = C + 1;
+    constexpr int GS = D + 4, MS = C + 1;  // G rows 16-byte aligned
     constexpr int NSB = NTI * 10;  // 4x4 sub-blocks on or below the diagonal of the diagonal blocks
-    constexpr int NQ = 4 * NSB <= kDplrThreads ? 4 : (2 * NSB <= kDplrThreads ? 2 : 1);
-    constexpr int NP = NQ > 1 ? NQ - 1 : 1, CQ = D / NQ;
+    constexpr int NQ = D / 16 < 8 ? D / 16 < 1 ? 1 : D / 16 : 8;  // channel parts per sub-block
+    constexpr int CQ = D / NQ;
     static_assert(NTI <= 4, "one wave per row / column tile of a chunk");
+    static_assert(NSB * NQ <= kDplrThreads && 64 % NQ == 0 && CQ % 4 == 0, "diagonal work layout");
 
-    __shared__ float sG[C][GS];      // G, cumulative log-decay
+    __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay
     __shared__ float sM[4][C][MS];   // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk
-    __shared__ float sPart[NP][NSB][64];
     __shared__ int sRst[C], sCnt[C];
     __shared__ int sLast;
 
@@ -106,6 +120,12 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     char *pkg = p.ws + static_cast<size_t>(blockIdx.x) * p.pkg_bytes;
     auto in = [&](const void *x, int i, int c) {
         return i < nvalid ? ld_in<BF>(x, ((tok0 + i) * H + h) * D + c) : 0.f;
+    };
+    auto in4 = [&](const void *x, int i, int c) {  // channels c .. c + 3 of token i
+        return i < nvalid ? ld_in4<BF>(x, ((tok0 + i) * H + h) * D + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto g4 = [&](int i, int c) {  // G[i][c .. c + 3], G[-1] = 0
+        return i >= 0 ? *reinterpret_cast<const f32x4 *>(&sG[i][c]) : f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
     // ---- cumulative decay and resets
@@ -128,7 +148,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             sG[i][c] = acc;
         }
     }
-    if (tid == 0) {
+    if (tid == kDplrThreads - 64) {  // a wave the scan above leaves free
         int cnt = 0, last = -1;
         for (int i = 0; i < C; ++i) {
             if (sRst[i]) {
@@ -145,7 +165,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     // ---- Gram blocks below the diagonal, one 16x16 block pair per wave
     {
         constexpr int NPAIR = NTI * (NTI - 1) / 2;
-        for (int pr = w; pr < NPAIR; pr += kDplrThreads / 64) {
+        // (the last waves first: the diagonal work below fills the first ones)
+        for (int pr = kDplrWaves - 1 - w; pr < NPAIR; pr += kDplrWaves) {
             int I = 1, J = pr;
             while (J >= I) {
                 J -= I;
@@ -153,18 +174,21 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             }
             const int m = 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
-#pragma unroll 4
-            for (int s4 = 0; s4 < D / 4; ++s4) {
-                const int c = 4 * s4 + kg;
-                const float Gm = sG[m][c];
-                const float e1 = __expf(sG[i - 1][c] - Gm), e2 = __expf(sG[i][c] - Gm);
-                const float e3 = __expf(Gm - sG[j][c]);
-                const float lb = in(p.b, i, c) * e1, lq = in(p.q, i, c) * e2;
-                const float ra = in(p.a, j, c) * e3, rk = in(p.k, j, c) * e3;
-                aab = mfma4(lb, ra, aab);
-                abk = mfma4(lb, rk, abk);
-                pqa = mfma4(lq, ra, pqa);
-                pqk = mfma4(lq, rk, pqk);
+#pragma unroll 2
+            for (int t = 0; t < D / 16; ++t) {
+                const int c = 16 * t + 4 * kg;  // this lane's channels c .. c + 3
+                const f32x4 gm = g4(m, c), gbi = g4(i - 1, c), gi = g4(i, c), gj = g4(j, c);
+                const f32x4 bv = in4(p.b, i, c), qv = in4(p.q, i, c), av = in4(p.a, j, c), kv = in4(p.k, j, c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float e3 = __expf(gm[e] - gj[e]);
+                    const float lb = bv[e] * __expf(gbi[e] - gm[e]), lq = qv[e] * __expf(gi[e] - gm[e]);
+                    const float ra = av[e] * e3, rk = kv[e] * e3;
+                    aab = mfma4(lb, ra, aab);
+                    abk = mfma4(lb, rk, abk);
+                    pqa = mfma4(lq, ra, pqa);
+                    pqk = mfma4(lq, rk, pqk);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -177,10 +201,11 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             }
         }
     }
-    // ---- diagonal blocks, exact decay per term: one 4x4 sub-block per thread,
-    //      its channels in NQ parts whose sums meet in LDS in a fixed order
+    // ---- diagonal blocks, exact decay per term: one 4x4 sub-block per group of
+    //      NQ adjacent lanes, each lane a part of the channels; the parts are
+    //      summed by lane exchange in a fixed order
     {
-        const int sb = tid % NSB, qt = tid / NSB;
+        const int sb = tid / NQ, qt = tid % NQ;
         int li = 0, lj = sb % 10;
         while (lj > li) {
             lj -= li + 1;
@@ -188,52 +213,49 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         }
         const int bi = 4 * (sb / 10) + li, bj = 4 * (sb / 10) + lj;
         float acc[4][4][4] = {};  // [Aab, Abk, Pqa, Pqk][x][y]
-        if (tid < NQ * NSB) {
-#pragma unroll 2
-            for (int c = qt * CQ; c < (qt + 1) * CQ; ++c) {
-                float gi[4], gbi[4], gj[4], qv[4], bv[4], av[4], kv[4];
+        if (sb < NSB) {
+#pragma unroll 1
+            for (int c = qt * CQ; c < (qt + 1) * CQ; c += 4) {
+                f32x4 gi[4], gbi[4], gj[4], qv[4], bv[4], av[4], kv[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const int i = 4 * bi + x, j = 4 * bj + x;
-                    gi[x] = sG[i][c];
-                    gbi[x] = i > 0 ? sG[i - 1][c] : 0.f;
-                    gj[x] = sG[j][c];
-                    qv[x] = in(p.q, i, c);
-                    bv[x] = in(p.b, i, c);
-                    av[x] = in(p.a, j, c);
-                    kv[x] = in(p.k, j, c);
+                    gi[x] = g4(i, c);
+                    gbi[x] = g4(i - 1, c);
+                    gj[x] = g4(j, c);
+                    qv[x] = in4(p.q, i, c);
+                    bv[x] = in4(p.b, i, c);
+                    av[x] = in4(p.a, j, c);
+                    kv[x] = in4(p.k, j, c);
                 }
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        const float eA = __expf(fminf(gbi[x] - gj[y], 0.f));
-                        const float eP = __expf(fminf(gi[x] - gj[y], 0.f));
-                        acc[0][x][y] += bv[x] * av[y] * eA;
-                        acc[1][x][y] += bv[x] * kv[y] * eA;
-                        acc[2][x][y] += qv[x] * av[y] * eP;
-                        acc[3][x][y] += qv[x] * kv[y] * eP;
-                    }
-            }
-            if (qt > 0) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int x = 0; x < 4; ++x)
 #pragma unroll
-                        for (int y = 0; y < 4; ++y) sPart[qt - 1][sb][16 * mt + 4 * x + y] = acc[mt][x][y];
+                        for (int y = 0; y < 4; ++y) {
+                            const float eA = __expf(fminf(gbi[x][e] - gj[y][e], 0.f));
+                            const float eP = __expf(fminf(gi[x][e] - gj[y][e], 0.f));
+                            acc[0][x][y] += bv[x][e] * av[y][e] * eA;
+                            acc[1][x][y] += bv[x][e] * kv[y][e] * eA;
+                            acc[2][x][y] += qv[x][e] * av[y][e] * eP;
+                            acc[3][x][y] += qv[x][e] * kv[y][e] * eP;
+                        }
             }
         }
-        __syncthreads();
-        if (tid < NSB) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+#pragma unroll
+                    for (int d = 1; d < NQ; d <<= 1) acc[mt][x][y] += __shfl_xor(acc[mt][x][y], d);
+        if (sb < NSB && qt == 0) {
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
                 for (int y = 0; y < 4; ++y) {
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int q = 1; q < NQ; ++q) acc[mt][x][y] += sPart[q - 1][sb][16 * mt + 4 * x + y];
                     const int i = 4 * bi + x, j = 4 * bj + y;
                     const bool okA = j < i && cnt_before(i) == sCnt[j];
                     const bool okP = j <= i && sCnt[i] == sCnt[j];
@@ -347,7 +369,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             *reinterpret_cast<f32x4 *>(dst) = v;
         }
     };
-    for (int job = w; job < NCT + NTD; job += kDplrThreads / 64) {
+    for (int job = w; job < NCT + NTD; job += kDplrWaves) {
         if (job < NCT) {
             const int ct = job, ks = ct >> 1, hc = ct & 1;
             if (ct >= NTD) {  // channels past Dk (Dk = 16): zero operands
@@ -379,16 +401,19 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     }
                 // acc[r] = (M X)[token 16 I + l16][channel 16 ct + 4 kg + r]
                 f32x4 val;
-                const int i = 16 * I + l16;
+                const int i = 16 * I + l16, c0 = 16 * ct + 4 * kg;
+                if (rt < NTI) {
+                    val = -acc;
+                } else {
+                    const f32x4 qv = in4(p.q, i, c0), gv = g4(i, c0);
+                    const bool live = sCnt[i] == 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int c = 16 * ct + 4 * kg + r;
-                    if (rt < NTI) val[r] = -acc[r];
-                    else val[r] = acc[r] + (sCnt[i] == 0 ? in(p.q, i, c) * __expf(sG[i][c]) : 0.f);
+                    for (int r = 0; r < 4; ++r) val[r] = acc[r] + (live ? qv[r] * __expf(gv[r]) : 0.f);
                 }
                 store4(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8 + 4 * hc, val);
             }
             // [At; Kt]: channel cx, tokens 32 s + 8 kg + e of each half
+#pragma unroll
             for (int s = 0; s < KSC2; ++s) {
                 const bool second = s >= KSC2 / 2;
                 const int s0 = second ? s - KSC2 / 2 : s;
