@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     using Op = typename F::Op;
     constexpr int NTI = C / 16, NTD = D / 16, CP = F::CP, DKP = F::DKP;
     constexpr int KSC2 = 2 * (CP / 32), KSK = DKP / 32;
-    constexpr int GS = D + 4, MS = C + 1;  // G rows 16-byte aligned
+    constexpr int GS = D + 4, MS = C + 4;  // rows 16-byte aligned
     constexpr int NSB = NTI * 10;  // 4x4 sub-blocks on or below the diagonal of the diagonal blocks
     constexpr int NQ = D / 16 < 8 ? D / 16 < 1 ? 1 : D / 16 : 8;  // channel parts per sub-block
     constexpr int CQ = D / NQ;
@@ -104,7 +104,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     static_assert(NSB * NQ <= kDplrThreads && 64 % NQ == 0 && CQ % 4 == 0, "diagonal work layout");
 
     __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay
-    __shared__ float sM[4][C][MS];   // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk
+    __shared__ __align__(16) float sM[4][C][MS];  // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk
+    constexpr int NSEG = kDplrThreads / D < C / 4 ? kDplrThreads / D : C / 4, RPS = C / NSEG;
+    __shared__ float sSeg[NSEG][D];  // per-segment decay sums of the scan
     __shared__ int sRst[C], sCnt[C];
     __shared__ int sLast;
 
@@ -141,23 +143,27 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         if (i < nvalid && sG[i][c] != kNegInf) sRst[i] = 0;
     }
     __syncthreads();
-    for (int c = tid; c < D; c += kDplrThreads) {
+    // the scan in NSEG segments of RPS tokens per channel, then the segments' offsets
+    const int sc = tid % D, sseg = tid / D;
+    if (sseg < NSEG) {
         float acc = 0.f;
-        for (int i = 0; i < C; ++i) {
-            acc += sRst[i] ? 0.f : fmaxf(sG[i][c], kGFloor);
-            sG[i][c] = acc;
+        for (int r = 0; r < RPS; ++r) {
+            const int i = sseg * RPS + r;
+            acc += sRst[i] ? 0.f : fmaxf(sG[i][sc], kGFloor);
+            sG[i][sc] = acc;
         }
+        sSeg[sseg][sc] = acc;
     }
-    if (tid == kDplrThreads - 64) {  // a wave the scan above leaves free
-        int cnt = 0, last = -1;
-        for (int i = 0; i < C; ++i) {
-            if (sRst[i]) {
-                ++cnt;
-                last = i;
-            }
-            sCnt[i] = cnt;
-        }
-        sLast = last;
+    if (w == kDplrWaves - 1) {  // reset counts by one wave-wide ballot (C <= 64 tokens)
+        const unsigned long long rm = __ballot(lane < C && sRst[lane] != 0);
+        if (lane < C) sCnt[lane] = __popcll(rm & ((2ull << lane) - 1ull));
+        if (lane == 0) sLast = rm ? 63 - __clzll(rm) : -1;
+    }
+    __syncthreads();
+    if (sseg > 0 && sseg < NSEG) {
+        float off = 0.f;
+        for (int q = 0; q < sseg; ++q) off += sSeg[q][sc];
+        for (int r = 0; r < RPS; ++r) sG[sseg * RPS + r][sc] += off;
     }
     __syncthreads();
     auto cnt_before = [&](int i) { return sCnt[i] - sRst[i]; };  // resets at tokens < i
@@ -395,9 +401,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
                 for (int t = 0; t < NTI; ++t)
                     if (t <= I) {
+                        const f32x4 mv = *reinterpret_cast<const f32x4 *>(&sM[mt][16 * I + l16][16 * t + 4 * kg]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = mfma4(xf[t][e], sM[mt][16 * I + l16][16 * t + 4 * kg + e], acc);
+                        for (int e = 0; e < 4; ++e) acc = mfma4(xf[t][e], mv[e], acc);
                     }
                 // acc[r] = (M X)[token 16 I + l16][channel 16 ct + 4 kg + r]
                 f32x4 val;
@@ -442,9 +448,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
                 for (int t = 0; t < NTI; ++t)
                     if (t <= I) {
+                        const f32x4 mv = *reinterpret_cast<const f32x4 *>(&sM[mt][16 * I + l16][16 * t + 4 * kg]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = mfma4(sM[mt][16 * I + l16][16 * t + 4 * kg + e], vf[t][e], acc);
+                        for (int e = 0; e < 4; ++e) acc = mfma4(mv[e], vf[t][e], acc);
                     }
                 f32x4 *dst = rt < NTI ? up : oi;
                 dst[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = acc;
