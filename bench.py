@@ -17,13 +17,15 @@ on the same tensors with one log gate per (token, head) -- gdn_chunk_fwd over
 the 1M-token workload and 64 gdn_decode_step calls -- and reported in the
 "gdn" object of the same JSON line; then the KDA layer (fused prologue and
 epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object;
-then the backward (kda_chunk_bwd) over the first 262,144 tokens of the same
-prefill inputs in the "backward" object.
+then the general diagonal-plus-low-rank recurrence (kda_dplr_chunk_fwd) over the
+same 1M-token q, k, v and gates in the "dplr" object; then the backward
+(kda_chunk_bwd) over the first 262,144 tokens of the same prefill inputs in the
+"backward" object.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
 Profiling helpers (the commands that made the summaries under profiles/):
-  python bench.py --only prefill|decode|copy ...   one part only, for rocprofv3
+  python bench.py --only prefill|decode|copy|backward|dplr ...   one part only, for rocprofv3
       (copy: a plain device-to-device copy of COPY_BYTES, the counter calibration)
   python bench.py --summarize-trace DIR            markdown table of rocprofv3
       --kernel-trace --stats output (DIR/run_kernel_stats.csv)
@@ -82,6 +84,12 @@ def backward_alg_bytes(T, H, Dk, Dv, in_bytes=2):
     return T * H * (read + write)
 
 
+def dplr_alg_bytes(T, H, D, N, in_bytes=2):
+    """kda_dplr_chunk_fwd: q, k, v, a, b read (in_bytes each element), log_alpha
+    read (fp32, per channel), o written (fp32), final state written."""
+    return T * H * (5 * in_bytes * D + 4 * D + 4 * D) + N * H * D * D * 4
+
+
 def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
     """State read and written once, plus the token's q, k, v, log_alpha, beta, o
     (gate_per_head: Dk for KDA, 1 for GDN)."""
@@ -125,6 +133,8 @@ GDN_DECODE = "kda::decode_step_kernel<128, 128, true, 1>"
 LAYER_INTRA = "kda::intra_wide_kernel<2>"
 LAYER_EPILOGUE = "kda::layer_epilogue_kernel"
 LAYER_DECODE = "kda::decode_step_kernel<128, 128, true, 2>"
+DPLR_INTRA = "kda::dplr_intra_kernel<64, 128, true>"
+DPLR_STATE = "kda::dplr_state_kernel<64, 128, 128, true>"
 LAUNCH_KERNELS = {
     "kda_chunk_fwd": (KDA_INTRA, STATE),
     "kda_decode_step": (KDA_DECODE,),
@@ -132,6 +142,7 @@ LAUNCH_KERNELS = {
     "gdn_decode_step": (GDN_DECODE,),
     "kda_layer_chunk_fwd": (LAYER_INTRA, STATE, LAYER_EPILOGUE),
     "kda_layer_decode_step": (LAYER_DECODE,),
+    "kda_dplr_chunk_fwd": (DPLR_INTRA, DPLR_STATE),
 }
 
 
@@ -295,6 +306,29 @@ def backward_leg(torch, kda, pin, dev, C):
     return backward, T_B
 
 
+def dplr_leg(torch, kda, workloads, pin, dev, C):
+    """kda_dplr_chunk_fwd over the long prefill inputs with low-rank vectors from
+    workloads.dplr_vectors (made in 128k-token slices to bound the temporaries),
+    preallocated output and workspace.  Returns (call, (a, b))."""
+    T, H, D = pin["T"], pin["H"], pin["q"].shape[-1]
+    a = torch.empty_like(pin["k"])
+    b = torch.empty_like(pin["k"])
+    step = 1 << 17
+    for i, t0 in enumerate(range(0, T, step)):
+        part = {n: pin[n][:, t0:t0 + step] for n in ("k", "beta", "log_alpha")}
+        a[:, t0:t0 + step], b[:, t0:t0 + step] = workloads.dplr_vectors(part, seed=10 + i)
+        del part
+    o = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
+    fs = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.dplr_workspace_size(1, T, H, D, 0, torch.bfloat16, C), dtype=torch.uint8, device=dev)
+
+    def dplr():
+        kda.dplr_chunk_fwd(pin["q"], pin["k"], pin["v"], a, b, pin["log_alpha"], None, None, C,
+                           out=o, final_state=fs, workspace=ws)
+
+    return dplr, (a, b)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +340,8 @@ def main():
                          "forward pass runs the same kernels at another size)")
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
+    ap.add_argument("--no-dplr", action="store_true", help="skip the general DPLR prefill leg")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "dplr"], default=None,
                     help="run one part only (for profilers); prints no JSON line")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
@@ -367,6 +402,13 @@ def main():
         kda.decode_step(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t],
                         din["beta"][t], state, out=od)
 
+    if args.only == "dplr":
+        del ws
+        dplr, _ = dplr_leg(torch, kda, workloads, pin, dev, C)
+        for _ in range(args.warmup + args.steps):
+            dplr()
+        torch.cuda.synchronize()
+        return
     if args.only == "backward":
         backward, _ = backward_leg(torch, kda, pin, dev, C)
         for _ in range(args.warmup + args.steps):
@@ -462,6 +504,23 @@ def main():
     warm(layer_prefill, layer_decode)
     l_pre_ms, l_dec_ms = timed(layer_prefill, layer_decode)
     del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g
+
+    # ---- the general DPLR recurrence on the same q, k, v and gates (kda_dplr_chunk_fwd)
+    d_ms = []
+    if not args.no_dplr:
+        dplr, d_bufs = dplr_leg(torch, kda, workloads, pin, dev, C)
+        for _ in range(args.warmup):
+            dplr()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            flush.zero_()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            dplr()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            d_ms.append(e0.elapsed_time(e1))
+        del dplr
 
     # ---- the backward (kda_chunk_bwd) over the first T_B tokens of the same inputs
     b_ms = []
@@ -612,6 +671,40 @@ def main():
             "traffic": measured_traffic("kda_layer_decode_step"),
         },
     }
+
+    if d_ms:
+        d_ms.sort()
+        d_t = d_ms[len(d_ms) // 2] / 1e3
+        d_bytes = dplr_alg_bytes(T, H, Dk, N)
+        result["dplr"] = {
+            "workload": "kda_dplr_chunk_fwd, S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T, over the "
+                        "same 1M-token q, k, v and log_alpha (H=32, d=128, chunk 64, bf16), a = -beta * k, "
+                        "b = alpha * unit(k + 0.5 N(0,1)) in bf16",
+            "ms_mean": sum(d_ms) / len(d_ms), "ms_median": d_t * 1e3,
+            "tokens_per_s": T / d_t,
+            "time_vs_kda_prefill": d_t / t_pre,
+            "alg_bytes": d_bytes,
+            "hbm_frac_algorithmic": d_bytes / d_t / HBM_PEAK,
+            "roofline": {"kernel": "kda_dplr_chunk_fwd (dplr_intra_kernel + dplr_state_kernel)",
+                         "bound": "hbm", "achieved": d_bytes / d_t / 1e9, "peak": HBM_PEAK / 1e9,
+                         "unit": "GB/s", "frac": d_bytes / d_t / HBM_PEAK,
+                         "traffic": measured_traffic("kda_dplr_chunk_fwd")},
+        }
+        if not args.no_cpu_baseline:
+            import oracle
+            threads = max(1, min(16, os.cpu_count() or 1))
+            heads, T_s = list(range(16)), 131072
+            sl = lambda x: x[:, :T_s, heads].detach().to("cpu").double().numpy()
+            args_d = [sl(pin[n]) for n in ("q", "k", "v")] + [sl(x) for x in d_bufs] + [sl(pin["log_alpha"])]
+            t0 = time.perf_counter()
+            oracle.dplr_forward(*args_d, n_threads=threads)
+            dtd = time.perf_counter() - t0
+            result["dplr"]["cpu_baseline"] = {
+                "value": T_s * len(heads) / dtd / H, "unit": "tokens/s", "cores": min(threads, len(heads)),
+                "kind": "oracle",
+                "sample": f"fp64 DPLR token loop on heads 0-15 x first {T_s} tokens of the same inputs "
+                          f"({dtd:.1f} s wall), scaled to H=32 tokens/s"}
+        del d_bufs
 
     if b_ms:
         b_ms.sort()
