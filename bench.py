@@ -17,8 +17,9 @@ on the same tensors with one log gate per (token, head) -- gdn_chunk_fwd over
 the 1M-token workload and 64 gdn_decode_step calls -- and reported in the
 "gdn" object of the same JSON line; then the KDA layer (fused prologue and
 epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object;
-then the general diagonal-plus-low-rank recurrence (kda_dplr_chunk_fwd) over the
-same 1M-token q, k, v and gates in the "dplr" object; then the backward
+then the general diagonal-plus-low-rank recurrence (kda_dplr_chunk_fwd over the
+same 1M-token q, k, v and gates, and 64 kda_dplr_decode_step calls on the decode
+workload) in the "dplr" object; then the backward
 (kda_chunk_bwd) over the first 262,144 tokens of the same prefill inputs in the
 "backward" object.
 
@@ -90,6 +91,11 @@ def dplr_alg_bytes(T, H, D, N, in_bytes=2):
     return T * H * (5 * in_bytes * D + 4 * D + 4 * D) + N * H * D * D * 4
 
 
+def dplr_decode_alg_bytes(N, H, D, in_bytes=2):
+    """State read and written once, plus the token's q, k, v, a, b, log_alpha and o."""
+    return N * H * (8 * D * D + 5 * in_bytes * D + 4 * D + 4 * D)
+
+
 def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
     """State read and written once, plus the token's q, k, v, log_alpha, beta, o
     (gate_per_head: Dk for KDA, 1 for GDN)."""
@@ -135,6 +141,7 @@ LAYER_EPILOGUE = "kda::layer_epilogue_kernel"
 LAYER_DECODE = "kda::decode_step_kernel<128, 128, true, 2>"
 DPLR_INTRA = "kda::dplr_intra_kernel<64, 128, true>"
 DPLR_STATE = "kda::dplr_state_kernel<64, 128, 128, true>"
+DPLR_DECODE = "kda::decode_step_kernel<128, 128, true, 3>"
 LAUNCH_KERNELS = {
     "kda_chunk_fwd": (KDA_INTRA, STATE),
     "kda_decode_step": (KDA_DECODE,),
@@ -143,6 +150,7 @@ LAUNCH_KERNELS = {
     "kda_layer_chunk_fwd": (LAYER_INTRA, STATE, LAYER_EPILOGUE),
     "kda_layer_decode_step": (LAYER_DECODE,),
     "kda_dplr_chunk_fwd": (DPLR_INTRA, DPLR_STATE),
+    "kda_dplr_decode_step": (DPLR_DECODE,),
 }
 
 
@@ -521,6 +529,37 @@ def main():
             torch.cuda.synchronize()
             d_ms.append(e0.elapsed_time(e1))
         del dplr
+        # DPLR decode steps on the decode workload's states and tokens
+        dg = torch.Generator(device=dev)
+        dg.manual_seed(5)
+        da, db_ = [], []
+        for t in range(dsteps):
+            kt = din["k"][t]
+            da.append((-din["beta"][t][..., None] * kt.float()).to(kt.dtype))
+            dub = kt.float() + 0.5 * torch.randn(kt.shape, generator=dg, device=dev)
+            db_.append((torch.exp(din["log_alpha"][t]) * dub / torch.linalg.vector_norm(dub, dim=-1, keepdim=True))
+                       .to(kt.dtype))
+        del dub
+        dstate = state0.clone()
+
+        def dplr_decode(t):
+            kda.dplr_decode_step(din["q"][t], din["k"][t], din["v"][t], da[t], db_[t], din["log_alpha"][t],
+                                 dstate, out=od)
+
+        for _ in range(args.warmup):
+            for t in range(dsteps):
+                dplr_decode(t)
+        torch.cuda.synchronize()
+        dd_ms = []
+        for _ in range(args.steps):
+            de = [ev() for _ in range(dsteps + 1)]
+            de[0].record(stream)
+            for t in range(dsteps):
+                dplr_decode(t)
+                de[t + 1].record(stream)
+            torch.cuda.synchronize()
+            dd_ms.extend(de[t].elapsed_time(de[t + 1]) for t in range(dsteps))
+        del da, db_, dstate
 
     # ---- the backward (kda_chunk_bwd) over the first T_B tokens of the same inputs
     b_ms = []
@@ -689,6 +728,17 @@ def main():
                          "bound": "hbm", "achieved": d_bytes / d_t / 1e9, "peak": HBM_PEAK / 1e9,
                          "unit": "GB/s", "frac": d_bytes / d_t / HBM_PEAK,
                          "traffic": measured_traffic("kda_dplr_chunk_fwd")},
+        }
+        dd_ms.sort()
+        dd_t = dd_ms[len(dd_ms) // 2] / 1e3
+        dd_bytes = dplr_decode_alg_bytes(dw.N, dw.H, dw.Dk)
+        result["dplr"]["decode"] = {
+            "workload": "kda_dplr_decode_step on the decode workload's 256 x 32 fp32 states and tokens, 64 "
+                        "consecutive steps, a = -beta * k, b = alpha * unit(k + 0.5 N(0,1)) (bf16)",
+            "us_per_step_mean": sum(dd_ms) / len(dd_ms) * 1e3, "us_per_step_median": dd_t * 1e6,
+            "GB_per_s": dd_bytes / dd_t / 1e9, "hbm_frac": dd_bytes / dd_t / HBM_PEAK,
+            "alg_bytes_per_step": dd_bytes,
+            "traffic": measured_traffic("kda_dplr_decode_step"),
         }
         if not args.no_cpu_baseline:
             import oracle

@@ -92,7 +92,8 @@ int kda_version(void) { return KDA_VERSION; }
 static kda_status decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                               const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                               int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream,
-                              int gate_mode, const LayerIn *L) {
+                              int gate_mode, const LayerIn *L, const void *lr_a = nullptr,
+                              const void *lr_b = nullptr) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -128,6 +129,10 @@ static kda_status decode_impl(const void *q, const void *k, const void *v, const
         in[n_in++] = {L->x_beta, "x_beta", bxb, 2, true};
         in[n_in++] = {L->out_gate, "out_gate", bog, 2, true};
         in[n_in++] = {L->norm_weight, "norm_weight", (size_t)Dv * 4, 16, true};
+    } else if (gate_mode == 3) {
+        in[n_in++] = {lr_a, "a", bq, 16, true};
+        in[n_in++] = {lr_b, "b", bq, 16, true};
+        in[n_in++] = {log_alpha, "log_alpha", bg, 16, true};
     } else {
         // a per-channel gate is read in 16-byte vectors; a scalar gate and beta one by one
         in[n_in++] = {log_alpha, "log_alpha", bg, gate_mode == 1 ? 4u : 16u, true};
@@ -161,6 +166,7 @@ static kda_status decode_impl(const void *q, const void *k, const void *v, const
         a.l2_eps = L->l2_eps;
         a.norm_eps = L->norm_eps;
     }
+    a.lr_a = lr_a; a.lr_b = lr_b;
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return KDA_OK;
@@ -170,6 +176,12 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *state, int32_t N, int32_t H, int32_t Dk,
                            int32_t Dv, kda_dtype in_dtype, float *o, hipStream_t stream) {
     return decode_impl(q, k, v, log_alpha, beta, state, N, H, Dk, Dv, in_dtype, o, stream, 0, nullptr);
+}
+
+kda_status kda_dplr_decode_step(const void *q, const void *k, const void *v, const void *a, const void *b,
+                                const float *log_alpha, float *state, int32_t N, int32_t H, int32_t D,
+                                kda_dtype in_dtype, float *o, hipStream_t stream) {
+    return decode_impl(q, k, v, log_alpha, nullptr, state, N, H, D, D, in_dtype, o, stream, 3, nullptr, a, b);
 }
 
 kda_status gdn_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,

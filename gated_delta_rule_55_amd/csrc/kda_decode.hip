@@ -14,7 +14,13 @@
 //
 // The Gated DeltaNet step (one scalar gate per head, the recurrence the same
 // page compares KDA against) is the same kernel with that gate read once per
-// (n, h) and applied to every row.
+// (n, h) and applied to every row.  The general diagonal-plus-low-rank step
+// (the form the same section contrasts KDA with) is
+//
+//   e = b^T S,  S' = Diag(exp(log_alpha)) S,  S = S' + a e^T + k v^T
+//   o = S^T q = S'^T q + (a . q) e + (k . q) v
+//
+// with the first reduction taken over the undecayed state.
 //
 // One workgroup of min(512, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
 // (one float4) of RPT rows spaced RG apart, so each wave reads and writes whole
@@ -46,8 +52,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     static_assert(NT >= DK, "one thread per key channel");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
+    __shared__ float s_la[GM == 3 ? DK : 1], s_lb[GM == 3 ? DK : 1];  // DPLR a, b
     __shared__ f32x4 s_red[NW][CG][2];
-    __shared__ float s_kq[NW][CG];
+    __shared__ float s_kq[NW][CG], s_aq[GM == 3 ? NW : 1][CG];
     __shared__ float s_nrm[NWK][2];
 
     const int t = threadIdx.x;
@@ -61,7 +68,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     f32x4 sv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
-    const float b = GM == 2 ? sigmoid_f(bf16_bits_to_f32(a.x_beta[unit])) : a.beta[unit];
+    const float b = GM == 2 ? sigmoid_f(bf16_bits_to_f32(a.x_beta[unit])) : GM == 3 ? 1.f : a.beta[unit];
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(a.v, unit * DV + 4 * cg + e);
@@ -70,6 +77,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
         const float kc = load_in<kBf16>(a.k, unit * DK + t), qc = load_in<kBf16>(a.q, unit * DK + t);
         s_k[t] = kc;
         s_q[t] = qc;
+        if constexpr (GM == 3) {
+            s_la[t] = load_in<kBf16>(a.lr_a, unit * DK + t);
+            s_lb[t] = load_in<kBf16>(a.lr_b, unit * DK + t);
+        }
         kk = kc * kc;
         qq = qc * qc;
         float g;
@@ -103,13 +114,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     }
 
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
-    float kq = 0.f;
+    float kq = 0.f, aq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
         const float al = s_a[row], kr = s_k[row] * rk, qr = s_q[row] * rq;
+        if constexpr (GM == 3) {
+            p += sv[i] * s_lb[row];  // e = b^T S before the decay
+            aq += s_la[row] * qr;
+        }
         sv[i] *= al;
-        p += sv[i] * kr;
+        if constexpr (GM != 3) p += sv[i] * kr;
         r += sv[i] * qr;
         kq += kr * qr;
     }
@@ -123,30 +138,38 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
             r[e] += __shfl_xor(r[e], off);
         }
         kq += __shfl_xor(kq, off);
+        if constexpr (GM == 3) aq += __shfl_xor(aq, off);
     }
     if (lane < CG) {
         s_red[w][lane][0] = p;
         s_red[w][lane][1] = r;
         s_kq[w][lane] = kq;
+        if constexpr (GM == 3) s_aq[w][lane] = aq;
     }
     __syncthreads();
     p = s_red[0][cg][0];
     r = s_red[0][cg][1];
     kq = s_kq[0][cg];
+    if constexpr (GM == 3) aq = s_aq[0][cg];
 #pragma unroll
     for (int ww = 1; ww < NW; ++ww) {
         p += s_red[ww][cg][0];
         r += s_red[ww][cg][1];
         kq += s_kq[ww][cg];
+        if constexpr (GM == 3) aq += s_aq[ww][cg];
     }
-    const f32x4 u = b * (vv - p);
+    // KDA: S += k u^T with u = beta (v - p);  DPLR: S += a e^T + k v^T with e = p
+    const f32x4 u = GM == 3 ? vv : b * (vv - p);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
-        __builtin_nontemporal_store(sv[i] + (s_k[row] * rk) * u, &S[row * CG + cg]);
+        f32x4 nv = sv[i] + (s_k[row] * rk) * u;
+        if constexpr (GM == 3) nv += s_la[row] * p;
+        __builtin_nontemporal_store(nv, &S[row * CG + cg]);
     }
     if (rg == 0) {
         f32x4 ot = r + kq * u;
+        if constexpr (GM == 3) ot += aq * p;
         if constexpr (GM == 2) {
             // RMSNorm over the DV columns held by lanes 0 .. CG-1 of wave 0
             float ss = ot[0] * ot[0] + ot[1] * ot[1] + ot[2] * ot[2] + ot[3] * ot[3];
@@ -169,6 +192,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     switch (a.gate_mode) {
         case 0: hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 0>), grid, dim3(NT), 0, stream, a); break;
         case 1: hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 1>), grid, dim3(NT), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 3>), grid, dim3(NT), 0, stream, a); break;
         case 2:
             if constexpr (kBf16) {
                 hipLaunchKernelGGL((decode_step_kernel<DK, DV, kBf16, 2>), grid, dim3(NT), 0, stream, a);

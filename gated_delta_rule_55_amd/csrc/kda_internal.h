@@ -14,12 +14,13 @@ struct DecodeArgs {
     float *state, *o;
     int32_t N, H, Dk, Dv;
     bool bf16;
-    int32_t gate_mode;  // 0 KDA, 1 GDN (log_alpha [N, H]), 2 KDA layer (below)
+    int32_t gate_mode;  // 0 KDA, 1 GDN (log_alpha [N, H]), 2 KDA layer (below), 3 DPLR
     // gate mode 2: q, k unnormalised; bf16 x_alpha [N, H, Dk], x_beta [N, H],
     // output gate [N, H, Dv]; RMSNorm weight [Dv]
     const uint16_t *x_alpha, *x_beta, *out_gate;
     const float *norm_weight;
     float l2_eps, norm_eps;
+    const void *lr_a, *lr_b;  // gate mode 3: low-rank vectors a, b [N, H, Dk] in_dtype (no beta)
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

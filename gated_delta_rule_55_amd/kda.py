@@ -61,6 +61,8 @@ def load():
     lib.kda_dplr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, ip, i32, i64, i32, i32, i32, ctypes.c_int, i32,
                                        fp, fp, vp, sz, vp]
     lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
+    lib.kda_dplr_decode_step.argtypes = [vp, vp, vp, vp, vp, fp, fp, i32, i32, i32, ctypes.c_int, fp, vp]
+    lib.kda_dplr_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
@@ -217,6 +219,18 @@ def decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
 def gdn_decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
     """One Gated DeltaNet step per (n, h): as ``decode_step`` with log_alpha [N,H]."""
     return _decode(load().gdn_decode_step, q, k, v, log_alpha, beta, state, out, stream)
+
+
+def dplr_decode_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):
+    """One step of the general DPLR recurrence per (n, h): q, k, v, a, b [N,H,D]
+    (one dtype), log_alpha [N,H,D] fp32; state [N,H,D,D] fp32 updated in place.
+    Returns o [N,H,D] fp32."""
+    N, H, D = q.shape
+    if out is None:
+        out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
+    _check(load().kda_dplr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
+                                       _ptr(state), N, H, D, _dtype_code(q), _ptr(out), _stream(stream)))
+    return out
 
 
 def _decode(fn, q, k, v, log_alpha, beta, state, out, stream):

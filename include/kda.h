@@ -58,8 +58,8 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 130 /* 1.3.0: adds kda_dplr_chunk_fwd (1.2.0: kda_chunk_bwd; 1.1.0: the gdn_* and
-                            kda_layer_* entry points) */
+#define KDA_VERSION 130 /* 1.3.0: adds kda_dplr_chunk_fwd and kda_dplr_decode_step (1.2.0: kda_chunk_bwd;
+                            1.1.0: the gdn_* and kda_layer_* entry points) */
 
 typedef enum {
     KDA_OK = 0,
@@ -235,6 +235,20 @@ kda_status kda_dplr_chunk_fwd(const void *q, const void *k, const void *v, const
                               int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs, kda_dtype in_dtype,
                               int32_t chunk_size, float *o, float *final_state, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_dplr_decode_step -- one token of the DPLR recurrence above for each of N
+ * independent sequences, the state updated in place (e = b^T S_{t-1} is taken
+ * before the decay).
+ *   q, k, a, b  [N, H, D] in_dtype, 16-byte aligned
+ *   v           [N, H, D] in_dtype
+ *   log_alpha   [N, H, D] fp32
+ *   state, o, N, H, in_dtype, stream and errors as for kda_decode_step with
+ *   Dk = Dv = D; there is no beta.
+ */
+kda_status kda_dplr_decode_step(const void *q, const void *k, const void *v, const void *a, const void *b,
+                                const float *log_alpha, float *state, int32_t N, int32_t H, int32_t D,
+                                kda_dtype in_dtype, float *o, hipStream_t stream);
 
 /*
  * gdn_decode_step -- one GDN token for each of N independent sequences, the

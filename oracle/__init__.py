@@ -85,6 +85,8 @@ def _load():
         lib.dplr_oracle_forward.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.dplr_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, dp]
+        lib.dplr_oracle_decode_step.restype = ctypes.c_int
         lib.gdn_oracle_decode_step.argtypes = lib.kda_oracle_decode_step.argtypes
         lib.gdn_oracle_decode_step.restype = ctypes.c_int
         lib.kda_oracle_backward.argtypes = [
@@ -235,6 +237,23 @@ def decode_step(q, k, v, log_alpha, beta, state):
     """One KDA step per (n, h); q, k, log_alpha [N,H,Dk], v [N,H,Dv],
     beta [N,H], state [N,H,Dk,Dv].  Returns (o [N,H,Dv], new_state), fp64."""
     return _decode(False, q, k, v, log_alpha, beta, state)
+
+
+def dplr_decode_step(q, k, v, a, b, log_alpha, state):
+    """One DPLR step per (n, h); q, k, a, b, log_alpha [N,H,Dk], v [N,H,Dv],
+    state [N,H,Dk,Dv].  Returns (o [N,H,Dv], new_state), fp64."""
+    q, k, v, a, b, la = (_f64(x) for x in (q, k, v, a, b, log_alpha))
+    st = _f64(state).copy()
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    assert k.shape == q.shape and a.shape == q.shape and b.shape == q.shape and la.shape == q.shape
+    assert v.shape == (N, H, Dv) and st.shape == (N, H, Dk, Dv)
+    o = np.zeros((N, H, Dv))
+    rc = _load().dplr_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(la), _ptr(st),
+                                         N, H, Dk, Dv, _ptr(o))
+    if rc != 0:
+        raise ValueError(f"dplr_oracle_decode_step failed with code {rc}")
+    return o, st
 
 
 def gdn_decode_step(q, k, v, log_alpha, beta, state):

@@ -363,6 +363,30 @@ int gdn_oracle_decode_step(const double *q, const double *k, const double *v,
     return 0;
 }
 
+/*
+ * dplr_oracle_decode_step: one DPLR token for each of N independent states,
+ * the state updated in place; q, k, a, b, log_alpha [N, H, Dk], v, o
+ * [N, H, Dv].  This is dplr_token_update applied once per (n, h).
+ */
+int dplr_oracle_decode_step(const double *q, const double *k, const double *v,
+                            const double *a, const double *b, const double *log_alpha,
+                            double *state, int64_t N, int64_t H, int64_t Dk,
+                            int64_t Dv, double *o)
+{
+    if (!q || !k || !v || !a || !b || !log_alpha || !state || !o) return -1;
+    if (N < 1 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    double *e = (double *)malloc(sizeof(double) * (size_t)Dv);
+    if (!e) return -2;
+    for (int64_t u = 0; u < N * H; ++u)
+        dplr_token_update(state + (size_t)u * (size_t)(Dk * Dv), Dk, Dv,
+                          q + (size_t)u * (size_t)Dk, k + (size_t)u * (size_t)Dk,
+                          v + (size_t)u * (size_t)Dv, a + (size_t)u * (size_t)Dk,
+                          b + (size_t)u * (size_t)Dk, log_alpha + (size_t)u * (size_t)Dk,
+                          e, o + (size_t)u * (size_t)Dv);
+    free(e);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Backward (reverse mode) of the KDA token loop.                            */
 /* ------------------------------------------------------------------------- */

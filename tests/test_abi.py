@@ -324,3 +324,24 @@ def _dplr(lib, **kw):
 def test_dplr_chunk_fwd_rejects(lib, kw, code, msg):
     assert _dplr(lib, **kw) == code
     assert msg in lib.kda_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=24), UNSUPPORTED, b"Dk=24"),
+    (dict(dtype=5), UNSUPPORTED, b"in_dtype"),
+    (dict(H=0), INVALID, b"H=0"),
+    (dict(a=None), INVALID, b"a is NULL"),
+    (dict(b=FAKE + 0x4000008), INVALID, b"b is not 16-byte aligned"),
+    (dict(log_alpha=None), INVALID, b"log_alpha is NULL"),
+    (dict(o=FAKE + 0x3000000), INVALID, b"overlaps"),
+])
+def test_dplr_decode_rejects(lib, kw, code, msg):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, a=FAKE + 0x3000000, b=FAKE + 0x4000000,
+             log_alpha=FAKE + 0x5000000, state=FAKE + 0x6000000, N=4, H=2, D=16, dtype=BF16,
+             o=FAKE + 0x8000000, stream=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = lib.kda_dplr_decode_step(p(a["q"]), p(a["k"]), p(a["v"]), p(a["a"]), p(a["b"]), p(a["log_alpha"]),
+                                  p(a["state"]), a["N"], a["H"], a["D"], a["dtype"], p(a["o"]), a["stream"])
+    assert rc == code
+    assert msg in lib.kda_last_error()

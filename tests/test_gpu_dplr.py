@@ -126,3 +126,35 @@ def test_dplr_empty_and_determinism_and_chunk_invariance():
         oc, fc = _run(inp, a, b, C)
         assert_parity(oc, host64(oa), TAU[torch.bfloat16], f"dplr C={C} vs C=64 o")
         assert_parity(fc, host64(fa), TAU[torch.bfloat16], f"dplr C={C} vs C=64 final_state")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 32), ("f32", 16)])
+def test_dplr_decode_steps(dtype, D):
+    """Three consecutive kda_dplr_decode_step calls on 64 sequences x 4 heads
+    (random fp32 states), against the oracle's step; one head's gate is -inf on
+    every channel in the second step, one channel in the third."""
+    log(f"dplr decode dtype={dtype} D={D}")
+    N, H = 64, 4
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(70 + D)
+    unit = lambda x: x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+    state = 0.02 * torch.randn((N, H, D, D), device="cuda", generator=g)
+    ref_state = host64(state)
+    for step in range(3):
+        q = unit(torch.randn((N, H, D), device="cuda", generator=g)).to(tdt)
+        k = unit(torch.randn((N, H, D), device="cuda", generator=g)).to(tdt)
+        v = torch.randn((N, H, D), device="cuda", generator=g).to(tdt)
+        la = -torch.nn.functional.softplus(torch.randn((N, H, D), device="cuda", generator=g) + 3)
+        if step == 1:
+            la[5, 2] = float("-inf")
+        if step == 2:
+            la[9, 1, 3] = float("-inf")
+        beta = torch.sigmoid(torch.randn((N, H), device="cuda", generator=g))
+        a = (-beta[..., None] * k.float()).to(tdt)
+        b = unit(k.float() + 0.5 * torch.randn((N, H, D), device="cuda", generator=g)).to(tdt)
+        o = kda.dplr_decode_step(q, k, v, a, b, la, state)
+        torch.cuda.synchronize()
+        ro, ref_state = oracle.dplr_decode_step(q, k, v, a, b, la, ref_state)
+        tau = TAU[tdt]
+        assert_parity(o, ro, tau, f"dplr decode {dtype} D={D} step {step} o")
+        assert_parity(state, ref_state, tau, f"dplr decode {dtype} D={D} step {step} state")

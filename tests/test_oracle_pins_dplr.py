@@ -126,3 +126,16 @@ def test_varlen_matches_separate_runs():
             np.testing.assert_array_equal(fs[n], fn[0])
         else:
             np.testing.assert_array_equal(fs[n], s0[n])
+
+
+def test_decode_step_is_one_explicit_transition():
+    """dplr_decode_step on N x H states against the explicit matrices of one
+    token (brute force at T = 1), -inf gates included."""
+    rng = np.random.default_rng(17)
+    q, k, v, a, b, la, s0 = _inputs(rng, 3, 1, 2, 5, 4)
+    la[1, 0, 1, :] = -np.inf
+    la[2, 0, 0, 3] = -np.inf
+    o, st = oracle.dplr_decode_step(q[:, 0], k[:, 0], v[:, 0], a[:, 0], b[:, 0], la[:, 0], s0)
+    bo, bfs = _brute(q, k, v, a, b, la, s0)
+    np.testing.assert_allclose(o, bo[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(st, bfs, rtol=0, atol=1e-12)
