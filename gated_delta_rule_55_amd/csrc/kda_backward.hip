@@ -369,6 +369,11 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
     __shared__ float sGC[D], sdGL[D];
     __shared__ float sPart[C][NTD], sPart2[C][NTI], sPart3[NTI][D];
     __shared__ int sFirst, sLast;
+    __shared__ uint8_t sNegInf[C][D];  // log_alpha is -inf here (its gradient is 0)
+    // the reverse cumulative sum of dG runs in NSEG segments of RPS tokens per channel
+    constexpr int NSEG = kBwdIntraThreads / D < C / 4 ? kBwdIntraThreads / D : C / 4, RPS = C / NSEG;
+    static_assert(NSEG * D <= kBwdIntraThreads && RPS <= 16, "cumulative sum layout");
+    static_assert(NSEG * D * sizeof(GT) <= 4 * C * MS * sizeof(float), "segment sums fit in sM");
 
     const int H = p.H;
     float *scr = p.scratch + static_cast<size_t>(blockIdx.x) * kNumScratch * C * D;
@@ -419,7 +424,9 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         __syncthreads();
         for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
-            if (i < nvalid && sG[i][c] != static_cast<GT>(kNegInf)) sNotRst[i] = 1;
+            const bool ninf = i < nvalid && sG[i][c] == static_cast<GT>(kNegInf);
+            if (i < nvalid && !ninf) sNotRst[i] = 1;
+            sNegInf[i][c] = ninf ? 1 : 0;
         }
         __syncthreads();
         for (int c = tid; c < D; c += kBwdIntraThreads) {
@@ -881,23 +888,32 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             DG[x] += qv * rowP + kv * rowA - kv * (colP + colA);
         }
         __syncthreads();
-        // ---- dlog_alpha = reverse cumulative sum of dG; dbeta
-        for (int c = tid; c < D; c += kBwdIntraThreads) {
-            GT acc = sdGL[c];
-            for (int i0 = C - 16; i0 >= 0; i0 -= 16) {  // 16 rows of the column per batch of loads
-                float dgc[16], la[16];
+        // ---- dlog_alpha = reverse cumulative sum of dG (from the last token's dG
+        //      term in sdGL), in NSEG segments of RPS tokens per channel: segment
+        //      totals meet in LDS (over sM, no longer in use), each segment then
+        //      adds the totals after it; dbeta
+        {
+            GT *segt = reinterpret_cast<GT *>(&sM[0][0][0]);  // [NSEG][D]
+            const int c = tid % D, sg = tid / D, i0 = sg * RPS;
+            float dgc[RPS];
+            GT tot = 0;
+            if (sg < NSEG) {
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const int i = i0 + x;
-                    dgc[x] = DG[i * D + c];
-                    la[x] = i < nvalid ? p.log_alpha[row_of(i) * D + c] : 0.f;
-                }
+                for (int x = 0; x < RPS; ++x) dgc[x] = DG[(i0 + x) * D + c];
 #pragma unroll
-                for (int x = 15; x >= 0; --x) {
+                for (int x = RPS - 1; x >= 0; --x) tot += dgc[x];
+                segt[sg * D + c] = tot;
+            }
+            __syncthreads();
+            if (sg < NSEG) {
+                GT acc = sdGL[c];
+                for (int q = NSEG - 1; q > sg; --q) acc += segt[q * D + c];
+#pragma unroll
+                for (int x = RPS - 1; x >= 0; --x) {
                     const int i = i0 + x;
                     acc += dgc[x];
                     if (i < nvalid)
-                        p.dlog_alpha[row_of(i) * D + c] = (sNotRst[i] && la[x] != kNegInf) ? static_cast<float>(acc) : 0.f;
+                        p.dlog_alpha[row_of(i) * D + c] = (sNotRst[i] && !sNegInf[i][c]) ? static_cast<float>(acc) : 0.f;
                 }
             }
         }
