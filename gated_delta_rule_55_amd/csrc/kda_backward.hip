@@ -370,8 +370,10 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
     __shared__ float sPart[C][NTD], sPart2[C][NTI], sPart3[NTI][D];
     __shared__ int sFirst, sLast;
     __shared__ uint8_t sNegInf[C][D];  // log_alpha is -inf here (its gradient is 0)
-    // the reverse cumulative sum of dG runs in NSEG segments of RPS tokens per channel
+    // the cumulative decay and the reverse cumulative sum of dG run in NSEG
+    // segments of RPS tokens per channel
     constexpr int NSEG = kBwdIntraThreads / D < C / 4 ? kBwdIntraThreads / D : C / 4, RPS = C / NSEG;
+    __shared__ GT sSegG[NSEG][D];
     static_assert(NSEG * D <= kBwdIntraThreads && RPS <= 16, "cumulative sum layout");
     static_assert(NSEG * D * sizeof(GT) <= 4 * C * MS * sizeof(float), "segment sums fit in sM");
 
@@ -429,26 +431,33 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             sNegInf[i][c] = ninf ? 1 : 0;
         }
         __syncthreads();
-        for (int c = tid; c < D; c += kBwdIntraThreads) {
-            GT acc = 0;
-            for (int i = 0; i < C; ++i) {
-                const GT g = sNotRst[i] ? (sG[i][c] > GT(kGFloor) ? sG[i][c] : GT(kGFloor)) : GT(0);
-                acc += g;
-                sG[i][c] = acc;
-            }
-        }
-        if (tid == 0) {
-            int cnt = 0, first = C, last = -1;
-            for (int i = 0; i < C; ++i) {
-                if (!sNotRst[i]) {
-                    ++cnt;
-                    if (first == C) first = i;
-                    last = i;
+        // cumulative decay: NSEG segments of RPS tokens per channel, then each
+        // segment adds the totals before it; reset counts by one wave-wide ballot
+        {
+            const int c = tid % D, sg = tid / D;
+            if (sg < NSEG) {
+                GT acc = 0;
+                for (int x = 0; x < RPS; ++x) {
+                    const int i = sg * RPS + x;
+                    acc += sNotRst[i] ? (sG[i][c] > GT(kGFloor) ? sG[i][c] : GT(kGFloor)) : GT(0);
+                    sG[i][c] = acc;
                 }
-                sCnt[i] = cnt;
+                sSegG[sg][c] = acc;
             }
-            sFirst = first;
-            sLast = last;
+            if (w == kIW - 1) {
+                const unsigned long long rm = __ballot(lane < C && !sNotRst[lane]);
+                if (lane < C) sCnt[lane] = __popcll(rm & ((2ull << lane) - 1ull));
+                if (lane == 0) {
+                    sFirst = rm ? __ffsll(static_cast<long long>(rm)) - 1 : C;
+                    sLast = rm ? 63 - __clzll(rm) : -1;
+                }
+            }
+            __syncthreads();
+            if (sg > 0 && sg < NSEG) {
+                GT off = 0;
+                for (int q = 0; q < sg; ++q) off += sSegG[q][c];
+                for (int x = 0; x < RPS; ++x) sG[sg * RPS + x][c] += off;
+            }
         }
         __syncthreads();
         const int first_rst = sFirst, last_rst = sLast;
