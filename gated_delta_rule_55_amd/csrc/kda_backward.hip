@@ -126,6 +126,40 @@ __device__ __forceinline__ void mm_f32_vb(f32x4 &acc, FA &&a4, const Frag<K> &bf
     }
 }
 
+// The tiles t = t0, t0 + step, .. < tend of products acc_t = A_t B with B a
+// preloaded fragment, software-pipelined: tile t + step's left-hand fragment
+// (a4t(t, r, k0) as mm_f32_v's a4) and its epilogue inputs (pre(t), 4 values)
+// are loaded before tile t's products, so their latency overlaps them.
+// epi(t, acc, pre_t) consumes a tile.
+template <int K, typename FA, typename FP, typename FE>
+__device__ __forceinline__ void tiles_vb(int t0, int tend, int step, FA &&a4t, const Frag<K> &bf, FP &&pre,
+                                         FE &&epi, int lane) {
+    const int r = lane & 15, kk = lane >> 4;
+    constexpr int NT = K / 16;
+    f32x4 cur[NT], nxt[NT], pc = {0.f, 0.f, 0.f, 0.f}, pn = pc;
+    if (t0 < tend) {
+#pragma unroll
+        for (int b = 0; b < NT; ++b) cur[b] = a4t(t0, r, 16 * b + 4 * kk);
+        pc = pre(t0);
+    }
+    for (int t = t0; t < tend; t += step) {
+        if (t + step < tend) {
+#pragma unroll
+            for (int b = 0; b < NT; ++b) nxt[b] = a4t(t + step, r, 16 * b + 4 * kk);
+            pn = pre(t + step);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[b][j], bf.v[b][j], acc, 0, 0, 0);
+        epi(t, acc, pc);
+#pragma unroll
+        for (int b = 0; b < NT; ++b) cur[b] = nxt[b];
+        pc = pn;
+    }
+}
+
 // sum over the 16 lanes of each row group (lanes 16 g .. 16 g + 15)
 __device__ __forceinline__ float sum16(float x) {
     x += __shfl_xor(x, 1);
@@ -621,18 +655,24 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             const float *b = S0 + static_cast<size_t>(k0) * D + 16 * (w % NTD) + nn;
             return f32x4{b[0], b[D], b[2 * D], b[3 * D]};
         }, lane);
-#pragma unroll 1
-        for (int t = w; t < NTI * NTD; t += kIW) {
-            const int ti = t / NTD, td = t % NTD;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_vb<D>(acc, [&](int r, int k0) { return ld4(KG + (16 * ti + r) * D + k0); }, bS0, lane);
+        tiles_vb<D>(w, NTI * NTD, kIW,
+            [&](int t, int r, int k0) { return ld4(KG + (16 * (t / NTD) + r) * D + k0); }, bS0,
+            [&](int t) {
+                f32x4 vv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * kg + r, cc = 16 * td + l16;
-                const float vv = i < nvalid ? toF(static_cast<const In *>(p.v)[row_of(i) * D + cc]) : 0.f;
-                R[i * D + cc] = vv - acc[r];
-            }
-        }
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * (t / NTD) + 4 * kg + r, cc = 16 * (t % NTD) + l16;
+                    vv[r] = i < nvalid ? toF(static_cast<const In *>(p.v)[row_of(i) * D + cc]) : 0.f;
+                }
+                return vv;
+            },
+            [&](int t, const f32x4 &acc, const f32x4 &vv) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * (t / NTD) + 4 * kg + r, cc = 16 * (t % NTD) + l16;
+                    R[i * D + cc] = vv[r] - acc[r];
+                }
+            }, lane);
         __syncthreads();
         // ---- U = T Diag(beta) R;  dU = P^T dO + Kt dS1
                 {
@@ -699,14 +739,13 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             const int j = 16 * (w % NTI) + nn;
             return sBeta[j] * ld4(R + j * D + k0);
         }, lane);
-#pragma unroll 1
-        for (int t = w; t < NTI * NTI; t += kIW) {
-            const int ti = t / NTI, tj = t % NTI;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_vb<D>(acc, [&](int r, int k0) { return ld4(DU + (16 * ti + r) * D + k0); }, bXT, lane);
+        tiles_vb<D>(w, NTI * NTI, kIW,
+            [&](int t, int r, int k0) { return ld4(DU + (16 * (t / NTI) + r) * D + k0); }, bXT,
+            [&](int) { return f32x4{0.f, 0.f, 0.f, 0.f}; },
+            [&](int t, const f32x4 &acc, const f32x4 &) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sM[3][16 * ti + 4 * kg + r][16 * tj + l16] = acc[r];
-        }
+                for (int r = 0; r < 4; ++r) sM[3][16 * (t / NTI) + 4 * kg + r][16 * (t % NTI) + l16] = acc[r];
+            }, lane);
         __syncthreads();
         // Y = dT T^T  (dT in sM[3] for now, Y into sM[1])
         #pragma unroll 1
@@ -739,17 +778,16 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         __syncthreads();
         // ---- dP = dO U^T (lower, no reset in (j, i]) into sM[1]
                 const Frag<D> bUT = frag_of<D>([&](int k0, int nn) { return ld4(U + (16 * (w % NTI) + nn) * D + k0); }, lane);
-#pragma unroll 1
-        for (int t = w; t < NTI * NTI; t += kIW) {
-            const int ti = t / NTI, tj = t % NTI;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mm_f32_vb<D>(acc, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bUT, lane);
+        tiles_vb<D>(w, NTI * NTI, kIW,
+            [&](int t, int r, int k0) { return dO4(16 * (t / NTI) + r, k0); }, bUT,
+            [&](int) { return f32x4{0.f, 0.f, 0.f, 0.f}; },
+            [&](int t, const f32x4 &acc, const f32x4 &) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * kg + r, j = 16 * tj + l16;
-                sM[1][i][j] = (j <= i && sCnt[i] == sCnt[j]) ? acc[r] : 0.f;
-            }
-        }
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * (t / NTI) + 4 * kg + r, j = 16 * (t % NTI) + l16;
+                    sM[1][i][j] = (j <= i && sCnt[i] == sCnt[j]) ? acc[r] : 0.f;
+                }
+            }, lane);
         // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
         //      their Gamma terms
                 const Frag<D> bS0T = frag_of<D>([&](int k0, int nn) {
