@@ -395,6 +395,16 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     const float gb = j > 0 ? sG[j - 1][cx] : 0.f;
                     xf[t][e] = cnt_before(j) == 0 ? in(p.b, j, cx) * __expf(gb) : 0.f;
                 }
+            // the Q e^G terms of the Q' rows, loaded before the products
+            f32x4 qg[NTI];
+#pragma unroll
+            for (int I = 0; I < NTI; ++I) {
+                const int i = 16 * I + l16, c0 = 16 * ct + 4 * kg;
+                const f32x4 qv = in4(p.q, i, c0), gv = g4(i, c0);
+                const bool live = sCnt[i] == 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) qg[I][r] = live ? qv[r] * __expf(gv[r]) : 0.f;
+            }
             for (int rt = 0; rt < 2 * NTI; ++rt) {
                 const int I = rt < NTI ? rt : rt - NTI, mt = rt < NTI ? 0 : 2;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -407,14 +417,14 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     }
                 // acc[r] = (M X)[token 16 I + l16][channel 16 ct + 4 kg + r]
                 f32x4 val;
-                const int i = 16 * I + l16, c0 = 16 * ct + 4 * kg;
                 if (rt < NTI) {
                     val = -acc;
                 } else {
-                    const f32x4 qv = in4(p.q, i, c0), gv = g4(i, c0);
-                    const bool live = sCnt[i] == 0;
+                    f32x4 q4 = qg[0];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) val[r] = acc[r] + (live ? qv[r] * __expf(gv[r]) : 0.f);
+                    for (int J = 1; J < NTI; ++J)
+                        if (J == I) q4 = qg[J];
+                    val = acc + q4;
                 }
                 store4(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8 + 4 * hc, val);
             }
