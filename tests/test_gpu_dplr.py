@@ -158,3 +158,25 @@ def test_dplr_decode_steps(dtype, D):
         tau = TAU[tdt]
         assert_parity(o, ro, tau, f"dplr decode {dtype} D={D} step {step} o")
         assert_parity(state, ref_state, tau, f"dplr decode {dtype} D={D} step {step} state")
+
+
+def test_dplr_strong_decay_and_dense_batch():
+    """B = 2 dense sequences of 100 tokens, fp32, decays of about e^-20 per token
+    (-softplus(N(0,1) + 20)): every factored exponent stays <= 0 and nothing
+    overflows; o and final states at the fp32 bar."""
+    g = torch.Generator(device="cuda").manual_seed(80)
+    B, T, H, D = 2, 100, 2, 32
+    unit = lambda x: x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+    q = unit(torch.randn((B, T, H, D), device="cuda", generator=g))
+    k = unit(torch.randn((B, T, H, D), device="cuda", generator=g))
+    v = torch.randn((B, T, H, D), device="cuda", generator=g)
+    la = -torch.nn.functional.softplus(torch.randn((B, T, H, D), device="cuda", generator=g) + 20)
+    beta = torch.sigmoid(torch.randn((B, T, H), device="cuda", generator=g))
+    a = -beta[..., None] * k
+    b = unit(k + 0.5 * torch.randn((B, T, H, D), device="cuda", generator=g))
+    s0 = 0.05 * torch.randn((B, H, D, D), device="cuda", generator=g)
+    inp = dict(q=q, k=k, v=v, log_alpha=la, init_state=s0, cu_seqlens=None)
+    for C in (16, 64):
+        o, fs = _run(inp, a, b, C)
+        assert torch.isfinite(o).all() and torch.isfinite(fs).all()
+        _check(inp, a, b, o, fs, TAU[torch.float32], label=f"dplr strong decay C={C}")
