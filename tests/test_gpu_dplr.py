@@ -180,3 +180,51 @@ def test_dplr_strong_decay_and_dense_batch():
         o, fs = _run(inp, a, b, C)
         assert torch.isfinite(o).all() and torch.isfinite(fs).all()
         _check(inp, a, b, o, fs, TAU[torch.float32], label=f"dplr strong decay C={C}")
+
+
+def test_dplr_long_workload_sampled_and_split_resume():
+    """T = 1,048,576, H = 32, d = 128, bf16, chunk 64 (the launch the bench times):
+    o of four heads over the first 32,768 tokens against the oracle, and the run
+    split at T/2 (the second half started from the first half's final state)
+    against the whole run for every output and the final state."""
+    inp = workloads.make_prefill("long", "cuda", 0)
+    log("dplr long workload T=1M H=32")
+    a, b = workloads.dplr_vectors(inp, seed=90)
+    o, fs = _run(inp, a, b, 64)
+    assert torch.isfinite(o).all() and torch.isfinite(fs).all()
+    heads, Tp = [0, 11, 20, 31], 32768
+    cut = lambda x, t0, t1: x[:, t0:t1, heads].contiguous()
+    ro, _ = oracle.dplr_forward(*(cut(x, 0, Tp) for x in (inp["q"], inp["k"], inp["v"], a, b, inp["log_alpha"])),
+                                n_threads=oracle_threads())
+    assert_parity(o[:, :Tp, heads], ro, TAU[torch.bfloat16], "dplr long o (4 heads, 32k tokens)")
+    del ro
+    T2 = inp["T"] // 2
+    half = lambda x, t0, t1: x[:, t0:t1].contiguous()
+    names = ("q", "k", "v")
+    o1, f1 = kda.dplr_chunk_fwd(*(half(inp[n], 0, T2) for n in names), half(a, 0, T2), half(b, 0, T2),
+                                half(inp["log_alpha"], 0, T2), None, None, 64)
+    o2, f2 = kda.dplr_chunk_fwd(*(half(inp[n], T2, inp["T"]) for n in names), half(a, T2, inp["T"]),
+                                half(b, T2, inp["T"]), half(inp["log_alpha"], T2, inp["T"]), f1, None, 64)
+    torch.cuda.synchronize()
+    tau = TAU[torch.bfloat16]
+    assert torch.equal(o1, o[:, :T2])  # the same kernels on the same chunks
+    assert_parity(o2, host64(o[:, T2:]), tau, "dplr long split second half o")
+    assert_parity(f2, host64(fs), tau, "dplr long split final state")
+
+
+def test_dplr_prefill_equals_decode_steps():
+    inp = workloads.make_prefill("prefill", "cuda", seed=91, T=96, H=2, dtype="f32")
+    inp = _shrink(inp, 64)
+    a, b = workloads.dplr_vectors(inp, seed=92)
+    o, fs = _run(inp, a, b, 32)
+    st = inp["init_state"].clone()
+    outs = []
+    for t in range(96):
+        col = lambda x: x[:, t].contiguous()
+        outs.append(kda.dplr_decode_step(col(inp["q"]), col(inp["k"]), col(inp["v"]), col(a), col(b),
+                                         col(inp["log_alpha"]), st))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, dim=1)
+    tau = TAU[torch.float32]
+    assert_parity(o, host64(od), tau, "dplr prefill vs decode steps o")
+    assert_parity(fs, host64(st), tau, "dplr prefill vs decode steps final state")
