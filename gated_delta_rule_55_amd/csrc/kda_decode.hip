@@ -22,7 +22,7 @@
 //
 // with the first reduction taken over the undecayed state.
 //
-// One workgroup of min(512, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
+// One workgroup of min(1024, Dk*Dv/4) threads per (n, h).  Thread t owns 4 adjacent columns
 // (one float4) of RPT rows spaced RG apart, so each wave reads and writes whole
 // contiguous rows (coalesced 16-byte accesses).  Reductions: butterfly
 // shuffles inside a wave over the lanes that share a column group, then LDS
@@ -32,7 +32,7 @@
 
 namespace kda {
 
-constexpr int kDecodeThreads = 512;
+constexpr int kDecodeThreads = 1024;  // 16 waves: 4 float4 of the state per thread at d = 128
 
 // Gate modes: 0 KDA (log_alpha [N, H, Dk]); 1 Gated DeltaNet (one log_alpha per
 // (n, h), [N, H]); 2 KDA layer: q and k arrive unnormalised and are divided by
