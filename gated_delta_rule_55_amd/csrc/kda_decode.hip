@@ -68,7 +68,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     f32x4 sv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
-    const float b = GM == 2 ? sigmoid_f(bf16_bits_to_f32(a.x_beta[unit])) : GM == 3 ? 1.f : a.beta[unit];
+    // zero, in a form the compiler does not treat as uniform: the (n, h) scalars below
+    // become vector loads issued here with the token's others (as scalar loads they
+    // would be placed after the whole state stream has arrived)
+    const int z0 = static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u));
+    const float b = GM == 2 ? sigmoid_f(bf16_bits_to_f32(a.x_beta[unit])) : GM == 3 ? 1.f : a.beta[unit + z0];
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(a.v, unit * DV + 4 * cg + e);
@@ -85,7 +89,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
         qq = qc * qc;
         float g;
         if constexpr (GM == 2) g = neg_softplus(bf16_bits_to_f32(a.x_alpha[unit * DK + t]));
-        else if constexpr (GM == 1) g = a.log_alpha[unit];
+        else if constexpr (GM == 1) g = a.log_alpha[unit + z0];
         else g = a.log_alpha[unit * DK + t];
         s_a[t] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
     }
