@@ -52,7 +52,6 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     static_assert(NT >= DK, "one thread per key channel");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
-    __shared__ float s_la[GM == 3 ? DK : 1], s_lb[GM == 3 ? DK : 1];  // DPLR a, b
     __shared__ f32x4 s_red[NW][CG][2];
     __shared__ float s_kq[NW][CG], s_aq[GM == 3 ? NW : 1][CG];
     __shared__ float s_nrm[NWK][2];
@@ -76,22 +75,34 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = load_in<kBf16>(a.v, unit * DV + 4 * cg + e);
+    // Per-row token values: gate mode 2 needs the norms of k and q over all rows
+    // first, so it goes through LDS and a barrier; the other modes read the rows
+    // a thread owns directly (cache-resident), after the state stream is issued,
+    // and need no barrier before the reductions.
     float kk = 0.f, qq = 0.f;
-    if (t < DK) {
+    float rkv[GM == 2 ? 1 : RPT], rqv[GM == 2 ? 1 : RPT], rav[GM == 2 ? 1 : RPT];
+    float rla[GM == 3 ? RPT : 1], rlb[GM == 3 ? RPT : 1];
+    if constexpr (GM != 2) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * RG;
+            rkv[i] = load_in<kBf16>(a.k, unit * DK + row);
+            rqv[i] = load_in<kBf16>(a.q, unit * DK + row);
+            const float g = GM == 1 ? a.log_alpha[unit + z0] : a.log_alpha[unit * DK + row];
+            rav[i] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
+            if constexpr (GM == 3) {
+                rla[i] = load_in<kBf16>(a.lr_a, unit * DK + row);
+                rlb[i] = load_in<kBf16>(a.lr_b, unit * DK + row);
+            }
+        }
+    }
+    if (GM == 2 && t < DK) {
         const float kc = load_in<kBf16>(a.k, unit * DK + t), qc = load_in<kBf16>(a.q, unit * DK + t);
         s_k[t] = kc;
         s_q[t] = qc;
-        if constexpr (GM == 3) {
-            s_la[t] = load_in<kBf16>(a.lr_a, unit * DK + t);
-            s_lb[t] = load_in<kBf16>(a.lr_b, unit * DK + t);
-        }
         kk = kc * kc;
         qq = qc * qc;
-        float g;
-        if constexpr (GM == 2) g = neg_softplus(bf16_bits_to_f32(a.x_alpha[unit * DK + t]));
-        else if constexpr (GM == 1) g = a.log_alpha[unit + z0];
-        else g = a.log_alpha[unit * DK + t];
-        s_a[t] = fast_exp2(g * kLog2e);  // exp(-inf) -> 0
+        s_a[t] = fast_exp2(neg_softplus(bf16_bits_to_f32(a.x_alpha[unit * DK + t])) * kLog2e);
     }
     if constexpr (GM == 2) {
 #pragma unroll
@@ -103,8 +114,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
             s_nrm[w][0] = kk;
             s_nrm[w][1] = qq;
         }
+        __syncthreads();
     }
-    __syncthreads();
     float rk = 1.f, rq = 1.f;  // 1 / |k|, 1 / |q| (gate mode 2)
     if constexpr (GM == 2) {
         float nk = 0.f, nq = 0.f;
@@ -122,10 +133,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
-        const float al = s_a[row], kr = s_k[row] * rk, qr = s_q[row] * rq;
+        float al, kr, qr;
+        if constexpr (GM == 2) {
+            al = s_a[row];
+            kr = s_k[row] * rk;
+            qr = s_q[row] * rq;
+        } else {
+            al = rav[i];
+            kr = rkv[i];
+            qr = rqv[i];
+        }
         if constexpr (GM == 3) {
-            p += sv[i] * s_lb[row];  // e = b^T S before the decay
-            aq += s_la[row] * qr;
+            p += sv[i] * rlb[i];  // e = b^T S before the decay
+            aq += rla[i] * qr;
         }
         sv[i] *= al;
         if constexpr (GM != 3) p += sv[i] * kr;
@@ -167,8 +187,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_step_kernel(DecodeArgs 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + i * RG;
-        f32x4 nv = sv[i] + (s_k[row] * rk) * u;
-        if constexpr (GM == 3) nv += s_la[row] * p;
+        const float kr = GM == 2 ? s_k[row] * rk : rkv[GM == 2 ? 0 : i];
+        f32x4 nv = sv[i] + kr * u;
+        if constexpr (GM == 3) nv += rla[i] * p;
         __builtin_nontemporal_store(nv, &S[row * CG + cg]);
     }
     if (rg == 0) {
