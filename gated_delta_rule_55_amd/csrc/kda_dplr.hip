@@ -25,7 +25,8 @@
 // products of C x C matrices instead of one, and a state update of rank 2C
 // instead of C.  dplr_intra_kernel writes one package per (chunk, head) in the
 // layouts of the KDA state pass, which then walks the chunks in its DPLR form
-// (W stored negated; [At; Kt] against [U; V] as one contraction over 2C tokens).
+// (W stored negated; [At; Kt] against [U; V] as one contraction over 2C tokens,
+// V from the package's VX section).
 //
 // Gram matrices: 16x16 blocks below the diagonal on the fp32 matrix cores with
 // the reference m = the last token of the column block, e^{x_i - G_j} =
@@ -365,6 +366,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     Op *kt = reinterpret_cast<Op *>(pkg + p.L.kt);
     f32x4 *up = reinterpret_cast<f32x4 *>(pkg + p.L.up);
     f32x4 *oi = reinterpret_cast<f32x4 *>(pkg + p.L.oi);
+    f32x4 *vx = reinterpret_cast<f32x4 *>(pkg + p.L.vx);
     constexpr int NCT = DKP / 16;
     const int last_rst = sLast, cnt_last = sCnt[C - 1];
     auto store4 = [&](Op *dst, const f32x4 &v) {
@@ -464,6 +466,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     }
                 f32x4 *dst = rt < NTI ? up : oi;
                 dst[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = acc;
+                // V itself for the state pass: vf[I] holds rows 16 I + 4 kg + e of
+                // column col, the UP layout of row tile I
+                if (rt < NTI) vx[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = vf[I];
             }
         }
     }
@@ -489,7 +494,7 @@ hipError_t launch_dplr_t(const PrefillArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state, nullptr,
-                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, L, a.v};
+                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, L};
     return launch_dplr_state<C, D, BF>(sp, stream);
 }
 

@@ -45,6 +45,7 @@ namespace kda {
 //   GL  Gamma of the chunk's last token per key channel, fp32 [Dk].
 struct PackageLayout {
     size_t wq, kt, up, oi, gl, bytes;  // offsets of sections and total size
+    size_t vx;                         // DPLR only: the chunk's V in the UP layout
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -61,13 +62,15 @@ __host__ __device__ inline PackageLayout package_layout(int C, int Dk, int Dv, b
     L.oi = off; off += align256((size_t)C * Dv * 4);
     L.gl = off; off += align256((size_t)Dk * 4);
     L.bytes = off;
+    L.vx = 0;  // no V section
     return L;
 }
 
 // The DPLR form's package (kda_dplr.hip): WQ, UP, OI and GL as above with W
 // stored negated and UP holding U' = T Abk V; KT holds 2 CP tokens, the
 // decayed low-rank vectors A-tilde (k-steps 0 .. CP/32 - 1) then the decayed
-// keys K-tilde.
+// keys K-tilde; VX holds the chunk's V (fp32, zero past its last token) in the
+// UP layout.
 __host__ __device__ inline PackageLayout dplr_package_layout(int C, int Dk, int Dv, bool bf16) {
     const size_t osz = bf16 ? 2 : 4;
     const size_t dkp = Dk < 32 ? 32 : Dk;
@@ -79,6 +82,7 @@ __host__ __device__ inline PackageLayout dplr_package_layout(int C, int Dk, int 
     L.up = off; off += align256((size_t)C * Dv * 4);
     L.oi = off; off += align256((size_t)C * Dv * 4);
     L.gl = off; off += align256((size_t)Dk * 4);
+    L.vx = off; off += align256((size_t)C * Dv * 4);
     L.bytes = off;
     return L;
 }

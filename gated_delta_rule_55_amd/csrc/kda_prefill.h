@@ -44,7 +44,6 @@ struct StateParams {
     const char *ws;
     size_t pkg_bytes;
     PackageLayout L;
-    const void *v;        // DPLR state pass only: the values [.., H, Dv] of the input
 };
 
 struct BwdStateParams {

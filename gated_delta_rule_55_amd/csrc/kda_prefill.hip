@@ -673,7 +673,7 @@ __device__ __forceinline__ void unpack8(const Vec8<false> &x, float (&o)[8]) {
 // registers so the next chunk's loads are in flight while this one computes.
 // LR2: the DPLR form (kda_dplr.hip), whose state update adds a second
 // low-rank term: the Kt section holds 2 CP tokens, [A-tilde; K-tilde], and the
-// chunk's values V (read from the input) follow U in the contraction.
+// chunk's values V (the package's VX section) follow U in the contraction.
 template <int C, int DK, int DV, bool BF, bool LR2 = false>
 struct StateFrags {
     using F = Cfg<C, DK, DV, BF>;
@@ -686,23 +686,6 @@ struct StateFrags {
     Vec8<BF> kt[SPW][KSC2];
     f32x4 gl[SPW];
     f32x4 vx[LR2 ? RPW : 1];  // LR2: V rows 16 rt + 4 (lane / 16) + r, column 16 ct + lane % 16
-
-    // LR2: this wave's V values of chunk c (zero past the sequence's L tokens)
-    __device__ __forceinline__ void load_v(const StateParams &p, int64_t tok_base, int64_t L, int64_t c, int h,
-                                           int w, int lane, int ct) {
-        using In = typename F::In;
-#pragma unroll
-        for (int rw = 0; rw < RPW; ++rw) {
-            const int rt = w + 4 * rw;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t j = c * C + 16 * rt + 4 * (lane >> 4) + r;
-                const bool ok = rt < F::NT16 && j < L;
-                const int64_t off = ((tok_base + (ok ? j : 0)) * p.H + h) * DV + 16 * ct + (lane & 15);
-                vx[rw][r] = ok ? in_to_f32<BF>(static_cast<const In *>(p.v)[off]) : 0.f;
-            }
-        }
-    }
 
     __device__ __forceinline__ void load(const char *pkg, const PackageLayout &L, int w, int lane,
                                          int ct) {
@@ -719,6 +702,10 @@ struct StateFrags {
                 const size_t off = rt < NT16 ? L.up : L.oi;
                 const int I = rt < NT16 ? rt : rt - NT16;
                 uo[rw] = reinterpret_cast<const f32x4 *>(pkg + off)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane];
+                if constexpr (LR2) {
+                    vx[rw] = rt < NT16 ? reinterpret_cast<const f32x4 *>(pkg + L.vx)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane]
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
         const Op *ktp = reinterpret_cast<const Op *>(pkg + L.kt);
@@ -910,10 +897,7 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
     using Part = std::true_type;
     const int64_t nfull = L / C;  // chunks with C valid tokens
     Frags f0, f1, f2;
-    auto load = [&](Frags &f, int64_t cc) {
-        f.load(pkg_of(cc), p.L, w, lane, ct);
-        if constexpr (LR2) f.load_v(p, tok_base, L, cc, h, w, lane, ct);
-    };
+    auto load = [&](Frags &f, int64_t cc) { f.load(pkg_of(cc), p.L, w, lane, ct); };
     if (nchunks > 0) load(f0, 0);
     if (nchunks > 1) load(f1, 1);
     int64_t c = 0;
