@@ -312,7 +312,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                     workspace, need_ws);
     if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    const Range ro = span(o, bo), rws = span(workspace, need_ws);
+    // at T = 0 the workspace is not used (see below), so it can overlap nothing
+    const Range ro = span(o, bo), rws = span(workspace, T > 0 ? need_ws : 0);
     const Range rfs = span(final_state, final_state ? bs : 0);
     const Range rinit = span(init_state, init_state ? bs : 0);
     for (int i = 0; i < n_in; ++i) {
@@ -345,6 +346,16 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
                              : nullptr;
+    if (T == 0) {
+        // Every sequence is empty (cu[N] = T = 0): only final_state <- init_state
+        // remains.  Run it as a dense batch of N empty sequences so that neither
+        // the varlen plan nor the workspace (which may be NULL here) is touched.
+        a.cu_seqlens = nullptr;
+        a.B = N;
+        a.n_slots = 0;
+        a.workspace = nullptr;
+        a.chunk_offsets = nullptr;
+    }
     a.lr_a = lr_a; a.lr_b = lr_b;
     hipError_t e = gate_mode == 3 ? kda::launch_dplr(a, stream) : kda::launch_prefill(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));

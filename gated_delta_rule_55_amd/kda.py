@@ -91,6 +91,67 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_F32 = (torch.float32,)
+_IN = (torch.bfloat16, torch.float32)
+_BF16 = (torch.bfloat16,)
+
+
+def _validate(specs, devices=True):
+    """Checks every tensor argument before anything is launched.
+
+    specs: (name, tensor, expected shape, allowed dtypes, required) tuples; a
+    shape entry of None matches any size.  The library sizes every buffer from
+    q's dtype and the dimensions it is given and reads dense row-major memory,
+    so a wrong dtype, a non-contiguous view (a head slice of a [B, T, H, D]
+    tensor, for instance), a CPU tensor or a tensor on another device would be
+    read out of bounds or with the wrong stride; each raises KdaError here.
+    Structure (dtype, shape, layout) is checked first, then (unless devices is
+    False) that every tensor sits on the CUDA device of the first one.
+    """
+    present = []
+    for name, t, shape, dtypes, required in specs:
+        if t is None:
+            if required:
+                raise KdaError(f"{name} is required")
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise KdaError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dtype not in dtypes:
+            raise KdaError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+        if shape is not None:
+            if t.dim() != len(shape) or any(e is not None and int(n) != int(e) for n, e in zip(t.shape, shape)):
+                want = "[" + ", ".join("*" if e is None else str(int(e)) for e in shape) + "]"
+                raise KdaError(f"{name} has shape {list(t.shape)}; expected {want}")
+        if not t.is_contiguous():
+            raise KdaError(f"{name} is not contiguous (the kernels read dense row-major memory; "
+                           f"copy it with .contiguous() first)")
+        present.append((name, t))
+    if not devices:
+        return
+    ref_name, ref = present[0]
+    if ref.device.type != "cuda":
+        raise KdaError(f"{ref_name} is on {ref.device}; the library runs on a CUDA (HIP) device")
+    for name, t in present:
+        if t.device != ref.device:
+            raise KdaError(f"{name} is on {t.device}, {ref_name} on {ref.device}: all tensors must share one device")
+
+
+def _seq_count(B, cu_seqlens):
+    """(n_seqs for the ABI, N) with a 1-D int32 cu_seqlens of N + 1 entries."""
+    if cu_seqlens is None:
+        return 0, B
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise KdaError("cu_seqlens must be a 1-D tensor of N + 1 >= 2 offsets")
+    if cu_seqlens.dtype != torch.int32:
+        raise KdaError(f"cu_seqlens has dtype {cu_seqlens.dtype}; expected torch.int32")
+    n = cu_seqlens.numel() - 1
+    return n, n
+
+
+def _workspace_spec(workspace):
+    return ("workspace", workspace, (None,), (torch.uint8,), False)
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -115,16 +176,24 @@ def gdn_chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     """Gated DeltaNet chunked prefill: as ``chunk_fwd`` with log_alpha [B,T,H] fp32
     (one scalar gate per token and head)."""
     return _chunk_fwd(load().gdn_chunk_fwd, q, k, v, log_alpha, beta, init_state, cu_seqlens,
-                      chunk_size, out, final_state, output_final_state, workspace, stream)
+                      chunk_size, out, final_state, output_final_state, workspace, stream, scalar_gate=True)
 
 
 def _chunk_fwd(fn, q, k, v, log_alpha, beta, init_state, cu_seqlens, chunk_size, out,
-               final_state, output_final_state, workspace, stream):
-    lib = load()
+               final_state, output_final_state, workspace, stream, scalar_gate=False):
+    _validate([("q", q, (None,) * 4, _IN, True)], devices=False)  # q fixes the sizes below
     B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    N = B if cu_seqlens is None else n_seqs
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 4 else None
+    n_seqs, N = _seq_count(B, cu_seqlens)
+    _validate([("q", q, (B, T, H, Dk), _IN, True), ("k", k, (B, T, H, Dk), (q.dtype,), True),
+               ("v", v, (B, T, H, Dv), (q.dtype,), True),
+               ("log_alpha", log_alpha, (B, T, H) if scalar_gate else (B, T, H, Dk), _F32, True),
+               ("beta", beta, (B, T, H), _F32, True),
+               ("init_state", init_state, (N, H, Dk, Dv), _F32, False),
+               ("cu_seqlens", cu_seqlens, (N + 1,), (torch.int32,), False),
+               ("out", out, (B, T, H, Dv), _F32, False),
+               ("final_state", final_state, (N, H, Dk, Dv), _F32, False), _workspace_spec(workspace)])
+    lib = load()
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
@@ -153,10 +222,18 @@ def dplr_chunk_fwd(q, k, v, a, b, log_alpha, init_state=None, cu_seqlens=None, c
     S_t = (Diag(exp(log_alpha_t)) + a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
     q, k, v, a, b [B,T,H,D] (one dtype); log_alpha [B,T,H,D] fp32; the rest as
     ``chunk_fwd``.  Returns (o [B,T,H,D] fp32, final_state [N,H,D,D] or None)."""
-    lib = load()
+    _validate([("q", q, (None,) * 4, _IN, True)], devices=False)
     B, T, H, D = q.shape
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    N = B if cu_seqlens is None else n_seqs
+    n_seqs, N = _seq_count(B, cu_seqlens)
+    x4 = (B, T, H, D)
+    _validate([("q", q, x4, _IN, True), ("k", k, x4, (q.dtype,), True), ("v", v, x4, (q.dtype,), True),
+               ("a", a, x4, (q.dtype,), True), ("b", b, x4, (q.dtype,), True),
+               ("log_alpha", log_alpha, x4, _F32, True),
+               ("init_state", init_state, (N, H, D, D), _F32, False),
+               ("cu_seqlens", cu_seqlens, (N + 1,), (torch.int32,), False),
+               ("out", out, x4, _F32, False), ("final_state", final_state, (N, H, D, D), _F32, False),
+               _workspace_spec(workspace)])
+    lib = load()
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
@@ -185,11 +262,25 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_o, init_state=None, cu_seqlens=None, d
     d_final_state [N,H,Dk,Dv]), returns (dq, dk, dv, dlog_alpha, dbeta,
     d_init_state) in fp32, d_init_state None unless requested.  Dk must equal Dv.
     ``grads`` may supply the six output tensors."""
-    lib = load()
+    _validate([("q", q, (None,) * 4, _IN, True)], devices=False)
     B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    N = B if cu_seqlens is None else n_seqs
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 4 else None
+    n_seqs, N = _seq_count(B, cu_seqlens)
+    specs = [("q", q, (B, T, H, Dk), _IN, True), ("k", k, (B, T, H, Dk), (q.dtype,), True),
+             ("v", v, (B, T, H, Dv), (q.dtype,), True), ("log_alpha", log_alpha, (B, T, H, Dk), _F32, True),
+             ("beta", beta, (B, T, H), _F32, True), ("d_o", d_o, (B, T, H, Dv), _F32, True),
+             ("init_state", init_state, (N, H, Dk, Dv), _F32, False),
+             ("cu_seqlens", cu_seqlens, (N + 1,), (torch.int32,), False),
+             ("d_final_state", d_final_state, (N, H, Dk, Dv), _F32, False), _workspace_spec(workspace)]
+    if grads is not None:
+        if len(grads) != 6:
+            raise KdaError("grads must hold (dq, dk, dv, dlog_alpha, dbeta, d_init_state)")
+        for name, t, shape in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "d_init_state"), grads,
+                                  ((B, T, H, Dk), (B, T, H, Dk), (B, T, H, Dv), (B, T, H, Dk), (B, T, H),
+                                   (N, H, Dk, Dv))):
+            specs.append((name, t, shape, _F32, name != "d_init_state"))
+    _validate(specs)
+    lib = load()
     dev = q.device
     if grads is None:
         f32 = dict(dtype=torch.float32, device=dev)
@@ -218,14 +309,20 @@ def decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
 
 def gdn_decode_step(q, k, v, log_alpha, beta, state, out=None, stream=None):
     """One Gated DeltaNet step per (n, h): as ``decode_step`` with log_alpha [N,H]."""
-    return _decode(load().gdn_decode_step, q, k, v, log_alpha, beta, state, out, stream)
+    return _decode(load().gdn_decode_step, q, k, v, log_alpha, beta, state, out, stream, scalar_gate=True)
 
 
 def dplr_decode_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):
     """One step of the general DPLR recurrence per (n, h): q, k, v, a, b [N,H,D]
     (one dtype), log_alpha [N,H,D] fp32; state [N,H,D,D] fp32 updated in place.
     Returns o [N,H,D] fp32."""
+    _validate([("q", q, (None,) * 3, _IN, True)], devices=False)
     N, H, D = q.shape
+    x3 = (N, H, D)
+    _validate([("q", q, x3, _IN, True), ("k", k, x3, (q.dtype,), True), ("v", v, x3, (q.dtype,), True),
+               ("a", a, x3, (q.dtype,), True), ("b", b, x3, (q.dtype,), True),
+               ("log_alpha", log_alpha, x3, _F32, True), ("state", state, (N, H, D, D), _F32, True),
+               ("out", out, x3, _F32, False)])
     if out is None:
         out = torch.empty((N, H, D), dtype=torch.float32, device=q.device)
     _check(load().kda_dplr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha),
@@ -233,9 +330,15 @@ def dplr_decode_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):
     return out
 
 
-def _decode(fn, q, k, v, log_alpha, beta, state, out, stream):
+def _decode(fn, q, k, v, log_alpha, beta, state, out, stream, scalar_gate=False):
+    _validate([("q", q, (None,) * 3, _IN, True)], devices=False)
     N, H, Dk = q.shape
-    Dv = v.shape[-1]
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 3 else None
+    _validate([("q", q, (N, H, Dk), _IN, True), ("k", k, (N, H, Dk), (q.dtype,), True),
+               ("v", v, (N, H, Dv), (q.dtype,), True),
+               ("log_alpha", log_alpha, (N, H) if scalar_gate else (N, H, Dk), _F32, True),
+               ("beta", beta, (N, H), _F32, True), ("state", state, (N, H, Dk, Dv), _F32, True),
+               ("out", out, (N, H, Dv), _F32, False)])
     if out is None:
         out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
@@ -250,11 +353,19 @@ def layer_chunk_fwd(q, k, v, x_alpha, x_beta, out_gate, norm_weight, l2_eps=1e-6
     beta = sigmoid(x_beta), the recurrence, then RMSNorm(o) * norm_weight *
     sigmoid(out_gate).  q, k, x_alpha [B,T,H,128], v, out_gate [B,T,H,128],
     x_beta [B,T,H], all bf16; norm_weight [128] fp32.  Returns (out fp32, final_state)."""
-    lib = load()
+    _validate([("q", q, (None,) * 4, _BF16, True)], devices=False)
     B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    N = B if cu_seqlens is None else n_seqs
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 4 else None
+    n_seqs, N = _seq_count(B, cu_seqlens)
+    _validate([("q", q, (B, T, H, Dk), _BF16, True), ("k", k, (B, T, H, Dk), _BF16, True),
+               ("v", v, (B, T, H, Dv), _BF16, True), ("x_alpha", x_alpha, (B, T, H, Dk), _BF16, True),
+               ("x_beta", x_beta, (B, T, H), _BF16, True), ("out_gate", out_gate, (B, T, H, Dv), _BF16, True),
+               ("norm_weight", norm_weight, (Dv,), _F32, True),
+               ("init_state", init_state, (N, H, Dk, Dv), _F32, False),
+               ("cu_seqlens", cu_seqlens, (N + 1,), (torch.int32,), False),
+               ("out", out, (B, T, H, Dv), _F32, False),
+               ("final_state", final_state, (N, H, Dk, Dv), _F32, False), _workspace_spec(workspace)])
+    lib = load()
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
@@ -275,8 +386,14 @@ def layer_decode_step(q, k, v, x_alpha, x_beta, out_gate, norm_weight, state, l2
                       norm_eps=1e-5, out=None, stream=None):
     """One KDA-layer token per (n, h); bf16 q, k, x_alpha [N,H,Dk], v, out_gate
     [N,H,Dv], x_beta [N,H]; state [N,H,Dk,Dv] fp32 updated in place.  Returns out fp32."""
+    _validate([("q", q, (None,) * 3, _BF16, True)], devices=False)
     N, H, Dk = q.shape
-    Dv = v.shape[-1]
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 3 else None
+    _validate([("q", q, (N, H, Dk), _BF16, True), ("k", k, (N, H, Dk), _BF16, True),
+               ("v", v, (N, H, Dv), _BF16, True), ("x_alpha", x_alpha, (N, H, Dk), _BF16, True),
+               ("x_beta", x_beta, (N, H), _BF16, True), ("out_gate", out_gate, (N, H, Dv), _BF16, True),
+               ("norm_weight", norm_weight, (Dv,), _F32, True), ("state", state, (N, H, Dk, Dv), _F32, True),
+               ("out", out, (N, H, Dv), _F32, False)])
     if out is None:
         out = torch.empty((N, H, Dv), dtype=torch.float32, device=q.device)
     _check(load().kda_layer_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(x_alpha), _ptr(x_beta),

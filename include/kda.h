@@ -19,9 +19,11 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are device pointers (hipMalloc'd memory of the current device)
- *     unless stated otherwise, dense and row-major, 16-byte aligned except
- *     beta and cu_seqlens (4-byte aligned), so a slice of a larger tensor
- *     along tokens or heads may be passed directly.
+ *     unless stated otherwise, 16-byte aligned except beta and cu_seqlens
+ *     (4-byte aligned).  Every tensor is dense and row-major in the layout
+ *     below: a range of tokens of a B = 1 tensor is dense and may be passed
+ *     directly; a subset of heads is not (its rows lie H * D elements apart)
+ *     and must be copied into a dense tensor first.
  *   - Layouts: q, k, log_alpha [B, T, H, Dk]; v, o [B, T, H, Dv];
  *     beta [B, T, H]; states [N, H, Dk, Dv] (row c of a head's state is key
  *     channel c).  bf16 inputs are raw IEEE bfloat16 bit patterns.
@@ -104,7 +106,9 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
  *   o           [B, T, H, Dv] fp32 output; must not overlap any input
  *   final_state [N, H, Dk, Dv] fp32, nullable; may alias init_state
  *   workspace   device scratch of at least kda_chunk_fwd_workspace_size()
- *               bytes (256-byte aligned); contents on entry are ignored
+ *               bytes (256-byte aligned); contents on entry are ignored.  At
+ *               T = 0 (every sequence empty) it is not used and may be NULL:
+ *               the call then only writes final_state = init_state (or zeros)
  *   stream      HIP stream the kernels are enqueued on
  *
  * cu_seqlens must satisfy cu[0] = 0, cu[N] = T and be non-decreasing (the

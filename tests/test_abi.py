@@ -345,3 +345,22 @@ def test_dplr_decode_rejects(lib, kw, code, msg):
                                   p(a["state"]), a["N"], a["H"], a["D"], a["dtype"], p(a["o"]), a["stream"])
     assert rc == code
     assert msg in lib.kda_last_error()
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "gdn_chunk_fwd", "kda_dplr_chunk_fwd"])
+def test_empty_varlen_needs_no_workspace(lib, fn):
+    """T = 0 with cu_seqlens: every sequence is empty, so the call only copies
+    init_state to final_state and never touches the workspace (which may be
+    NULL or small).  Validation passes; with no GPU here the launch itself then
+    reports KDA_ERR_HIP, never KDA_ERR_WORKSPACE or an argument error."""
+    kw = dict(T=0, cu_seqlens=FAKE + 0x8000000, n_seqs=3, final_state=FAKE + 0x9000000, ws=None, ws_bytes=0)
+    rc = _dplr(lib, **kw) if fn == "kda_dplr_chunk_fwd" else _chunk(lib, fn, **kw)
+    assert rc in (OK, 4), lib.kda_last_error()
+    # a small workspace placed right below final_state is not taken to overlap it at T = 0
+    kw.update(ws=FAKE + 0x9000000 - 256, ws_bytes=256)
+    rc = _dplr(lib, **kw) if fn == "kda_dplr_chunk_fwd" else _chunk(lib, fn, **kw)
+    assert rc in (OK, 4), lib.kda_last_error()
+    # with tokens the workspace is required again
+    kw.update(T=64, ws=None, ws_bytes=0)
+    rc = _dplr(lib, **kw) if fn == "kda_dplr_chunk_fwd" else _chunk(lib, fn, **kw)
+    assert rc == WORKSPACE

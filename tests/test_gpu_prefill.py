@@ -213,6 +213,37 @@ def test_zero_length_and_empty():
     assert torch.equal(fs, inp["init_state"])
 
 
+def test_empty_varlen_without_workspace():
+    """T = 0 with cu_seqlens (three empty sequences) and a NULL workspace, through
+    the C ABI: each final state is its initial state, nothing else is written."""
+    import ctypes
+    lib = kda.load()
+    H, D, N = 2, 128, 3
+    q = torch.zeros((1, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    la = torch.zeros((1, 0, H, D), device="cuda")
+    be = torch.zeros((1, 0, H), device="cuda")
+    o = torch.zeros((1, 0, H, D), device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(21)
+    s0 = torch.randn((N, H, D, D), device="cuda", generator=g)
+    fs = torch.full((N, H, D, D), float("nan"), device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    for fn in (lib.kda_chunk_fwd, lib.gdn_chunk_fwd):
+        fs.fill_(float("nan"))
+        gate = la if fn is lib.kda_chunk_fwd else be
+        rc = fn(p(q), p(q), p(q), p(gate), p(be), p(s0), p(cu), 1, 0, H, D, D, N, kda.KDA_BF16, 64,
+                p(o), p(fs), None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, lib.kda_last_error()
+        torch.cuda.synchronize()
+        assert torch.equal(fs, s0)
+    fs.fill_(float("nan"))
+    rc = lib.kda_dplr_chunk_fwd(p(q), p(q), p(q), p(q), p(q), p(la), p(s0), p(cu), 1, 0, H, D, N, kda.KDA_BF16,
+                                64, p(o), p(fs), None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, lib.kda_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(fs, s0)
+
+
 @pytest.mark.parametrize("D,dtype", [(128, "bf16"), (32, "f32")])
 def test_dense_batch_with_resets(D, dtype):
     """B = 3 independent sequences in one dense call (partial last chunk, random
