@@ -24,6 +24,12 @@ page contrasts KDA with (KDA ties both low-rank vectors to the key), read with
 free per-token vectors a_t, b_t and an unscaled write:
 ``S_t = (Diag(alpha_t) + a_t b_t^T) S_{t-1} + k_t v_t^T``, ``o_t = S_t^T q_t``.
 
+``forward_native`` and ``decode_step_native`` run the same KDA token update on
+inputs in the types the GPU path receives (bf16 or fp32 q, k, v; fp32 gates),
+for a range of heads, widening each token's values to fp64 in C: the check of
+a 1M-token, 32-head output then needs no fp64 copy of whole inputs, and the
+decode step is threaded over its states.
+
 ``backward`` differentiates the KDA token loop in reverse mode, one token at
 a time (the gradients with respect to q, k, v, log_alpha, beta and the initial
 state, given those of o and of the final state).
@@ -77,6 +83,12 @@ def _load():
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
             i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
         lib.kda_oracle_forward.restype = ctypes.c_int
+        vp = ctypes.c_void_p
+        fp32p = ctypes.POINTER(ctypes.c_float)
+        lib.kda_oracle_forward_native.argtypes = [
+            vp, vp, vp, ctypes.c_int, fp32p, fp32p, dp, ctypes.POINTER(ctypes.c_int32),
+            i64, i64, i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
+        lib.kda_oracle_forward_native.restype = ctypes.c_int
         lib.gdn_oracle_forward.argtypes = lib.kda_oracle_forward.argtypes
         lib.gdn_oracle_forward.restype = ctypes.c_int
         lib.dplr_oracle_forward.argtypes = [
@@ -119,6 +131,75 @@ def forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_thread
     Returns (o [B, T, H, Dv], final_state [N, H, Dk, Dv]) as fp64 numpy arrays.
     """
     return _forward(False, q, k, v, log_alpha, beta, init_state, cu_seqlens, n_threads)
+
+
+def _host_native(x, want):
+    """A contiguous host copy of a torch tensor in one of the dtypes ``want``."""
+    import torch
+    x = x.detach()
+    if x.dtype not in want:
+        raise TypeError(f"dtype {x.dtype} is not one of {want}")
+    return x.to("cpu").contiguous()
+
+
+def forward_native(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, heads=None,
+                   n_threads=None):
+    """``forward`` for the heads ``heads = (h_lo, h_hi)`` (default: all) of
+    inputs in the types the GPU path receives: q, k, v torch bfloat16 or
+    float32, log_alpha and beta float32 (CPU or CUDA tensors; copied to host
+    memory as they are).  Each token's values are widened exactly to fp64 in
+    C, so the result equals ``forward`` on the widened arrays, without the
+    fp64 copies of whole inputs that a 1M-token check would need.
+
+    init_state: [N, h_hi - h_lo, Dk, Dv] (any float dtype; widened) or None.
+    Returns (o [B, T, h_hi - h_lo, Dv], final_state [N, h_hi - h_lo, Dk, Dv]), fp64.
+    """
+    import torch
+    qh, kh, vh = (_host_native(x, (torch.bfloat16, torch.float32)) for x in (q, k, v))
+    if not (qh.dtype == kh.dtype == vh.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    lah, beh = (_host_native(x, (torch.float32,)) for x in (log_alpha, beta))
+    B, T, H, Dk = qh.shape
+    Dv = vh.shape[3]
+    assert kh.shape == qh.shape and lah.shape == qh.shape
+    assert vh.shape == (B, T, H, Dv) and beh.shape == (B, T, H)
+    h_lo, h_hi = (0, H) if heads is None else (int(heads[0]), int(heads[1]))
+    Hs = h_hi - h_lo
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens), dtype=np.int32)
+        N = cu.size - 1
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        cu, N, cu_p = None, B, None
+    s0 = None if init_state is None else _f64(init_state)
+    if s0 is not None:
+        assert s0.shape == (N, Hs, Dk, Dv)
+    o = np.zeros((B, T, Hs, Dv), dtype=np.float64)
+    fs = np.zeros((N, Hs, Dk, Dv), dtype=np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    fptr = lambda t: ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+    rc = _load().kda_oracle_forward_native(
+        ctypes.c_void_p(qh.data_ptr()), ctypes.c_void_p(kh.data_ptr()), ctypes.c_void_p(vh.data_ptr()),
+        1 if qh.dtype == torch.bfloat16 else 0, fptr(lah), fptr(beh), _ptr(s0), cu_p,
+        B, T, H, Dk, Dv, N, h_lo, h_hi, _ptr(o), _ptr(fs), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_forward_native failed with code {rc}")
+    return o, fs
+
+
+def decode_step_native(q, k, v, log_alpha, beta, state, n_threads=None):
+    """``decode_step`` on native-typed inputs (q, k, v [N, H, Dk|Dv] bfloat16
+    or float32, log_alpha [N, H, Dk] and beta [N, H] float32), threaded over
+    the N * H states: one token of ``forward_native`` per state, which is the
+    same token update.  state: [N, H, Dk, Dv] (fp64 numpy, or any float tensor).
+    Returns (o [N, H, Dv], new_state), fp64."""
+    N, H, Dk = q.shape
+    r = lambda x: x.reshape(N, 1, *x.shape[1:])
+    o, st = forward_native(r(q), r(k), r(v), r(log_alpha), beta.reshape(N, 1, H), state,
+                           n_threads=n_threads)
+    return o[:, 0], st
 
 
 def gdn_forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, n_threads=None):

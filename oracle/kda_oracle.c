@@ -85,9 +85,30 @@ typedef struct {
     int64_t B, T, H, Dk, Dv, N;
     int scalar_gate;        /* 0: KDA, log_alpha [.., Dk]; 1: GDN, log_alpha [..]; 2: DPLR */
     double *o, *final_state;
+    /* native-typed inputs (kda_oracle_forward_native only): q, k, v as bf16
+       bit patterns or fp32, log_alpha and beta fp32, read for the heads
+       [h_lo, h_lo + Hs) of H; o, init_state and final_state then hold those
+       Hs heads only ([B, T, Hs, Dv] and [N, Hs, Dk, Dv]). */
+    const void *nq, *nk, *nv;
+    const float *nla, *nbeta;
+    int native, native_bf16;
+    int64_t h_lo, Hs;
     int64_t next_unit;      /* work counter, guarded by lock */
     pthread_mutex_t lock;
 } oracle_job;
+
+/* Element i of a native-typed array, widened exactly to fp64 (a bf16 bit
+ * pattern is the high half of an fp32 word). */
+static double widen(const void *base, int bf16, size_t i)
+{
+    if (bf16) {
+        const uint32_t w = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &w, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[i];
+}
 
 /* One token of the recurrence on one head's state S [Dk x Dv] (fp64).
  * p is caller scratch of length Dv.  Writes o_t (length Dv). */
@@ -166,6 +187,36 @@ static void dplr_token_update(double *S, int64_t Dk, int64_t Dv,
     }
 }
 
+/* The token loop of one (sequence n, head h) unit on native-typed inputs:
+ * each token's q, k, v, log_alpha and beta are widened to fp64 (exactly) into
+ * the caller's buffers x (2 Dk + Dv + Dk), then token_update runs as in
+ * run_unit below. */
+static void run_unit_native(const oracle_job *J, int64_t n, int64_t h, double *S, double *p, double *x)
+{
+    const int64_t Dk = J->Dk, Dv = J->Dv, H = J->H, hs = h - J->h_lo;
+    double *qb = x, *kb = qb + Dk, *vb = kb + Dk, *lab = vb + Dv;
+    int64_t b, t0, t1;
+    if (J->cu_seqlens) { b = 0; t0 = J->cu_seqlens[n]; t1 = J->cu_seqlens[n + 1]; }
+    else               { b = n; t0 = 0;               t1 = J->T; }
+
+    const size_t sidx = (size_t)(n * J->Hs + hs) * (size_t)(Dk * Dv);
+    if (J->init_state) memcpy(S, J->init_state + sidx, sizeof(double) * (size_t)(Dk * Dv));
+    else               memset(S, 0, sizeof(double) * (size_t)(Dk * Dv));
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const size_t row = (size_t)((b * J->T + t) * H + h);
+        for (int64_t c = 0; c < Dk; ++c) {
+            qb[c] = widen(J->nq, J->native_bf16, row * (size_t)Dk + (size_t)c);
+            kb[c] = widen(J->nk, J->native_bf16, row * (size_t)Dk + (size_t)c);
+            lab[c] = (double)J->nla[row * (size_t)Dk + (size_t)c];
+        }
+        for (int64_t j = 0; j < Dv; ++j) vb[j] = widen(J->nv, J->native_bf16, row * (size_t)Dv + (size_t)j);
+        const size_t orow = (size_t)((b * J->T + t) * J->Hs + hs);
+        token_update(S, Dk, Dv, qb, kb, vb, lab, (double)J->nbeta[row], p, J->o + orow * (size_t)Dv);
+    }
+    if (J->final_state) memcpy(J->final_state + sidx, S, sizeof(double) * (size_t)(Dk * Dv));
+}
+
 /* Runs the whole token loop of one (sequence n, head h) unit. */
 static void run_unit(const oracle_job *J, int64_t n, int64_t h, double *S, double *p)
 {
@@ -205,18 +256,47 @@ static void *worker(void *arg)
     oracle_job *J = (oracle_job *)arg;
     double *S = (double *)malloc(sizeof(double) * (size_t)(J->Dk * J->Dv));
     double *p = (double *)malloc(sizeof(double) * (size_t)J->Dv);
-    if (!S || !p) { free(S); free(p); return (void *)1; }
-    const int64_t units = J->N * J->H;
+    double *x = (double *)malloc(sizeof(double) * (size_t)(3 * J->Dk + J->Dv));
+    if (!S || !p || !x) { free(S); free(p); free(x); return (void *)1; }
+    const int64_t hs = J->native ? J->Hs : J->H;
+    const int64_t units = J->N * hs;
     for (;;) {
         pthread_mutex_lock(&J->lock);
         int64_t u = J->next_unit++;
         pthread_mutex_unlock(&J->lock);
         if (u >= units) break;
-        run_unit(J, u / J->H, u % J->H, S, p);
+        if (J->native) run_unit_native(J, u / hs, J->h_lo + u % hs, S, p, x);
+        else           run_unit(J, u / hs, u % hs, S, p);
     }
     free(S);
     free(p);
+    free(x);
     return NULL;
+}
+
+/* Spreads the job's (sequence, head) units over n_threads POSIX threads. */
+static int run_job(oracle_job *J, int n_threads)
+{
+    const int64_t units = J->N * (J->native ? J->Hs : J->H);
+    pthread_mutex_init(&J->lock, NULL);
+    if (n_threads < 1) n_threads = 1;
+    if ((int64_t)n_threads > units) n_threads = (int)(units > 0 ? units : 1);
+    int rc = 0;
+    pthread_t *tid = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    int started = 0;
+    if (!tid) rc = -2;
+    for (int i = 0; i < n_threads && rc == 0; ++i) {
+        if (pthread_create(&tid[i], NULL, worker, J) != 0) rc = -2;
+        else ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(tid[i], &ret);
+        if (ret) rc = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J->lock);
+    return rc;
 }
 
 /*
@@ -255,25 +335,7 @@ static int forward_impl(const double *q, const double *k, const double *v,
     } else {
         J.N = B;
     }
-    pthread_mutex_init(&J.lock, NULL);
-    if (n_threads < 1) n_threads = 1;
-    if ((int64_t)n_threads > J.N * H) n_threads = (int)(J.N * H);
-    int rc = 0;
-    pthread_t *tid = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
-    int started = 0;
-    if (!tid) rc = -2;
-    for (int i = 0; i < n_threads && rc == 0; ++i) {
-        if (pthread_create(&tid[i], NULL, worker, &J) != 0) rc = -2;
-        else ++started;
-    }
-    for (int i = 0; i < started; ++i) {
-        void *ret = NULL;
-        pthread_join(tid[i], &ret);
-        if (ret) rc = -2;
-    }
-    free(tid);
-    pthread_mutex_destroy(&J.lock);
-    return rc;
+    return run_job(&J, n_threads);
 }
 
 int kda_oracle_forward(const double *q, const double *k, const double *v,
@@ -284,6 +346,48 @@ int kda_oracle_forward(const double *q, const double *k, const double *v,
 {
     return forward_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv,
                         n_seqs, o, final_state, n_threads, 0, NULL, NULL);
+}
+
+/*
+ * kda_oracle_forward_native: kda_oracle_forward on inputs in the types the
+ * GPU path receives, for the heads [h_lo, h_hi) of H only.  q, k
+ * [B, T, H, Dk] and v [B, T, H, Dv] are bf16 bit patterns (in_bf16 = 1) or
+ * fp32 (in_bf16 = 0); log_alpha [B, T, H, Dk] and beta [B, T, H] are fp32.
+ * Each token's values are widened exactly to fp64 and the same token_update
+ * runs, so the result equals kda_oracle_forward on the widened arrays.
+ * init_state (nullable), o and final_state (nullable) are fp64 and hold the
+ * selected heads only: [N, h_hi - h_lo, Dk, Dv] and [B, T, h_hi - h_lo, Dv].
+ * cu_seqlens, threads and return codes as in kda_oracle_forward.
+ */
+int kda_oracle_forward_native(const void *q, const void *k, const void *v, int in_bf16,
+                              const float *log_alpha, const float *beta,
+                              const double *init_state, const int32_t *cu_seqlens,
+                              int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                              int64_t n_seqs, int64_t h_lo, int64_t h_hi,
+                              double *o, double *final_state, int n_threads)
+{
+    if (!q || !k || !v || !log_alpha || !beta || !o) return -1;
+    if (B < 1 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return -1;
+    if (h_lo < 0 || h_hi > H || h_lo >= h_hi) return -1;
+    oracle_job J;
+    memset(&J, 0, sizeof(J));
+    J.native = 1;
+    J.native_bf16 = in_bf16 ? 1 : 0;
+    J.nq = q; J.nk = k; J.nv = v; J.nla = log_alpha; J.nbeta = beta;
+    J.h_lo = h_lo; J.Hs = h_hi - h_lo;
+    J.init_state = init_state; J.cu_seqlens = cu_seqlens;
+    J.B = B; J.T = T; J.H = H; J.Dk = Dk; J.Dv = Dv;
+    J.o = o; J.final_state = final_state;
+    if (cu_seqlens) {
+        if (B != 1 || n_seqs < 1) return -1;
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != T) return -1;
+        for (int64_t n = 0; n < n_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+        J.N = n_seqs;
+    } else {
+        J.N = B;
+    }
+    return run_job(&J, n_threads);
 }
 
 /*

@@ -311,3 +311,32 @@ def test_dplr_identity():
     M2 = np.diag(a) @ (np.eye(Dk) - b * np.outer(kk, kk))
     assert np.max(np.abs(M1 - M2)) > 1e-3
     np.testing.assert_allclose(M1, np.diag(a) - np.outer(b * kk, a * kk), rtol=0, atol=1e-15)
+
+
+def test_native_entry_equals_fp64_entry_bitwise():
+    """forward_native (native-typed inputs, a range of heads, widened per token
+    in C) runs the same token update as forward on the widened arrays: equal
+    bit for bit, dense and varlen, with and without an initial state; and
+    decode_step_native equals decode_step."""
+    import torch
+    g = torch.Generator().manual_seed(5)
+    B, T, H, Dk, Dv = 1, 37, 5, 8, 6
+    for dt in (torch.bfloat16, torch.float32):
+        q = torch.randn(B, T, H, Dk, generator=g).to(dt)
+        k = (torch.randn(B, T, H, Dk, generator=g) / 3).to(dt)
+        v = torch.randn(B, T, H, Dv, generator=g).to(dt)
+        la = -torch.nn.functional.softplus(torch.randn(B, T, H, Dk, generator=g))
+        la[0, 9] = float("-inf")
+        be = torch.sigmoid(torch.randn(B, T, H, generator=g))
+        s0 = 0.1 * torch.randn(3, H, Dk, Dv, generator=g, dtype=torch.float64)
+        cu = np.array([0, 10, 10, T], dtype=np.int32)
+        o, fs = oracle.forward(q, k, v, la, be, s0, cu, n_threads=3)
+        on, fn = oracle.forward_native(q, k, v, la, be, s0[:, 1:4], cu, heads=(1, 4), n_threads=2)
+        assert np.array_equal(on, o[:, :, 1:4]) and np.array_equal(fn, fs[:, 1:4])
+        o, fs = oracle.forward(q, k, v, la, be)
+        on, fn = oracle.forward_native(q, k, v, la, be)
+        assert np.array_equal(on, o) and np.array_equal(fn, fs)
+        st = 0.1 * np.random.default_rng(1).standard_normal((T, H, Dk, Dv))
+        od, sd = oracle.decode_step(q[0], k[0], v[0], la[0], be[0], st)
+        odn, sdn = oracle.decode_step_native(q[0], k[0], v[0], la[0], be[0], st, n_threads=4)
+        assert np.array_equal(od, odn) and np.array_equal(sd, sdn)
