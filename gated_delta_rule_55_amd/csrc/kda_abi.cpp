@@ -230,7 +230,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                                  int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                                  kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                                  void *workspace, size_t ws_bytes, hipStream_t stream, int gate_mode,
-                                 const LayerIn *L, const void *lr_a = nullptr, const void *lr_b = nullptr) {
+                                 const LayerIn *L, const void *lr_a = nullptr, const void *lr_b = nullptr,
+                                 bool static_ws = false) {
     g_err[0] = '\0';
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d is not KDA_BF16 or KDA_F32", (int)in_dtype);
@@ -307,13 +308,26 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     int64_t slots = 0;
     if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots, gate_mode == 3))
         return fail(KDA_ERR_INVALID_ARG, "workspace size overflows size_t");
-    if (T > 0 && (!workspace || ws_bytes < need_ws))
-        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu needed", ws_bytes,
-                    workspace, need_ws);
-    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
-        return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    // at T = 0 the workspace is not used (see below), so it can overlap nothing
-    const Range ro = span(o, bo), rws = span(workspace, T > 0 ? need_ws : 0);
+    if (static_ws) {
+        // the library's own device array stands in for the workspace; it is
+        // looked up only once every argument has passed validation
+        if (need_ws > kda::kNoallocScratchBytes)
+            return fail(KDA_ERR_WORKSPACE,
+                        "these sizes need %zu bytes of workspace; the static scratch of "
+                        "kda_chunk_fwd_noalloc holds %zu (use kda_chunk_fwd with a caller workspace)",
+                        need_ws, kda::kNoallocScratchBytes);
+        workspace = nullptr;
+        ws_bytes = 0;
+    } else {
+        if (T > 0 && (!workspace || ws_bytes < need_ws))
+            return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu needed", ws_bytes,
+                        workspace, need_ws);
+        if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+            return fail(KDA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    }
+    // at T = 0 the workspace is not used (see below), so it can overlap nothing;
+    // neither can the static scratch, a buffer of the library's own
+    const Range ro = span(o, bo), rws = span(workspace, T > 0 && !static_ws ? need_ws : 0);
     const Range rfs = span(final_state, final_state ? bs : 0);
     const Range rinit = span(init_state, init_state ? bs : 0);
     for (int i = 0; i < n_in; ++i) {
@@ -328,6 +342,12 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         return fail(KDA_ERR_INVALID_ARG, "final_state partially overlaps init_state");
     if (overlap(ro, rws) || overlap(ro, rfs) || overlap(rws, rfs))
         return fail(KDA_ERR_INVALID_ARG, "o, final_state and workspace must not overlap");
+    if (static_ws && T > 0) {
+        const hipError_t e = kda::noalloc_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(KDA_ERR_HIP, "device address of the static scratch: %s", hipGetErrorString(e));
+        ws_bytes = kda::kNoallocScratchBytes;
+    }
 
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
@@ -370,6 +390,18 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
                           in_dtype, chunk_size, o, final_state, workspace, ws_bytes, stream, 0, nullptr);
 }
+
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                                 const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                                 int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                                 kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                                 hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, init_state, cu_seqlens, B, T, H, Dk, Dv, n_seqs,
+                          in_dtype, chunk_size, o, final_state, nullptr, 0, stream, 0, nullptr, nullptr,
+                          nullptr, true);
+}
+
+size_t kda_chunk_fwd_noalloc_max_workspace(void) { return kda::kNoallocScratchBytes; }
 
 size_t kda_dplr_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t D, int32_t n_seqs,
                                          kda_dtype in_dtype, int32_t chunk_size) {

@@ -141,6 +141,14 @@ constexpr int kBwdScratchMats = 10;    // fp32 [C][D] scratch matrices per workg
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
 
+// kda_chunk_fwd_noalloc takes its workspace from a static device array of
+// this many bytes (one copy per device, held until the process ends).
+constexpr size_t kNoallocScratchBytes = size_t(256) << 20;
+
+// Device address of the current device's copy of that array, looked up with
+// hipGetSymbolAddress on the first call on each device and kept.
+hipError_t noalloc_scratch(void **ptr);
+
 // Chunk size the kernels use for a requested one (the fp32 path at d = 128 is
 // limited to 32 tokens by LDS capacity).  Results do not depend on it beyond
 // rounding.

@@ -38,6 +38,11 @@ def load():
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32,
                                   ctypes.c_int, i32, fp, fp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32,
+                                          ctypes.c_int, i32, fp, fp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc_max_workspace.argtypes = []
+    lib.kda_chunk_fwd_noalloc_max_workspace.restype = sz
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, fp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = lib.kda_chunk_fwd.argtypes
@@ -208,6 +213,35 @@ def _chunk_fwd(fn, q, k, v, log_alpha, beta, init_state, cu_seqlens, chunk_size,
               chunk_size, _ptr(out), _ptr(final_state), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, out, init_state=None, cu_seqlens=None, chunk_size=64,
+                      final_state=None, stream=None):
+    """``chunk_fwd`` through kda_chunk_fwd_noalloc: no workspace and nothing
+    allocated here or in the library (the caller supplies ``out`` and, if
+    wanted, ``final_state``); the library's static device scratch stands in
+    for the workspace, so the sizes are limited (KdaError beyond them) and
+    calls that overlap on one GPU race.  Returns (out, final_state)."""
+    _validate([("q", q, (None,) * 4, _IN, True)], devices=False)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 4 else None
+    n_seqs, N = _seq_count(B, cu_seqlens)
+    _validate([("q", q, (B, T, H, Dk), _IN, True), ("k", k, (B, T, H, Dk), (q.dtype,), True),
+               ("v", v, (B, T, H, Dv), (q.dtype,), True), ("log_alpha", log_alpha, (B, T, H, Dk), _F32, True),
+               ("beta", beta, (B, T, H), _F32, True), ("out", out, (B, T, H, Dv), _F32, True),
+               ("init_state", init_state, (N, H, Dk, Dv), _F32, False),
+               ("cu_seqlens", cu_seqlens, (N + 1,), (torch.int32,), False),
+               ("final_state", final_state, (N, H, Dk, Dv), _F32, False)])
+    _check(load().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                        _ptr(init_state), _ptr(cu_seqlens), B, T, H, Dk, Dv, n_seqs,
+                                        _dtype_code(q), chunk_size, _ptr(out), _ptr(final_state),
+                                        _stream(stream)))
+    return out, final_state
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the static scratch behind ``chunk_fwd_noalloc``."""
+    return int(load().kda_chunk_fwd_noalloc_max_workspace())
 
 
 def dplr_workspace_size(B, T, H, D, n_seqs=0, dtype=torch.bfloat16, chunk_size=64) -> int:

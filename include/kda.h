@@ -60,8 +60,9 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 130 /* 1.3.0: adds kda_dplr_chunk_fwd and kda_dplr_decode_step (1.2.0: kda_chunk_bwd;
-                            1.1.0: the gdn_* and kda_layer_* entry points) */
+#define KDA_VERSION 140 /* 1.4.0: adds kda_chunk_fwd_noalloc (1.3.0: kda_dplr_chunk_fwd and
+                            kda_dplr_decode_step; 1.2.0: kda_chunk_bwd; 1.1.0: the gdn_* and
+                            kda_layer_* entry points) */
 
 typedef enum {
     KDA_OK = 0,
@@ -121,6 +122,34 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
                          kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and bit-identical results.  The workspace is the library's own
+ * static device array of kda_chunk_fwd_noalloc_max_workspace() bytes
+ * (256 MiB): one copy per GPU, set up on the first call on that device and
+ * held until the process ends.  The call itself allocates nothing and calls
+ * no allocating routine.
+ *
+ * Sizes whose kda_chunk_fwd_workspace_size() exceeds that limit return
+ * KDA_ERR_WORKSPACE before anything is enqueued (at Dk = Dv = 128, bf16,
+ * 64-token chunks that is T * H above about 149,000 token-heads of a dense
+ * batch; e.g. T = 4096 with H = 32 fits).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one device (other streams, other host
+ * threads) race on it and must be serialised by the caller.  Its contents on
+ * entry are ignored.  A failure to look up the array's device address
+ * returns KDA_ERR_HIP.
+ */
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *log_alpha,
+                                 const float *beta, const float *init_state, const int32_t *cu_seqlens,
+                                 int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t n_seqs,
+                                 kda_dtype in_dtype, int32_t chunk_size, float *o, float *final_state,
+                                 hipStream_t stream);
+
+/* Bytes of the static scratch behind kda_chunk_fwd_noalloc (host only, pure). */
+size_t kda_chunk_fwd_noalloc_max_workspace(void);
 
 /*
  * kda_chunk_bwd_workspace_size -- bytes of device workspace kda_chunk_bwd

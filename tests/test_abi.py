@@ -42,7 +42,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 130
+    assert lib.kda_version() == 140
     for code, name in [(0, b"KDA_OK"), (1, b"KDA_ERR_INVALID_ARG"), (2, b"KDA_ERR_UNSUPPORTED"),
                        (3, b"KDA_ERR_WORKSPACE"), (4, b"KDA_ERR_HIP")]:
         assert lib.kda_status_string(code) == name
@@ -364,3 +364,33 @@ def test_empty_varlen_needs_no_workspace(lib, fn):
     kw.update(T=64, ws=None, ws_bytes=0)
     rc = _dplr(lib, **kw) if fn == "kda_dplr_chunk_fwd" else _chunk(lib, fn, **kw)
     assert rc == WORKSPACE
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, log_alpha=FAKE + 0x3000000,
+             beta=FAKE + 0x4000000, init_state=None, cu_seqlens=None, B=1, T=64, H=1, Dk=16,
+             Dv=16, n_seqs=0, dtype=BF16, chunk=16, o=FAKE + 0x5000000, final_state=None, stream=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd_noalloc(p(a["q"]), p(a["k"]), p(a["v"]), p(a["log_alpha"]), p(a["beta"]),
+                                     p(a["init_state"]), p(a["cu_seqlens"]), a["B"], a["T"], a["H"],
+                                     a["Dk"], a["Dv"], a["n_seqs"], a["dtype"], a["chunk"], p(a["o"]),
+                                     p(a["final_state"]), a["stream"])
+
+
+def test_noalloc_entry_limits_and_validation(lib):
+    """kda_chunk_fwd_noalloc: sizes whose workspace exceeds the static scratch
+    are refused on the host (KDA_ERR_WORKSPACE, before any HIP call); other
+    argument errors are the ones kda_chunk_fwd reports."""
+    cap = lib.kda_chunk_fwd_noalloc_max_workspace()
+    assert cap == 256 << 20
+    ws = lib.kda_chunk_fwd_workspace_size
+    assert ws(1, 4096, 32, 128, 128, 0, BF16, 64) <= cap < ws(1, 8192, 32, 128, 128, 0, BF16, 64)
+    assert _noalloc(lib, T=8192, H=32, Dk=128, Dv=128, chunk=64) == WORKSPACE
+    assert b"static scratch" in lib.kda_last_error()
+    assert _noalloc(lib, q=None) == INVALID
+    assert _noalloc(lib, Dk=24) == UNSUPPORTED
+    assert _noalloc(lib, o=FAKE) == INVALID  # o aliases q
+    # a valid call passes validation; with no GPU here the scratch lookup then fails
+    assert _noalloc(lib) == 4
+    assert b"static scratch" in lib.kda_last_error()
