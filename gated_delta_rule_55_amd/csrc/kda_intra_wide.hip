@@ -14,10 +14,13 @@
 //       ch(e) = 32 w + 16 (e / 4) + 4 (l / 16) + e % 4,   e = 0 .. 7,
 //   of k, q, v (bf16 bits) and of G (fp32).
 //
-// That is the k-slot layout of the 16x16x32 bf16 matrix instruction for the
-// Gram tiles (a sum over channels may take them in any order as long as both
-// operands agree; operands split in bf16 hi/lo, three products), so every
-// wave forms its channels' share of all ten Gram tiles without touching LDS.  It is also the row layout of the [W; Q']
+// That is the k-slot layout of the 16x16x32 bf16 / fp16 matrix instructions
+// for the Gram tiles (a sum over channels may take them in any order as long
+// as both operands agree; diagonal tiles with operands split in bf16 hi/lo,
+// three products, for the fp32 exponent range their midpoint factors need;
+// tiles below the diagonal, whose factors are all <= 1, with plain fp16
+// operands, one product), so every wave forms its channels' share of all ten
+// Gram tiles without touching LDS.  It is also the row layout of the [W; Q']
 // fragments, so Q*Gamma adds into Q' in place.  The cumulative decay is a scan
 // over the 16 lanes of a row (DPP) plus a carry over the four tiles.  The four
 // shares of each Gram tile are summed in a fixed order through LDS, then T, R
@@ -214,7 +217,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
 
     // work items are visited in order; varlen grids end with empty slots, so
     // the first empty slot ends the walk
-    int64_t item = blockIdx.x;
+    int64_t item = p.item0 + blockIdx.x;
     int64_t tok0;
     int nvalid;
     int64_t slot, h0;
@@ -386,12 +389,16 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
             float gm[8];  // G at token 16 J + 15
 #pragma unroll
             for (int e = 0; e < 8; ++e) gm[e] = row_bcast<15>(G[J][e]);
-            if constexpr (J < 3) {  // tiles below the diagonal, reference = last token of column tile J
+            if constexpr (J < 3) {
+                // tiles below the diagonal, reference = last token of column tile
+                // J: both factors are <= 1 and |k|, |q| <= 1, so every operand
+                // lies in [-1, 1] and plain fp16 operands (11-bit significands,
+                // one product per tile) keep the parity error where bf16 hi/lo
+                // splits put it; bf16 alone would not
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = Kf(J, e) * fast_exp2(gm[e] - G[J][e]);
-                bf16x8 yh, yl;
-                split_bf16(y, yh, yl);
+                const f16x8 y16 = pack_f16(y);
                 static_for<J + 1, 4>([&](auto Ic) {
                     constexpr int I = decltype(Ic)::value;
                     float xk[8], xq[8];
@@ -401,8 +408,9 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
                         xk[e] = Kf(I, e) * fa;
                         xq[e] = Qf(I, e) * fa;
                     }
-                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, gram_bf16x3(xk, yh, yl));
-                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, gram_bf16x3(xq, yh, yl));
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    emit(std::integral_constant<int, I * (I + 1) / 2 + J>{}, mfma_f16(pack_f16(xk), y16, z));
+                    emit(std::integral_constant<int, 10 + I * (I + 1) / 2 + J>{}, mfma_f16(pack_f16(xq), y16, z));
                 });
             }
             // diagonal tile, reference = token 16 J + 7; a channel whose half-span
@@ -751,14 +759,15 @@ static hipError_t launch_intra_wide_t(const IntraParams &p, int64_t n_items, hip
             nb = 1;
         per_cu = nb;
     }
-    const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
+    const int cus = p.grid_cus > 0 ? p.grid_cus : device_cu_count();
+    const int64_t grid = std::min<int64_t>(n_items - p.item0, static_cast<int64_t>(cus) * per_cu);
     hipLaunchKernelGGL(intra_wide_kernel<GM>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
                        p, n_items);
     return hipGetLastError();
 }
 
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
-    if (n_items <= 0) return hipSuccess;
+    if (n_items <= p.item0) return hipSuccess;
     switch (p.gate_mode) {
         case 0: return launch_intra_wide_t<0>(p, n_items, stream);
         case 1: return launch_intra_wide_t<1>(p, n_items, stream);

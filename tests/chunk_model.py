@@ -49,8 +49,9 @@ def chunk_forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     """Chunked forward over [B,T,H,D] inputs (numpy); returns (o, final_state).
 
     ``rnd`` maps a product-group name to a function (X, Y) -> X @ Y that
-    emulates the operand precision of that product; groups: 'AP', 'WU', 'WS',
-    'QS', 'PU', 'KU', 'QW'.  Default: exact (fp64) products.  ``fold`` selects
+    emulates the operand precision of that product; groups: 'AP' (Gram tiles;
+    'APo' / 'APd' override it for the tiles below / on the diagonal), 'WU',
+    'WS', 'QS', 'PU', 'KU', 'QW'.  Default: exact (fp64) products.  ``fold`` selects
     the form the HIP state pass uses, O = (Qg - P W) S0 + P U'.
     """
     q, k, v, la, be = (np.asarray(a, dtype=np.float64) for a in (q, k, v, log_alpha, beta))
@@ -65,6 +66,8 @@ def chunk_forward(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, ch
     mm = {} if rnd is None else dict(rnd)
     for g in ("AP", "WU", "WS", "QS", "PU", "KU", "QW"):
         mm.setdefault(g, lambda X, Y: X @ Y)
+    mm.setdefault("APo", mm["AP"])
+    mm.setdefault("APd", mm["AP"])
     o = np.zeros((B, T, H, Dv))
     fs = np.zeros((N, H, Dk, Dv))
     for n, (b, t0, t1) in enumerate(seqs):
@@ -111,8 +114,8 @@ def _one_chunk(q, k, v, la, be, S0, C, mm, fold):
                 Xq = q[ri] * np.exp(G[ri] - G[m])
                 Xk = k[ri] * np.exp(G[ri] - G[m])
                 Y = k[rj] * np.exp(G[m] - G[rj])
-                Aprime[ri, rj] = mm["AP"](Xk, Y.T)
-                P[ri, rj] = mm["AP"](Xq, Y.T)
+                Aprime[ri, rj] = mm["APo"](Xk, Y.T)
+                P[ri, rj] = mm["APo"](Xq, Y.T)
             else:
                 m = I * TILE + TILE // 2 - 1
                 span = np.maximum(G[I * TILE] - G[m], G[m] - G[(I + 1) * TILE - 1])
@@ -120,8 +123,8 @@ def _one_chunk(q, k, v, la, be, S0, C, mm, fold):
                 Xq = np.where(safe, q[ri] * np.exp(np.where(safe, G[ri] - G[m], 0.0)), 0.0)
                 Xk = np.where(safe, k[ri] * np.exp(np.where(safe, G[ri] - G[m], 0.0)), 0.0)
                 Y = np.where(safe, k[rj] * np.exp(np.where(safe, G[m] - G[rj], 0.0)), 0.0)
-                Ad = mm["AP"](Xk, Y.T)
-                Pd = mm["AP"](Xq, Y.T)
+                Ad = mm["APd"](Xk, Y.T)
+                Pd = mm["APd"](Xq, Y.T)
                 for c in np.nonzero(~safe)[0]:       # exact per-element path
                     E = np.exp(np.minimum(G[ri, c][:, None] - G[rj, c][None, :], 0.0))
                     Ad += np.outer(k[ri, c], k[rj, c]) * E
