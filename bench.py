@@ -103,6 +103,13 @@ def decode_alg_bytes(N, H, Dk, Dv, in_bytes=2, gate_per_head=None):
     return N * H * (8 * Dk * Dv + in_bytes * (2 * Dk + Dv) + 4 * g + 4 + 4 * Dv)
 
 
+# what the line's copied counter fields are: figures of the committed summary,
+# not measured in the run that prints them (null when the summary was taken on
+# other kernel sources)
+COUNTER_SOURCE = ("profiles/traffic.json: rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                  "MfmaUtil) of an earlier run on these exact kernel sources (source digest checked)")
+
+
 def source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_55_amd", "csrc")
@@ -180,7 +187,7 @@ def summarize_trace(d):
 
 
 def _last_dispatch_counters(d, counter):
-    """{kernel short name: value of `counter` (summed over instances) in its last dispatch}."""
+    """{kernel name: value of `counter` (summed over instances) in its last dispatch}."""
     import glob
     (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     per = {}
@@ -200,7 +207,7 @@ def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma
     each run's output is the directory given here) and this summary's command line."""
     prof = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/{d} -o run -- " \
            "python3 <repo>/bench.py {a}"
-    bench_args = "--steps 1 --warmup 0 --no-cpu-baseline --no-backward"
+    bench_args = "--steps 1 --warmup 0 --no-cpu-baseline --no-backward --no-configs"
     cmds = [prof.format(c="FETCH_SIZE", d=fetch_dir, a=bench_args),
             prof.format(c="WRITE_SIZE", d=write_dir, a=bench_args),
             prof.format(c="FETCH_SIZE", d=copy_fetch_dir, a="--only copy --steps 2"),
@@ -280,16 +287,6 @@ def host_cpu_model():
     return "unknown"
 
 
-def cpu_baseline(inp, heads, T_sample, threads):
-    import oracle
-    sl = lambda x: x[:, :T_sample, heads].detach().to("cpu").double().numpy()
-    args = [sl(inp[k]) for k in ("q", "k", "v", "log_alpha", "beta")]
-    t0 = time.perf_counter()
-    oracle.forward(*args, None, None, n_threads=threads)
-    dt = time.perf_counter() - t0
-    return dt
-
-
 def backward_leg(torch, kda, pin, dev, C):
     """kda_chunk_bwd over the first 262,144 tokens of the long prefill inputs
     (its workspace holds two fp32 states per (chunk, head), so the full 1M
@@ -337,6 +334,207 @@ def dplr_leg(torch, kda, workloads, pin, dev, C):
     return dplr, (a, b)
 
 
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _parity(got, ref):
+    """max|got - ref| / RMS(ref) over the whole tensor (got: torch, ref: fp64 numpy)."""
+    import numpy as np
+    g = got.detach().to("cpu").double().numpy()
+    return float(np.max(np.abs(g - ref)) / np.sqrt(np.mean(ref * ref)))
+
+
+def config_legs(torch, kda, workloads, oracle, dev, steps, flush, threads):
+    """The other workloads, each timed and checked against the oracle in full:
+    the tiny fp32 case (a launch-latency figure), the 4096-token prefill, the
+    packed varlen prefill and the decode workload; the oracle is timed on the
+    same inputs on all host threads and on one.  Returns {name: record}."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def prefill_record(name, inp, reps, flush_each, tau):
+        q = inp["q"]
+        B, T, H, Dk = q.shape
+        Dv = inp["v"].shape[-1]
+        N, C = inp["N"], inp["chunk"]
+        bf = q.dtype == torch.bfloat16
+        cu = inp["cu_seqlens"]
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+        fs = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, kda.workspace_size(B, T, H, Dk, Dv, 0 if cu is None else N, q.dtype, C)),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: kda.chunk_fwd(q, inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["init_state"],
+                                     cu, C, out=o, final_state=fs, workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            if flush_each:
+                flush.zero_()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        t = _median(ts)
+        Ttot = B * T
+        by = prefill_alg_bytes(Ttot, H, Dk, Dv, N, in_bytes=2 if bf else 4, init=inp["init_state"] is not None)
+        fl = prefill_alg_flops(Ttot, H, Dk, Dv, C)
+        # the oracle on the same inputs: all host threads, then one thread on head 0
+        t0 = time.perf_counter()
+        o_ref, s_ref = oracle.forward_native(q, inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                             inp["init_state"], cu, n_threads=threads)
+        t_all = time.perf_counter() - t0
+        s0 = None if inp["init_state"] is None else inp["init_state"][:, :1]
+        t0 = time.perf_counter()
+        oracle.forward_native(q, inp["k"], inp["v"], inp["log_alpha"], inp["beta"], s0, cu, heads=(0, 1),
+                              n_threads=1)
+        t_one = time.perf_counter() - t0
+        rec = {"T": Ttot, "H": H, "d_k": Dk, "d_v": Dv, "chunk": C, "dtype": "bf16" if bf else "f32",
+               "ms_median": t * 1e3, "ms_mean": sum(ts) / len(ts) * 1e3, "tokens_per_s": Ttot / t,
+               "alg_bytes": by, "alg_flops": fl, "hbm_frac_algorithmic": by / t / HBM_PEAK,
+               "mfma_frac_algorithmic": fl / t / BF16_PEAK,
+               "parity": {"o": _parity(o, o_ref), "final_state": _parity(fs, s_ref), "tau": tau,
+                          "scope": "every output and final state against the fp64 oracle"},
+               "cpu_baseline": {"value": Ttot / t_all, "unit": "tokens/s", "cores": min(threads, N * H),
+                                "kind": "oracle", "sample": f"the whole workload ({t_all:.2f} s wall)",
+                                "value_1_thread": Ttot / t_one / H,
+                                "sample_1_thread": f"head 0, every token, one thread ({t_one:.2f} s wall), "
+                                                   f"scaled to H={H} tokens/s"}}
+        return rec, call
+
+    # tiny fp32 workload: T=64, H=1, d=16, 16-token chunks -- launch-bound
+    tiny = workloads.make_prefill("tiny", dev, 0)
+    rec, call = prefill_record("tiny", tiny, 200, False, 1e-4)
+    n_calls = 1000
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_calls):
+        call()
+    torch.cuda.synchronize()
+    rec["us_per_call_back_to_back"] = (time.perf_counter() - t0) / n_calls * 1e6
+    rec["us_per_call_median"] = rec.pop("ms_median") * 1e3
+    rec["us_per_call_mean"] = rec.pop("ms_mean") * 1e3
+    rec["workload"] = "KDA tiny: B=1 T=64 H=1 d=16 chunk=16 fp32, zero initial state (HIP events around each call)"
+    out["tiny"] = rec
+
+    # the 4096-token prefill, 240 MB: fits in the 256 MB MALL, so each timed call
+    # follows the cache flush
+    pre = workloads.make_prefill("prefill", dev, 0)
+    rec, _ = prefill_record("prefill", pre, steps, True, 2e-2)
+    rec["workload"] = ("KDA prefill: B=1 T=4096 H=32 d=128 chunk=64 bf16, log_alpha=-softplus(N(0,1)+2), "
+                       "initial state N(0,0.02^2); L2 and MALL flushed before each timed call")
+    out["prefill"] = rec
+    del pre
+
+    # the packed varlen prefill: 16 sequences, ragged lengths, 5% resets
+    var = workloads.make_prefill("varlen", dev, 0)
+    rec, _ = prefill_record("varlen", var, steps, True, 2e-2)
+    rec["workload"] = ("KDA varlen: 16 packed sequences, lengths U[1,16384] (none a multiple of 64), H=32 d=128 "
+                       "chunk=64 bf16, log_alpha=-softplus(N(0,1)), 5% full-token resets, zero initial states")
+    rec["n_seqs"] = var["N"]
+    out["varlen"] = rec
+    del var
+
+    # the decode workload in full: 64 steps on 256 x 32 states, against the
+    # oracle (threaded over the states)
+    din = workloads.make_decode("decode", dev, 0)
+    dw = din["workload"]
+    st = din["state"].clone()
+    outs = [torch.empty((dw.N, dw.H, dw.Dv), dtype=torch.float32, device=dev) for _ in range(dw.steps)]
+    for t in range(dw.steps):
+        kda.decode_step(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t], din["beta"][t], st, out=outs[t])
+    torch.cuda.synchronize()
+    import numpy as np
+    st_ref = din["state"].detach().to("cpu").double().numpy()
+    err_o, ss_o, n_o = 0.0, 0.0, 0
+    t0 = time.perf_counter()
+    for t in range(dw.steps):
+        o_ref, st_ref = oracle.decode_step_native(din["q"][t], din["k"][t], din["v"][t], din["log_alpha"][t],
+                                                  din["beta"][t], st_ref, n_threads=threads)
+        g = outs[t].detach().to("cpu").double().numpy()
+        err_o = max(err_o, float(np.max(np.abs(g - o_ref))))
+        ss_o += float(np.sum(o_ref * o_ref))
+        n_o += o_ref.size
+    t_all = time.perf_counter() - t0
+    sub = slice(0, 16)  # one thread: 16 sequences x 32 heads, 64 steps
+    st1 = din["state"][sub].detach().to("cpu").double().numpy()
+    t0 = time.perf_counter()
+    for t in range(dw.steps):
+        _, st1 = oracle.decode_step_native(din["q"][t][sub], din["k"][t][sub], din["v"][t][sub],
+                                           din["log_alpha"][t][sub], din["beta"][t][sub], st1, n_threads=1)
+    t_one = time.perf_counter() - t0
+    out["decode"] = {
+        "workload": "KDA decode: 256 seqs x 32 heads, 128x128 fp32 states N(0,0.02^2), 64 steps, bf16 tokens",
+        "parity": {"o": err_o / np.sqrt(ss_o / n_o), "final_state": _parity(st, st_ref), "tau": 2e-2,
+                   "scope": "every output of the 64 steps and every final state against the fp64 oracle"},
+        "cpu_baseline": {"value": dw.N * dw.steps / t_all, "unit": "tokens/s (one token per sequence and step)",
+                         "cores": threads, "kind": "oracle",
+                         "sample": f"the whole workload, 8192 states x 64 steps ({t_all:.2f} s wall)",
+                         "value_1_thread": 16 * dw.steps / t_one,
+                         "sample_1_thread": f"16 sequences x 32 heads x 64 steps on one thread ({t_one:.2f} s wall)"},
+    }
+    del din, outs, st
+    return out
+
+
+def context_legs(torch, kda, pin, o, fs, ws, C, steps, flush):
+    """Prefill tokens/s at T = 65,536, 262,144 and 1,048,576 (prefixes of the
+    long workload, flushed before each call), and one decode step of the 32
+    heads continuing from each prefill's final state: the per-token cost of a
+    linear-time recurrence with a fixed-size state does not grow with T."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    H = pin["H"]
+    rec = {"prefill": [], "decode_step_after_prefill": []}
+    Ts = [t for t in (1 << 16, 1 << 18, 1 << 20) if t <= pin["T"]]
+    od = torch.empty((1, H, o.shape[-1]), dtype=torch.float32, device=dev_of(o))
+    for T in Ts:
+        args = [pin[n][:, :T] for n in ("q", "k", "v", "log_alpha", "beta")]
+        oo = o[:, :T]
+        call = lambda: kda.chunk_fwd(*args, None, None, C, out=oo, final_state=fs, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, steps // 2)):
+            flush.zero_()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        t = _median(ts)
+        rec["prefill"].append({"T": T, "ms_median": t * 1e3, "tokens_per_s": T / t})
+        # decode steps continuing this sequence (token T from the inputs' next row)
+        nt = T % pin["T"]
+        tok = [pin[n][0, nt:nt + 1].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        st = fs.clone()
+        for _ in range(3):
+            kda.decode_step(*tok, st, out=od)
+        ds = []
+        for _ in range(20):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            kda.decode_step(*tok, st, out=od)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ds.append(e0.elapsed_time(e1) * 1e3)
+        rec["decode_step_after_prefill"].append({"context_T": T, "us_per_step_median": _median(ds)})
+    rec["note"] = ("decode steps here are one sequence x 32 heads (2 MiB of state): launch-bound, "
+                   "the figure shows no dependence on the context length")
+    return rec
+
+
+def dev_of(t):
+    return t.device
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +547,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None, help="prefill chunk size (default: the workload's)")
     ap.add_argument("--no-dplr", action="store_true", help="skip the general DPLR prefill leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload legs (tiny, 4096-token, varlen, decode) and the T sweep")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "dplr"], default=None,
                     help="run one part only (for profilers); prints no JSON line")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None)
@@ -470,6 +670,47 @@ def main():
     pre_ms, dec_ms = timed(prefill, decode)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+
+    # the oracle on a sample of the same 1M-token workload: its time is the CPU
+    # baseline, its outputs check the prefill just timed (o still holds them)
+    long_cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        heads = (0, 16)
+        T_s = 262144
+        hostq = {n: pin[n][:, :T_s].detach().to("cpu") for n in ("q", "k", "v", "log_alpha", "beta")}
+        t0 = time.perf_counter()
+        o_ref, _ = oracle.forward_native(hostq["q"], hostq["k"], hostq["v"], hostq["log_alpha"], hostq["beta"],
+                                         heads=heads, n_threads=threads)
+        dt = time.perf_counter() - t0
+        par = _parity(o[:, :T_s, heads[0]:heads[1]], o_ref)
+        del o_ref
+        T_1 = 65536
+        t0 = time.perf_counter()
+        oracle.forward_native(hostq["q"][:, :T_1], hostq["k"][:, :T_1], hostq["v"][:, :T_1],
+                              hostq["log_alpha"][:, :T_1], hostq["beta"][:, :T_1], heads=(0, 1), n_threads=1)
+        dt1 = time.perf_counter() - t0
+        del hostq
+        # the metric's unit is tokens/s at H=32: token-heads/s divided by 32
+        long_cpu = {
+            "value": T_s * (heads[1] - heads[0]) / dt / H,
+            "unit": "tokens/s",
+            "cores": min(threads, heads[1] - heads[0]),
+            "kind": "oracle",
+            "sample": f"fp64 token loop on heads 0-15 x first {T_s} tokens of the long "
+                      f"prefill workload ({dt:.1f} s wall), scaled to H=32 tokens/s",
+            "value_1_thread": T_1 / dt1 / H,
+            "sample_1_thread": f"head 0 x first {T_1} tokens on one thread ({dt1:.1f} s wall), "
+                               f"scaled to H=32 tokens/s",
+            "host_cpu": host_cpu_model(),
+            "host_threads": os.cpu_count(),
+        }
+        long_parity = {"o": par, "tau": 2e-2,
+                       "scope": f"o of heads 0-15 over the first {T_s} tokens (the oracle sample above) of the "
+                                f"timed call; every output is checked in the GPU tests"}
+
+    ctx = None if args.no_configs else context_legs(torch, kda, pin, o, fs, ws, C, args.steps, flush)
 
     # ---- Gated DeltaNet on the same tensors: one log gate per (token, head) ----
     gdn_la = workloads.scalar_log_alpha((1, T, H), w.shift, dev, seed=1)
@@ -629,6 +870,7 @@ def main():
             "hbm_frac_algorithmic": pb / t_pre / HBM_PEAK,
             "mfma_frac_algorithmic": pf / t_pre / BF16_PEAK,
             "mfma_busy_pct_counter": measured_mfma_busy("kda_chunk_fwd") or None,
+            "mfma_busy_pct_counter_source": COUNTER_SOURCE,
             "alg_bytes": pb, "alg_flops": pf,
         },
         "decode": {
@@ -646,6 +888,7 @@ def main():
             "unit": "GB/s",
             "frac": pb / t_pre / HBM_PEAK,
             "traffic": measured_traffic("kda_chunk_fwd"),
+            "traffic_source": COUNTER_SOURCE,
         },
         "decode_roofline": {
             "kernel": "decode_step_kernel<128,128,bf16,0>",
@@ -793,27 +1036,16 @@ def main():
             "sample": f"fp64 reverse-mode token loop on heads 0-15 x first {T_s} tokens of the long prefill "
                       f"workload ({dtb:.1f} s wall), scaled to H=32 tokens/s"}
 
-    if not args.no_cpu_baseline:
+    if long_cpu is not None:
+        result["cpu_baseline"] = long_cpu
+        result["prefill"]["parity"] = long_parity
+    if ctx is not None:
+        result["context_sweep"] = ctx
+    if not args.no_configs:
+        import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
-        heads = list(range(16))
-        T_s = 262144
-        dt = cpu_baseline(pin, heads, T_s, threads)
-        T_1 = 65536
-        dt1 = cpu_baseline(pin, [0], T_1, 1)
-        # the metric's unit is tokens/s at H=32: token-heads/s divided by 32
-        result["cpu_baseline"] = {
-            "value": T_s * len(heads) / dt / H,
-            "unit": "tokens/s",
-            "cores": min(threads, len(heads)),
-            "kind": "oracle",
-            "sample": f"fp64 token loop on heads 0-15 x first {T_s} tokens of the long "
-                      f"prefill workload ({dt:.1f} s wall), scaled to H=32 tokens/s",
-            "value_1_thread": T_1 / dt1 / H,
-            "sample_1_thread": f"head 0 x first {T_1} tokens on one thread ({dt1:.1f} s wall), "
-                               f"scaled to H=32 tokens/s",
-            "host_cpu": host_cpu_model(),
-            "host_threads": os.cpu_count(),
-        }
+        del ws
+        result["configs"] = config_legs(torch, kda, workloads, oracle, dev, args.steps, flush, threads)
     print(json.dumps(result))
 
 

@@ -204,26 +204,8 @@ static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t
         if (total > SIZE_MAX - plan) return false;
         total += plan;
     }
-    if (!dplr && kda::head_state_path(C, Dk, Dv, bf16)) {
-        // the state carried between the segments of a pipelined prefill
-        size_t carry = 4;
-        if (!mul_ok(carry, (uint64_t)N) || !mul_ok(carry, (uint64_t)H) || !mul_ok(carry, (uint64_t)Dk) ||
-            !mul_ok(carry, (uint64_t)Dv))
-            return false;
-        carry = kda::align256(carry);
-        total = kda::align256(total);
-        if (total > SIZE_MAX - carry) return false;
-        total += carry;
-    }
     out = total;
     return true;
-}
-
-// Offset of the state-carry region in a forward workspace (see workspace_bytes).
-static size_t carry_offset(size_t pkg, int64_t slots, int32_t H, int32_t N, bool varlen) {
-    size_t off = pkg * (size_t)slots * (size_t)H;
-    if (varlen) off += kda::align256(((size_t)N + 1) * sizeof(int32_t));
-    return kda::align256(off);
 }
 
 size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv,
@@ -384,9 +366,6 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
                              : nullptr;
-    a.state_carry = (gate_mode != 3 && kda::head_state_path(chunk_size, Dk, Dv, bf16) && a.workspace)
-                        ? reinterpret_cast<float *>(a.workspace + carry_offset(pkg, slots, H, N, varlen))
-                        : nullptr;
     if (T == 0) {
         // Every sequence is empty (cu[N] = T = 0): only final_state <- init_state
         // remains.  Run it as a dense batch of N empty sequences so that neither
@@ -396,7 +375,6 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         a.n_slots = 0;
         a.workspace = nullptr;
         a.chunk_offsets = nullptr;
-        a.state_carry = nullptr;
     }
     a.lr_a = lr_a; a.lr_b = lr_b;
     hipError_t e = gate_mode == 3 ? kda::launch_dplr(a, stream) : kda::launch_prefill(a, stream);

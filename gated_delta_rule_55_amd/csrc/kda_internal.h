@@ -106,12 +106,7 @@ struct PrefillArgs {
     int64_t n_slots;            // chunk slots in the workspace
     size_t pkg_bytes;
     int32_t *chunk_offsets;     // varlen: [N + 1] in the workspace
-    float *state_carry;         // [N, H, Dk, Dv] fp32 in the workspace (whole-head state pass), or null
 };
-
-// Shapes whose state pass runs one workgroup per (sequence, head)
-// (kda_state_head.hip): 64-token chunks, d_k = d_v = 128, bf16 inputs.
-inline bool head_state_path(int C, int Dk, int Dv, bool bf16) { return bf16 && C == 64 && Dk == 128 && Dv == 128; }
 
 // Chunk slots the workspace reserves: every chunk of every sequence.
 inline int64_t prefill_slots(int32_t B, int64_t T, int32_t N, int32_t C, bool varlen) {

@@ -217,7 +217,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
 
     // work items are visited in order; varlen grids end with empty slots, so
     // the first empty slot ends the walk
-    int64_t item = p.item0 + blockIdx.x;
+    int64_t item = blockIdx.x;
     int64_t tok0;
     int nvalid;
     int64_t slot, h0;
@@ -759,15 +759,14 @@ static hipError_t launch_intra_wide_t(const IntraParams &p, int64_t n_items, hip
             nb = 1;
         per_cu = nb;
     }
-    const int cus = p.grid_cus > 0 ? p.grid_cus : device_cu_count();
-    const int64_t grid = std::min<int64_t>(n_items - p.item0, static_cast<int64_t>(cus) * per_cu);
+    const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
     hipLaunchKernelGGL(intra_wide_kernel<GM>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
                        p, n_items);
     return hipGetLastError();
 }
 
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
-    if (n_items <= p.item0) return hipSuccess;
+    if (n_items <= 0) return hipSuccess;
     switch (p.gate_mode) {
         case 0: return launch_intra_wide_t<0>(p, n_items, stream);
         case 1: return launch_intra_wide_t<1>(p, n_items, stream);

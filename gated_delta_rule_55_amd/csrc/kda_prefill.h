@@ -32,10 +32,6 @@ struct IntraParams {
     int32_t gate_mode;
     const uint16_t *x_alpha, *x_beta;
     float l2_eps;
-    // the wide kernel (kda_intra_wide.hip) walks items [item0, n_items) on a
-    // grid sized for grid_cus compute units (0: all of the device's)
-    int64_t item0;
-    int32_t grid_cus;
 };
 
 struct StateParams {

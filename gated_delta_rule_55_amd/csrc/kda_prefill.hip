@@ -40,7 +40,6 @@
 #include <algorithm>
 
 #include "kda_prefill.h"
-#include "kda_state_head.h"
 
 namespace kda {
 
@@ -985,10 +984,6 @@ static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream) {
 
 template <int C, int DK, int DV, bool BF>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
-    if constexpr (C == 64 && DK == 128 && DV == 128 && BF) {
-        const hipError_t ep = launch_prefill_pipelined(a, stream);
-        if (ep != hipErrorNotSupported) return ep;
-    }
     const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream);
     if (ei != hipSuccess) return ei;
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state, nullptr,
