@@ -20,7 +20,7 @@ epilogue, kda_layer_chunk_fwd / kda_layer_decode_step) in the "layer" object;
 then the general diagonal-plus-low-rank recurrence (kda_dplr_chunk_fwd over the
 same 1M-token q, k, v and gates, and 64 kda_dplr_decode_step calls on the decode
 workload) in the "dplr" object; then the backward
-(kda_chunk_bwd) over the first 262,144 tokens of the same prefill inputs in the
+(kda_chunk_bwd) over all 1,048,576 tokens of the same prefill inputs in the
 "backward" object.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -30,8 +30,10 @@ Profiling helpers (the commands that made the summaries under profiles/):
       (copy: a plain device-to-device copy of COPY_BYTES, the counter calibration)
   python bench.py --summarize-trace DIR            markdown table of rocprofv3
       --kernel-trace --stats output (DIR/run_kernel_stats.csv)
-  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
-      writes profiles/traffic.json from four rocprofv3 --pmc runs
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_DIR]
+          [--backward-counters BWD_FETCH_DIR BWD_WRITE_DIR]
+      writes profiles/traffic.json from the rocprofv3 --pmc runs (the backward's: every
+      dispatch of one --only backward call summed)
 """
 from __future__ import annotations
 
@@ -202,7 +204,20 @@ def _last_dispatch_counters(d, counter):
     return last
 
 
-def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir):
+def _call_counters(d, counter):
+    """`counter` summed over every dispatch of the library's kernels in a run
+    that makes one C-ABI call (the backward: many dispatches per call)."""
+    import glob
+    (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    tot, n = 0.0, set()
+    for r in _kernel_rows(path):
+        if r["Counter_Name"] == counter and "kda::" in r["Kernel_Name"]:
+            tot += float(r["Counter_Value"])
+            n.add(int(r["Dispatch_Id"]))
+    return tot, len(n)
+
+
+def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir, bwd_dirs=None):
     """The rocprofv3 runs (each counter in its own run; <repo> is the repository root and
     each run's output is the directory given here) and this summary's command line."""
     prof = "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/{d} -o run -- " \
@@ -214,12 +229,18 @@ def _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma
             prof.format(c="WRITE_SIZE", d=copy_write_dir, a="--only copy --steps 2")]
     if mfma_dir:
         cmds.append(prof.format(c="MfmaUtil", d=mfma_dir, a=bench_args))
+    if bwd_dirs:
+        cmds.append(prof.format(c="FETCH_SIZE", d=bwd_dirs[0], a="--only backward --steps 1 --warmup 0"))
+        cmds.append(prof.format(c="WRITE_SIZE", d=bwd_dirs[1], a="--only backward --steps 1 --warmup 0"))
     dirs = [fetch_dir, write_dir, copy_fetch_dir, copy_write_dir] + ([mfma_dir] if mfma_dir else [])
-    cmds.append("python bench.py --summarize-counters " + " ".join(dirs))
+    cmd = "python bench.py --summarize-counters " + " ".join(dirs)
+    if bwd_dirs:
+        cmd += " --backward-counters " + " ".join(bwd_dirs)
+    cmds.append(cmd)
     return cmds
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None, bwd_dirs=None):
     fetch = _last_dispatch_counters(fetch_dir, "FETCH_SIZE")
     write = _last_dispatch_counters(write_dir, "WRITE_SIZE")
     cf = _last_dispatch_counters(copy_fetch_dir, "FETCH_SIZE")
@@ -246,8 +267,15 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfm
         if all(n in kernels for n in names):
             launches[launch] = {"kernels": list(names),
                                 "hbm_bytes": sum(kernels[n]["hbm_bytes"] for n in names)}
+    if bwd_dirs:  # one kda_chunk_bwd call over the 1M-token workload: every dispatch summed
+        bf, nf = _call_counters(bwd_dirs[0], "FETCH_SIZE")
+        bw, nw = _call_counters(bwd_dirs[1], "WRITE_SIZE")
+        launches["kda_chunk_bwd"] = {"kernels": "every dispatch of one call", "dispatches": nf,
+                                     "fetch_bytes": bf * 1024.0 * fetch_scale,
+                                     "write_bytes": bw * 1024.0 * write_scale,
+                                     "hbm_bytes": bf * 1024.0 * fetch_scale + bw * 1024.0 * write_scale}
     rec = {"source_digest": source_digest(),
-           "commands": _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir),
+           "commands": _counter_commands(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir, bwd_dirs),
            "note": "per-launch bytes of the last dispatch of each kernel; each counter scaled by what it reads "
                    "for a plain device copy of copy_bytes (read once, written once)",
            "calibration": {"copy_bytes": COPY_BYTES, "copy_kernel": _short(copy_name),
@@ -288,12 +316,12 @@ def host_cpu_model():
 
 
 def backward_leg(torch, kda, pin, dev, C):
-    """kda_chunk_bwd over the first 262,144 tokens of the long prefill inputs
-    (its workspace holds two fp32 states per (chunk, head), so the full 1M
-    tokens would not fit beside the forward's buffers), with d_o ~ N(0, 1) and
-    preallocated gradients and workspace.  Returns (call, T_B)."""
+    """kda_chunk_bwd over all tokens of the long prefill inputs, with
+    d_o ~ N(0, 1) and preallocated gradients and workspace (one segment's
+    packages and states, and a checkpoint per segment: about 4.4 GB at 1M
+    tokens).  Returns (call, T_B)."""
     T, H, Dk, Dv = pin["T"], pin["H"], pin["q"].shape[-1], pin["v"].shape[-1]
-    T_B = min(T, 1 << 18)
+    T_B = T
     bq, bk, bv, bla, bbeta = (pin[n][:, :T_B] for n in ("q", "k", "v", "log_alpha", "beta"))
     bgen = torch.Generator(device=dev)
     bgen.manual_seed(4)
@@ -422,6 +450,7 @@ def config_legs(torch, kda, workloads, oracle, dev, steps, flush, threads):
     rec["us_per_call_mean"] = rec.pop("ms_mean") * 1e3
     rec["workload"] = "KDA tiny: B=1 T=64 H=1 d=16 chunk=16 fp32, zero initial state (HIP events around each call)"
     out["tiny"] = rec
+    _step("tiny workload done")
 
     # the 4096-token prefill, 240 MB: fits in the 256 MB MALL, so each timed call
     # follows the cache flush
@@ -431,6 +460,7 @@ def config_legs(torch, kda, workloads, oracle, dev, steps, flush, threads):
                        "initial state N(0,0.02^2); L2 and MALL flushed before each timed call")
     out["prefill"] = rec
     del pre
+    _step("4096-token workload done")
 
     # the packed varlen prefill: 16 sequences, ragged lengths, 5% resets
     var = workloads.make_prefill("varlen", dev, 0)
@@ -440,6 +470,7 @@ def config_legs(torch, kda, workloads, oracle, dev, steps, flush, threads):
     rec["n_seqs"] = var["N"]
     out["varlen"] = rec
     del var
+    _step("varlen workload done")
 
     # the decode workload in full: 64 steps on 256 x 32 states, against the
     # oracle (threaded over the states)
@@ -480,6 +511,7 @@ def config_legs(torch, kda, workloads, oracle, dev, steps, flush, threads):
                          "sample_1_thread": f"16 sequences x 32 heads x 64 steps on one thread ({t_one:.2f} s wall)"},
     }
     del din, outs, st
+    _step("decode workload done")
     return out
 
 
@@ -531,6 +563,14 @@ def context_legs(torch, kda, pin, o, fs, ws, C, steps, flush):
     return rec
 
 
+_T0 = time.perf_counter()
+
+
+def _step(msg):
+    """One progress line on stderr as each leg of the run ends."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 def dev_of(t):
     return t.device
 
@@ -551,7 +591,11 @@ def main():
                     help="skip the per-workload legs (tiny, 4096-token, varlen, decode) and the T sweep")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "dplr"], default=None,
                     help="run one part only (for profilers); prints no JSON line")
+    ap.add_argument("--workload", choices=["long", "prefill", "varlen", "tiny"], default="long",
+                    help="with --only prefill: the prefill workload to run (default: the 1M-token one)")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None)
+    ap.add_argument("--backward-counters", nargs=2, metavar="DIR", default=None,
+                    help="with --summarize-counters: FETCH_DIR WRITE_DIR of one backward call")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_UTIL_DIR]")
     args = ap.parse_args()
@@ -559,7 +603,7 @@ def main():
         summarize_trace(args.summarize_trace)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, bwd_dirs=args.backward_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the KDA operator here runs on a single "
@@ -580,6 +624,18 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(max(1, args.steps)):
             dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+
+    if args.only == "prefill" and args.workload != "long":
+        # one of the smaller prefill workloads alone (a kernel trace per workload)
+        pw = workloads.make_prefill(args.workload, dev, 0)
+        wl = pw["workload"]
+        ow = torch.empty(tuple(pw["q"].shape[:3]) + (wl.Dv,), dtype=torch.float32, device=dev)
+        fw = torch.empty((pw["N"], wl.H, wl.Dk, wl.Dv), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup + args.steps):
+            kda.chunk_fwd(pw["q"], pw["k"], pw["v"], pw["log_alpha"], pw["beta"], pw["init_state"],
+                          pw["cu_seqlens"], wl.chunk, out=ow, final_state=fw)
         torch.cuda.synchronize()
         return
 
@@ -670,6 +726,7 @@ def main():
     pre_ms, dec_ms = timed(prefill, decode)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    _step("1M-token prefill and decode timed")
 
     # the oracle on a sample of the same 1M-token workload: its time is the CPU
     # baseline, its outputs check the prefill just timed (o still holds them)
@@ -710,8 +767,11 @@ def main():
                        "scope": f"o of heads 0-15 over the first {T_s} tokens (the oracle sample above) of the "
                                 f"timed call; every output is checked in the GPU tests"}
 
+        _step("oracle sample of the 1M-token prefill done")
+
     ctx = None if args.no_configs else context_legs(torch, kda, pin, o, fs, ws, C, args.steps, flush)
 
+    _step("context sweep done")
     # ---- Gated DeltaNet on the same tensors: one log gate per (token, head) ----
     gdn_la = workloads.scalar_log_alpha((1, T, H), w.shift, dev, seed=1)
     gdn_dla = workloads.scalar_log_alpha((dsteps, dw.N, dw.H), dw.shift, dev, seed=2)
@@ -729,6 +789,7 @@ def main():
     g_pre_ms, g_dec_ms = timed(gdn_prefill, gdn_decode)
     del gdn_la, gdn_dla
 
+    _step("Gated DeltaNet timed")
     # ---- the KDA layer: raw bf16 projections in, prologue and epilogue fused ----
     lg = torch.Generator(device=dev)
     lg.manual_seed(3)
@@ -754,6 +815,7 @@ def main():
     l_pre_ms, l_dec_ms = timed(layer_prefill, layer_decode)
     del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g
 
+    _step("KDA layer timed")
     # ---- the general DPLR recurrence on the same q, k, v and gates (kda_dplr_chunk_fwd)
     d_ms = []
     if not args.no_dplr:
@@ -802,7 +864,10 @@ def main():
             dd_ms.extend(de[t].elapsed_time(de[t + 1]) for t in range(dsteps))
         del da, db_, dstate
 
-    # ---- the backward (kda_chunk_bwd) over the first T_B tokens of the same inputs
+    _step("DPLR timed")
+    # ---- the backward (kda_chunk_bwd) over the same inputs (the forward's
+    # workspace is no longer needed)
+    del ws
     b_ms = []
     if not args.no_backward:
         backward, T_B = backward_leg(torch, kda, pin, dev, C)
@@ -819,6 +884,7 @@ def main():
             b_ms.append(e0.elapsed_time(e1))
         del backward
 
+    _step("backward timed")
     pre_ms.sort()
     dec_sorted = sorted(dec_ms)
     # medians of the timed calls and steps (means reported beside them)
@@ -1004,7 +1070,7 @@ def main():
         b_t = b_ms[len(b_ms) // 2] / 1e3
         b_bytes = backward_alg_bytes(T_B, H, Dk, Dv)
         result["backward"] = {
-            "workload": f"kda_chunk_bwd over the first {T_B} tokens of the long prefill workload (H=32, "
+            "workload": f"kda_chunk_bwd over the {T_B} tokens of the long prefill workload (H=32, "
                         f"d=128, chunk 64, bf16 q/k/v, fp32 gates), d_o ~ N(0,1) fp32, no initial or "
                         f"final state: gradients of q, k, v, log_alpha and beta (fp32)",
             "T": T_B,
@@ -1012,8 +1078,8 @@ def main():
             "tokens_per_s": T_B / b_t,
             "alg_bytes": b_bytes,
             "hbm_frac_algorithmic": b_bytes / b_t / HBM_PEAK,
-            "roofline": {"kernel": "kda_chunk_bwd (forward packages and saved states, bwd_state_kernel, "
-                                   "intra_bwd_kernel)",
+            "roofline": {"kernel": "kda_chunk_bwd (segment checkpoints, then per segment: packages and "
+                                   "saved states recomputed, bwd_state_kernel, intra_bwd_kernel)",
                          "bound": "hbm", "achieved": b_bytes / b_t / 1e9, "peak": HBM_PEAK / 1e9,
                          "unit": "GB/s", "frac": b_bytes / b_t / HBM_PEAK,
                          "traffic": measured_traffic("kda_chunk_bwd")},
@@ -1044,7 +1110,6 @@ def main():
     if not args.no_configs:
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
-        del ws
         result["configs"] = config_legs(torch, kda, workloads, oracle, dev, args.steps, flush, threads)
     print(json.dumps(result))
 

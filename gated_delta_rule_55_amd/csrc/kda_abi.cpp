@@ -449,21 +449,46 @@ kda_status kda_layer_chunk_fwd(const void *q, const void *k, const void *v, cons
                           KDA_BF16, 64, o, final_state, workspace, ws_bytes, stream, 2, &L);
 }
 
-// Backward workspace: the forward's (packages, varlen plan), then the state
-// entering and the state gradient leaving every chunk, then the gradient
-// kernel's per-workgroup scratch; sections 256-byte aligned.
-static bool bwd_workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t D, int32_t N, bool varlen, bool bf16,
-                                int32_t C, size_t &out, size_t &fwd, size_t &pkg, int64_t &slots, size_t &states) {
-    if (!workspace_bytes(B, T, H, D, D, N, varlen, bf16, C, fwd, pkg, slots)) return false;
-    fwd = kda::align256(fwd);
-    states = 4;
-    if (!mul_ok(states, (uint64_t)slots) || !mul_ok(states, (uint64_t)H) || !mul_ok(states, (uint64_t)D) ||
-        !mul_ok(states, (uint64_t)D))
+// Backward workspace, sections 256-byte aligned: one segment's packages, the
+// varlen plan, the checkpoints (the state entering segments 1, 2, ...), the
+// two state-gradient carries, one segment's states and state gradients, and
+// the gradient kernel's per-workgroup scratch.
+struct BwdLayout {
+    size_t pkg;                // bytes of one (chunk, head) package
+    int64_t slots, seg, nseg;  // chunk slots (a bound for varlen), per segment, segments
+    size_t plan, ckpt, dcarry, states, dstates, scratch, total;  // section offsets; total size
+};
+
+static bool bwd_layout(int32_t B, int64_t T, int32_t H, int32_t D, int32_t N, bool varlen, bool bf16, int32_t C,
+                       BwdLayout &o) {
+    const kda::PackageLayout L = kda::package_layout(C, D, D, bf16);
+    o.pkg = L.bytes;
+    o.slots = kda::prefill_slots(B, T, N, C, varlen);
+    const int64_t K = kda::bwd_segment_slots(H);
+    o.seg = o.slots < K ? o.slots : K;
+    o.nseg = o.slots > 0 ? (o.slots + K - 1) / K : 1;
+    const size_t state = (size_t)H * D * D * 4;  // one [H, D, D] fp32 state per head; T-independent
+    size_t pk = o.pkg, st = state, ck = state;
+    if (!mul_ok(pk, (uint64_t)o.seg) || !mul_ok(pk, (uint64_t)H) || !mul_ok(st, (uint64_t)o.seg) ||
+        !mul_ok(ck, (uint64_t)(o.nseg - 1)))
         return false;
-    states = kda::align256(states);
-    const size_t scratch = (size_t)kda::kBwdMaxGroups * kda::kBwdScratchMats * (size_t)C * (size_t)D * 4;
-    if (states > (SIZE_MAX - fwd - scratch) / 2) return false;
-    out = fwd + 2 * states + scratch;
+    const size_t sizes[] = {
+        pk,                                                   // packages
+        varlen ? ((size_t)N + 1) * sizeof(int32_t) : 0,       // plan
+        ck,                                                   // checkpoints
+        o.nseg > 1 ? 2 * state : 0,                           // dcarry
+        st, st,                                               // states, dstates
+        (size_t)kda::kBwdMaxGroups * kda::kBwdScratchMats * (size_t)C * (size_t)D * 4,
+    };
+    size_t off[7], at = 0;
+    for (int i = 0; i < 7; ++i) {
+        off[i] = at;
+        const size_t a = kda::align256(sizes[i]);
+        if (a < sizes[i] || at > SIZE_MAX - a) return false;
+        at += a;
+    }
+    o.plan = off[1]; o.ckpt = off[2]; o.dcarry = off[3]; o.states = off[4]; o.dstates = off[5]; o.scratch = off[6];
+    o.total = at;
     return true;
 }
 
@@ -476,12 +501,9 @@ size_t kda_chunk_bwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return 0;
     chunk_size = kda::prefill_effective_chunk(chunk_size, Dk, Dv, in_dtype == KDA_BF16);
     const bool varlen = n_seqs > 0 && B == 1;
-    size_t out = 0, fwd = 0, pkg = 0, states = 0;
-    int64_t slots = 0;
-    if (!bwd_workspace_bytes(B, T, H, Dk, varlen ? n_seqs : B, varlen, in_dtype == KDA_BF16, chunk_size, out, fwd,
-                             pkg, slots, states))
-        return 0;
-    return out;
+    BwdLayout lay{};
+    if (!bwd_layout(B, T, H, Dk, varlen ? n_seqs : B, varlen, in_dtype == KDA_BF16, chunk_size, lay)) return 0;
+    return lay.total;
 }
 
 kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
@@ -542,10 +564,10 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
         if (x.required && !x.p && T > 0) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", x.name);
         if (x.p && !aligned(x.p, x.align)) return fail(KDA_ERR_INVALID_ARG, "%s is not %u-byte aligned", x.name, x.align);
     }
-    size_t need_ws = 0, fwd = 0, pkg = 0, states = 0;
-    int64_t slots = 0;
-    if (!bwd_workspace_bytes(B, T, H, Dk, N, varlen, bf16, chunk_size, need_ws, fwd, pkg, slots, states))
+    BwdLayout lay{};
+    if (!bwd_layout(B, T, H, Dk, N, varlen, bf16, chunk_size, lay))
         return fail(KDA_ERR_INVALID_ARG, "workspace size overflows size_t");
+    const size_t need_ws = lay.total;
     if (!workspace || ws_bytes < need_ws)
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu needed", ws_bytes, workspace, need_ws);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -570,13 +592,16 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
     f.B = B; f.H = H; f.Dk = Dk; f.Dv = Dv; f.N = N; f.C = chunk_size; f.T = T;
     f.bf16 = bf16; f.gate_mode = 0;
     f.workspace = static_cast<char *>(workspace);
-    f.n_slots = slots; f.pkg_bytes = pkg;
-    f.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(f.workspace + pkg * (size_t)slots * (size_t)H) : nullptr;
+    f.n_slots = lay.slots; f.pkg_bytes = lay.pkg;
+    f.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(f.workspace + lay.plan) : nullptr;
     a.d_o = d_o; a.d_final_state = d_final_state;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.d_init_state = d_init_state;
-    a.chunk_states = reinterpret_cast<float *>(f.workspace + fwd);
-    a.chunk_dstates = reinterpret_cast<float *>(f.workspace + fwd + states);
-    a.scratch = reinterpret_cast<float *>(f.workspace + fwd + 2 * states);
+    a.checkpoints = reinterpret_cast<float *>(f.workspace + lay.ckpt);
+    a.dcarry = reinterpret_cast<float *>(f.workspace + lay.dcarry);
+    a.chunk_states = reinterpret_cast<float *>(f.workspace + lay.states);
+    a.chunk_dstates = reinterpret_cast<float *>(f.workspace + lay.dstates);
+    a.scratch = reinterpret_cast<float *>(f.workspace + lay.scratch);
+    a.seg_slots = lay.seg > 0 ? lay.seg : 1;
     hipError_t e = kda::launch_backward(a, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return KDA_OK;

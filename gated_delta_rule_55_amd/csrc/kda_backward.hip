@@ -298,12 +298,22 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
         slot_base = static_cast<int64_t>(n) * ((p.T + C - 1) / C);
     }
     const int64_t nchunks = (L + C - 1) / C;
+    // this launch's chunks of the sequence: [cb, ce), walked backwards
+    const int64_t cb = p.s0 > slot_base ? p.s0 - slot_base : 0;
+    const int64_t ce = p.s1 - slot_base < nchunks ? p.s1 - slot_base : nchunks;
+    if (nchunks == 0 ? !p.do_empty : cb >= ce) return;
     const int col = 16 * ct + l16;
     const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
-    auto pkg_of = [&](int64_t c) { return p.ws + (static_cast<size_t>(slot_base + c) * H + h) * p.pkg_bytes; };
+    auto pkg_of = [&](int64_t c) {
+        return p.ws + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * p.pkg_bytes;
+    };
     auto nvalid_of = [&](int64_t c) { return static_cast<int>(L - c * C < C ? L - c * C : C); };
 
-    // dS slab: wave w owns the 16-channel tiles tk = w, w + 4, ...
+    // dS slab: wave w owns the 16-channel tiles tk = w, w + 4, ...; it starts
+    // as the gradient of the state leaving chunk ce - 1 (the final state's, or
+    // the one carried in from the slots after s1)
+    const float *ds_in = ce == nchunks ? (p.d_final ? p.d_final + sbase : nullptr)
+                                       : p.dcarry_in + static_cast<size_t>(h) * D * D;
     constexpr int SPW = (NTK + 3) / 4;
     f32x4 dS[SPW];
 #pragma unroll
@@ -311,15 +321,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
         const int tk = w + 4 * sl;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            dS[sl][r] = (tk < NTK && p.d_final) ? p.d_final[sbase + static_cast<size_t>(16 * tk + 4 * kg + r) * D + col]
-                                                : 0.f;
+            dS[sl][r] = (tk < NTK && ds_in) ? ds_in[static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] : 0.f;
     }
 
     Frags cur, nxt;
-    if (nchunks > 0) cur.load(p, pkg_of(nchunks - 1), tok_base + (nchunks - 1) * C, nvalid_of(nchunks - 1), ct, h, tid);
-    for (int64_t c = nchunks - 1; c >= 0; --c) {
+    if (ce > cb) cur.load(p, pkg_of(ce - 1), tok_base + (ce - 1) * C, nvalid_of(ce - 1), ct, h, tid);
+    for (int64_t c = ce - 1; c >= cb; --c) {
         // dS1 of this chunk: to the chunk-state buffer and to LDS
-        float *cds = p.chunk_dstates + (static_cast<size_t>(slot_base + c) * H + h) * D * D;
+        float *cds = p.chunk_dstates + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * D * D;
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
@@ -333,7 +342,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
             }
         }
         cur.template store<GS, SS>(sW, sQ, sKt, sGL, sdO, tid);
-        if (c > 0) nxt.load(p, pkg_of(c - 1), tok_base + (c - 1) * C, nvalid_of(c - 1), ct, h, tid);
+        if (c > cb) nxt.load(p, pkg_of(c - 1), tok_base + (c - 1) * C, nvalid_of(c - 1), ct, h, tid);
         __syncthreads();
         // X = Kt dS1 (C x 16), one 16-token tile per wave
         if (w < NT16) {
@@ -362,13 +371,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
         __syncthreads();  // LDS is refilled by the next (earlier) chunk
         cur = nxt;
     }
-    if (p.d_init) {
+    // the gradient of the state entering chunk cb: of the initial state, or
+    // carried out to the slots before s0
+    float *ds_out = cb == 0 ? (p.d_init ? p.d_init + sbase : nullptr)
+                            : (p.dcarry_out ? p.dcarry_out + static_cast<size_t>(h) * D * D : nullptr);
+    if (ds_out) {
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
             if (tk < NTK) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p.d_init[sbase + static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] = dS[sl][r];
+                for (int r = 0; r < 4; ++r) ds_out[static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] = dS[sl][r];
             }
         }
     }
@@ -421,7 +434,7 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         else return x;
     };
 
-    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    for (int64_t item = p.item0 + blockIdx.x; item < n_items; item += gridDim.x) {
         // lane-dependent addresses are recomputed per item: hoisted out of the
         // loop they would be held in registers across all of it
         int tid = threadIdx.x;
@@ -434,8 +447,8 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         int64_t tok0;
         int nvalid;
         if (!locate_chunk(slot, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) break;
-        const float *S0 = p.chunk_states + (static_cast<size_t>(slot) * H + h) * D * D;
-        const float *dS1 = p.chunk_dstates + (static_cast<size_t>(slot) * H + h) * D * D;
+        const float *S0 = p.chunk_states + (static_cast<size_t>(slot - p.s0) * H + h) * D * D;
+        const float *dS1 = p.chunk_dstates + (static_cast<size_t>(slot - p.s0) * H + h) * D * D;
         auto row_of = [&](int i) { return (tok0 + i) * H + h; };
         auto dO_at = [&](int i, int col) { return i < nvalid ? p.d_o[row_of(i) * D + col] : 0.f; };
         auto dO4 = [&](int i, int col) {
@@ -974,28 +987,52 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
     }
 }
 
+// The chunk slots are taken in segments of a.seg_slots.  First the forward
+// runs over segments 0 .. n_seg - 2 keeping only the state entering each next
+// segment (a checkpoint); then, from the last segment to the first, each
+// segment's forward is recomputed from its checkpoint (packages and the state
+// entering each chunk), the state gradients walk it backwards from the
+// gradient carried in from the segment after it, and the gradient kernel
+// takes its (chunk, head) items.
 template <int C, int D, bool BF>
 hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t stream) {
     PrefillArgs f = a.fwd;
     f.o = nullptr;
     f.final_state = nullptr;
-    hipError_t e = launch_forward_states<C, D, D, BF>(f, a.chunk_states, stream);
-    if (e != hipSuccess) return e;
+    const int64_t K = a.seg_slots, slots = f.n_slots;
+    const int64_t nseg = slots > 0 ? (slots + K - 1) / K : 1;
+    const size_t hd2 = static_cast<size_t>(f.H) * D * D;
+    auto ckpt = [&](int64_t g) { return g > 0 ? a.checkpoints + static_cast<size_t>(g - 1) * hd2 : nullptr; };
+    hipError_t e = hipSuccess;
+    for (int64_t g = 0; g + 1 < nseg; ++g) {
+        const FwdSegment fs{g * K, (g + 1) * K, f.workspace, true, g == 0, false, ckpt(g), ckpt(g + 1), nullptr};
+        e = launch_forward_segment<C, D, D, BF>(f, fs, stream);
+        if (e != hipSuccess) return e;
+    }
     const PackageLayout L = package_layout(C, D, D, BF);
-    BwdStateParams sp{f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N, f.workspace, f.pkg_bytes, L,
-                      a.d_o, a.d_final_state, a.chunk_dstates, a.d_init_state};
-    hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t n_items = f.n_slots * f.H;
-    if (n_items <= 0) return hipSuccess;
-    const int64_t grid = std::min<int64_t>(n_items, std::min<int64_t>(kBwdMaxGroups, device_cu_count()));
-    BwdIntraParams ip{f.q, f.k, f.v, f.log_alpha, f.beta, f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N,
-                      a.d_o, a.chunk_states, a.chunk_dstates, a.scratch,
-                      a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta};
-    hipLaunchKernelGGL((intra_bwd_kernel<C, D, BF>), dim3(static_cast<unsigned>(grid)), dim3(kBwdIntraThreads), 0, stream,
-                       ip, n_items);
-    return hipGetLastError();
+    for (int64_t g = nseg - 1; g >= 0; --g) {
+        const int64_t s0 = g * K, s1 = std::min(slots, s0 + K);
+        const FwdSegment fs{s0, s1, f.workspace, true, nseg == 1, false, ckpt(g), nullptr, a.chunk_states};
+        e = launch_forward_segment<C, D, D, BF>(f, fs, stream);
+        if (e != hipSuccess) return e;
+        BwdStateParams sp{f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N, f.workspace, f.pkg_bytes, L,
+                          a.d_o, a.d_final_state, a.chunk_dstates, a.d_init_state,
+                          s0, s1, a.dcarry + ((g + 1) & 1) * hd2, a.dcarry + (g & 1) * hd2, g == 0};
+        hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t n_items = (s1 - s0) * f.H;
+        if (n_items <= 0) continue;
+        const int64_t grid = std::min<int64_t>(n_items, std::min<int64_t>(kBwdMaxGroups, device_cu_count()));
+        BwdIntraParams ip{f.q, f.k, f.v, f.log_alpha, f.beta, f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N,
+                          a.d_o, a.chunk_states, a.chunk_dstates, a.scratch,
+                          a.dq, a.dk, a.dv, a.dlog_alpha, a.dbeta, s0 * f.H, s0};
+        hipLaunchKernelGGL((intra_bwd_kernel<C, D, BF>), dim3(static_cast<unsigned>(grid)), dim3(kBwdIntraThreads), 0,
+                           stream, ip, s1 * f.H);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int C, bool BF>

@@ -129,15 +129,29 @@ hipError_t launch_layer_epilogue(float *o, const uint16_t *g, const float *w, in
 // the chunk plan).  chunk_states / chunk_dstates: [slots, H, Dk, Dv] fp32, the
 // state entering each chunk and the gradient with respect to the state leaving
 // it; scratch: kBwdMaxGroups * kBwdScratchMats * C * Dk fp32.
+// The backward walks the chunk slots in segments of seg_slots (the last one
+// first), recomputing each segment's forward from the state that enters it:
+// fwd.workspace holds one segment's packages, chunk_states / chunk_dstates
+// one segment's states and state gradients ([seg_slots, H, D, D] fp32 each),
+// checkpoints the state entering segments 1, 2, ... ([n_seg - 1, H, D, D]),
+// dcarry two [H, D, D] buffers for the state gradient crossing a segment
+// boundary.
 struct BackwardArgs {
     PrefillArgs fwd;
     const float *d_o, *d_final_state;  // d_final_state nullable (zero)
     float *dq, *dk, *dv, *dlog_alpha, *dbeta;
     float *d_init_state;               // nullable
     float *chunk_states, *chunk_dstates, *scratch;
+    float *checkpoints, *dcarry;
+    int64_t seg_slots;
 };
 constexpr int kBwdMaxGroups = 1024;    // persistent workgroups of the gradient kernel
 constexpr int kBwdScratchMats = 10;    // fp32 [C][D] scratch matrices per workgroup
+// (chunk, head) items per backward segment: 16384 keeps every pass of a
+// segment wide enough to fill the chip (64 items per compute unit) while the
+// segment's buffers stay a few GB at d = 128
+constexpr int64_t kBwdSegmentItems = 16384;
+inline int64_t bwd_segment_slots(int32_t H) { return (kBwdSegmentItems + H - 1) / H; }
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
 
@@ -152,6 +166,9 @@ hipError_t noalloc_scratch(void **ptr);
 // Chunk size the kernels use for a requested one (the fp32 path at d = 128 is
 // limited to 32 tokens by LDS capacity).  Results do not depend on it beyond
 // rounding.
-int prefill_effective_chunk(int C, int Dk, int Dv, bool bf16);
+inline int prefill_effective_chunk(int C, int Dk, int Dv, bool bf16) {
+    if (!bf16 && (Dk > 64 || Dv > 64) && C > 32) return 32;
+    return C;
+}
 
 }  // namespace kda

@@ -217,7 +217,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
 
     // work items are visited in order; varlen grids end with empty slots, so
     // the first empty slot ends the walk
-    int64_t item = blockIdx.x;
+    int64_t item = p.item0 + blockIdx.x;
     int64_t tok0;
     int nvalid;
     int64_t slot, h0;
@@ -236,7 +236,7 @@ intra_wide_kernel(IntraParams p, int64_t n_items) {
         const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int t16 = lane & 15, kg = lane >> 4;
         uint16_t *xb = reinterpret_cast<uint16_t *>(smem + kApBytes + w * kXBytes);  // [2][32][kXS]
-        char *pkg = p.ws + static_cast<size_t>(item) * p.pkg_bytes;
+        char *pkg = p.ws + static_cast<size_t>(item - p.item0) * p.pkg_bytes;
 
         // ---- unpack this lane's tokens and channels (tokens >= nvalid are zeros)
         uint32_t kr[4][4], qr[4][4], vr[4][4];
@@ -759,14 +759,14 @@ static hipError_t launch_intra_wide_t(const IntraParams &p, int64_t n_items, hip
             nb = 1;
         per_cu = nb;
     }
-    const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
+    const int64_t grid = std::min<int64_t>(n_items - p.item0, static_cast<int64_t>(device_cu_count()) * per_cu);
     hipLaunchKernelGGL(intra_wide_kernel<GM>, dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0, stream,
                        p, n_items);
     return hipGetLastError();
 }
 
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream) {
-    if (n_items <= 0) return hipSuccess;
+    if (n_items <= p.item0) return hipSuccess;
     switch (p.gate_mode) {
         case 0: return launch_intra_wide_t<0>(p, n_items, stream);
         case 1: return launch_intra_wide_t<1>(p, n_items, stream);

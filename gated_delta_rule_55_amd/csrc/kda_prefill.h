@@ -32,6 +32,9 @@ struct IntraParams {
     int32_t gate_mode;
     const uint16_t *x_alpha, *x_beta;
     float l2_eps;
+    // the kernels walk items [item0, n_items) (item = slot * H + head) and
+    // write item's package at ws + (item - item0) * pkg_bytes
+    int64_t item0 = 0;
 };
 
 struct StateParams {
@@ -44,6 +47,16 @@ struct StateParams {
     const char *ws;
     size_t pkg_bytes;
     PackageLayout L;
+    // Chunk slots [s0, s1) only (the backward's segments; the prefill takes
+    // them all).  Slot X's package is at ws + ((X - s0) H + h) pkg_bytes and its
+    // saved state at chunk_states + ((X - s0) H + h) Dk Dv.  A sequence that
+    // begins before s0 starts from carry_in[h]; one that goes on past s1 leaves
+    // the state entering slot s1 in carry_out[h] (nullable).  A sequence with
+    // no tokens is handled only where do_empty is set.
+    int64_t s0 = 0, s1 = INT64_MAX;
+    const float *carry_in = nullptr;
+    float *carry_out = nullptr;
+    bool do_empty = true;
 };
 
 struct BwdStateParams {
@@ -56,6 +69,14 @@ struct BwdStateParams {
     const float *d_o, *d_final;  // d_final nullable
     float *chunk_dstates;
     float *d_init;               // nullable
+    // chunk slots [s0, s1), as in StateParams, walked backwards: a sequence
+    // that goes on past s1 starts from dcarry_in[h] (the gradient of the state
+    // entering slot s1); one that begins before s0 leaves the gradient of the
+    // state entering slot s0 in dcarry_out[h]
+    int64_t s0 = 0, s1 = INT64_MAX;
+    const float *dcarry_in = nullptr;
+    float *dcarry_out = nullptr;
+    bool do_empty = true;
 };
 
 struct BwdIntraParams {
@@ -67,6 +88,9 @@ struct BwdIntraParams {
     const float *d_o, *chunk_states, *chunk_dstates;
     float *scratch;
     float *dq, *dk, *dv, *dlog_alpha, *dbeta;
+    // items [item0, n_items); the states of item's chunk slot X at
+    // chunk_states + ((X - s0) H + h) D D (and chunk_dstates alike)
+    int64_t item0 = 0, s0 = 0;
 };
 
 template <int C, int DK, int DV, bool BF>
@@ -202,12 +226,24 @@ inline int device_cu_count() {
 // d_k = d_v = 128 with bf16 inputs (kda_intra_wide.hip).
 hipError_t launch_intra_wide(const IntraParams &p, int64_t n_items, hipStream_t stream);
 
-// The forward's intra-chunk pass (packages in a.workspace) followed by the
-// state pass in its saving variant: the state entering every chunk is written
-// to chunk_states [slots, H, DK, DV] fp32 and no output is produced
-// (kda_prefill.hip; instantiated for the shapes the backward supports).
+// One segment of the backward's forward pass: chunk slots [s0, s1) of every
+// sequence.  With intra set, their packages are made first (into pkgs, slot
+// s0's first; plan: also the varlen plan); then the state pass in its saving
+// variant walks them, writing the state entering each chunk to chunk_states
+// ([s1 - s0, H, DK, DV] fp32, nullable) and no output.  carry_in / carry_out
+// hold, per head, the state entering slot s0 / s1 of a sequence that crosses
+// that boundary (see StateParams).  kda_prefill.hip; instantiated for the
+// shapes the backward supports.
+struct FwdSegment {
+    int64_t s0, s1;
+    char *pkgs;
+    bool intra, plan, do_empty;
+    const float *carry_in;
+    float *carry_out;
+    float *chunk_states;
+};
 template <int C, int DK, int DV, bool BF>
-hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipStream_t stream);
+hipError_t launch_forward_segment(const PrefillArgs &a, const FwdSegment &g, hipStream_t stream);
 
 // chunk_offsets[n] = sum_{m<n} ceil(len_m / C) for varlen batches, on the device
 hipError_t launch_plan(const int32_t *cu_seqlens, int32_t N, int C, int32_t *chunk_offsets, hipStream_t stream);

@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(kIntraThreads) intra_kernel(IntraParams p, int
     const int l16 = lane & 15, kg = lane >> 4;
     const int cc = tid % DK, seg = tid / DK;
 
-    int64_t item = blockIdx.x;
+    int64_t item = p.item0 + blockIdx.x;
     const int64_t stride = gridDim.x;
     for (; item < n_items; item += stride) {
       const int64_t item_next = item + stride;
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kIntraThreads) intra_kernel(IntraParams p, int
         float gr[TPS];
 #pragma unroll
         for (int u = 0; u < TPS; ++u) gr[u] = cur.g[u];
-        char *pkg = p.ws + static_cast<size_t>(item) * p.pkg_bytes;
+        char *pkg = p.ws + static_cast<size_t>(item - p.item0) * p.pkg_bytes;
         __syncthreads();  // the previous chunk's LDS reads are done
 
     // ---- 1. stage k, q, v in LDS from registers (rows >= nvalid hold zeros)
@@ -756,8 +756,12 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
         slot_base = static_cast<int64_t>(n) * ((p.T + C - 1) / C);
     }
     const int64_t nchunks = (L + C - 1) / C;
+    // this launch's chunks of the sequence: [cb, ce)
+    const int64_t cb = p.s0 > slot_base ? p.s0 - slot_base : 0;
+    const int64_t ce = p.s1 - slot_base < nchunks ? p.s1 - slot_base : nchunks;
+    if (nchunks == 0 ? !p.do_empty : cb >= ce) return;
     auto pkg_of = [&](int64_t c) {
-        return p.ws + (static_cast<size_t>(slot_base + c) * H + h) * p.pkg_bytes;
+        return p.ws + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * p.pkg_bytes;
     };
 
     for (int idx = tid; idx < 16 * SSS; idx += 256) (&sS[0][0])[idx] = static_cast<Op>(0.f);
@@ -765,6 +769,9 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 
     const int col = 16 * ct + l16;
     const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+    // the state entering chunk cb: the initial state, or the one carried in
+    const float *s_in = cb == 0 ? (p.init_state ? p.init_state + sbase : nullptr)
+                                : p.carry_in + static_cast<size_t>(h) * DK * DV;
     f32x4 S[SPW];
 #pragma unroll
     for (int sl = 0; sl < SPW; ++sl) {
@@ -772,8 +779,7 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * tk + 4 * kg + r;
-            S[sl][r] = (tk < NTK && p.init_state) ? p.init_state[sbase + static_cast<size_t>(row) * DV + col]
-                                                   : 0.f;
+            S[sl][r] = (tk < NTK && s_in) ? s_in[static_cast<size_t>(row) * DV + col] : 0.f;
         }
     }
     __syncthreads();
@@ -802,7 +808,8 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
         const int64_t rem = L - c * C;
         const int nvalid = static_cast<int>(rem < C ? rem : C);
         if constexpr (SAVE) {
-            float *cs = p.chunk_states + (static_cast<size_t>(slot_base + c) * H + h) * DK * DV;
+          if (p.chunk_states) {
+            float *cs = p.chunk_states + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * DK * DV;
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl) {
                 const int tk = w + 4 * sl;
@@ -811,6 +818,7 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
                     for (int r = 0; r < 4; ++r) cs[static_cast<size_t>(16 * tk + 4 * kg + r) * DV + col] = S[sl][r];
                 }
             }
+          }
         }
         __syncthreads();  // sS holds this chunk's incoming state
 
@@ -895,12 +903,12 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
     // its loads are in flight)
     using Full = std::false_type;
     using Part = std::true_type;
-    const int64_t nfull = L / C;  // chunks with C valid tokens
+    const int64_t nfull = L / C < ce ? L / C : ce;  // chunks with C valid tokens
     Frags f0, f1, f2;
     auto load = [&](Frags &f, int64_t cc) { f.load(pkg_of(cc), p.L, w, lane, ct); };
-    if (nchunks > 0) load(f0, 0);
-    if (nchunks > 1) load(f1, 1);
-    int64_t c = 0;
+    if (ce > cb) load(f0, cb);
+    if (ce > cb + 1) load(f1, cb + 1);
+    int64_t c = cb;
     for (; c + 4 < nfull; c += 3) {  // chunks c .. c + 2 are full; c + 3 and c + 4 exist
         load(f2, c + 2);
         step(f0, c, Full{});
@@ -910,15 +918,18 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
         step(f2, c + 2, Full{});
     }
     // tail: f0 holds chunk c and f1 chunk c + 1 (when it exists)
-    for (; c < nchunks; ++c) {
-        if (c + 2 < nchunks) load(f2, c + 2);
+    for (; c < ce; ++c) {
+        if (c + 2 < ce) load(f2, c + 2);
         if (c < nfull) step(f0, c, Full{});
         else step(f0, c, Part{});
         f0 = f1;
         f1 = f2;
     }
 
-    if (p.final_state) {
+    // the state leaving chunk ce - 1: the final state, or the one carried out
+    float *s_out = ce == nchunks ? (p.final_state ? p.final_state + sbase : nullptr)
+                                 : (p.carry_out ? p.carry_out + static_cast<size_t>(h) * DK * DV : nullptr);
+    if (s_out) {
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl) {
             const int tk = w + 4 * sl;
@@ -926,7 +937,7 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * tk + 4 * kg + r;
-                p.final_state[sbase + static_cast<size_t>(row) * DV + col] = S[sl][r];
+                s_out[static_cast<size_t>(row) * DV + col] = S[sl][r];
             }
         }
     }
@@ -945,22 +956,25 @@ __global__ void __launch_bounds__(256) dplr_state_kernel(StateParams p) {
 // -----------------------------------------------------------------------------
 // launch
 // -----------------------------------------------------------------------------
-// The intra-chunk pass: every (chunk, head) package into a.workspace.
+// The intra-chunk pass: the packages of chunk slots [s0, s1) (every head) into
+// pkgs, slot s0's first (the prefill: every slot, into a.workspace).  The
+// varlen plan is made only where plan is set.
 template <int C, int DK, int DV, bool BF>
-static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream) {
+static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream, int64_t s0, int64_t s1, char *pkgs,
+                                 bool plan) {
     const PackageLayout L = package_layout(C, DK, DV, BF);
-    if (a.cu_seqlens) {
+    if (a.cu_seqlens && plan) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.N, C,
                            a.chunk_offsets);
     }
-    if (a.n_slots > 0) {
+    if (s1 > s0) {
         IntraParams ip{a.q, a.k, a.v, a.log_alpha, a.beta, a.cu_seqlens, a.chunk_offsets,
-                       a.T, a.H, a.N, a.workspace, a.pkg_bytes, L,
+                       a.T, a.H, a.N, pkgs, a.pkg_bytes, L,
                        a.gate_mode == 1 ? 1 : DK, a.gate_mode == 1 ? 0 : 1,
-                       a.gate_mode, a.x_alpha, a.x_beta, a.l2_eps};
+                       a.gate_mode, a.x_alpha, a.x_beta, a.l2_eps, s0 * a.H};
         // persistent: a few workgroups per compute unit walk the (chunk, head)
         // items, each loading the next item's inputs while computing one
-        const int64_t n_items = a.n_slots * a.H;
+        const int64_t n_items = s1 * a.H;
         if constexpr (C == 64 && DK == 128 && DV == 128 && BF) {
             const hipError_t e = launch_intra_wide(ip, n_items, stream);
             if (e != hipSuccess) return e;
@@ -974,7 +988,7 @@ static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream) {
                 nb = 1;
             per_cu = nb;
         }
-        const int64_t grid = std::min<int64_t>(n_items, static_cast<int64_t>(device_cu_count()) * per_cu);
+        const int64_t grid = std::min<int64_t>((s1 - s0) * a.H, static_cast<int64_t>(device_cu_count()) * per_cu);
         hipLaunchKernelGGL((intra_kernel<C, DK, DV, BF>), dim3(static_cast<unsigned>(grid)), dim3(kIntraThreads), 0,
                            stream, ip, n_items);
         }
@@ -984,7 +998,7 @@ static hipError_t launch_intra_t(const PrefillArgs &a, hipStream_t stream) {
 
 template <int C, int DK, int DV, bool BF>
 static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
-    const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream);
+    const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream, 0, a.n_slots, a.workspace, true);
     if (ei != hipSuccess) return ei;
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state, nullptr,
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
@@ -999,11 +1013,14 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
 }
 
 template <int C, int DK, int DV, bool BF>
-hipError_t launch_forward_states(const PrefillArgs &a, float *chunk_states, hipStream_t stream) {
-    const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream);
-    if (ei != hipSuccess) return ei;
-    StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, nullptr, nullptr, chunk_states,
-                   a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
+hipError_t launch_forward_segment(const PrefillArgs &a, const FwdSegment &g, hipStream_t stream) {
+    if (g.intra) {
+        const hipError_t ei = launch_intra_t<C, DK, DV, BF>(a, stream, g.s0, g.s1, g.pkgs, g.plan);
+        if (ei != hipSuccess) return ei;
+    }
+    StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, nullptr, nullptr, g.chunk_states,
+                   a.T, a.H, a.N, g.pkgs, a.pkg_bytes, package_layout(C, DK, DV, BF),
+                   g.s0, g.s1, g.carry_in, g.carry_out, g.do_empty};
     hipLaunchKernelGGL((state_kernel<C, DK, DV, BF, true>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
@@ -1023,7 +1040,7 @@ template hipError_t launch_dplr_state<64, 128, true>(const StateParams &, hipStr
 
 // the shapes the backward supports: d_k = d_v, the chunk the forward uses
 #define KDA_FWD_STATES(C, D, BF) \
-    template hipError_t launch_forward_states<C, D, D, BF>(const PrefillArgs &, float *, hipStream_t);
+    template hipError_t launch_forward_segment<C, D, D, BF>(const PrefillArgs &, const FwdSegment &, hipStream_t);
 KDA_FWD_STATES(16, 16, true) KDA_FWD_STATES(16, 32, true) KDA_FWD_STATES(16, 64, true) KDA_FWD_STATES(16, 128, true)
 KDA_FWD_STATES(32, 16, true) KDA_FWD_STATES(32, 32, true) KDA_FWD_STATES(32, 64, true) KDA_FWD_STATES(32, 128, true)
 KDA_FWD_STATES(64, 16, true) KDA_FWD_STATES(64, 32, true) KDA_FWD_STATES(64, 64, true) KDA_FWD_STATES(64, 128, true)
@@ -1058,11 +1075,6 @@ static hipError_t dispatch_d(const PrefillArgs &a, hipStream_t s) {
             else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
-}
-
-int prefill_effective_chunk(int C, int Dk, int Dv, bool bf16) {
-    if (!bf16 && (Dk > 64 || Dv > 64) && C > 32) return 32;
-    return C;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

@@ -229,12 +229,24 @@ def test_layer_decode_rejects(lib):
 
 def test_bwd_workspace_size(lib):
     fws, bws = lib.kda_chunk_fwd_workspace_size, lib.kda_chunk_bwd_workspace_size
-    # the forward's packages, two fp32 states per (chunk, head), a fixed scratch
+    st = 32 * 128 * 128 * 4  # one fp32 state per head, H = 32, d = 128
+    # within one segment (16384 (chunk, head) items: 512 chunks at H = 32) the
+    # workspace holds every chunk's package and two fp32 states per (chunk, head)
     a = bws(1, 4096, 32, 128, 128, 0, BF16, 64)
     b = bws(1, 8192, 32, 128, 128, 0, BF16, 64)
-    states = 2 * 64 * 32 * 128 * 128 * 4  # 64 more chunks of 32 heads
-    assert b - a == (fws(1, 8192, 32, 128, 128, 0, BF16, 64) - fws(1, 4096, 32, 128, 128, 0, BF16, 64)) + states
-    assert a > fws(1, 4096, 32, 128, 128, 0, BF16, 64) + 2 * 64 * 32 * 128 * 128 * 4
+    assert b - a == (fws(1, 8192, 32, 128, 128, 0, BF16, 64) - fws(1, 4096, 32, 128, 128, 0, BF16, 64)) + 2 * 64 * st
+    assert a > fws(1, 4096, 32, 128, 128, 0, BF16, 64) + 2 * 64 * st
+    # past one segment it holds one segment's packages and states, one
+    # checkpoint per further segment and two carries: 1M tokens are 32
+    # segments of 512 chunks, 2M tokens 64
+    seg = bws(1, 512 * 64, 32, 128, 128, 0, BF16, 64)
+    m1 = bws(1, 1 << 20, 32, 128, 128, 0, BF16, 64)
+    m2 = bws(1, 1 << 21, 32, 128, 128, 0, BF16, 64)
+    assert m1 == seg + 31 * st + 2 * st
+    assert m2 - m1 == 32 * st
+    assert m1 < 5 * 2**30 < fws(1, 1 << 20, 32, 128, 128, 0, BF16, 64)
+    # the segment is 16384 items at any H: H = 64 takes 256 chunks per segment
+    assert bws(1, 1 << 20, 64, 128, 128, 0, BF16, 64) == bws(1, 256 * 64, 64, 128, 128, 0, BF16, 64) + 65 * 2 * st
     for bad in [(1, 64, 1, 16, 32, 0, BF16, 16), (1, 64, 1, 24, 24, 0, BF16, 16), (1, 64, 1, 16, 16, 0, BF16, 48),
                 (0, 64, 1, 16, 16, 0, BF16, 16), (1, 64, 1, 16, 16, 0, 7, 16)]:
         assert bws(*bad) == 0, bad

@@ -165,3 +165,59 @@ def test_bwd_state_gradient_chains_across_a_split():
         whole = host64(full[i])
         assert_parity(torch.cat([g1[i], g2[i]], dim=1), whole, tau, f"bwd split {name}")
     assert_parity(g1[5], host64(full[5]), tau, "bwd split d_init_state")
+
+
+def _heads(inp, heads):
+    """The same inputs restricted to a few heads (heads are independent)."""
+    out = dict(inp)
+    for n in ("q", "k", "v", "log_alpha", "beta"):
+        out[n] = inp[n][:, :, heads].contiguous()
+    if inp["init_state"] is not None:
+        out["init_state"] = inp["init_state"][:, heads].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("f32", 32, 32)])
+def test_bwd_segments_match_one_pass(dtype, D, C):
+    """At H = 4096 a backward segment is 4 chunk slots (16384 (chunk, head)
+    items), so these packed sequences cross segment boundaries, one of them
+    twice, with an empty sequence among them; each segment is recomputed from
+    its checkpoint.  The gradients of four heads equal, bit for bit, those of
+    the same heads run alone (H = 4, one segment), and match the oracle."""
+    H = 4096
+    lens = [130, 0, 1, 520, 64, 251] if C == 64 else [100, 0, 33, 300, 20, 97]
+    log(f"bwd segments dtype={dtype} D={D} C={C} H={H} lengths={lens}")
+    inp = workloads.make_prefill("varlen", "cuda", seed=61, H=H, lengths=lens, dtype=dtype)
+    if D != 128:
+        inp = _shrink(inp, D)
+    g = torch.Generator(device="cuda").manual_seed(62)
+    inp["init_state"] = 0.02 * torch.randn((len(lens), H, D, D), device="cuda", generator=g)
+    d_o, dsf = _cotangents(inp, 63)
+    seg = _run(inp, d_o, dsf, C)
+    heads = [0, 1, 2049, H - 1]
+    sub = _heads(inp, heads)
+    one = _run(sub, d_o[:, :, heads].contiguous(), dsf[:, heads].contiguous(), C)
+    for i, name in enumerate(NAMES):
+        x = seg[i][:, heads] if name == "d_init_state" else seg[i][:, :, heads]
+        assert torch.equal(x, one[i]), f"{name}: segmented and one-pass gradients differ"
+    del seg
+    _check(sub, one, d_o[:, :, heads].contiguous(), dsf[:, heads].contiguous(),
+           TAU[torch.bfloat16 if dtype == "bf16" else torch.float32], label=f"bwd segments {dtype}")
+
+
+def test_bwd_long_workload_sampled_heads():
+    """The first 262,144 tokens of the 1M-token workload (H = 32, d = 128,
+    bf16; 8 segments of 512 chunks): every gradient of four heads against the
+    oracle, each head over all 262,144 tokens."""
+    T_B = 1 << 18
+    log(f"bwd long workload T={T_B} H=32, heads 0 11 22 31")
+    full = workloads.make_prefill("long", "cuda", seed=0)
+    inp = {n: full[n][:, :T_B].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+    del full
+    inp.update(init_state=None, cu_seqlens=None, N=1)
+    d_o, _ = _cotangents(inp, 71, with_final=False)
+    grads = _run(inp, d_o, None, 64)
+    for x in grads[:5]:
+        assert torch.isfinite(x).all()
+    heads = [0, 11, 22, 31]
+    _check(inp, grads, d_o, None, TAU[torch.bfloat16], heads=heads, label="bwd long")
