@@ -13,7 +13,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkda.so")
+# KDA_LIBRARY names another build of the library to load instead of the
+# in-tree one (e.g. a host-only build of the argument checks under the
+# sanitizers)
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None

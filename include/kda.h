@@ -43,8 +43,13 @@
  *   - Numerical preconditions: log_alpha <= 0 (alpha in [0,1]); q and k are
  *     expected L2-normalised as the KDA layer produces them (not checked);
  *     NaN inputs propagate.  On the bf16 path the state and the per-chunk
- *     innovation U = beta (v - ...) are fed to fp16 matrix cores and must stay
- *     below 65504 in magnitude.  A log_alpha of -inf on every channel of a
+ *     innovation U = beta (v - ...) are fed to fp16 matrix cores: above 65504
+ *     in magnitude they overflow (the output is not finite), and where the
+ *     whole state is below about 1e-4 they lose precision to fp16's subnormal
+ *     range.  On the tested workloads (unit q and k, v ~ N(0, 1) times s,
+ *     slow decay) the stated accuracy holds for s from 2^-10 to 2^14 and
+ *     s = 2^15 overflows.  The fp32-input path has
+ *     fp32's range.  A log_alpha of -inf on every channel of a
  *     token is an exact state reset; -inf on only some channels is taken as
  *     -88 (alpha ~ 6e-39).
  */

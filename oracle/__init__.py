@@ -56,7 +56,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIBRARY: another build of kda_oracle.c to load (the sanitizer test)
+_LIB = os.environ.get("KDA_ORACLE_LIBRARY") or os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 

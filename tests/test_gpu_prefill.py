@@ -345,3 +345,29 @@ def test_degenerate_token_values(dtype):
     o, fs = _gpu(inp)
     _check(inp, o, fs, TAU[torch.bfloat16 if dtype == "bf16" else torch.float32], label=f"degenerate {dtype}")
     assert torch.all(o[0, 60:70, 1] == 0)
+
+
+@pytest.mark.parametrize("e", [-10, -8, 7, 10, 14])
+def test_value_scale_within_the_fp16_operand_range(e):
+    """v (and the initial state) scaled by 2^e, exact in bf16: o and the final
+    state scale by 2^e and stay within the bound while the state and U fit
+    fp16's range (v ~ N(0,1) times 2^-10 .. 2^14; 2^7 is the "v x 100" case)."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=81, T=777, H=2, shift=-2.0)
+    inp["v"] = (inp["v"].float() * 2.0 ** e).to(torch.bfloat16)
+    inp["init_state"] = inp["init_state"] * 2.0 ** e
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label=f"v x 2^{e}")
+
+
+def test_value_scale_past_the_fp16_operand_range():
+    """At v ~ N(0,1) x 2^16 (|v| up to ~3e5), U exceeds fp16's largest finite
+    value and the bf16 path's output is not finite: the limit the header
+    states.  The fp32-input path (fp32 matrix cores throughout) is finite and
+    within its bound on the same inputs."""
+    inp = workloads.make_prefill("prefill", "cuda", seed=82, T=300, H=2, shift=-2.0, init="zeros")
+    inp["v"] = (inp["v"].float() * 2.0 ** 16).to(torch.bfloat16)
+    o, fs = _gpu(inp)
+    assert not bool(torch.isfinite(o).all())
+    f32 = {**inp, **{n: inp[n].float() for n in ("q", "k", "v")}}
+    o32, fs32 = _gpu(f32, chunk=64)
+    _check(f32, o32, fs32, TAU[torch.float32], label="fp32 path, v x 2^16")
