@@ -272,6 +272,56 @@ struct BwdFrags {
             if (x < C * 16) sdO[x / 16][x % 16] = dO[j];
         }
     }
+
+    // The 16-bit path's LDS copies, laid out as the fp16 matrix-core operands
+    // want them (8 consecutive k per lane): W^T and Q'^T [channel][token], Kt
+    // [token][channel] (the package's fp16 values as they are), and dO as an
+    // fp16 hi + lo pair [column][token].
+    template <int TS, int CS>
+    __device__ __forceinline__ void store16(_Float16 (*sWT)[TS], _Float16 (*sQT)[TS], _Float16 (*sKt)[CS], float *sGL,
+                                            _Float16 (*sdOh)[TS], _Float16 (*sdOl)[TS], int tid) const {
+        static_assert(BF, "the fp16 layout holds the 16-bit path's operands");
+        const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < WQB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NRT * KSK) {
+                const int rt = b / KSK, ks = b % KSK, i = 16 * (rt % NT16) + l16;
+                _Float16(*dst)[TS] = rt < NT16 ? sWT : sQT;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ch = 32 * ks + (e < 4 ? 4 * kg + e : 16 + 4 * kg + e - 4);
+                    if (ch < D) dst[ch][i] = wq[j].v[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KTB; ++j) {
+            const int b = w + 4 * j;
+            if (b < NTK * KSC) {
+                const int tk = b / KSC, ks = b % KSC;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 32 * ks + 8 * kg + e;
+                    if (i < C) sKt[i][16 * tk + l16] = kt[j].v[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GLE; ++j) {
+            const int x = tid + kBwdThreads * j;
+            if (x < D) sGL[x] = gl[j];
+        }
+#pragma unroll
+        for (int j = 0; j < DOE; ++j) {
+            const int x = tid + kBwdThreads * j;
+            if (x < C * 16) {
+                const _Float16 hi = static_cast<_Float16>(dO[j]);
+                sdOh[x % 16][x / 16] = hi;
+                sdOl[x % 16][x / 16] = static_cast<_Float16>(dO[j] - static_cast<float>(hi));
+            }
+        }
+    }
 };
 
 template <int C, int D, bool BF>
@@ -387,14 +437,167 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
     }
 }
 
+// The same reverse state pass on the 16-bit path with fp16 matrix cores: the
+// package's W, Q' and Kt are fp16 values already, and each fp32 right-hand
+// operand (dS1, dO, X) enters as an fp16 hi + lo pair, two products per K step
+// of 32 instead of eight fp32 ones per 4.  Channel and token dimensions below
+// 32 are padded with zeros to one K step.
+template <int C, int D>
+__global__ void __launch_bounds__(kBwdThreads) bwd_state_f16_kernel(BwdStateParams p) {
+    using Frags = BwdFrags<C, D, true>;
+    constexpr int NT16 = C / 16, NTK = D / 16;
+    constexpr int CP = C < 32 ? 32 : C, DP = D < 32 ? 32 : D;
+    constexpr int TS = CP + 8, CS = DP + 8;  // LDS row strides (fp16 elements)
+    __shared__ __align__(16) _Float16 sWT[DP][TS], sQT[DP][TS];  // [channel][token]
+    __shared__ __align__(16) _Float16 sKt[CP][CS];               // [token][channel]
+    __shared__ __align__(16) _Float16 sdSh[16][CS], sdSl[16][CS];  // dS1 [column][channel]
+    __shared__ __align__(16) _Float16 sdOh[16][TS], sdOl[16][TS];  // dO [column][token]
+    __shared__ __align__(16) _Float16 sXh[16][TS], sXl[16][TS];    // -X [column][token]
+    __shared__ float sGL[D];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
+    const int H = p.H;
+    int64_t tok_base, L, slot_base;
+    if (p.cu_seqlens) {
+        tok_base = p.cu_seqlens[n];
+        L = p.cu_seqlens[n + 1] - tok_base;
+        slot_base = p.chunk_offsets[n];
+    } else {
+        tok_base = static_cast<int64_t>(n) * p.T;
+        L = p.T;
+        slot_base = static_cast<int64_t>(n) * ((p.T + C - 1) / C);
+    }
+    const int64_t nchunks = (L + C - 1) / C;
+    const int64_t cb = p.s0 > slot_base ? p.s0 - slot_base : 0;
+    const int64_t ce = p.s1 - slot_base < nchunks ? p.s1 - slot_base : nchunks;
+    if (nchunks == 0 ? !p.do_empty : cb >= ce) return;
+    const int col = 16 * ct + l16;
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
+    auto pkg_of = [&](int64_t c) {
+        return p.ws + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * p.pkg_bytes;
+    };
+    auto nvalid_of = [&](int64_t c) { return static_cast<int>(L - c * C < C ? L - c * C : C); };
+
+    // the padding (channels >= D, tokens >= C) stays zero; the rest is
+    // rewritten every chunk
+    for (int x = tid; x < DP * TS; x += kBwdThreads) {
+        (&sWT[0][0])[x] = _Float16(0.f);
+        (&sQT[0][0])[x] = _Float16(0.f);
+    }
+    for (int x = tid; x < CP * CS; x += kBwdThreads) (&sKt[0][0])[x] = _Float16(0.f);
+    for (int x = tid; x < 16 * CS; x += kBwdThreads) (&sdSh[0][0])[x] = (&sdSl[0][0])[x] = _Float16(0.f);
+    for (int x = tid; x < 16 * TS; x += kBwdThreads) {
+        (&sdOh[0][0])[x] = (&sdOl[0][0])[x] = _Float16(0.f);
+        (&sXh[0][0])[x] = (&sXl[0][0])[x] = _Float16(0.f);
+    }
+
+    const float *ds_in = ce == nchunks ? (p.d_final ? p.d_final + sbase : nullptr)
+                                       : p.dcarry_in + static_cast<size_t>(h) * D * D;
+    constexpr int SPW = (NTK + 3) / 4;
+    f32x4 dS[SPW];
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl) {
+        const int tk = w + 4 * sl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dS[sl][r] = (tk < NTK && ds_in) ? ds_in[static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] : 0.f;
+    }
+    __syncthreads();  // the zero fill is done before any chunk's writes
+
+    Frags cur, nxt;
+    if (ce > cb) cur.load(p, pkg_of(ce - 1), tok_base + (ce - 1) * C, nvalid_of(ce - 1), ct, h, tid);
+    for (int64_t c = ce - 1; c >= cb; --c) {
+        // dS1 of this chunk: to the chunk-state buffer and, as hi + lo, to LDS
+        float *cds = p.chunk_dstates + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * D * D;
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * tk + 4 * kg + r;
+                    cds[static_cast<size_t>(row) * D + col] = dS[sl][r];
+                    const _Float16 hi = static_cast<_Float16>(dS[sl][r]);
+                    sdSh[l16][row] = hi;
+                    sdSl[l16][row] = static_cast<_Float16>(dS[sl][r] - static_cast<float>(hi));
+                }
+            }
+        }
+        cur.template store16<TS, CS>(sWT, sQT, sKt, sGL, sdOh, sdOl, tid);
+        if (c > cb) nxt.load(p, pkg_of(c - 1), tok_base + (c - 1) * C, nvalid_of(c - 1), ct, h, tid);
+        __syncthreads();
+        // -X = -(Kt dS1) (C x 16), one 16-token tile per wave, into LDS as hi + lo
+        if (w < NT16) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DP / 32; ++ks) {
+                const f16x8 a = *reinterpret_cast<const f16x8 *>(&sKt[16 * w + l16][32 * ks + 8 * kg]);
+                const f16x8 bh = *reinterpret_cast<const f16x8 *>(&sdSh[l16][32 * ks + 8 * kg]);
+                const f16x8 bl = *reinterpret_cast<const f16x8 *>(&sdSl[l16][32 * ks + 8 * kg]);
+                acc = mfma_f16(a, bl, acc);
+                acc = mfma_f16(a, bh, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = -acc[r];
+                const _Float16 hi = static_cast<_Float16>(x);
+                sXh[l16][16 * w + 4 * kg + r] = hi;
+                sXl[l16][16 * w + 4 * kg + r] = static_cast<_Float16>(x - static_cast<float>(hi));
+            }
+        }
+        __syncthreads();
+        // dS0 = Diag(Gamma_C) dS1 + Q'^T dO + W^T (-X)
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+                f32x4 acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = sGL[16 * tk + 4 * kg + r] * dS[sl][r];
+#pragma unroll
+                for (int ks = 0; ks < CP / 32; ++ks) {
+                    const f16x8 aq = *reinterpret_cast<const f16x8 *>(&sQT[16 * tk + l16][32 * ks + 8 * kg]);
+                    const f16x8 aw = *reinterpret_cast<const f16x8 *>(&sWT[16 * tk + l16][32 * ks + 8 * kg]);
+                    acc = mfma_f16(aq, *reinterpret_cast<const f16x8 *>(&sdOl[l16][32 * ks + 8 * kg]), acc);
+                    acc = mfma_f16(aw, *reinterpret_cast<const f16x8 *>(&sXl[l16][32 * ks + 8 * kg]), acc);
+                    acc = mfma_f16(aq, *reinterpret_cast<const f16x8 *>(&sdOh[l16][32 * ks + 8 * kg]), acc);
+                    acc = mfma_f16(aw, *reinterpret_cast<const f16x8 *>(&sXh[l16][32 * ks + 8 * kg]), acc);
+                }
+                dS[sl] = acc;
+            }
+        }
+        __syncthreads();  // LDS is refilled by the next (earlier) chunk
+        cur = nxt;
+    }
+    float *ds_out = cb == 0 ? (p.d_init ? p.d_init + sbase : nullptr)
+                            : (p.dcarry_out ? p.dcarry_out + static_cast<size_t>(h) * D * D : nullptr);
+    if (ds_out) {
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            const int tk = w + 4 * sl;
+            if (tk < NTK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ds_out[static_cast<size_t>(16 * tk + 4 * kg + r) * D + col] = dS[sl][r];
+            }
+        }
+    }
+}
+
 // -----------------------------------------------------------------------------
 // gradients of one (chunk, head) at a time; persistent workgroups
 // -----------------------------------------------------------------------------
 // Per-workgroup fp32 [C][D] scratch matrices in the workspace.
-enum Scratch { kKG, kQG, kKT, kR, kU, kDU, kDR, kDQ, kDK, kDG, kNumScratch };
+enum Scratch { kKG, kKT, kR, kU, kDU, kDR, kNumScratch };
 static_assert(kNumScratch == kBwdScratchMats, "scratch matrices per workgroup");
 
 constexpr int kBwdIntraThreads = 512;  // 8 waves: two per SIMD hide the products' memory latency
+// On a diagonal 16-token block the decay-weighted products go through the
+// matrix cores with the block's token 7 as the reference: a channel whose
+// cumulative log-decay spans more than this on either side of it (factors up
+// to e^40) takes the exact per-pair path instead.
+constexpr float kDiagSpan = 40.0f;
 constexpr int kIW = kBwdIntraThreads / 64;
 
 template <int C, int D, bool BF>
@@ -427,8 +630,7 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
     const int H = p.H;
     float *scr = p.scratch + static_cast<size_t>(blockIdx.x) * kNumScratch * C * D;
     auto S_ = [&](int m) { return scr + static_cast<size_t>(m) * C * D; };
-    float *KG = S_(kKG), *QG = S_(kQG), *KT = S_(kKT), *R = S_(kR), *U = S_(kU), *DU = S_(kDU), *DR = S_(kDR);
-    float *DQ = S_(kDQ), *DK = S_(kDK), *DG = S_(kDG);
+    float *KG = S_(kKG), *KT = S_(kKT), *R = S_(kR), *U = S_(kU), *DU = S_(kDU), *DR = S_(kDR);
     auto toF = [](In x) {
         if constexpr (BF) return bf16_bits_to_f32(x);
         else return x;
@@ -509,14 +711,13 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         __syncthreads();
         const int first_rst = sFirst, last_rst = sLast;
 
-        // ---- K*Gamma, Q*Gamma, Kt (scratch); Gamma_C
+        // ---- K*Gamma and Kt (scratch: left operands of the products below); Gamma_C
         for (int x = tid; x < C * D; x += kBwdIntraThreads) {
             const int i = x / D, c = x % D;
             const GT G = sG[i][c];
-            const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
+            const float kv = toF(sK[i][c]);
             const float eg = i < first_rst ? __expf(static_cast<float>(G)) : 0.f;
             KG[x] = kv * eg;
-            QG[x] = qv * eg;
             KT[x] = i >= last_rst ? kv * __expf(static_cast<float>(sG[C - 1][c] - G)) : 0.f;
         }
         for (int c = tid; c < D; c += kBwdIntraThreads)
@@ -801,36 +1002,46 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                     sM[1][i][j] = (j <= i && sCnt[i] == sCnt[j]) ? acc[r] : 0.f;
                 }
             }, lane);
+        // From here to dlog_alpha, wave w < NTD owns the 16-channel column tile w
+        // for every token and keeps dq, dk and dG of its tile in registers:
+        // element r of tile I is token 16 I + 4 (lane / 16) + r, channel
+        // 16 w + lane % 16 (the matrix cores' output layout).
+        f32x4 DQr[NTI], DKr[NTI], DGr[NTI];
         // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
         //      their Gamma terms
-                const Frag<D> bS0T = frag_of<D>([&](int k0, int nn) {
-            return ld4(S0 + static_cast<size_t>(16 * (w % NTD) + nn) * D + k0);
-        }, lane);
-        const Frag<D> bS1T = frag_of<D>([&](int k0, int nn) {
-            return ld4(dS1 + static_cast<size_t>(16 * (w % NTD) + nn) * D + k0);
-        }, lane);
-#pragma unroll 1
-        for (int t = w; t < NTI * NTD; t += kIW) {
-            const int ti = t / NTD, tc = t % NTD;
-            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
-            mm_f32_vb<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bS0T, lane);
-            mm_f32_vb<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); }, bS0T, lane);
-            mm_f32_vb<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); }, bS1T, lane);
-            float colsum = 0.f;
+        if (w < NTD) {
+            const int c = 16 * w + l16;  // this lane's channel
+            const Frag<D> bS0T = frag_of<D>([&](int k0, int nn) {
+                return ld4(S0 + static_cast<size_t>(16 * w + nn) * D + k0);
+            }, lane);
+            const Frag<D> bS1T = frag_of<D>([&](int k0, int nn) {
+                return ld4(dS1 + static_cast<size_t>(16 * w + nn) * D + k0);
+            }, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ti + 4 * kg + r, c = 16 * tc + l16;
-                const float qg = QG[i * D + c], kgm = KG[i * D + c], ktv = KT[i * D + c];
-                const float eg = i < first_rst ? __expf(static_cast<float>(sG[i][c])) : 0.f;
-                const float et = i >= last_rst ? __expf(static_cast<float>(sG[C - 1][c] - sG[i][c])) : 0.f;
-                DQ[i * D + c] = aq[r] * eg;
-                DK[i * D + c] = -ak[r] * eg + at[r] * et;
-                DG[i * D + c] = aq[r] * qg - ak[r] * kgm - at[r] * ktv;
-                colsum += at[r] * ktv;
+            for (int ti = 0; ti < NTI; ++ti) {
+                f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
+                mm_f32_vb<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bS0T, lane);
+                mm_f32_vb<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); }, bS0T, lane);
+                mm_f32_vb<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); }, bS1T, lane);
+                float colsum = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * ti + 4 * kg + r;
+                    // Q*Gamma, K*Gamma and Kt at (i, c), formed from LDS
+                    const float eg = i < first_rst ? __expf(static_cast<float>(sG[i][c])) : 0.f;
+                    const float et = i >= last_rst ? __expf(static_cast<float>(sG[C - 1][c] - sG[i][c])) : 0.f;
+                    const float kv = toF(sK[i][c]);
+                    const float qg = i < first_rst ? toF(sQ[i][c]) * eg : 0.f, kgm = i < first_rst ? kv * eg : 0.f;
+                    const float ktv = i >= last_rst ? kv * et : 0.f;
+                    DQr[ti][r] = aq[r] * eg;
+                    DKr[ti][r] = -ak[r] * eg + at[r] * et;
+                    DGr[ti][r] = aq[r] * qg - ak[r] * kgm - at[r] * ktv;
+                    colsum += at[r] * ktv;
+                }
+                colsum += __shfl_xor(colsum, 16);
+                colsum += __shfl_xor(colsum, 32);
+                if (kg == 0) sPart3[ti][c] = colsum;
             }
-            colsum += __shfl_xor(colsum, 16);
-            colsum += __shfl_xor(colsum, 32);
-            if (kg == 0) sPart3[ti][16 * tc + l16] = colsum;
         }
         __syncthreads();
         // dG of the chunk's last token: dKt terms and dGamma_C = rowsum(S0 * dS1),
@@ -847,134 +1058,159 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                 sdGL[c] = acc;
             }
         }
-        // ---- the decay-weighted products of the blocks below the diagonal, on the
-        //      fp32 matrix cores.  For 16-token blocks I > J and the reference m =
-        //      the last token of J, e^{G_i - G_j} = e^{G_i - G_m} e^{G_m - G_j}
-        //      with both factors <= 1, so (dM = dP with X = Q, dM = dAbar with X = K)
+        __syncthreads();  // sdGL complete
+        // ---- the decay-weighted products e^{G_i - G_j} of dP (with q_i, k_j) and
+        //      dAbar (with k_i, k_j), on the fp32 matrix cores, one 16-token block
+        //      pair (I >= J) at a time.  With a reference token m,
+        //      e^{G_i - G_j} = e^{G_i - G_m} e^{G_m - G_j}, so (dM = dP with X = Q,
+        //      dM = dAbar with X = K)
         //        row sums of block I    += e^{G_I - G_m} * (dM_IJ (e^{G_m - G_J} * K_J))
         //        column sums of block J += e^{G_m - G_J} * (dM_IJ^T (e^{G_I - G_m} * X_I)).
-        //      A wave owns a 16-channel column tile for every token, so it adds its
-        //      sums into DQ, DK and DG alone and in a fixed order.
-        for (int td = w; td < NTD; td += kIW) {
-            const int c = 16 * td + l16;  // this lane's channel
-            f32x4 rP[NTI], rA[NTI];
+        //      Below the diagonal m is the last token of J and both factors are
+        //      <= 1.  On the diagonal m is the block's token 7 and the factors
+        //      are bounded by e^{half-span}; a channel whose half-span there
+        //      exceeds kDiagSpan takes the exact exponential of every pair
+        //      instead (its matrix-core operands are zero), and so does every
+        //      channel on the fp32-input path, where the two-factor form's extra
+        //      rounding would be a visible part of the tighter bound.
+        if (w < NTD) {
+            const int c = 16 * w + l16;  // this lane's channel
+            f32x4 rP[NTI], rA[NTI], cS[NTI];  // row sums of dP, dAbar; column sums of both
 #pragma unroll
-            for (int I = 0; I < NTI; ++I) rP[I] = rA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int I = 0; I < NTI; ++I) rP[I] = rA[I] = cS[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int J = 0; J + 1 < NTI; ++J) {
-                const int m = 16 * J + 15;
-                const GT Gm = sG[m][c];
-                f32x4 cP = {0.f, 0.f, 0.f, 0.f}, cA = cP;  // block J's column sums: complete after the I loop
-                float ys[4];  // e^{G_m - G_j} k_j at j = 16 J + 4 s + lane / 16
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int j = 16 * J + 4 * s4 + kg;
-                    ys[s4] = __expf(static_cast<float>(Gm - sG[j][c])) * toF(sK[j][c]);
-                }
-#pragma unroll
-                for (int I = J + 1; I < NTI; ++I) {
-                    f32x4 zp = {0.f, 0.f, 0.f, 0.f}, za = zp, wp = zp, wa = zp;
-                    float xq[4], xk[4];  // e^{G_i - G_m} q_i, k_i at i = 16 I + 4 s + lane / 16
+            for (int J = 0; J < NTI; ++J) {
+                // diagonal block J
+                {
+                    const int m = 16 * J + 7;
+                    const GT Gm = sG[m][c];
+                    const bool safe = BF && sG[16 * J][c] - Gm <= GT(kDiagSpan) && Gm - sG[16 * J + 15][c] <= GT(kDiagSpan);
+                    float ys[4], xq[4], xk[4];
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) {
-                        const int i = 16 * I + 4 * s4 + kg;
-                        const float f = __expf(static_cast<float>(sG[i][c] - Gm));
-                        xq[s4] = f * toF(sQ[i][c]);
-                        xk[s4] = f * toF(sK[i][c]);
+                        const int j = 16 * J + 4 * s4 + kg;
+                        const float kj = toF(sK[j][c]);
+                        const float fb = safe ? __expf(static_cast<float>(Gm - sG[j][c])) : 0.f;
+                        const float fa = safe ? __expf(static_cast<float>(sG[j][c] - Gm)) : 0.f;
+                        ys[s4] = fb * kj;
+                        xq[s4] = fa * toF(sQ[j][c]);
+                        xk[s4] = fa * kj;
                     }
+                    f32x4 zp = {0.f, 0.f, 0.f, 0.f}, za = zp, wp = zp, wa = zp;
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) {
-                        zp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], zp, 0,
-                                                                  0, 0);
-                        za = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], za, 0,
-                                                                  0, 0);
-                        wp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + 4 * s4 + kg][16 * J + l16], xq[s4], wp, 0,
-                                                                  0, 0);
-                        wa = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + 4 * s4 + kg][16 * J + l16], xk[s4], wa, 0,
-                                                                  0, 0);
+                        zp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * J + l16][16 * J + 4 * s4 + kg], ys[s4], zp, 0, 0, 0);
+                        za = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * J + l16][16 * J + 4 * s4 + kg], ys[s4], za, 0, 0, 0);
+                        wp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * J + 4 * s4 + kg][16 * J + l16], xq[s4], wp, 0, 0, 0);
+                        wa = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * J + 4 * s4 + kg][16 * J + l16], xk[s4], wa, 0, 0, 0);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float ei = __expf(static_cast<float>(sG[16 * I + 4 * kg + r][c] - Gm));
-                        const float ej = __expf(static_cast<float>(Gm - sG[16 * J + 4 * kg + r][c]));
-                        rP[I][r] += ei * zp[r];
-                        rA[I][r] += ei * za[r];
-                        cP[r] += ej * wp[r];
-                        cA[r] += ej * wa[r];
+                        const int i = 16 * J + 4 * kg + r;
+                        const float ei = safe ? __expf(static_cast<float>(sG[i][c] - Gm)) : 0.f;
+                        const float ej = safe ? __expf(static_cast<float>(Gm - sG[i][c])) : 0.f;
+                        rP[J][r] += ei * zp[r];
+                        rA[J][r] += ei * za[r];
+                        cS[J][r] += ej * (wp[r] + wa[r]);
+                    }
+                    if (!safe) {  // rare: every pair of the block with its exact decay
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = 16 * J + 4 * kg + r, i0 = 16 * J;
+                            const GT Gi = sG[i][c];
+                            float rowP = 0.f, rowA = 0.f, col = 0.f;
+                            for (int j = i0; j <= i; ++j) {
+                                const float e = __expf(static_cast<float>(Gi - sG[j][c])) * toF(sK[j][c]);
+                                rowP += sM[1][i][j] * e;
+                                rowA += sM[3][i][j] * e;
+                            }
+                            for (int mm = i; mm < i0 + 16; ++mm) {
+                                const float e = __expf(static_cast<float>(sG[mm][c] - Gi));
+                                col += sM[1][mm][i] * e * toF(sQ[mm][c]) + sM[3][mm][i] * e * toF(sK[mm][c]);
+                            }
+                            rP[J][r] += rowP;
+                            rA[J][r] += rowA;
+                            cS[J][r] += col;
+                        }
                     }
                 }
+                // the blocks below it
+                if (J + 1 < NTI) {
+                    const int m = 16 * J + 15;
+                    const GT Gm = sG[m][c];
+                    float ys[4];  // e^{G_m - G_j} k_j at j = 16 J + 4 s + lane / 16
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * J + 4 * kg + r;
-                    DK[j * D + c] += cP[r] + cA[r];
-                    DG[j * D + c] -= toF(sK[j][c]) * (cP[r] + cA[r]);
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int j = 16 * J + 4 * s4 + kg;
+                        ys[s4] = __expf(static_cast<float>(Gm - sG[j][c])) * toF(sK[j][c]);
+                    }
+#pragma unroll
+                    for (int I = J + 1; I < NTI; ++I) {
+                        f32x4 zp = {0.f, 0.f, 0.f, 0.f}, za = zp, wp = zp, wa = zp;
+                        float xq[4], xk[4];  // e^{G_i - G_m} q_i, k_i at i = 16 I + 4 s + lane / 16
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            const int i = 16 * I + 4 * s4 + kg;
+                            const float f = __expf(static_cast<float>(sG[i][c] - Gm));
+                            xq[s4] = f * toF(sQ[i][c]);
+                            xk[s4] = f * toF(sK[i][c]);
+                        }
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            zp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], zp, 0, 0, 0);
+                            za = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + l16][16 * J + 4 * s4 + kg], ys[s4], za, 0, 0, 0);
+                            wp = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[1][16 * I + 4 * s4 + kg][16 * J + l16], xq[s4], wp, 0, 0, 0);
+                            wa = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[3][16 * I + 4 * s4 + kg][16 * J + l16], xk[s4], wa, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float ei = __expf(static_cast<float>(sG[16 * I + 4 * kg + r][c] - Gm));
+                            const float ej = __expf(static_cast<float>(Gm - sG[16 * J + 4 * kg + r][c]));
+                            rP[I][r] += ei * zp[r];
+                            rA[I][r] += ei * za[r];
+                            cS[J][r] += ej * (wp[r] + wa[r]);
+                        }
+                    }
                 }
             }
+            // dq, dk out; dG
 #pragma unroll
-            for (int I = 1; I < NTI; ++I)
+            for (int I = 0; I < NTI; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * I + 4 * kg + r;
                     const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
-                    DQ[i * D + c] += rP[I][r];
-                    DK[i * D + c] += rA[I][r];
-                    DG[i * D + c] += qv * rP[I][r] + kv * rA[I][r];
+                    const float dq = DQr[I][r] + rP[I][r], dk = DKr[I][r] + rA[I][r] + cS[I][r];
+                    DGr[I][r] += qv * rP[I][r] + kv * rA[I][r] - kv * cS[I][r];
+                    if (i < nvalid) {
+                        p.dq[row_of(i) * D + c] = dq;
+                        p.dk[row_of(i) * D + c] = dk;
+                    }
                 }
-        }
-        __syncthreads();
-        // ---- the diagonal blocks' decay-weighted products, exact decay per term;
-        //      dq, dk out
-        for (int x = tid; x < C * D; x += kBwdIntraThreads) {
-            const int i = x / D, c = x % D, i0 = i & ~15;
-            const GT Gi = sG[i][c];
-            float rowP = 0.f, rowA = 0.f, colP = 0.f, colA = 0.f;
-#pragma unroll 4
-            for (int j = i0; j <= i; ++j) {
-                const float e = __expf(static_cast<float>(Gi - sG[j][c])) * toF(sK[j][c]);
-                rowP += sM[1][i][j] * e;
-                rowA += sM[3][i][j] * e;
-            }
-#pragma unroll 4
-            for (int m = i; m < i0 + 16; ++m) {
-                const float e = __expf(static_cast<float>(sG[m][c] - Gi));
-                colP += sM[1][m][i] * e * toF(sQ[m][c]);
-                colA += sM[3][m][i] * e * toF(sK[m][c]);
-            }
-            const float kv = toF(sK[i][c]), qv = toF(sQ[i][c]);
-            if (i < nvalid) {
-                p.dq[row_of(i) * D + c] = DQ[x] + rowP;
-                p.dk[row_of(i) * D + c] = DK[x] + rowA + colP + colA;
-            }
-            DG[x] += qv * rowP + kv * rowA - kv * (colP + colA);
-        }
-        __syncthreads();
-        // ---- dlog_alpha = reverse cumulative sum of dG (from the last token's dG
-        //      term in sdGL), in NSEG segments of RPS tokens per channel: segment
-        //      totals meet in LDS (over sM, no longer in use), each segment then
-        //      adds the totals after it; dbeta
-        {
-            GT *segt = reinterpret_cast<GT *>(&sM[0][0][0]);  // [NSEG][D]
-            const int c = tid % D, sg = tid / D, i0 = sg * RPS;
-            float dgc[RPS];
-            GT tot = 0;
-            if (sg < NSEG) {
+            // ---- dlog_alpha = reverse cumulative sum of dG over the chunk, from
+            //      the last token's dG term in sdGL: within each lane's four tokens
+            //      of a block, then over the four lanes of the channel (lane / 16),
+            //      then over the blocks, last first
+            GT after_blocks = sdGL[c];
 #pragma unroll
-                for (int x = 0; x < RPS; ++x) dgc[x] = DG[(i0 + x) * D + c];
+            for (int I = NTI - 1; I >= 0; --I) {
+                GT suf[4];
+                suf[3] = DGr[I][3];
 #pragma unroll
-                for (int x = RPS - 1; x >= 0; --x) tot += dgc[x];
-                segt[sg * D + c] = tot;
-            }
-            __syncthreads();
-            if (sg < NSEG) {
-                GT acc = sdGL[c];
-                for (int q = NSEG - 1; q > sg; --q) acc += segt[q * D + c];
+                for (int r = 2; r >= 0; --r) suf[r] = suf[r + 1] + GT(DGr[I][r]);
+                const GT tot = suf[0];
+                const GT t1 = __shfl_down(tot, 16), t2 = __shfl_down(tot, 32), t3 = __shfl_down(tot, 48);
+                const GT after_lanes = (kg < 3 ? t1 : GT(0)) + (kg < 2 ? t2 : GT(0)) + (kg < 1 ? t3 : GT(0));
+                GT block = tot + __shfl_xor(tot, 16);
+                block += __shfl_xor(block, 32);
 #pragma unroll
-                for (int x = RPS - 1; x >= 0; --x) {
-                    const int i = i0 + x;
-                    acc += dgc[x];
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * kg + r;
+                    const GT acc = after_blocks + after_lanes + suf[r];
                     if (i < nvalid)
                         p.dlog_alpha[row_of(i) * D + c] = (sNotRst[i] && !sNegInf[i][c]) ? static_cast<float>(acc) : 0.f;
                 }
+                after_blocks += block;
             }
         }
         for (int i = tid; i < nvalid; i += kBwdIntraThreads) {
@@ -1018,7 +1254,10 @@ hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t stream) {
         BwdStateParams sp{f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N, f.workspace, f.pkg_bytes, L,
                           a.d_o, a.d_final_state, a.chunk_dstates, a.d_init_state,
                           s0, s1, a.dcarry + ((g + 1) & 1) * hd2, a.dcarry + (g & 1) * hd2, g == 0};
-        hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+        if constexpr (BF)
+            hipLaunchKernelGGL((bwd_state_f16_kernel<C, D>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+        else
+            hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n_items = (s1 - s0) * f.H;

@@ -146,7 +146,7 @@ struct BackwardArgs {
     int64_t seg_slots;
 };
 constexpr int kBwdMaxGroups = 1024;    // persistent workgroups of the gradient kernel
-constexpr int kBwdScratchMats = 10;    // fp32 [C][D] scratch matrices per workgroup
+constexpr int kBwdScratchMats = 6;     // fp32 [C][D] scratch matrices per workgroup
 // (chunk, head) items per backward segment: 16384 keeps every pass of a
 // segment wide enough to fill the chip (64 items per compute unit) while the
 // segment's buffers stay a few GB at d = 128

@@ -158,10 +158,13 @@ size_t kda_chunk_fwd_noalloc_max_workspace(void);
 
 /*
  * kda_chunk_bwd_workspace_size -- bytes of device workspace kda_chunk_bwd
- * needs (host only, pure; 0 for invalid or unsupported arguments).  It holds
- * the forward's packages, the state entering every chunk and the gradient of
- * the state leaving it ([chunks, H, Dk, Dv] fp32 each), and a fixed scratch of
- * 1024 x 10 x C x Dk fp32.
+ * needs (host only, pure; 0 for invalid or unsupported arguments).  The
+ * backward takes the chunk slots in segments of ceil(16384 / H) chunks and
+ * recomputes each segment's forward from the state entering it, so the
+ * workspace holds one segment's packages and its states and state gradients
+ * ([segment chunks, H, Dk, Dv] fp32 each), one [H, Dk, Dv] fp32 checkpoint per
+ * segment boundary, two [H, Dk, Dv] fp32 carries and a fixed scratch of
+ * 1024 x 6 x C x Dk fp32: about 4.3 GB at T = 1M, H = 32, d = 128.
  */
 size_t kda_chunk_bwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv,
                                     int32_t n_seqs, kda_dtype in_dtype, int32_t chunk_size);
