@@ -318,7 +318,7 @@ def host_cpu_model():
 def backward_leg(torch, kda, pin, dev, C):
     """kda_chunk_bwd over all tokens of the long prefill inputs, with
     d_o ~ N(0, 1) and preallocated gradients and workspace (one segment's
-    packages and states, and a checkpoint per segment: about 4.4 GB at 1M
+    packages and states, and a checkpoint per segment: about 4.3 GB at 1M
     tokens).  Returns (call, T_B)."""
     T, H, Dk, Dv = pin["T"], pin["H"], pin["q"].shape[-1], pin["v"].shape[-1]
     T_B = T

@@ -652,9 +652,17 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         const float *S0 = p.chunk_states + (static_cast<size_t>(slot - p.s0) * H + h) * D * D;
         const float *dS1 = p.chunk_dstates + (static_cast<size_t>(slot - p.s0) * H + h) * D * D;
         auto row_of = [&](int i) { return (tok0 + i) * H + h; };
-        auto dO_at = [&](int i, int col) { return i < nvalid ? p.d_o[row_of(i) * D + col] : 0.f; };
+        // loads of token i's inputs are unconditional, from a row inside the chunk,
+        // and the value selected after them (a load under a branch waits before
+        // the branch rejoins, which serialises a batch of them)
+        auto rowc = [&](int i) { return row_of(i < nvalid ? i : nvalid - 1); };
+        auto dO_at = [&](int i, int col) {
+            const float x = p.d_o[rowc(i) * D + col];
+            return i < nvalid ? x : 0.f;
+        };
         auto dO4 = [&](int i, int col) {
-            return i < nvalid ? ld4(p.d_o + row_of(i) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 x = ld4(p.d_o + rowc(i) * D + col);
+            return i < nvalid ? x : f32x4{0.f, 0.f, 0.f, 0.f};
         };
 
         // ---- inputs, resets, cumulative decay (natural-log units)
@@ -876,7 +884,8 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * (t / NTD) + 4 * kg + r, cc = 16 * (t % NTD) + l16;
-                    vv[r] = i < nvalid ? toF(static_cast<const In *>(p.v)[row_of(i) * D + cc]) : 0.f;
+                    const float x = toF(static_cast<const In *>(p.v)[rowc(i) * D + cc]);
+                    vv[r] = i < nvalid ? x : 0.f;
                 }
                 return vv;
             },

@@ -121,11 +121,18 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     int nvalid;
     if (!locate_chunk(slot, C, p.T, p.N, p.cu_seqlens, p.chunk_offsets, tok0, nvalid)) return;
     char *pkg = p.ws + static_cast<size_t>(blockIdx.x) * p.pkg_bytes;
+    // Inputs of token i (0 for i >= nvalid).  The load itself is unconditional,
+    // from a row inside the chunk, and the value selected after it: a load
+    // under a branch gets a wait of its own before the branch rejoins, which
+    // would serialise every load of the loops below.
+    auto row = [&](int i) { return ((tok0 + (i < nvalid ? i : nvalid - 1)) * H + h) * D; };
     auto in = [&](const void *x, int i, int c) {
-        return i < nvalid ? ld_in<BF>(x, ((tok0 + i) * H + h) * D + c) : 0.f;
+        const float v = ld_in<BF>(x, row(i) + c);
+        return i < nvalid ? v : 0.f;
     };
     auto in4 = [&](const void *x, int i, int c) {  // channels c .. c + 3 of token i
-        return i < nvalid ? ld_in4<BF>(x, ((tok0 + i) * H + h) * D + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 v = ld_in4<BF>(x, row(i) + c);
+        return i < nvalid ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     };
     auto g4 = [&](int i, int c) {  // G[i][c .. c + 3], G[-1] = 0
         return i >= 0 ? *reinterpret_cast<const f32x4 *>(&sG[i][c]) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -387,6 +394,17 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 continue;
             }
             const int cx = 16 * ct + l16;  // this lane's channel as the left operand
+            // this job's b and q values, all loads issued before any is used (the
+            // scheduling barrier keeps the compiler from sinking each load to its
+            // use, which would wait out every load's latency in turn)
+            f32x4 braw[NTI], qraw[NTI];
+#pragma unroll
+            for (int t = 0; t < NTI; ++t) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) braw[t][e] = in(p.b, 16 * t + 4 * kg + e, cx);
+                qraw[t] = in4(p.q, 16 * t + l16, 16 * ct + 4 * kg);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // X^T fragment: xf[t][e] = X[16 t + 4 kg + e][cx]
             f32x4 xf[NTI];
 #pragma unroll
@@ -395,17 +413,17 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * t + 4 * kg + e;
                     const float gb = j > 0 ? sG[j - 1][cx] : 0.f;
-                    xf[t][e] = cnt_before(j) == 0 ? in(p.b, j, cx) * __expf(gb) : 0.f;
+                    xf[t][e] = cnt_before(j) == 0 ? braw[t][e] * __expf(gb) : 0.f;
                 }
-            // the Q e^G terms of the Q' rows, loaded before the products
+            // the Q e^G terms of the Q' rows
             f32x4 qg[NTI];
 #pragma unroll
             for (int I = 0; I < NTI; ++I) {
                 const int i = 16 * I + l16, c0 = 16 * ct + 4 * kg;
-                const f32x4 qv = in4(p.q, i, c0), gv = g4(i, c0);
+                const f32x4 gv = g4(i, c0);
                 const bool live = sCnt[i] == 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) qg[I][r] = live ? qv[r] * __expf(gv[r]) : 0.f;
+                for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * __expf(gv[r]) : 0.f;
             }
             for (int rt = 0; rt < 2 * NTI; ++rt) {
                 const int I = rt < NTI ? rt : rt - NTI, mt = rt < NTI ? 0 : 2;
@@ -430,7 +448,20 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 }
                 store4(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8 + 4 * hc, val);
             }
-            // [At; Kt]: channel cx, tokens 32 s + 8 kg + e of each half
+            // [At; Kt]: channel cx, tokens 32 s + 8 kg + e of each half; the a and
+            // k values loaded in one batch first
+            float akraw[KSC2][8];
+#pragma unroll
+            for (int s = 0; s < KSC2; ++s) {
+                const bool second = s >= KSC2 / 2;
+                const int s0 = second ? s - KSC2 / 2 : s;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * s0 + 8 * kg + e;
+                    akraw[s][e] = in(second ? p.k : p.a, j < C ? j : C - 1, cx);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < KSC2; ++s) {
                 const bool second = s >= KSC2 / 2;
@@ -438,22 +469,20 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 float v8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * s0 + 8 * kg + e;
-                    float x = 0.f;
-                    if (j < C && sCnt[j] == cnt_last)
-                        x = in(second ? p.k : p.a, j, cx) * __expf(sG[C - 1][cx] - sG[j][cx]);
-                    v8[e] = x;
+                    const int j = 32 * s0 + 8 * kg + e, jj = j < C ? j : C - 1;
+                    v8[e] = (j < C && sCnt[jj] == cnt_last) ? akraw[s][e] * __expf(sG[C - 1][cx] - sG[jj][cx]) : 0.f;
                 }
                 store8(kt + ((static_cast<size_t>(ct) * KSC2 + s) * 64 + lane) * 8, v8);
             }
         } else {
             const int vt = job - NCT, col = 16 * vt + l16;
-            // V fragment: vf[t][e] = V[16 t + 4 kg + e][col]
+            // V fragment: vf[t][e] = V[16 t + 4 kg + e][col], loaded in one batch
             f32x4 vf[NTI];
 #pragma unroll
             for (int t = 0; t < NTI; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vf[t][e] = in(p.v, 16 * t + 4 * kg + e, col);
+            __builtin_amdgcn_sched_barrier(0);
             for (int rt = 0; rt < 2 * NTI; ++rt) {
                 const int I = rt < NTI ? rt : rt - NTI, mt = rt < NTI ? 1 : 3;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
