@@ -44,6 +44,9 @@ namespace kda {
 namespace {
 
 constexpr int kDplrThreads = 512;  // 8 waves
+// half-span (natural log) of the cumulative decay around a diagonal block's
+// reference token up to which that block goes through the matrix cores
+constexpr float kDplrDiagSpan = 30.0f;
 constexpr int kDplrWaves = kDplrThreads / 64;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -138,10 +141,21 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         return i >= 0 ? *reinterpret_cast<const f32x4 *>(&sG[i][c]) : f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // ---- cumulative decay and resets
-    for (int x = tid; x < C * D; x += kDplrThreads) {
-        const int i = x / D, c = x % D;
-        sG[i][c] = i < nvalid ? p.log_alpha[((tok0 + i) * H + h) * D + c] : 0.f;
+    // ---- cumulative decay and resets (the chunk's log_alpha in 16-byte
+    //      vectors, every load issued before the first is used)
+    {
+        constexpr int NV = C * D / 4, NL = (NV + kDplrThreads - 1) / kDplrThreads;
+        f32x4 la[NL];
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int x = 4 * (tid + kDplrThreads * u), i = (x < C * D ? x : 0) / D, c = (x < C * D ? x : 0) % D;
+            la[u] = *reinterpret_cast<const f32x4 *>(p.log_alpha + row(i) + c);
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int x = 4 * (tid + kDplrThreads * u), i = x / D, c = x % D;
+            if (x < C * D) *reinterpret_cast<f32x4 *>(&sG[i][c]) = i < nvalid ? la[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     for (int i = tid; i < C; i += kDplrThreads) sRst[i] = i < nvalid ? 1 : 0;
     for (int x = tid; x < 4 * C * MS; x += kDplrThreads) (&sM[0][0][0])[x] = 0.f;
@@ -215,10 +229,82 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             }
         }
     }
-    // ---- diagonal blocks, exact decay per term: one 4x4 sub-block per group of
-    //      NQ adjacent lanes, each lane a part of the channels; the parts are
-    //      summed by lane exchange in a fixed order
-    {
+    // ---- diagonal blocks on the 16-bit path: on the matrix cores as the blocks
+    //      below, one wave per block, with the block's token 7 as the reference
+    //      m (e^{x_i - G_j} = e^{x_i - G_m} e^{G_m - G_j}, both factors at most
+    //      e^{kDplrDiagSpan}); a channel whose cumulative decay spans more than
+    //      that on either side of m is left out of the products (zero operands)
+    //      and added exactly afterwards.  The entries above the diagonal come
+    //      out finite and are masked.
+    if constexpr (BF) {
+        for (int J = w; J < NTI; J += kDplrWaves) {
+            const int m = 16 * J + 7, i = 16 * J + l16, j = i;
+            f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
+            uint32_t unsafe[4] = {0u, 0u, 0u, 0u};  // bit c % 32 of word c / 32: channel c
+#pragma unroll 2
+            for (int t = 0; t < D / 16; ++t) {
+                const int c = 16 * t + 4 * kg;  // this lane's channels c .. c + 3
+                const f32x4 gm = g4(m, c), gfirst = g4(16 * J - 1, c), glast = g4(16 * J + 15, c);
+                const f32x4 gbi = g4(i - 1, c), gi = g4(i, c), gj = g4(j, c);
+                const f32x4 bv = in4(p.b, i, c), qv = in4(p.q, i, c), av = in4(p.a, j, c), kv = in4(p.k, j, c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool safe = gfirst[e] - gm[e] <= kDplrDiagSpan && gm[e] - glast[e] <= kDplrDiagSpan;
+                    const float e3 = safe ? __expf(gm[e] - gj[e]) : 0.f;
+                    const float lb = safe ? bv[e] * __expf(gbi[e] - gm[e]) : 0.f;
+                    const float lq = safe ? qv[e] * __expf(gi[e] - gm[e]) : 0.f;
+                    const float ra = av[e] * e3, rk = kv[e] * e3;
+                    aab = mfma4(lb, ra, aab);
+                    abk = mfma4(lb, rk, abk);
+                    pqa = mfma4(lq, ra, pqa);
+                    pqk = mfma4(lq, rk, pqk);
+                    const uint64_t ub = __ballot(!safe);  // lanes 16 g: channel 16 t + 4 g + e
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        if ((ub >> (16 * g)) & 1u) {
+                            const int ch = 16 * t + 4 * g + e;
+                            unsafe[ch >> 5] |= 1u << (ch & 31);
+                        }
+                }
+            }
+            // rare: the left-out channels, exact decay per term
+#pragma unroll
+            for (int word = 0; word < 4; ++word) {
+                uint32_t bits = unsafe[word];
+                while (bits) {
+                    const int ch = 32 * word + __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const float aj = in(p.a, j, ch), kj = in(p.k, j, ch);
+                    const float gjc = sG[j][ch];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int ii = 16 * J + 4 * kg + r;
+                        const float bi = in(p.b, ii, ch), qi = in(p.q, ii, ch);
+                        const float gbc = ii > 0 ? sG[ii - 1][ch] : 0.f;
+                        const float eA = __expf(fminf(gbc - gjc, 0.f)), eP = __expf(fminf(sG[ii][ch] - gjc, 0.f));
+                        aab[r] += bi * aj * eA;
+                        abk[r] += bi * kj * eA;
+                        pqa[r] += qi * aj * eP;
+                        pqk[r] += qi * kj * eP;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ii = 16 * J + 4 * kg + r;
+                const bool okA = j < ii && cnt_before(ii) == sCnt[j];
+                const bool okP = j <= ii && sCnt[ii] == sCnt[j];
+                sM[0][ii][j] = okA ? -aab[r] : 0.f;
+                sM[1][ii][j] = okA ? abk[r] : 0.f;
+                sM[2][ii][j] = okP ? pqa[r] : 0.f;
+                sM[3][ii][j] = okP ? pqk[r] : 0.f;
+            }
+        }
+    }
+    // ---- diagonal blocks on the fp32 path, exact decay per term: one 4x4
+    //      sub-block per group of NQ adjacent lanes, each lane a part of the
+    //      channels; the parts are summed by lane exchange in a fixed order
+    if constexpr (!BF) {
         const int sb = tid / NQ, qt = tid % NQ;
         int li = 0, lj = sb % 10;
         while (lj > li) {
@@ -279,8 +365,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     sM[3][i][j] = okP ? acc[3][x][y] : 0.f;
                 }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- T = (I + sM[0])^-1 = (I - Aab)^-1 in place: diagonal 16x16 blocks by
     //      forward substitution (one lane per column), then block rows in order,
