@@ -137,6 +137,21 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         const f32x4 v = ld_in4<BF>(x, row(i) + c);
         return i < nvalid ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     };
+    // the same split in two: the raw load (one 8-byte bf16 or 16-byte fp32
+    // vector, held while a loop step computes) and its widening
+    using Raw4 = std::conditional_t<BF, uint2, f32x4>;
+    auto raw4 = [&](const void *x, int i, int c) {
+        if constexpr (BF) return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + row(i) + c);
+        else return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(x) + row(i) + c);
+    };
+    auto widen4 = [&](const Raw4 &r, int i) {
+        f32x4 v;
+        if constexpr (BF)
+            v = f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                      __uint_as_float(r.y & 0xffff0000u)};
+        else v = r;
+        return i < nvalid ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
     auto g4 = [&](int i, int c) {  // G[i][c .. c + 3], G[-1] = 0
         return i >= 0 ? *reinterpret_cast<const f32x4 *>(&sG[i][c]) : f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -202,11 +217,23 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             }
             const int m = 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
-#pragma unroll 2
+            // the next step's b, q, a, k are loaded while one computes
+            Raw4 rb[2], rq[2], ra4[2], rk4[2];
+            auto issue = [&](int t, int sl) {
+                const int c = 16 * t + 4 * kg;
+                rb[sl] = raw4(p.b, i, c);
+                rq[sl] = raw4(p.q, i, c);
+                ra4[sl] = raw4(p.a, j, c);
+                rk4[sl] = raw4(p.k, j, c);
+            };
+            issue(0, 0);
+#pragma unroll
             for (int t = 0; t < D / 16; ++t) {
+                if (t + 1 < D / 16) issue(t + 1, (t + 1) & 1);
                 const int c = 16 * t + 4 * kg;  // this lane's channels c .. c + 3
                 const f32x4 gm = g4(m, c), gbi = g4(i - 1, c), gi = g4(i, c), gj = g4(j, c);
-                const f32x4 bv = in4(p.b, i, c), qv = in4(p.q, i, c), av = in4(p.a, j, c), kv = in4(p.k, j, c);
+                const f32x4 bv = widen4(rb[t & 1], i), qv = widen4(rq[t & 1], i), av = widen4(ra4[t & 1], j),
+                            kv = widen4(rk4[t & 1], j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float e3 = __expf(gm[e] - gj[e]);
@@ -241,12 +268,23 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             const int m = 16 * J + 7, i = 16 * J + l16, j = i;
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
             uint32_t unsafe[4] = {0u, 0u, 0u, 0u};  // bit c % 32 of word c / 32: channel c
-#pragma unroll 2
+            Raw4 rb[2], rq[2], ra4[2], rk4[2];
+            auto issue = [&](int t, int sl) {
+                const int c = 16 * t + 4 * kg;
+                rb[sl] = raw4(p.b, i, c);
+                rq[sl] = raw4(p.q, i, c);
+                ra4[sl] = raw4(p.a, j, c);
+                rk4[sl] = raw4(p.k, j, c);
+            };
+            issue(0, 0);
+#pragma unroll
             for (int t = 0; t < D / 16; ++t) {
+                if (t + 1 < D / 16) issue(t + 1, (t + 1) & 1);
                 const int c = 16 * t + 4 * kg;  // this lane's channels c .. c + 3
                 const f32x4 gm = g4(m, c), gfirst = g4(16 * J - 1, c), glast = g4(16 * J + 15, c);
                 const f32x4 gbi = g4(i - 1, c), gi = g4(i, c), gj = g4(j, c);
-                const f32x4 bv = in4(p.b, i, c), qv = in4(p.q, i, c), av = in4(p.a, j, c), kv = in4(p.k, j, c);
+                const f32x4 bv = widen4(rb[t & 1], i), qv = widen4(rq[t & 1], i), av = widen4(ra4[t & 1], j),
+                            kv = widen4(rk4[t & 1], j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bool safe = gfirst[e] - gm[e] <= kDplrDiagSpan && gm[e] - glast[e] <= kDplrDiagSpan;
