@@ -205,6 +205,101 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     __syncthreads();
     auto cnt_before = [&](int i) { return sCnt[i] - sRst[i]; };  // resets at tokens < i
 
+    // One Gram block pair (I, J) on the 16-bit path with bf16 hi/lo matrix-core
+    // products (three per K step of 32 channels, about 16 significant bits per
+    // operand as the KDA Gram tiles): rows i = 16 I + l16 of the left operands
+    // b e^{Gb_i - G_m} and q e^{G_i - G_m}, columns j = 16 J + l16 of the right
+    // ones a e^{G_m - G_j} and k e^{G_m - G_j}.  Below the diagonal m is the last
+    // token of J; on it (kDiag) m is the block's token 7, and channels whose span
+    // around m exceeds kDplrDiagSpan are left out (zero operands) and reported
+    // in `unsafe` (bit c % 32 of word c / 32).  Each lane loads 8 consecutive
+    // channels of its token as one 16-byte vector, the next step's while one
+    // computes.
+    auto gram16 = [&](int I, int J, auto diag_tag, f32x4 &aab, f32x4 &abk, f32x4 &pqa, f32x4 &pqk,
+                      uint32_t (&unsafe)[4]) {
+        constexpr bool kDiag = decltype(diag_tag)::value;
+        const int m = kDiag ? 16 * J + 7 : 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
+        auto raw8 = [&](const void *x, int ii, int c) {
+            return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row(ii) + c);
+        };
+        auto widen8 = [&](const uint4 &r, int ii, float (&v)[8]) {
+            const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                v[2 * q2] = ii < nvalid ? __uint_as_float(wd[q2] << 16) : 0.f;
+                v[2 * q2 + 1] = ii < nvalid ? __uint_as_float(wd[q2] & 0xffff0000u) : 0.f;
+            }
+        };
+        uint4 rb[2], rq[2], ra[2], rk[2];
+        auto issue = [&](int st, int sl) {
+            const int c = 32 * st + 8 * kg;
+            rb[sl] = raw8(p.b, i, c);
+            rq[sl] = raw8(p.q, i, c);
+            ra[sl] = raw8(p.a, j, c);
+            rk[sl] = raw8(p.k, j, c);
+        };
+        issue(0, 0);
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) {
+            if (st + 1 < D / 32) issue(st + 1, (st + 1) & 1);
+            const int c = 32 * st + 8 * kg;  // this lane's channels c .. c + 7
+            float bv[8], qv[8], av[8], kv[8];
+            widen8(rb[st & 1], i, bv);
+            widen8(rq[st & 1], i, qv);
+            widen8(ra[st & 1], j, av);
+            widen8(rk[st & 1], j, kv);
+            float lb[8], lq[8], xa[8], xk[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c4 = c + 4 * hh;
+                const f32x4 gm = g4(m, c4), gbi = g4(i - 1, c4), gi = g4(i, c4), gj = g4(j, c4);
+                f32x4 gfirst = gm, glast = gm;
+                if constexpr (kDiag) {
+                    gfirst = g4(16 * J - 1, c4);
+                    glast = g4(16 * J + 15, c4);
+                }
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int e = 4 * hh + e4;
+                    bool safe = true;
+                    if constexpr (kDiag) {
+                        safe = gfirst[e4] - gm[e4] <= kDplrDiagSpan && gm[e4] - glast[e4] <= kDplrDiagSpan;
+                        const uint64_t ub = __ballot(!safe);  // lanes 16 g: channel 32 st + 8 g + e
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            if ((ub >> (16 * g)) & 1u) {
+                                const int ch = 32 * st + 8 * g + e;
+                                unsafe[ch >> 5] |= 1u << (ch & 31);
+                            }
+                    }
+                    const float e3 = safe ? __expf(gm[e4] - gj[e4]) : 0.f;
+                    lb[e] = safe ? bv[e] * __expf(gbi[e4] - gm[e4]) : 0.f;
+                    lq[e] = safe ? qv[e] * __expf(gi[e4] - gm[e4]) : 0.f;
+                    xa[e] = av[e] * e3;
+                    xk[e] = kv[e] * e3;
+                }
+            }
+            bf16x8 lbh, lbl, lqh, lql, xah, xal, xkh, xkl;
+            split_bf16(lb, lbh, lbl);
+            split_bf16(lq, lqh, lql);
+            split_bf16(xa, xah, xal);
+            split_bf16(xk, xkh, xkl);
+            aab = mfma_bf16(lbl, xah, aab);
+            aab = mfma_bf16(lbh, xal, aab);
+            aab = mfma_bf16(lbh, xah, aab);
+            abk = mfma_bf16(lbl, xkh, abk);
+            abk = mfma_bf16(lbh, xkl, abk);
+            abk = mfma_bf16(lbh, xkh, abk);
+            pqa = mfma_bf16(lql, xah, pqa);
+            pqa = mfma_bf16(lqh, xal, pqa);
+            pqa = mfma_bf16(lqh, xah, pqa);
+            pqk = mfma_bf16(lql, xkh, pqk);
+            pqk = mfma_bf16(lqh, xkl, pqk);
+            pqk = mfma_bf16(lqh, xkh, pqk);
+        }
+    };
+    constexpr bool kGram16 = BF && D >= 32;  // the bf16 matrix-core Gram path
+
     // ---- Gram blocks below the diagonal, one 16x16 block pair per wave
     {
         constexpr int NPAIR = NTI * (NTI - 1) / 2;
@@ -217,6 +312,10 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             }
             const int m = 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
+            if constexpr (kGram16) {
+                uint32_t none[4] = {0u, 0u, 0u, 0u};
+                gram16(I, J, std::false_type{}, aab, abk, pqa, pqk, none);
+            } else {
             // the next step's b, q, a, k are loaded while one computes
             Raw4 rb[2], rq[2], ra4[2], rk4[2];
             auto issue = [&](int t, int sl) {
@@ -245,6 +344,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     pqk = mfma4(lq, rk, pqk);
                 }
             }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ii = 16 * I + 4 * kg + r;
@@ -268,6 +368,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             const int m = 16 * J + 7, i = 16 * J + l16, j = i;
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
             uint32_t unsafe[4] = {0u, 0u, 0u, 0u};  // bit c % 32 of word c / 32: channel c
+            if constexpr (kGram16) {
+                gram16(J, J, std::true_type{}, aab, abk, pqa, pqk, unsafe);
+            } else {
             Raw4 rb[2], rq[2], ra4[2], rk4[2];
             auto issue = [&](int t, int sl) {
                 const int c = 16 * t + 4 * kg;
@@ -304,6 +407,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                             unsafe[ch >> 5] |= 1u << (ch & 31);
                         }
                 }
+            }
             }
             // rare: the left-out channels, exact decay per term
 #pragma unroll
