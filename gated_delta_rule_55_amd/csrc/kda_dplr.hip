@@ -546,53 +546,80 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         __syncthreads();
     }
 
-    // ---- R = Pqa T in place (a wave per row block: it alone reads and writes those rows)
-    if (w < NTI) {
-        const int I = w;
-        f32x4 acc[NTI];
-#pragma unroll
-        for (int Jc = 0; Jc < NTI; ++Jc) {
-            acc[Jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (Jc <= I)
-                for (int K = Jc; K <= I; ++K)
-                    mm16(acc[Jc], [&](int r, int k) { return sM[2][16 * I + r][16 * K + k]; },
-                         [&](int k, int n) { return sM[0][16 * K + k][16 * Jc + n]; }, lane);
-        }
-#pragma unroll
-        for (int Jc = 0; Jc < NTI; ++Jc)
-            if (Jc <= I) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sM[2][16 * I + 4 * kg + r][16 * Jc + l16] = acc[Jc][r];
+    // ---- R = Pqa T, then T Abk and R Abk + Pqk, tile by tile over all the
+    //      waves: the 16x16 tiles (I, Jc), Jc <= I, heaviest (I - Jc largest)
+    //      first, wave w taking tiles w, w + 8, ...  Each product is formed in
+    //      registers and written in place only after every wave has read its
+    //      operands (barrier between).
+    {
+        constexpr int NTL = NTI * (NTI + 1) / 2, TPW = (NTL + kDplrWaves - 1) / kDplrWaves;
+        auto tile_of = [](int t, int &I, int &Jc) {
+            int d = NTI - 1, n = 1;
+            while (t >= n) {
+                t -= n;
+                --d;
+                ++n;
             }
-    }
-    __syncthreads();
-    // ---- T Abk and R Abk + Pqk in place (a wave per column block of Abk)
-    if (w < NTI) {
-        const int Jc = w;
-        f32x4 m1[NTI], m2[NTI];
+            Jc = t;
+            I = t + d;
+        };
+        f32x4 a1[TPW], a2[TPW];
 #pragma unroll
-        for (int I = 0; I < NTI; ++I) {
-            m1[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < TPW; ++u) {
+            const int t = w + kDplrWaves * u;
+            a1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < NTL) {
+                int I, Jc;
+                tile_of(t, I, Jc);
+                for (int K = Jc; K <= I; ++K)
+                    mm16(a1[u], [&](int r, int k) { return sM[2][16 * I + r][16 * K + k]; },
+                         [&](int k, int n) { return sM[0][16 * K + k][16 * Jc + n]; }, lane);
+            }
+        }
+        __syncthreads();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) m2[I][r] = sM[3][16 * I + 4 * kg + r][16 * Jc + l16];
-            if (I >= Jc)
+        for (int u = 0; u < TPW; ++u) {
+            const int t = w + kDplrWaves * u;
+            if (t < NTL) {
+                int I, Jc;
+                tile_of(t, I, Jc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sM[2][16 * I + 4 * kg + r][16 * Jc + l16] = a1[u][r];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int t = w + kDplrWaves * u;
+            a1[u] = a2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < NTL) {
+                int I, Jc;
+                tile_of(t, I, Jc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a2[u][r] = sM[3][16 * I + 4 * kg + r][16 * Jc + l16];
                 for (int K = Jc; K <= I; ++K) {
                     auto bk = [&](int k, int n) { return sM[1][16 * K + k][16 * Jc + n]; };
-                    mm16(m1[I], [&](int r, int k) { return sM[0][16 * I + r][16 * K + k]; }, bk, lane);
-                    mm16(m2[I], [&](int r, int k) { return sM[2][16 * I + r][16 * K + k]; }, bk, lane);
-                }
-        }
-#pragma unroll
-        for (int I = 0; I < NTI; ++I)
-            if (I >= Jc) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sM[1][16 * I + 4 * kg + r][16 * Jc + l16] = m1[I][r];
-                    sM[3][16 * I + 4 * kg + r][16 * Jc + l16] = m2[I][r];
+                    mm16(a1[u], [&](int r, int k) { return sM[0][16 * I + r][16 * K + k]; }, bk, lane);
+                    mm16(a2[u], [&](int r, int k) { return sM[2][16 * I + r][16 * K + k]; }, bk, lane);
                 }
             }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int t = w + kDplrWaves * u;
+            if (t < NTL) {
+                int I, Jc;
+                tile_of(t, I, Jc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    sM[1][16 * I + 4 * kg + r][16 * Jc + l16] = a1[u][r];
+                    sM[3][16 * I + 4 * kg + r][16 * Jc + l16] = a2[u][r];
+                }
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- the package.  Channel-tile jobs: -W = -T X and Q' = Q e^G + R X in
     //      the WQ layout, [At; Kt] in the KT layout.  Value-tile jobs: U' =
