@@ -752,7 +752,17 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 dst[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = acc;
                 // V itself for the state pass: vf[I] holds rows 16 I + 4 kg + e of
                 // column col, the UP layout of row tile I
-                if (rt < NTI) vx[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = vf[I];
+                if (rt < NTI) {
+                    const size_t vi = (static_cast<size_t>(vt) * NTI + I) * 64 + lane;
+                    if constexpr (BF) {  // exact: V is bf16 (the low halves are zero)
+                        const f32x4 x = vf[I];
+                        reinterpret_cast<uint2 *>(vx)[vi] =
+                            uint2{(__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xffff0000u),
+                                  (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xffff0000u)};
+                    } else {
+                        vx[vi] = vf[I];
+                    }
+                }
             }
         }
     }

@@ -82,7 +82,7 @@ __host__ __device__ inline PackageLayout dplr_package_layout(int C, int Dk, int 
     L.up = off; off += align256((size_t)C * Dv * 4);
     L.oi = off; off += align256((size_t)C * Dv * 4);
     L.gl = off; off += align256((size_t)Dk * 4);
-    L.vx = off; off += align256((size_t)C * Dv * 4);
+    L.vx = off; off += align256((size_t)C * Dv * (bf16 ? 2 : 4));  // V rows: bf16 as given, or fp32
     L.bytes = off;
     return L;
 }

@@ -703,8 +703,19 @@ struct StateFrags {
                 const int I = rt < NT16 ? rt : rt - NT16;
                 uo[rw] = reinterpret_cast<const f32x4 *>(pkg + off)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane];
                 if constexpr (LR2) {
-                    vx[rw] = rt < NT16 ? reinterpret_cast<const f32x4 *>(pkg + L.vx)[(static_cast<size_t>(ct) * NT16 + I) * 64 + lane]
-                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+                    // V rows of tile I (bf16 on the 16-bit path); loaded for every
+                    // row tile and kept for the U tiles only, so the load is not
+                    // under a branch
+                    const size_t vi = (static_cast<size_t>(ct) * NT16 + I) * 64 + lane;
+                    f32x4 v;
+                    if constexpr (BF) {
+                        const uint2 r = reinterpret_cast<const uint2 *>(pkg + L.vx)[vi];
+                        v = f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                                  __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+                    } else {
+                        v = reinterpret_cast<const f32x4 *>(pkg + L.vx)[vi];
+                    }
+                    vx[rw] = rt < NT16 ? v : f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }

@@ -298,6 +298,8 @@ def test_dplr_workspace_size(lib):
     assert per * 64 * 32 == ws(1, 4096, 32, 128, 0, BF16, 64)
     # W and Q' (fp16), [A-tilde; K-tilde] (fp16, 2 x 64 tokens), U', O_intra, Gamma_last
     assert per >= 2 * 64 * 128 * 2 + 128 * 128 * 2 + 2 * 64 * 128 * 4 + 128 * 4
+    # ... and V's rows for the state pass, kept in bf16 as given: 144 KiB in all
+    assert per == 2 * 64 * 128 * 2 + 128 * 128 * 2 + 2 * 64 * 128 * 4 + 512 + 64 * 128 * 2
     assert ws(1, 4096, 32, 128, 0, BF16, 64) > kda_ws(1, 4096, 32, 128, 128, 0, BF16, 64)
     assert ws(1, 4096, 32, 128, 0, BF16, 0) == ws(1, 4096, 32, 128, 0, BF16, 64)
     assert ws(1, 1000, 2, 64, 5, BF16, 64) > ws(1, 1000, 2, 64, 0, BF16, 64)
