@@ -28,14 +28,20 @@
 // (W stored negated; [At; Kt] against [U; V] as one contraction over 2C tokens,
 // V from the package's VX section).
 //
-// Gram matrices: 16x16 blocks below the diagonal on the fp32 matrix cores with
-// the reference m = the last token of the column block, e^{x_i - G_j} =
-// e^{x_i - G_m} e^{G_m - G_j} (both factors <= 1); the diagonal blocks with the
-// exact exponential of every pair.  A token whose log_alpha is -inf on every
-// channel zeroes the diagonal part of its transition but not the low-rank
-// part: it adds 0 to G, and the couplings it cuts are masked (Aab, Abk and X
-// through a reset strictly before token i; P, At, Kt through one in (j, i]).
-// Other -inf values are clamped to -88.  All arithmetic of this kernel is fp32.
+// Gram matrices: 16x16 block pairs with a reference token m,
+// e^{x_i - G_j} = e^{x_i - G_m} e^{G_m - G_j}: below the diagonal m is the last
+// token of the column block (both factors <= 1), on it the block's token 7
+// (factors <= e^30; channels spanning more are added with the exact exponential
+// per pair).  On the 16-bit path (d >= 32) the Gram blocks, and (C >= 32) the
+// package's products against X and V, are bf16 hi/lo matrix-core products (V is
+// exact in bf16, so only its partner is split); the fp32 path keeps fp32
+// matrix cores below the diagonal and the exact exponential per pair on it.
+// T and the C x C products run on the fp32 matrix cores on both paths, and all
+// accumulation is fp32.  A token whose log_alpha is -inf on
+// every channel zeroes the diagonal part of its transition but not the
+// low-rank part: it adds 0 to G, and the couplings it cuts are masked (Aab, Abk
+// and X through a reset strictly before token i; P, At, Kt through one in
+// (j, i]).  Other -inf values are clamped to -88.
 #include <algorithm>
 
 #include "kda_prefill.h"
@@ -107,8 +113,17 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     static_assert(NTI <= 4, "one wave per row / column tile of a chunk");
     static_assert(NSB * NQ <= kDplrThreads && 64 % NQ == 0 && CQ % 4 == 0, "diagonal work layout");
 
+    // the package's products on the 16-bit path: bf16 matrix cores with the
+    // four C x C matrices as hi/lo planes, 32 tokens per step
+    constexpr bool kPk16 = BF && C % 32 == 0;
+    constexpr int MP = C + 8;  // bf16 row stride of the hi/lo planes (16-byte rows)
+    constexpr size_t kMF = sizeof(float) * 4 * C * MS, kMB = kPk16 ? sizeof(__bf16) * 8 * C * MP : 0;
     __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay
-    __shared__ __align__(16) float sM[4][C][MS];  // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk
+    // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk (fp32); on the
+    // 16-bit path overlaid at the end by the same four as bf16 hi/lo planes
+    __shared__ __align__(16) unsigned char sMraw[kMF > kMB ? kMF : kMB];
+    auto sM = reinterpret_cast<float (*)[C][MS]>(sMraw);
+    __bf16 *Mp = reinterpret_cast<__bf16 *>(sMraw);  // plane 2 m + (0 hi, 1 lo) of matrix m: C x MP
     constexpr int NSEG = kDplrThreads / D < C / 4 ? kDplrThreads / D : C / 4, RPS = C / NSEG;
     __shared__ float sSeg[NSEG][D];  // per-segment decay sums of the scan
     __shared__ int sRst[C], sCnt[C];
@@ -563,7 +578,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             Jc = t;
             I = t + d;
         };
-        f32x4 a1[TPW], a2[TPW];
+        f32x4 a1[TPW], a2[TPW], tv[TPW], rv[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int t = w + kDplrWaves * u;
@@ -596,7 +611,11 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 int I, Jc;
                 tile_of(t, I, Jc);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a2[u][r] = sM[3][16 * I + 4 * kg + r][16 * Jc + l16];
+                for (int r = 0; r < 4; ++r) {
+                    a2[u][r] = sM[3][16 * I + 4 * kg + r][16 * Jc + l16];
+                    tv[u][r] = sM[0][16 * I + 4 * kg + r][16 * Jc + l16];
+                    rv[u][r] = sM[2][16 * I + 4 * kg + r][16 * Jc + l16];
+                }
                 for (int K = Jc; K <= I; ++K) {
                     auto bk = [&](int k, int n) { return sM[1][16 * K + k][16 * Jc + n]; };
                     mm16(a1[u], [&](int r, int k) { return sM[0][16 * I + r][16 * K + k]; }, bk, lane);
@@ -604,17 +623,49 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();  // every fp32 read of the four matrices is done
+        if constexpr (kPk16) {
+            // the planes: this wave's tiles of T, T Abk, R, R Abk + Pqk from
+            // registers, and zeros in the tiles (I, I + 1), I even, that the
+            // 32-token steps of row tile I also read
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            const int t = w + kDplrWaves * u;
-            if (t < NTL) {
-                int I, Jc;
-                tile_of(t, I, Jc);
+            for (int u = 0; u < TPW; ++u) {
+                const int t = w + kDplrWaves * u;
+                if (t < NTL) {
+                    int I, Jc;
+                    tile_of(t, I, Jc);
+                    const f32x4 *mats[4] = {&tv[u], &a1[u], &rv[u], &a2[u]};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sM[1][16 * I + 4 * kg + r][16 * Jc + l16] = a1[u][r];
-                    sM[3][16 * I + 4 * kg + r][16 * Jc + l16] = a2[u][r];
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float x = (*mats[m])[r];
+                            const __bf16 hi = static_cast<__bf16>(x);
+                            const int o = ((2 * m) * C + 16 * I + 4 * kg + r) * MP + 16 * Jc + l16;
+                            Mp[o] = hi;
+                            Mp[o + C * MP] = static_cast<__bf16>(x - static_cast<float>(hi));
+                        }
+                }
+            }
+            constexpr int NZ = 8 * (NTI / 2) * 16 * 2;  // 16-byte pieces: planes x tiles x rows x 2
+            for (int z = tid; z < NZ; z += kDplrThreads) {
+                const int half = z & 1, rr = (z >> 1) & 15, zt = (z >> 5) % (NTI / 2), pl = (z >> 5) / (NTI / 2);
+                const int I = 2 * zt;
+                *reinterpret_cast<uint4 *>(Mp + (pl * C + 16 * I + rr) * MP + 16 * (I + 1) + 8 * half) =
+                    uint4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                const int t = w + kDplrWaves * u;
+                if (t < NTL) {
+                    int I, Jc;
+                    tile_of(t, I, Jc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        sM[1][16 * I + 4 * kg + r][16 * Jc + l16] = a1[u][r];
+                        sM[3][16 * I + 4 * kg + r][16 * Jc + l16] = a2[u][r];
+                    }
                 }
             }
         }
@@ -639,6 +690,16 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             *reinterpret_cast<f32x4 *>(dst) = v;
         }
     };
+    // row 16 rt + l16 of matrix m's planes at tokens 32 s + 8 kg .. + 7
+    auto m_frag = [&](int m, int rt, int s, bf16x8 &hi, bf16x8 &lo) {
+        const int o = (2 * m * C + 16 * rt + l16) * MP + 32 * s + 8 * kg;
+        hi = *reinterpret_cast<const bf16x8 *>(Mp + o);
+        lo = *reinterpret_cast<const bf16x8 *>(Mp + o + C * MP);
+    };
+    auto raw1 = [&](const void *x, int i, int c) {  // bf16 bits of x[token i][c], clamped row
+        return static_cast<const uint16_t *>(x)[row(i) + c];
+    };
+    constexpr int KS = C / 32 > 0 ? C / 32 : 1;  // 32-token steps of the 16-bit products
     for (int job = w; job < NCT + NTD; job += kDplrWaves) {
         if (job < NCT) {
             const int ct = job, ks = ct >> 1, hc = ct & 1;
@@ -649,6 +710,58 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 continue;
             }
             const int cx = 16 * ct + l16;  // this lane's channel as the left operand
+            if constexpr (kPk16) {
+                // X^T operand: X[32 s + 8 kg + e][cx], split in bf16 hi/lo; the
+                // products M X over the 32-token steps holding row tile I's nonzeros
+                uint16_t braw[KS][8];
+                f32x4 qraw[NTI];
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) braw[s2][e] = raw1(p.b, 32 * s2 + 8 * kg + e, cx);
+#pragma unroll
+                for (int t = 0; t < NTI; ++t) qraw[t] = in4(p.q, 16 * t + l16, 16 * ct + 4 * kg);
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 xh[KS], xl[KS];
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    float xv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * s2 + 8 * kg + e;
+                        const float gb = j > 0 ? sG[j - 1][cx] : 0.f;
+                        const float bv = __uint_as_float(static_cast<uint32_t>(braw[s2][e]) << 16);
+                        xv[e] = j < nvalid && cnt_before(j) == 0 ? bv * __expf(gb) : 0.f;
+                    }
+                    split_bf16(xv, xh[s2], xl[s2]);
+                }
+                f32x4 qg[NTI];
+#pragma unroll
+                for (int I = 0; I < NTI; ++I) {
+                    const int i = 16 * I + l16, c0 = 16 * ct + 4 * kg;
+                    const f32x4 gv = g4(i, c0);
+                    const bool live = sCnt[i] == 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * __expf(gv[r]) : 0.f;
+                }
+#pragma unroll
+                for (int rt = 0; rt < 2 * NTI; ++rt) {
+                    const int I = rt < NTI ? rt : rt - NTI, m = rt < NTI ? 0 : 2;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2)
+                        if (32 * s2 <= 16 * I + 15) {
+                            bf16x8 mh, ml;
+                            m_frag(m, I, s2, mh, ml);
+                            acc = mfma_bf16(xl[s2], mh, acc);
+                            acc = mfma_bf16(xh[s2], ml, acc);
+                            acc = mfma_bf16(xh[s2], mh, acc);
+                        }
+                    // acc[r] = (M X)[token 16 I + l16][channel 16 ct + 4 kg + r]
+                    store4(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8 + 4 * hc,
+                           rt < NTI ? -acc : acc + qg[I]);
+                }
+            } else {
             // this job's b and q values, all loads issued before any is used (the
             // scheduling barrier keeps the compiler from sinking each load to its
             // use, which would wait out every load's latency in turn)
@@ -703,6 +816,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 }
                 store4(wq + ((static_cast<size_t>(rt) * KSK + ks) * 64 + lane) * 8 + 4 * hc, val);
             }
+            }
             // [At; Kt]: channel cx, tokens 32 s + 8 kg + e of each half; the a and
             // k values loaded in one batch first
             float akraw[KSC2][8];
@@ -732,15 +846,49 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         } else {
             const int vt = job - NCT, col = 16 * vt + l16;
             // V fragment: vf[t][e] = V[16 t + 4 kg + e][col], loaded in one batch
+            // (on the 16-bit path also V[32 s + 8 kg + e][col] as the B operand
+            // of the bf16 products: V is exact in bf16, only M is split)
             f32x4 vf[NTI];
+            uint16_t vraw[kPk16 ? KS : 1][8];
 #pragma unroll
             for (int t = 0; t < NTI; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vf[t][e] = in(p.v, 16 * t + 4 * kg + e, col);
+            if constexpr (kPk16) {
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vraw[s2][e] = raw1(p.v, 32 * s2 + 8 * kg + e, col);
+            }
             __builtin_amdgcn_sched_barrier(0);
+            bf16x8 vb[kPk16 ? KS : 1];
+            if constexpr (kPk16) {
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2) {
+                        const int j = 32 * s2 + 8 * kg + 2 * q2;
+                        const uint32_t lo = j < nvalid ? vraw[s2][2 * q2] : 0u;
+                        const uint32_t hi = j + 1 < nvalid ? vraw[s2][2 * q2 + 1] : 0u;
+                        wd[q2] = lo | (hi << 16);
+                    }
+                    vb[s2] = __builtin_bit_cast(bf16x8, (uint4{wd[0], wd[1], wd[2], wd[3]}));
+                }
+            }
             for (int rt = 0; rt < 2 * NTI; ++rt) {
                 const int I = rt < NTI ? rt : rt - NTI, mt = rt < NTI ? 1 : 3;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (kPk16) {
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2)
+                        if (32 * s2 <= 16 * I + 15) {
+                            bf16x8 mh, ml;
+                            m_frag(mt, I, s2, mh, ml);
+                            acc = mfma_bf16(ml, vb[s2], acc);
+                            acc = mfma_bf16(mh, vb[s2], acc);
+                        }
+                } else {
 #pragma unroll
                 for (int t = 0; t < NTI; ++t)
                     if (t <= I) {
@@ -748,6 +896,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc = mfma4(mv[e], vf[t][e], acc);
                     }
+                }
                 f32x4 *dst = rt < NTI ? up : oi;
                 dst[(static_cast<size_t>(vt) * NTI + I) * 64 + lane] = acc;
                 // V itself for the state pass: vf[I] holds rows 16 I + 4 kg + e of
