@@ -50,9 +50,10 @@ namespace kda {
 namespace {
 
 constexpr int kDplrThreads = 512;  // 8 waves
-// half-span (natural log) of the cumulative decay around a diagonal block's
-// reference token up to which that block goes through the matrix cores
-constexpr float kDplrDiagSpan = 30.0f;
+// half-span of the cumulative decay around a diagonal block's reference token
+// up to which that block goes through the matrix cores: e^30, in the kernel's
+// base-2 units of G
+constexpr float kDplrDiagSpan = 30.0f * kLog2e;
 constexpr int kDplrWaves = kDplrThreads / 64;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -118,7 +119,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     constexpr bool kPk16 = BF && C % 32 == 0;
     constexpr int MP = C + 8;  // bf16 row stride of the hi/lo planes (16-byte rows)
     constexpr size_t kMF = sizeof(float) * 4 * C * MS, kMB = kPk16 ? sizeof(__bf16) * 8 * C * MP : 0;
-    __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay
+    __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay in base 2 (log2 e times the natural one)
     // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk (fp32); on the
     // 16-bit path overlaid at the end by the same four as bf16 hi/lo planes
     __shared__ __align__(16) unsigned char sMraw[kMF > kMB ? kMF : kMB];
@@ -171,6 +172,30 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         return i >= 0 ? *reinterpret_cast<const f32x4 *>(&sG[i][c]) : f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
+    // The first Gram job of this wave (a block pair below the diagonal, else
+    // its diagonal block) has its first channel step of b, q, a, k loaded now,
+    // ahead of the decay scan (16-bit Gram path).
+    constexpr int NPAIR = NTI * (NTI - 1) / 2;
+    static_assert(NPAIR <= kDplrWaves && NTI <= kDplrWaves, "at most one job of each kind per wave");
+    const bool has_pair = kDplrWaves - 1 - w < NPAIR;
+    uint4 pre[4];
+    if constexpr (BF && D >= 32) {
+        int fI = w < NTI ? w : 0, fJ = fI;
+        if (has_pair) {
+            fI = 1;
+            fJ = kDplrWaves - 1 - w;
+            while (fJ >= fI) {
+                fJ -= fI;
+                ++fI;
+            }
+        }
+        const int c = 8 * kg;
+        pre[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.b) + row(16 * fI + l16) + c);
+        pre[1] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.q) + row(16 * fI + l16) + c);
+        pre[2] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.a) + row(16 * fJ + l16) + c);
+        pre[3] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.k) + row(16 * fJ + l16) + c);
+    }
+
     // ---- cumulative decay and resets (the chunk's log_alpha in 16-byte
     //      vectors, every load issued before the first is used)
     {
@@ -201,7 +226,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         float acc = 0.f;
         for (int r = 0; r < RPS; ++r) {
             const int i = sseg * RPS + r;
-            acc += sRst[i] ? 0.f : fmaxf(sG[i][sc], kGFloor);
+            acc += sRst[i] ? 0.f : fmaxf(sG[i][sc], kGFloor) * kLog2e;
             sG[i][sc] = acc;
         }
         sSeg[sseg][sc] = acc;
@@ -230,19 +255,21 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     // in `unsafe` (bit c % 32 of word c / 32).  Each lane loads 8 consecutive
     // channels of its token as one 16-byte vector, the next step's while one
     // computes.
-    auto gram16 = [&](int I, int J, auto diag_tag, f32x4 &aab, f32x4 &abk, f32x4 &pqa, f32x4 &pqk,
-                      uint32_t (&unsafe)[4]) {
-        constexpr bool kDiag = decltype(diag_tag)::value;
+    auto gram16 = [&](int I, int J, auto diag_tag, auto pre_tag, f32x4 &aab, f32x4 &abk, f32x4 &pqa,
+                      f32x4 &pqk, uint32_t (&unsafe)[4]) {
+        constexpr bool kDiag = decltype(diag_tag)::value, kPre = decltype(pre_tag)::value;
         const int m = kDiag ? 16 * J + 7 : 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
         auto raw8 = [&](const void *x, int ii, int c) {
             return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row(ii) + c);
         };
-        auto widen8 = [&](const uint4 &r, int ii, float (&v)[8]) {
+        // (tokens past nvalid read the last valid row; their Gram entries are
+        // zeroed where the blocks are stored)
+        auto widen8 = [&](const uint4 &r, float (&v)[8]) {
             const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
-                v[2 * q2] = ii < nvalid ? __uint_as_float(wd[q2] << 16) : 0.f;
-                v[2 * q2 + 1] = ii < nvalid ? __uint_as_float(wd[q2] & 0xffff0000u) : 0.f;
+                v[2 * q2] = __uint_as_float(wd[q2] << 16);
+                v[2 * q2 + 1] = __uint_as_float(wd[q2] & 0xffff0000u);
             }
         };
         uint4 rb[2], rq[2], ra[2], rk[2];
@@ -253,16 +280,23 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             ra[sl] = raw8(p.a, j, c);
             rk[sl] = raw8(p.k, j, c);
         };
-        issue(0, 0);
+        if constexpr (kPre) {  // step 0 loaded at the start of the kernel
+            rb[0] = pre[0];
+            rq[0] = pre[1];
+            ra[0] = pre[2];
+            rk[0] = pre[3];
+        } else {
+            issue(0, 0);
+        }
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {
             if (st + 1 < D / 32) issue(st + 1, (st + 1) & 1);
             const int c = 32 * st + 8 * kg;  // this lane's channels c .. c + 7
             float bv[8], qv[8], av[8], kv[8];
-            widen8(rb[st & 1], i, bv);
-            widen8(rq[st & 1], i, qv);
-            widen8(ra[st & 1], j, av);
-            widen8(rk[st & 1], j, kv);
+            widen8(rb[st & 1], bv);
+            widen8(rq[st & 1], qv);
+            widen8(ra[st & 1], av);
+            widen8(rk[st & 1], kv);
             float lb[8], lq[8], xa[8], xk[8];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -287,9 +321,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                                 unsafe[ch >> 5] |= 1u << (ch & 31);
                             }
                     }
-                    const float e3 = safe ? __expf(gm[e4] - gj[e4]) : 0.f;
-                    lb[e] = safe ? bv[e] * __expf(gbi[e4] - gm[e4]) : 0.f;
-                    lq[e] = safe ? qv[e] * __expf(gi[e4] - gm[e4]) : 0.f;
+                    const float e3 = safe ? fast_exp2(gm[e4] - gj[e4]) : 0.f;
+                    lb[e] = safe ? bv[e] * fast_exp2(gbi[e4] - gm[e4]) : 0.f;
+                    lq[e] = safe ? qv[e] * fast_exp2(gi[e4] - gm[e4]) : 0.f;
                     xa[e] = av[e] * e3;
                     xk[e] = kv[e] * e3;
                 }
@@ -317,7 +351,6 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 
     // ---- Gram blocks below the diagonal, one 16x16 block pair per wave
     {
-        constexpr int NPAIR = NTI * (NTI - 1) / 2;
         // (the last waves first: the diagonal work below fills the first ones)
         for (int pr = kDplrWaves - 1 - w; pr < NPAIR; pr += kDplrWaves) {
             int I = 1, J = pr;
@@ -329,7 +362,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
             if constexpr (kGram16) {
                 uint32_t none[4] = {0u, 0u, 0u, 0u};
-                gram16(I, J, std::false_type{}, aab, abk, pqa, pqk, none);
+                gram16(I, J, std::false_type{}, std::true_type{}, aab, abk, pqa, pqk, none);
             } else {
             // the next step's b, q, a, k are loaded while one computes
             Raw4 rb[2], rq[2], ra4[2], rk4[2];
@@ -350,8 +383,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                             kv = widen4(rk4[t & 1], j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float e3 = __expf(gm[e] - gj[e]);
-                    const float lb = bv[e] * __expf(gbi[e] - gm[e]), lq = qv[e] * __expf(gi[e] - gm[e]);
+                    const float e3 = fast_exp2(gm[e] - gj[e]);
+                    const float lb = bv[e] * fast_exp2(gbi[e] - gm[e]), lq = qv[e] * fast_exp2(gi[e] - gm[e]);
                     const float ra = av[e] * e3, rk = kv[e] * e3;
                     aab = mfma4(lb, ra, aab);
                     abk = mfma4(lb, rk, abk);
@@ -363,7 +396,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ii = 16 * I + 4 * kg + r;
-                const bool okA = cnt_before(ii) == sCnt[j], okP = sCnt[ii] == sCnt[j];
+                const bool live = ii < nvalid && j < nvalid;
+                const bool okA = live && cnt_before(ii) == sCnt[j], okP = live && sCnt[ii] == sCnt[j];
                 sM[0][ii][j] = okA ? -aab[r] : 0.f;
                 sM[1][ii][j] = okA ? abk[r] : 0.f;
                 sM[2][ii][j] = okP ? pqa[r] : 0.f;
@@ -384,7 +418,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             f32x4 aab = {0.f, 0.f, 0.f, 0.f}, abk = aab, pqa = aab, pqk = aab;
             uint32_t unsafe[4] = {0u, 0u, 0u, 0u};  // bit c % 32 of word c / 32: channel c
             if constexpr (kGram16) {
-                gram16(J, J, std::true_type{}, aab, abk, pqa, pqk, unsafe);
+                if (has_pair) gram16(J, J, std::true_type{}, std::false_type{}, aab, abk, pqa, pqk, unsafe);
+                else gram16(J, J, std::true_type{}, std::true_type{}, aab, abk, pqa, pqk, unsafe);
             } else {
             Raw4 rb[2], rq[2], ra4[2], rk4[2];
             auto issue = [&](int t, int sl) {
@@ -406,9 +441,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bool safe = gfirst[e] - gm[e] <= kDplrDiagSpan && gm[e] - glast[e] <= kDplrDiagSpan;
-                    const float e3 = safe ? __expf(gm[e] - gj[e]) : 0.f;
-                    const float lb = safe ? bv[e] * __expf(gbi[e] - gm[e]) : 0.f;
-                    const float lq = safe ? qv[e] * __expf(gi[e] - gm[e]) : 0.f;
+                    const float e3 = safe ? fast_exp2(gm[e] - gj[e]) : 0.f;
+                    const float lb = safe ? bv[e] * fast_exp2(gbi[e] - gm[e]) : 0.f;
+                    const float lq = safe ? qv[e] * fast_exp2(gi[e] - gm[e]) : 0.f;
                     const float ra = av[e] * e3, rk = kv[e] * e3;
                     aab = mfma4(lb, ra, aab);
                     abk = mfma4(lb, rk, abk);
@@ -438,7 +473,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                         const int ii = 16 * J + 4 * kg + r;
                         const float bi = in(p.b, ii, ch), qi = in(p.q, ii, ch);
                         const float gbc = ii > 0 ? sG[ii - 1][ch] : 0.f;
-                        const float eA = __expf(fminf(gbc - gjc, 0.f)), eP = __expf(fminf(sG[ii][ch] - gjc, 0.f));
+                        const float eA = fast_exp2(fminf(gbc - gjc, 0.f)), eP = fast_exp2(fminf(sG[ii][ch] - gjc, 0.f));
                         aab[r] += bi * aj * eA;
                         abk[r] += bi * kj * eA;
                         pqa[r] += qi * aj * eP;
@@ -449,8 +484,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ii = 16 * J + 4 * kg + r;
-                const bool okA = j < ii && cnt_before(ii) == sCnt[j];
-                const bool okP = j <= ii && sCnt[ii] == sCnt[j];
+                const bool live = ii < nvalid && j < nvalid;
+                const bool okA = live && j < ii && cnt_before(ii) == sCnt[j];
+                const bool okP = live && j <= ii && sCnt[ii] == sCnt[j];
                 sM[0][ii][j] = okA ? -aab[r] : 0.f;
                 sM[1][ii][j] = okA ? abk[r] : 0.f;
                 sM[2][ii][j] = okP ? pqa[r] : 0.f;
@@ -491,8 +527,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     for (int x = 0; x < 4; ++x)
 #pragma unroll
                         for (int y = 0; y < 4; ++y) {
-                            const float eA = __expf(fminf(gbi[x][e] - gj[y][e], 0.f));
-                            const float eP = __expf(fminf(gi[x][e] - gj[y][e], 0.f));
+                            const float eA = fast_exp2(fminf(gbi[x][e] - gj[y][e], 0.f));
+                            const float eP = fast_exp2(fminf(gi[x][e] - gj[y][e], 0.f));
                             acc[0][x][y] += bv[x][e] * av[y][e] * eA;
                             acc[1][x][y] += bv[x][e] * kv[y][e] * eA;
                             acc[2][x][y] += qv[x][e] * av[y][e] * eP;
@@ -731,7 +767,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                         const int j = 32 * s2 + 8 * kg + e;
                         const float gb = j > 0 ? sG[j - 1][cx] : 0.f;
                         const float bv = __uint_as_float(static_cast<uint32_t>(braw[s2][e]) << 16);
-                        xv[e] = j < nvalid && cnt_before(j) == 0 ? bv * __expf(gb) : 0.f;
+                        xv[e] = j < nvalid && cnt_before(j) == 0 ? bv * fast_exp2(gb) : 0.f;
                     }
                     split_bf16(xv, xh[s2], xl[s2]);
                 }
@@ -742,7 +778,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                     const f32x4 gv = g4(i, c0);
                     const bool live = sCnt[i] == 0;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * __expf(gv[r]) : 0.f;
+                    for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * fast_exp2(gv[r]) : 0.f;
                 }
 #pragma unroll
                 for (int rt = 0; rt < 2 * NTI; ++rt) {
@@ -781,7 +817,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * t + 4 * kg + e;
                     const float gb = j > 0 ? sG[j - 1][cx] : 0.f;
-                    xf[t][e] = cnt_before(j) == 0 ? braw[t][e] * __expf(gb) : 0.f;
+                    xf[t][e] = cnt_before(j) == 0 ? braw[t][e] * fast_exp2(gb) : 0.f;
                 }
             // the Q e^G terms of the Q' rows
             f32x4 qg[NTI];
@@ -791,7 +827,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                 const f32x4 gv = g4(i, c0);
                 const bool live = sCnt[i] == 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * __expf(gv[r]) : 0.f;
+                for (int r = 0; r < 4; ++r) qg[I][r] = live ? qraw[I][r] * fast_exp2(gv[r]) : 0.f;
             }
             for (int rt = 0; rt < 2 * NTI; ++rt) {
                 const int I = rt < NTI ? rt : rt - NTI, mt = rt < NTI ? 0 : 2;
@@ -839,7 +875,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = 32 * s0 + 8 * kg + e, jj = j < C ? j : C - 1;
-                    v8[e] = (j < C && sCnt[jj] == cnt_last) ? akraw[s][e] * __expf(sG[C - 1][cx] - sG[jj][cx]) : 0.f;
+                    v8[e] = (j < C && sCnt[jj] == cnt_last) ? akraw[s][e] * fast_exp2(sG[C - 1][cx] - sG[jj][cx]) : 0.f;
                 }
                 store8(kt + ((static_cast<size_t>(ct) * KSC2 + s) * 64 + lane) * 8, v8);
             }
@@ -916,7 +952,7 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         }
     }
     float *glp = reinterpret_cast<float *>(pkg + p.L.gl);
-    for (int c = tid; c < D; c += kDplrThreads) glp[c] = last_rst >= 0 ? 0.f : __expf(sG[C - 1][c]);
+    for (int c = tid; c < D; c += kDplrThreads) glp[c] = last_rst >= 0 ? 0.f : fast_exp2(sG[C - 1][c]);
 }
 
 template <int C, int D, bool BF>
