@@ -120,6 +120,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
     constexpr int MP = C + 8;  // bf16 row stride of the hi/lo planes (16-byte rows)
     constexpr size_t kMF = sizeof(float) * 4 * C * MS, kMB = kPk16 ? sizeof(__bf16) * 8 * C * MP : 0;
     __shared__ __align__(16) float sG[C][GS];  // G, cumulative log-decay in base 2 (log2 e times the natural one)
+    constexpr bool kGram16 = BF && D >= 32;  // the bf16 matrix-core Gram path
+    // alpha_i = e^{G_i - G_{i-1}} (16-bit Gram path): q's factor is b's times alpha_i
+    __shared__ __align__(16) float sAl[kGram16 ? C : 1][GS];
     // -Aab -> T, Abk -> T Abk, Pqa -> Pqa T, Pqk -> Pqa T Abk + Pqk (fp32); on the
     // 16-bit path overlaid at the end by the same four as bf16 hi/lo planes
     __shared__ __align__(16) unsigned char sMraw[kMF > kMB ? kMF : kMB];
@@ -226,7 +229,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
         float acc = 0.f;
         for (int r = 0; r < RPS; ++r) {
             const int i = sseg * RPS + r;
-            acc += sRst[i] ? 0.f : fmaxf(sG[i][sc], kGFloor) * kLog2e;
+            const float dg = sRst[i] ? 0.f : fmaxf(sG[i][sc], kGFloor) * kLog2e;
+            if constexpr (kGram16) sAl[i][sc] = fast_exp2(dg);
+            acc += dg;
             sG[i][sc] = acc;
         }
         sSeg[sseg][sc] = acc;
@@ -301,7 +306,8 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int c4 = c + 4 * hh;
-                const f32x4 gm = g4(m, c4), gbi = g4(i - 1, c4), gi = g4(i, c4), gj = g4(j, c4);
+                const f32x4 gm = g4(m, c4), gbi = g4(i - 1, c4), gj = g4(j, c4);
+                const f32x4 al = *reinterpret_cast<const f32x4 *>(&sAl[i][c4]);
                 f32x4 gfirst = gm, glast = gm;
                 if constexpr (kDiag) {
                     gfirst = g4(16 * J - 1, c4);
@@ -322,8 +328,9 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
                             }
                     }
                     const float e3 = safe ? fast_exp2(gm[e4] - gj[e4]) : 0.f;
-                    lb[e] = safe ? bv[e] * fast_exp2(gbi[e4] - gm[e4]) : 0.f;
-                    lq[e] = safe ? qv[e] * fast_exp2(gi[e4] - gm[e4]) : 0.f;
+                    const float fb = safe ? fast_exp2(gbi[e4] - gm[e4]) : 0.f;
+                    lb[e] = bv[e] * fb;
+                    lq[e] = qv[e] * (fb * al[e4]);
                     xa[e] = av[e] * e3;
                     xk[e] = kv[e] * e3;
                 }
@@ -347,7 +354,6 @@ __global__ void __launch_bounds__(kDplrThreads) dplr_intra_kernel(DplrIntraParam
             pqk = mfma_bf16(lqh, xkh, pqk);
         }
     };
-    constexpr bool kGram16 = BF && D >= 32;  // the bf16 matrix-core Gram path
 
     // ---- Gram blocks below the diagonal, one 16x16 block pair per wave
     {
