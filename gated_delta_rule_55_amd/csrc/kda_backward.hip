@@ -616,8 +616,8 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
     __shared__ float sM[4][C][MS];  // Abar; P -> dT -> dAbar; T; Y -> dP
     __shared__ float sBeta[C];
     __shared__ int sCnt[C], sNotRst[C];
-    __shared__ float sGC[D], sdGL[D];
-    __shared__ float sPart[C][NTD], sPart2[C][NTI], sPart3[NTI][D];
+    __shared__ float sGC[D];
+    __shared__ float sPart[C][NTD], sPart2[C][NTI];
     __shared__ int sFirst, sLast;
     __shared__ uint8_t sNegInf[C][D];  // log_alpha is -inf here (its gradient is 0)
     // the cumulative decay and the reverse cumulative sum of dG run in NSEG
@@ -1016,6 +1016,9 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         // element r of tile I is token 16 I + 4 (lane / 16) + r, channel
         // 16 w + lane % 16 (the matrix cores' output layout).
         f32x4 DQr[NTI], DKr[NTI], DGr[NTI];
+        // dG of the chunk's last token at this lane's channel (wave w < NTD):
+        // dGamma_C = rowsum(S0 * dS1) times Gamma_C, plus the dKt terms
+        float dgl = 0.f;
         // ---- d(Q*Gamma) = dO S0^T, d(K*Gamma) = -dR S0^T, dKt = U dS1^T and
         //      their Gamma terms
         if (w < NTD) {
@@ -1026,12 +1029,48 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
             const Frag<D> bS1T = frag_of<D>([&](int k0, int nn) {
                 return ld4(dS1 + static_cast<size_t>(16 * w + nn) * D + k0);
             }, lane);
+            // row c of S0 and dS1 are in the two fragments already: this lane holds
+            // columns 16 t + 4 (lane / 16) + j, the four lanes of row c all of them
+            {
+                float rs = 0.f;
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rs += bS0T.v[t][j] * bS1T.v[t][j];
+                rs += __shfl_xor(rs, 16);
+                rs += __shfl_xor(rs, 32);
+                dgl = rs * sGC[c];
+            }
+            // the 3 NTI products dO_I S0^T, dR_I S0^T, U_I dS1^T in that order, each
+            // one's left-hand rows loaded while the product before it runs
+            constexpr int NKT = D / 16;
+            f32x4 Ab[2][NKT];
+            auto lda = [&](int pidx, f32x4 (&a)[NKT]) {
+                const int ti = pidx / 3, which = pidx % 3, row = 16 * ti + l16;
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    const int k0 = 16 * t + 4 * kg;
+                    if (which == 0) a[t] = dO4(row, k0);
+                    else a[t] = ld4((which == 1 ? DR : U) + row * D + k0);
+                }
+            };
+            auto mma_pre = [&](f32x4 &acc, const f32x4 (&a)[NKT], const Frag<D> &bf) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][j], bf.v[t][j], acc, 0, 0, 0);
+            };
+            lda(0, Ab[0]);
 #pragma unroll
             for (int ti = 0; ti < NTI; ++ti) {
                 f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, at = aq;
-                mm_f32_vb<D>(aq, [&](int r, int k0) { return dO4(16 * ti + r, k0); }, bS0T, lane);
-                mm_f32_vb<D>(ak, [&](int r, int k0) { return ld4(DR + (16 * ti + r) * D + k0); }, bS0T, lane);
-                mm_f32_vb<D>(at, [&](int r, int k0) { return ld4(U + (16 * ti + r) * D + k0); }, bS1T, lane);
+                const int p0 = 3 * ti;
+                lda(p0 + 1, Ab[(p0 + 1) & 1]);
+                mma_pre(aq, Ab[p0 & 1], bS0T);
+                lda(p0 + 2, Ab[(p0 + 2) & 1]);
+                mma_pre(ak, Ab[(p0 + 1) & 1], bS0T);
+                if (ti + 1 < NTI) lda(p0 + 3, Ab[(p0 + 3) & 1]);
+                mma_pre(at, Ab[(p0 + 2) & 1], bS1T);
                 float colsum = 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -1049,25 +1088,10 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                 }
                 colsum += __shfl_xor(colsum, 16);
                 colsum += __shfl_xor(colsum, 32);
-                if (kg == 0) sPart3[ti][c] = colsum;
+                dgl += colsum;
             }
         }
-        __syncthreads();
-        // dG of the chunk's last token: dKt terms and dGamma_C = rowsum(S0 * dS1),
-        // one wave per row (coalesced), rows c = w, w + 8, ...
-        for (int c = w; c < D; c += kIW) {
-            float s = 0.f;
-#pragma unroll
-            for (int v = lane; v < D; v += 64) s += S0[static_cast<size_t>(c) * D + v] * dS1[static_cast<size_t>(c) * D + v];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-            if (lane == 0) {
-                float acc = s * sGC[c];
-                for (int ti = 0; ti < NTI; ++ti) acc += sPart3[ti][c];
-                sdGL[c] = acc;
-            }
-        }
-        __syncthreads();  // sdGL complete
+        __syncthreads();  // dP complete
         // ---- the decay-weighted products e^{G_i - G_j} of dP (with q_i, k_j) and
         //      dAbar (with k_i, k_j), on the fp32 matrix cores, one 16-token block
         //      pair (I >= J) at a time.  With a reference token m,
@@ -1197,10 +1221,10 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                     }
                 }
             // ---- dlog_alpha = reverse cumulative sum of dG over the chunk, from
-            //      the last token's dG term in sdGL: within each lane's four tokens
+            //      the last token's dG term (dgl): within each lane's four tokens
             //      of a block, then over the four lanes of the channel (lane / 16),
             //      then over the blocks, last first
-            GT after_blocks = sdGL[c];
+            GT after_blocks = dgl;
 #pragma unroll
             for (int I = NTI - 1; I >= 0; --I) {
                 GT suf[4];
