@@ -740,7 +740,7 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
         //      sM[2] and sM[3], not yet in use) and are added in a fixed order.
         {
             constexpr int NPAIR = NTI * (NTI - 1) / 2;
-            for (int pr = w; pr < NPAIR; pr += kIW) {
+            auto pair_job = [&](int pr) {
                 int I = 1, J = pr;
                 while (J >= I) { J -= I; ++I; }
                 const int m = 16 * J + 15, i = 16 * I + l16, j = 16 * J + l16;
@@ -761,7 +761,68 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                     sM[0][ii][j] = nores ? acA[r] : 0.f;
                     sM[1][ii][j] = nores ? acP[r] : 0.f;
                 }
+            };
+            if constexpr (BF) {
+            // 16-bit path: the diagonal blocks on the matrix cores too, with the
+            // block's token 7 as the reference (factors up to e^kDiagSpan); a
+            // channel spanning more on either side of it is left out of the
+            // products and added with the exact exponential of every pair.  Jobs:
+            // the NPAIR blocks below the diagonal, then the NTI diagonal ones.
+            for (int jb = w; jb < NPAIR + NTI; jb += kIW) {
+                if (jb < NPAIR) {
+                    pair_job(jb);
+                    continue;
+                }
+                const int J = jb - NPAIR, m = 16 * J + 7, j = 16 * J + l16;
+                f32x4 acA = {0.f, 0.f, 0.f, 0.f}, acP = acA;
+                constexpr int NWD = (D + 31) / 32, SPW = D / 4 < 8 ? D / 4 : 8;  // words, 4-channel steps per word
+                uint32_t uns[NWD];  // bit c % 32 of word c / 32: channel c left out
+#pragma unroll
+                for (int wd = 0; wd < NWD; ++wd) {
+                    uint32_t bits = 0u;
+#pragma unroll 4
+                    for (int s8 = 0; s8 < SPW; ++s8) {
+                        const int c = 32 * wd + 4 * s8 + kg;
+                        const GT Gm = sG[m][c];
+                        const bool safe = sG[16 * J][c] - Gm <= GT(kDiagSpan) && Gm - sG[16 * J + 15][c] <= GT(kDiagSpan);
+                        const float fa = safe ? __expf(static_cast<float>(sG[j][c] - Gm)) : 0.f;
+                        const float fb = safe ? __expf(static_cast<float>(Gm - sG[j][c])) * toF(sK[j][c]) : 0.f;
+                        acA = __builtin_amdgcn_mfma_f32_16x16x4f32(fa * toF(sK[j][c]), fb, acA, 0, 0, 0);
+                        acP = __builtin_amdgcn_mfma_f32_16x16x4f32(fa * toF(sQ[j][c]), fb, acP, 0, 0, 0);
+                        const uint64_t ub = __ballot(!safe);  // lane 16 g: channel 32 wd + 4 s8 + g
+                        const uint32_t nib = static_cast<uint32_t>((ub & 1u) | ((ub >> 15) & 2u) | ((ub >> 30) & 4u) |
+                                                                   ((ub >> 45) & 8u));
+                        bits |= nib << (4 * s8);
+                    }
+                    uns[wd] = bits;
+                }
+#pragma unroll
+                for (int wd = 0; wd < NWD; ++wd) {
+                    uint32_t bits = uns[wd];
+                    while (bits) {  // rare
+                        const int ch = 32 * wd + __builtin_ctz(bits);
+                        bits &= bits - 1u;
+                        const GT Gj = sG[j][ch];
+                        const float kj = toF(sK[j][ch]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int ii = 16 * J + 4 * kg + r;
+                            const float e = __expf(fminf(static_cast<float>(sG[ii][ch] - Gj), 0.f)) * kj;
+                            acA[r] += toF(sK[ii][ch]) * e;
+                            acP[r] += toF(sQ[ii][ch]) * e;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ii = 16 * J + 4 * kg + r;
+                    const bool nores = sCnt[ii] == sCnt[j];
+                    sM[0][ii][j] = (j < ii && nores) ? acA[r] : 0.f;
+                    sM[1][ii][j] = (j <= ii && nores) ? acP[r] : 0.f;
+                }
             }
+            } else {
+            for (int pr = w; pr < NPAIR; pr += kIW) pair_job(pr);
             constexpr int NSB = NTI * 10;
             constexpr int NQ = (4 * NSB <= kBwdIntraThreads && 3 * NSB * 32 <= 2 * C * MS) ? 4
                              : (2 * NSB <= kBwdIntraThreads && NSB * 32 <= 2 * C * MS) ? 2 : 1;
@@ -821,6 +882,7 @@ __global__ void __launch_bounds__(kBwdIntraThreads) intra_bwd_kernel(BwdIntraPar
                         sM[0][i][j] = (j < i && nores) ? a[x][y] : 0.f;
                         sM[1][i][j] = (j <= i && nores) ? pp[x][y] : 0.f;
                     }
+            }
             }
         }
         __syncthreads();
