@@ -30,8 +30,12 @@
 // state entering every chunk (kda_prefill.hip), then bwd_state_kernel walks
 // each (sequence, head, 16-column slab) backwards writing dS1 of every chunk
 // and dS0 of the sequence, then intra_bwd_kernel computes every gradient of
-// one (chunk, head) at a time.  All arithmetic after the package is fp32
-// (fp32 matrix cores, exact exponentials of every decay pair).
+// one (chunk, head) at a time.  Products after the package run on the fp32
+// matrix cores with fp32 accumulation (on the 16-bit path the reverse state
+// pass uses fp16 hi/lo operands); the decay factors of a 16-token block pair
+// go through a reference token (both factors <= 1 below the diagonal; on the
+// diagonal, 16-bit path only, the block's token 7 with an exact per-pair
+// fallback for channels whose decay spans more than e^40).
 #include <algorithm>
 #include <type_traits>
 
