@@ -138,15 +138,15 @@ def measured_traffic(key):
 
 # Kernels of each C-ABI launch on the 1M-token prefill / 256x32-state decode
 # workloads (rocprofv3 names, shortened).  The state pass is one kernel for
-# every prefill variant: its last dispatch in a bench run is the layer's, and
-# its traffic is the same for all (the package does not depend on the gate).
+# the KDA and GDN prefills (its traffic does not depend on the gate); the
+# layer's is its own kernel with the RMSNorm and output gate fused.
 KDA_INTRA = "kda::intra_wide_kernel<0>"
 GDN_INTRA = "kda::intra_wide_kernel<1>"
 STATE = "kda::state_kernel<64, 128, 128, true, false>"
 KDA_DECODE = "kda::decode_step_kernel<128, 128, true, 0>"
 GDN_DECODE = "kda::decode_step_kernel<128, 128, true, 1>"
 LAYER_INTRA = "kda::intra_wide_kernel<2>"
-LAYER_EPILOGUE = "kda::layer_epilogue_kernel"
+LAYER_STATE = "kda::layer_state_kernel"
 LAYER_DECODE = "kda::decode_step_kernel<128, 128, true, 2>"
 DPLR_INTRA = "kda::dplr_intra_kernel<64, 128, true>"
 DPLR_STATE = "kda::dplr_state_kernel<64, 128, 128, true>"
@@ -156,7 +156,7 @@ LAUNCH_KERNELS = {
     "kda_decode_step": (KDA_DECODE,),
     "gdn_chunk_fwd": (GDN_INTRA, STATE),
     "gdn_decode_step": (GDN_DECODE,),
-    "kda_layer_chunk_fwd": (LAYER_INTRA, STATE, LAYER_EPILOGUE),
+    "kda_layer_chunk_fwd": (LAYER_INTRA, LAYER_STATE),
     "kda_layer_decode_step": (LAYER_DECODE,),
     "kda_dplr_chunk_fwd": (DPLR_INTRA, DPLR_STATE),
     "kda_dplr_decode_step": (DPLR_DECODE,),
@@ -803,9 +803,12 @@ def main():
     ld_g = bfn((dsteps, dw.N, dw.H, dw.Dv))
     lstate = state0.clone()
 
+    # the layer's workspace: the prefill's plus its row-norm exchange
+    l_ws = torch.empty(kda.layer_workspace_size(1, T, H), dtype=torch.uint8, device=dev)
+
     def layer_prefill():
         kda.layer_chunk_fwd(pin["q"], pin["k"], pin["v"], l_xa, l_xb, l_g, l_w, 1e-6, 1e-5,
-                            out=o, final_state=fs, workspace=ws)
+                            out=o, final_state=fs, workspace=l_ws)
 
     def layer_decode(t):
         kda.layer_decode_step(din["q"][t], din["k"][t], din["v"][t], ld_xa[t], ld_xb[t], ld_g[t], l_w,
@@ -813,7 +816,7 @@ def main():
 
     warm(layer_prefill, layer_decode)
     l_pre_ms, l_dec_ms = timed(layer_prefill, layer_decode)
-    del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g
+    del l_xa, l_xb, l_g, ld_xa, ld_xb, ld_g, l_ws
 
     _step("KDA layer timed")
     # ---- the general DPLR recurrence on the same q, k, v and gates (kda_dplr_chunk_fwd)
@@ -1003,8 +1006,7 @@ def main():
             "tokens_per_s": T / l_t_pre,
             "hbm_frac_algorithmic": l_pb / l_t_pre / HBM_PEAK,
             "alg_bytes": l_pb,
-            "roofline": {"kernel": "kda_layer_chunk_fwd (intra_wide_kernel<2> + state_kernel + "
-                                   "layer_epilogue_kernel)",
+            "roofline": {"kernel": "kda_layer_chunk_fwd (intra_wide_kernel<2> + layer_state_kernel)",
                          "bound": "hbm", "achieved": l_pb / l_t_pre / 1e9,
                          "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                          "frac": l_pb / l_t_pre / HBM_PEAK,

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
@@ -21,6 +23,18 @@ kda_status fail(kda_status s, const char *fmt, ...) {
 }
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// A nonzero tag per layer prefill call: the state pass marks its row-norm
+// partial sums with it, so words left in a reused workspace by an earlier call
+// never pass for this call's.
+uint32_t next_layer_tag() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t t;
+    do {
+        t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (t == 0);
+    return t;
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -192,7 +206,7 @@ kda_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
 
 static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t Dv, int32_t N,
                             bool varlen, bool bf16, int32_t C, size_t &out, size_t &pkg,
-                            int64_t &slots, bool dplr = false) {
+                            int64_t &slots, bool dplr = false, bool layer = false) {
     const kda::PackageLayout L = dplr ? kda::dplr_package_layout(C, Dk, Dv, bf16)
                                       : kda::package_layout(C, Dk, Dv, bf16);
     pkg = L.bytes;
@@ -203,6 +217,11 @@ static bool workspace_bytes(int32_t B, int64_t T, int32_t H, int32_t Dk, int32_t
         const size_t plan = kda::align256(((size_t)N + 1) * sizeof(int32_t));
         if (total > SIZE_MAX - plan) return false;
         total += plan;
+    }
+    if (layer) {  // the KDA layer's row-norm exchange
+        size_t x = kda::norm_xchg_bytes(C, Dv);
+        if (!mul_ok(x, (uint64_t)slots) || !mul_ok(x, (uint64_t)H) || total > SIZE_MAX - x) return false;
+        total += x;
     }
     out = total;
     return true;
@@ -221,6 +240,16 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t Dk,
     int64_t slots = 0;
     if (!workspace_bytes(B, T, H, Dk, Dv, varlen ? n_seqs : B, varlen, in_dtype == KDA_BF16,
                          chunk_size, out, pkg, slots))
+        return 0;
+    return out;
+}
+
+size_t kda_layer_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t n_seqs) {
+    if (B < 1 || T < 0 || H < 1 || n_seqs < 0) return 0;
+    const bool varlen = n_seqs > 0 && B == 1;
+    size_t out = 0, pkg = 0;
+    int64_t slots = 0;
+    if (!workspace_bytes(B, T, H, 128, 128, varlen ? n_seqs : B, varlen, true, 64, out, pkg, slots, false, true))
         return 0;
     return out;
 }
@@ -306,7 +335,8 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         return fail(KDA_ERR_INVALID_ARG, "final_state is not 16-byte aligned");
     size_t need_ws = 0, pkg = 0;
     int64_t slots = 0;
-    if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots, gate_mode == 3))
+    if (!workspace_bytes(B, T, H, Dk, Dv, N, varlen, bf16, chunk_size, need_ws, pkg, slots, gate_mode == 3,
+                         gate_mode == 2))
         return fail(KDA_ERR_INVALID_ARG, "workspace size overflows size_t");
     if (static_ws) {
         // the library's own device array stands in for the workspace; it is
@@ -361,11 +391,14 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         a.norm_weight = L->norm_weight;
         a.l2_eps = L->l2_eps;
         a.norm_eps = L->norm_eps;
+        a.layer_tag = next_layer_tag();
     }
     a.workspace = static_cast<char *>(workspace);
     a.n_slots = slots; a.pkg_bytes = pkg;
     a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
                              : nullptr;
+    if (gate_mode == 2)  // after the packages and the plan: the last bytes of the workspace
+        a.norm_xchg = a.workspace + need_ws - kda::norm_xchg_bytes(chunk_size, Dv) * (size_t)slots * (size_t)H;
     if (T == 0) {
         // Every sequence is empty (cu[N] = T = 0): only final_state <- init_state
         // remains.  Run it as a dense batch of N empty sequences so that neither
@@ -374,6 +407,7 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
         a.B = N;
         a.n_slots = 0;
         a.workspace = nullptr;
+        a.norm_xchg = nullptr;
         a.chunk_offsets = nullptr;
     }
     a.lr_a = lr_a; a.lr_b = lr_b;

@@ -102,11 +102,22 @@ struct PrefillArgs {
     const float *norm_weight;
     float l2_eps, norm_eps;
     float *o, *final_state;     // final_state nullable
+    uint32_t layer_tag;         // gate mode 2: this call's nonzero tag for the norm exchange
+    char *norm_xchg;            // gate mode 2: the row-norm exchange in the workspace
     char *workspace;
     int64_t n_slots;            // chunk slots in the workspace
     size_t pkg_bytes;
     int32_t *chunk_offsets;     // varlen: [N + 1] in the workspace
 };
+
+// The KDA layer's row-norm exchange, after the packages (and the varlen plan)
+// in the prefill workspace: per (chunk slot, head), 64-bit words [Dv / 16][CP],
+// word (slab s, token i) = (call tag << 32) | bits of the sum of o^2 over the
+// 16 columns of slab s for token i, written by that slab's state-pass
+// workgroup and read by the other slabs of the head.
+__host__ __device__ inline size_t norm_xchg_bytes(int C, int Dv) {
+    return align256((size_t)(Dv < 16 ? 1 : Dv / 16) * (C < 32 ? 32 : C) * 8);
+}
 
 // Chunk slots the workspace reserves: every chunk of every sequence.
 inline int64_t prefill_slots(int32_t B, int64_t T, int32_t N, int32_t C, bool varlen) {
@@ -118,11 +129,6 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 // The DPLR form's prefill (gate mode 3; Dk = Dv, packages of dplr_package_layout).
 hipError_t launch_dplr(const PrefillArgs &a, hipStream_t stream);
-
-// o <- o / sqrt(mean_j o_j^2 + eps) * w * sigmoid(g) over each row of Dv = 128
-// values, in place (the KDA layer's epilogue), rows = B * T * H.
-hipError_t launch_layer_epilogue(float *o, const uint16_t *g, const float *w, int64_t rows, float eps,
-                                 hipStream_t stream);
 
 // Backward of the prefill: fwd describes the forward call (its o and
 // final_state are unused; its workspace holds the packages and, for varlen,

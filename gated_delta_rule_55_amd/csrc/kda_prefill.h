@@ -57,6 +57,13 @@ struct StateParams {
     const float *carry_in = nullptr;
     float *carry_out = nullptr;
     bool do_empty = true;
+    // The KDA layer's epilogue (layer_state_kernel): out = o / sqrt(mean o^2 +
+    // norm_eps) * norm_weight * sigmoid(out_gate) per (token, head) row.
+    const uint16_t *out_gate = nullptr;
+    const float *norm_weight = nullptr;
+    float norm_eps = 0.f;
+    uint32_t layer_tag = 0;
+    uint64_t *norm_xchg = nullptr;  // [slots][H][Dv / 16][CP] words (norm_xchg_bytes each (slot, head))
 };
 
 struct BwdStateParams {

@@ -737,7 +737,37 @@ struct StateFrags {
 // SAVE: the saving variant (the backward's forward pass) writes the state
 // entering each chunk to p.chunk_states and stores no output.  LR2: the DPLR
 // form (see StateFrags).
-template <int C, int DK, int DV, bool BF, bool SAVE, bool LR2>
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
+                                                                 true));
+}
+// orders a wave's own LDS accesses around a change of a buffer's role
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// sum over each group of four lanes, in every lane of the group
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<0xb1>(x);    // quad_perm [1, 0, 3, 2]
+    return x + dpp_mov<0x4e>(x);  // quad_perm [2, 3, 0, 1]
+}
+
+// The KDA layer's fused epilogue (LAYER): a row's sum of o^2 is spread over the
+// eight slab workgroups of its head, so each writes its per-token partial sums
+// into the chunk's package (NP section, tagged with the call's tag in one 64-bit
+// relaxed atomic store) and scales its own o two chunk steps later, when the
+// other slabs' partials of that chunk are in L2 (read back with L1-bypassing
+// atomic loads until all eight tags match).  The layer's grid puts the eight
+// slabs of a (sequence, head) unit on one XCD (one L2) and next to each other in
+// that XCD's dispatch order, so all eight are resident together whenever the
+// XCD holds eight workgroups: no slab waits on one that cannot start.  Every
+// wait is bounded; a workgroup whose wait runs out writes NaN rows from then on.
+constexpr int kLayerLag = 4;             // chunk steps between writing and reading partials
+constexpr int kLayerSpinLimit = 1 << 16; // polls of one chunk's partials before giving up
+
+template <int C, int DK, int DV, bool BF, bool SAVE, bool LR2, bool LAYER = false>
 __device__ __forceinline__ void state_body(const StateParams &p) {
     using F = Cfg<C, DK, DV, BF>;
     using Op = typename F::Op;
@@ -750,11 +780,26 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 
     __shared__ __align__(16) Op sS[16][SSS];          // state slab as a B operand [col][channel]
     __shared__ __align__(16) Op sU[PARTS][16][SUS];   // U (hi, lo) as a B operand [col][token]
+    // LAYER: each wave's 16 x 16 tile of o, turned from the accumulator layout
+    // (lane l: rows 4 (l / 16) .. + 3 of column l % 16) into rows of four
+    // columns (lane l: row 4 (l / 16) + (l % 16) / 4, columns 4 (l % 4) .. + 3):
+    // a row's partial sum is then a sum over four lanes, and the lane reads its
+    // output gate and writes its output as one vector each
+    __shared__ __align__(16) float sO[LAYER ? 4 : 1][16][16];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
+    int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
     const int H = p.H;
+    if constexpr (LAYER) {
+        // one-dimensional grid: block 64 g + 8 ct + x is slab ct of unit 8 g + x
+        static_assert(DV == 128, "eight 16-column slabs");
+        const int b = blockIdx.x, unit = 8 * (b >> 6) + (b & 7);
+        ct = (b >> 3) & 7;
+        if (unit >= p.N * H) return;  // so are its seven siblings
+        n = unit / H;
+        h = unit - n * H;
+    }
 
     int64_t tok_base, L, slot_base;
     if (p.cu_seqlens) {
@@ -780,6 +825,24 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 
     const int col = 16 * ct + l16;
     const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+
+    // LAYER: o of a chunk waits kLayerLag steps for the other slabs' partial
+    // sums; this wave's 16 rows of it (o and the output gate's bf16 bits, in
+    // the row layout of sO below) wait in a queue: entry i holds chunk
+    // c - kLayerLag + i at step c, so no chunk index is kept
+    constexpr int QN = LAYER ? kLayerLag : 1;
+    f32x4 qov[QN];
+    uint2 qg[QN];
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+        qov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qg[i] = uint2{0u, 0u};
+    }
+    bool gave_up = false;
+    const int orow4 = 4 * kg + (l16 >> 2), ocol4 = 4 * (l16 & 3);  // this lane's row and columns of an o tile
+    f32x4 w4 = {0.f, 0.f, 0.f, 0.f};  // LAYER: RMSNorm weights of those columns (none needed at T = 0)
+    if constexpr (LAYER)
+        if (p.norm_weight) w4 = *reinterpret_cast<const f32x4 *>(p.norm_weight + 16 * ct + ocol4);
     // the state entering chunk cb: the initial state, or the one carried in
     const float *s_in = cb == 0 ? (p.init_state ? p.init_state + sbase : nullptr)
                                 : p.carry_in + static_cast<size_t>(h) * DK * DV;
@@ -810,6 +873,62 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
     };
     put_state();
 
+    // LAYER: this lane's two partial-sum words of chunk c - kLayerLag, loaded
+    // at the start of step c, before chunk c + 2's package, so that waiting for
+    // them at the end of the step never waits for package loads still in flight
+    uint64_t pwa = 0, pwb = 0;
+    // (lane l: slabs 2 (l % 4) and 2 (l % 4) + 1 of its o row, 16 w + orow4)
+    auto poll_words = [&](int64_t pc) {
+        return p.norm_xchg + (static_cast<size_t>(slot_base + pc - p.s0) * H + h) * (norm_xchg_bytes(C, DV) / 8) +
+               2 * (l16 & 3) * CP + 16 * w + orow4;
+    };
+    auto poll_issue = [&](int64_t c) {
+        if constexpr (LAYER) {
+            if (c - kLayerLag >= cb) {
+                const uint64_t *np = poll_words(c - kLayerLag);
+                pwa = __hip_atomic_load(np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pwb = __hip_atomic_load(np + CP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    };
+
+    // LAYER: scales and stores this wave's 16 rows of chunk pc once the eight
+    // slabs' partial sums of that chunk are readable
+    // (loaded: the words were loaded for this chunk at the start of the step;
+    // otherwise they are loaded here)
+    auto finish = [&](const f32x4 ov, const uint2 g, const int64_t pc, bool loaded) {
+        const int I = w;  // the wave's Q' row tile is w + NT16
+        const int64_t rem = L - pc * C;
+        const int nv = static_cast<int>(rem < C ? rem : C);
+        const uint64_t *np = poll_words(pc);
+        uint64_t a = pwa, b = pwb;
+        if (!gave_up) {
+            for (int it = 0;; ++it) {
+                if (!loaded || it > 0) {
+                    if (it > 0) __builtin_amdgcn_s_sleep(2);
+                    a = __hip_atomic_load(np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    b = __hip_atomic_load(np + CP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                const bool ok = static_cast<uint32_t>(a >> 32) == p.layer_tag &&
+                                static_cast<uint32_t>(b >> 32) == p.layer_tag;
+                if (__ballot(!ok) == 0) break;
+                if (it >= kLayerSpinLimit) {
+                    gave_up = true;
+                    break;
+                }
+            }
+        }
+        const float ss = quad_sum(__uint_as_float(static_cast<uint32_t>(a)) + __uint_as_float(static_cast<uint32_t>(b)));
+        const float rs = gave_up ? __builtin_nanf("") : 1.f / sqrtf(ss * (1.f / DV) + p.norm_eps);
+        const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
+                             __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xffff0000u)};
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = ov[e] * rs * w4[e] * sigmoid_f(gv[e]);
+        const int row = 16 * I + orow4;
+        if (row < nv) *reinterpret_cast<f32x4 *>(p.o + ((tok_base + pc * C + row) * H + h) * DV + 16 * ct + ocol4) = y;
+    };
+
     // one chunk of the recurrence on this slab, operands from registers;
     // kPartial: the sequence's last chunk has fewer than C tokens (its o stores
     // are masked; full chunks store unconditionally so the hot loop has no
@@ -818,6 +937,8 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
         constexpr bool kPartial = decltype(partial_tag)::value;
         const int64_t rem = L - c * C;
         const int nvalid = static_cast<int>(rem < C ? rem : C);
+        f32x4 cov = {0.f, 0.f, 0.f, 0.f};
+        uint2 cg = {0u, 0u};
         if constexpr (SAVE) {
           if (p.chunk_states) {
             float *cs = p.chunk_states + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * DK * DV;
@@ -867,6 +988,29 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
                         if constexpr (BF) sU[1][l16][CP + j] = static_cast<Op>(x - static_cast<float>(xh));
                     }
                 }
+            } else if constexpr (LAYER) {
+                // o in the row layout (sO); this slab's sum of o^2 per row,
+                // published for the other slabs; o and the output gate wait in
+                // the queue
+                const int I = rt - NT16;
+                const f32x4 ov = f.uo[rw] + acc;
+                float(*t)[16] = sO[w];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t[4 * kg + r][l16] = ov[r];
+                wave_lds_sync();
+                const f32x4 o4 = *reinterpret_cast<const f32x4 *>(&t[orow4][ocol4]);
+                const int row = 16 * I + orow4;  // o row of this lane in the chunk
+                const float ps = quad_sum(o4[0] * o4[0] + o4[1] * o4[1] + o4[2] * o4[2] + o4[3] * o4[3]);
+                if ((l16 & 3) == 0) {
+                    uint64_t *np =
+                        p.norm_xchg + (static_cast<size_t>(slot_base + c - p.s0) * H + h) * (norm_xchg_bytes(C, DV) / 8);
+                    const uint64_t word = (static_cast<uint64_t>(p.layer_tag) << 32) | __float_as_uint(ps);
+                    __hip_atomic_store(np + ct * CP + row, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (!kPartial || row < nvalid)
+                    cg = *reinterpret_cast<const uint2 *>(p.out_gate + ((tok_base + c * C + row) * H + h) * DV +
+                                                          16 * ct + ocol4);
+                cov = o4;
             } else if constexpr (!SAVE) {
                 const int I = rt - NT16;
                 const f32x4 ov = f.uo[rw] + acc;
@@ -907,6 +1051,17 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
             S[sl] = acc;
         }
         put_state();
+        if constexpr (LAYER) {
+            // chunk c - kLayerLag leaves the queue, chunk c joins it
+            if (c - kLayerLag >= cb) finish(qov[0], qg[0], c - kLayerLag, true);
+#pragma unroll
+            for (int i = 0; i + 1 < QN; ++i) {
+                qov[i] = qov[i + 1];
+                qg[i] = qg[i + 1];
+            }
+            qov[QN - 1] = cov;
+            qg[QN - 1] = cg;
+        }
     };
 
     // software pipeline, three packages deep: chunk c + 2 loads while chunk c
@@ -921,20 +1076,31 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
     if (ce > cb + 1) load(f1, cb + 1);
     int64_t c = cb;
     for (; c + 4 < nfull; c += 3) {  // chunks c .. c + 2 are full; c + 3 and c + 4 exist
+        poll_issue(c);
         load(f2, c + 2);
         step(f0, c, Full{});
+        poll_issue(c + 1);
         load(f0, c + 3);
         step(f1, c + 1, Full{});
+        poll_issue(c + 2);
         load(f1, c + 4);
         step(f2, c + 2, Full{});
     }
     // tail: f0 holds chunk c and f1 chunk c + 1 (when it exists)
     for (; c < ce; ++c) {
+        poll_issue(c);
         if (c + 2 < ce) load(f2, c + 2);
         if (c < nfull) step(f0, c, Full{});
         else step(f0, c, Part{});
         f0 = f1;
         f1 = f2;
+    }
+
+    if constexpr (LAYER) {  // the last chunks' rows, oldest first
+        // chunks ce - kLayerLag .. ce - 1 (those that exist) are still queued
+#pragma unroll
+        for (int i = 0; i < QN; ++i)
+            if (ce - QN + i >= cb) finish(qov[i], qg[i], ce - QN + i, false);
     }
 
     // the state leaving chunk ce - 1: the final state, or the one carried out
@@ -957,6 +1123,12 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 template <int C, int DK, int DV, bool BF, bool SAVE = false>
 __global__ void __launch_bounds__(256) state_kernel(StateParams p) {
     state_body<C, DK, DV, BF, SAVE, false>(p);
+}
+
+// The KDA layer's state pass with its RMSNorm and output-gate epilogue fused
+// (one-dimensional grid, see state_body).
+__global__ void __launch_bounds__(256) layer_state_kernel(StateParams p) {
+    state_body<64, 128, 128, true, false, false, true>(p);
 }
 
 template <int C, int DK, int DV, bool BF>
@@ -1013,13 +1185,24 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
     if (ei != hipSuccess) return ei;
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, a.o, a.final_state, nullptr,
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
-    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
-    if (a.gate_mode == 2 && a.T > 0) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_layer_epilogue(a.o, a.out_gate, a.norm_weight, static_cast<int64_t>(a.B) * a.T * a.H,
-                                     a.norm_eps, stream);
+    if constexpr (C == 64 && DK == 128 && DV == 128 && BF) {
+        if (a.gate_mode == 2) {
+            // blocks 64 g + 8 ct + x: slab ct of (sequence, head) unit 8 g + x
+            sp.out_gate = a.out_gate;
+            sp.norm_weight = a.norm_weight;
+            sp.norm_eps = a.norm_eps;
+            sp.layer_tag = a.layer_tag;
+            sp.norm_xchg = reinterpret_cast<uint64_t *>(a.norm_xchg);
+            if (a.T > 0 && (sp.norm_xchg == nullptr || sp.out_gate == nullptr || sp.norm_weight == nullptr))
+                return hipErrorInvalidValue;
+            const int64_t units = static_cast<int64_t>(a.N) * a.H;
+            const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 64);
+            hipLaunchKernelGGL(layer_state_kernel, dim3(grid), dim3(256), 0, stream, sp);
+            return hipGetLastError();
+        }
     }
+    if (a.gate_mode == 2) return hipErrorInvalidValue;  // the layer runs at C = 64, d = 128, bf16 only
+    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ def load():
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_layer_chunk_fwd_workspace_size.argtypes = [i32, i64, i32, i32]
+    lib.kda_layer_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i64, i32, i32, i32, i32,
                                   ctypes.c_int, i32, fp, fp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
@@ -168,6 +170,11 @@ def _stream(stream=None):
 def workspace_size(B, T, H, Dk, Dv, n_seqs=0, dtype=torch.bfloat16, chunk_size=64) -> int:
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     return int(load().kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, code, chunk_size))
+
+
+def layer_workspace_size(B, T, H, n_seqs=0) -> int:
+    """Workspace bytes of layer_chunk_fwd (Dk = Dv = 128, bf16, 64-token chunks)."""
+    return int(load().kda_layer_chunk_fwd_workspace_size(B, T, H, n_seqs))
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, chunk_size=64,
@@ -408,7 +415,7 @@ def layer_chunk_fwd(q, k, v, x_alpha, x_beta, out_gate, norm_weight, l2_eps=1e-6
         out = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
-    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, n_seqs, KDA_BF16, 64))
+    ws_bytes = int(lib.kda_layer_chunk_fwd_workspace_size(B, T, H, n_seqs))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _check(lib.kda_layer_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(x_alpha), _ptr(x_beta),

@@ -332,10 +332,22 @@ kda_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
  *
  * kda_layer_chunk_fwd -- prefill at Dk = Dv = 128 with 64-token chunks (other
  * sizes return KDA_ERR_UNSUPPORTED).  init_state, cu_seqlens, n_seqs,
- * final_state, workspace (kda_chunk_fwd_workspace_size(B, T, H, 128, 128,
- * n_seqs, KDA_BF16, 64) bytes), stream and every convention not stated here
- * are as for kda_chunk_fwd.
+ * final_state, workspace (kda_layer_chunk_fwd_workspace_size(B, T, H, n_seqs)
+ * bytes), stream and every convention not stated here are as for
+ * kda_chunk_fwd.  The RMSNorm and output gate run inside the state pass: the
+ * eight workgroups that each produce 16 of a row's 128 outputs exchange their
+ * per-row sums of squares through the workspace (64-bit words tagged with a
+ * per-call number), each waiting a bounded time for the others'.  They are
+ * launched so that the eight are resident together; should a wait still run
+ * out, the rows of that workgroup from then on are NaN rather than wrong.
+ *
+ * kda_layer_chunk_fwd_workspace_size -- bytes of device workspace
+ * kda_layer_chunk_fwd needs: kda_chunk_fwd_workspace_size(B, T, H, 128, 128,
+ * n_seqs, KDA_BF16, 64) plus 4 KiB per (chunk, head) for the row-norm
+ * exchange.  0 for invalid sizes.
  */
+size_t kda_layer_chunk_fwd_workspace_size(int32_t B, int64_t T, int32_t H, int32_t n_seqs);
+
 kda_status kda_layer_chunk_fwd(const void *q, const void *k, const void *v, const void *x_alpha,
                                const void *x_beta, const void *out_gate, const float *norm_weight,
                                float l2_eps, float norm_eps, const float *init_state,
