@@ -212,6 +212,18 @@ def test_layer_chunk_rejects(lib, kw, code, msg):
     assert msg in lib.kda_last_error()
 
 
+def test_layer_workspace_size(lib):
+    """The layer's workspace is the prefill's plus its row-norm exchange: 4 KiB
+    per (chunk slot, head); a prefill-sized workspace is refused."""
+    lws, ws = lib.kda_layer_chunk_fwd_workspace_size, lib.kda_chunk_fwd_workspace_size
+    for B, T, H, n in [(1, 4096, 32, 0), (1, 157, 3, 0), (2, 100, 4, 0), (1, 1000, 2, 5)]:
+        slots = (T + 63) // 64 * B + (n if n else 0)
+        assert lws(B, T, H, n) == ws(B, T, H, 128, 128, n, BF16, 64) + slots * H * 4096, (B, T, H, n)
+    assert lws(0, 64, 1, 0) == 0 and lws(1, -1, 1, 0) == 0 and lws(1, 64, 0, 0) == 0
+    small = ws(1, 64, 1, 128, 128, 0, BF16, 64)
+    assert _layer_chunk(lib, ws_bytes=small) == WORKSPACE
+
+
 def test_layer_decode_rejects(lib):
     p = lambda x: None if x is None else ctypes.c_void_p(x)
 

@@ -68,6 +68,43 @@ def test_layer_varlen_with_resets():
     _check(inp, o, fs, label="layer varlen")
 
 
+def test_layer_many_units_short_sequences():
+    """The state pass exchanges each row's sum of squares between the eight
+    workgroups of a (sequence, head) unit: 96 sequences x 5 heads = 480 units,
+    3,840 workgroups (many more than are resident at once), lengths 1..200."""
+    log("layer varlen 96 x 5 heads")
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(1, 201, size=96)]
+    inp = workloads.make_layer_prefill("varlen", "cuda", seed=31, H=5, lengths=lens)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, label="layer varlen 96x5")
+
+
+def test_layer_workspace_contents_and_reuse():
+    """The exchange words carry a per-call tag: a workspace full of leftover
+    bytes, or one last used by another call, gives the same output bit for bit
+    (and the oracle's)."""
+    log("layer workspace reuse")
+    inp = workloads.make_layer_prefill("prefill", "cuda", seed=32, T=300, H=5)
+    other = workloads.make_layer_prefill("prefill", "cuda", seed=33, T=300, H=5)
+    B, T, H, D = inp["q"].shape
+    ws = torch.full((kda.layer_workspace_size(B, T, H),), 0xFF, dtype=torch.uint8, device="cuda")
+
+    def run(x):
+        o = torch.full((B, T, H, D), float("nan"), device="cuda")
+        fs = torch.full((x["N"], H, D, D), float("nan"), device="cuda")
+        kda.layer_chunk_fwd(*(x[n] for n in NAMES), x["norm_weight"], L2_EPS, NORM_EPS, x["init_state"],
+                            None, out=o, final_state=fs, workspace=ws)
+        torch.cuda.synchronize()
+        return o, fs
+
+    o1, fs1 = run(inp)
+    run(other)
+    o2, fs2 = run(inp)
+    assert torch.equal(o1, o2) and torch.equal(fs1, fs2)
+    _check(inp, o1, fs1, label="layer, workspace of 0xff bytes")
+
+
 def test_layer_prologue_matches_unfused_operator():
     """The fused prologue against the plain operator's fp32 path fed the prologue
     computed by torch in fp32 (normalised q and k, -softplus, sigmoid); both
