@@ -339,8 +339,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_kernel(BwdStateParams p
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
     const int H = p.H;
+    int n, h, ct;
+    if (!state_unit<D / 16>(p.N, H, n, h, ct)) return;
     int64_t tok_base, L, slot_base;
     if (p.cu_seqlens) {
         tok_base = p.cu_seqlens[n];
@@ -461,8 +462,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_state_f16_kernel(BwdStatePara
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
     const int H = p.H;
+    int n, h, ct;
+    if (!state_unit<D / 16>(p.N, H, n, h, ct)) return;
     int64_t tok_base, L, slot_base;
     if (p.cu_seqlens) {
         tok_base = p.cu_seqlens[n];
@@ -1353,10 +1355,12 @@ hipError_t launch_bwd_t(const BackwardArgs &a, hipStream_t stream) {
         BwdStateParams sp{f.cu_seqlens, f.chunk_offsets, f.T, f.H, f.N, f.workspace, f.pkg_bytes, L,
                           a.d_o, a.d_final_state, a.chunk_dstates, a.d_init_state,
                           s0, s1, a.dcarry + ((g + 1) & 1) * hd2, a.dcarry + (g & 1) * hd2, g == 0};
+        dim3 sgrid;
+        if (!state_grid(f.N, f.H, D, sgrid)) return hipErrorInvalidValue;
         if constexpr (BF)
-            hipLaunchKernelGGL((bwd_state_f16_kernel<C, D>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+            hipLaunchKernelGGL((bwd_state_f16_kernel<C, D>), sgrid, dim3(kBwdThreads), 0, stream, sp);
         else
-            hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), dim3(f.N, f.H, D / 16), dim3(kBwdThreads), 0, stream, sp);
+            hipLaunchKernelGGL((bwd_state_kernel<C, D, BF>), sgrid, dim3(kBwdThreads), 0, stream, sp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t n_items = (s1 - s0) * f.H;

@@ -66,6 +66,34 @@ struct StateParams {
     uint64_t *norm_xchg = nullptr;  // [slots][H][Dv / 16][CP] words (norm_xchg_bytes each (slot, head))
 };
 
+// Grid of the sequential state passes (forward and reverse): one-dimensional,
+// with NS = DV / 16 column slabs per (sequence, head) unit, block 8 (NS g + ct)
+// + x is slab ct of unit 8 g + x.  Blocks go to the eight XCDs round-robin, so
+// the NS slabs of a unit run on one XCD, one after another in its dispatch
+// order: they are resident together and share the unit's packages in that
+// XCD's L2 whatever the number of units.  false when the grid exceeds the
+// one-dimensional limit.
+inline bool state_grid(int32_t N, int32_t H, int DV, dim3 &grid) {
+    const int64_t units = static_cast<int64_t>(N) * H;
+    const int64_t blocks = (units + 7) / 8 * 8 * (DV / 16);
+    if (blocks <= 0 || blocks > 0x7fffffff) return false;
+    grid = dim3(static_cast<unsigned>(blocks));
+    return true;
+}
+
+// (sequence n, head h, slab ct) of this block of a state_grid launch; false for
+// the blocks past the last unit.
+template <int NS>
+__device__ __forceinline__ bool state_unit(int32_t N, int32_t H, int &n, int &h, int &ct) {
+    const int blk = blockIdx.x, q8 = blk >> 3;
+    ct = q8 % NS;
+    const int unit = 8 * (q8 / NS) + (blk & 7);
+    if (unit >= N * H) return false;
+    n = unit / H;
+    h = unit - n * H;
+    return true;
+}
+
 struct BwdStateParams {
     const int32_t *cu_seqlens, *chunk_offsets;
     int64_t T;

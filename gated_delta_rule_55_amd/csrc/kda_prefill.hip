@@ -789,17 +789,10 @@ __device__ __forceinline__ void state_body(const StateParams &p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    int n = blockIdx.x, h = blockIdx.y, ct = blockIdx.z;
     const int H = p.H;
-    if constexpr (LAYER) {
-        // one-dimensional grid: block 64 g + 8 ct + x is slab ct of unit 8 g + x
-        static_assert(DV == 128, "eight 16-column slabs");
-        const int b = blockIdx.x, unit = 8 * (b >> 6) + (b & 7);
-        ct = (b >> 3) & 7;
-        if (unit >= p.N * H) return;  // so are its seven siblings
-        n = unit / H;
-        h = unit - n * H;
-    }
+    static_assert(!LAYER || DV == 128, "the layer's eight 16-column slabs");
+    int n, h, ct;
+    if (!state_unit<DV / 16>(p.N, H, n, h, ct)) return;  // so are its siblings
 
     int64_t tok_base, L, slot_base;
     if (p.cu_seqlens) {
@@ -1139,6 +1132,7 @@ __global__ void __launch_bounds__(256) dplr_state_kernel(StateParams p) {
 // -----------------------------------------------------------------------------
 // launch
 // -----------------------------------------------------------------------------
+
 // The intra-chunk pass: the packages of chunk slots [s0, s1) (every head) into
 // pkgs, slot s0's first (the prefill: every slot, into a.workspace).  The
 // varlen plan is made only where plan is set.
@@ -1187,7 +1181,6 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
                    a.T, a.H, a.N, a.workspace, a.pkg_bytes, package_layout(C, DK, DV, BF)};
     if constexpr (C == 64 && DK == 128 && DV == 128 && BF) {
         if (a.gate_mode == 2) {
-            // blocks 64 g + 8 ct + x: slab ct of (sequence, head) unit 8 g + x
             sp.out_gate = a.out_gate;
             sp.norm_weight = a.norm_weight;
             sp.norm_eps = a.norm_eps;
@@ -1195,14 +1188,16 @@ static hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
             sp.norm_xchg = reinterpret_cast<uint64_t *>(a.norm_xchg);
             if (a.T > 0 && (sp.norm_xchg == nullptr || sp.out_gate == nullptr || sp.norm_weight == nullptr))
                 return hipErrorInvalidValue;
-            const int64_t units = static_cast<int64_t>(a.N) * a.H;
-            const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 64);
-            hipLaunchKernelGGL(layer_state_kernel, dim3(grid), dim3(256), 0, stream, sp);
+            dim3 grid;
+            if (!state_grid(a.N, a.H, DV, grid)) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(layer_state_kernel, grid, dim3(256), 0, stream, sp);
             return hipGetLastError();
         }
     }
     if (a.gate_mode == 2) return hipErrorInvalidValue;  // the layer runs at C = 64, d = 128, bf16 only
-    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
+    dim3 grid;
+    if (!state_grid(a.N, a.H, DV, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF>), grid, dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
 
@@ -1215,12 +1210,16 @@ hipError_t launch_forward_segment(const PrefillArgs &a, const FwdSegment &g, hip
     StateParams sp{a.init_state, a.cu_seqlens, a.chunk_offsets, nullptr, nullptr, g.chunk_states,
                    a.T, a.H, a.N, g.pkgs, a.pkg_bytes, package_layout(C, DK, DV, BF),
                    g.s0, g.s1, g.carry_in, g.carry_out, g.do_empty};
-    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF, true>), dim3(a.N, a.H, DV / 16), dim3(256), 0, stream, sp);
+    dim3 grid;
+    if (!state_grid(a.N, a.H, DV, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((state_kernel<C, DK, DV, BF, true>), grid, dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
 template <int C, int D, bool BF>
 hipError_t launch_dplr_state(const StateParams &sp, hipStream_t stream) {
-    hipLaunchKernelGGL((dplr_state_kernel<C, D, D, BF>), dim3(sp.N, sp.H, D / 16), dim3(256), 0, stream, sp);
+    dim3 grid;
+    if (!state_grid(sp.N, sp.H, D, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dplr_state_kernel<C, D, D, BF>), grid, dim3(256), 0, stream, sp);
     return hipGetLastError();
 }
 #define KDA_DPLR_STATE(C, D) \
