@@ -285,6 +285,10 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     const int32_t N = varlen ? n_seqs : B;
     if ((int64_t)N * H > 0x7fffffff || T > ((int64_t)1 << 40))
         return fail(KDA_ERR_INVALID_ARG, "sizes exceed the supported range");
+    // the state pass runs Dv / 16 workgroups per (sequence, head) on a one-dimensional grid
+    if (((int64_t)N * H + 7) / 8 * 8 * (Dv / 16) > 0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "N*H=%lld (sequence, head) units: more than the state pass's grid takes",
+                    (long long)N * H);
     if (gate_mode == 2 && (!eps_ok(L->l2_eps) || !eps_ok(L->norm_eps)))
         return fail(KDA_ERR_INVALID_ARG, "l2_eps and norm_eps must be finite and >= 0");
     if (N == 0) return KDA_OK;
@@ -565,6 +569,10 @@ kda_status kda_chunk_bwd(const void *q, const void *k, const void *v, const floa
     const int32_t N = varlen ? n_seqs : B;
     if ((int64_t)N * H > 0x7fffffff || T > ((int64_t)1 << 40))
         return fail(KDA_ERR_INVALID_ARG, "sizes exceed the supported range");
+    // the state pass runs Dv / 16 workgroups per (sequence, head) on a one-dimensional grid
+    if (((int64_t)N * H + 7) / 8 * 8 * (Dv / 16) > 0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "N*H=%lld (sequence, head) units: more than the state pass's grid takes",
+                    (long long)N * H);
     if (N == 0) return KDA_OK;
     const bool bf16 = in_dtype == KDA_BF16;
     const size_t esz = bf16 ? 2 : 4;

@@ -81,6 +81,13 @@ def _chunk(lib, fn="kda_chunk_fwd", **kw):
                             p(a["final_state"]), p(a["ws"]), a["ws_bytes"], a["stream"])
 
 
+def test_unit_count_beyond_the_state_grid(lib):
+    """The state passes run Dv / 16 workgroups per (sequence, head) unit on a
+    one-dimensional grid: more units than it takes are refused before any launch."""
+    big = dict(B=1 << 20, T=1, H=1 << 10, Dk=128, Dv=128, chunk=64)  # 2^30 units x 8 slabs
+    assert _chunk(lib, **big) == INVALID and b"units" in lib.kda_last_error()
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), UNSUPPORTED),
     (dict(Dk=24, Dv=24), UNSUPPORTED),
