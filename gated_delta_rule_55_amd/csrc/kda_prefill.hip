@@ -755,15 +755,16 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // The KDA layer's fused epilogue (LAYER): a row's sum of o^2 is spread over the
-// eight slab workgroups of its head, so each writes its per-token partial sums
-// into the chunk's package (NP section, tagged with the call's tag in one 64-bit
-// relaxed atomic store) and scales its own o two chunk steps later, when the
-// other slabs' partials of that chunk are in L2 (read back with L1-bypassing
-// atomic loads until all eight tags match).  The layer's grid puts the eight
-// slabs of a (sequence, head) unit on one XCD (one L2) and next to each other in
+// eight slab workgroups of its head, so each writes its per-row partial sums
+// into the workspace's row-norm exchange (one 64-bit word per row, the call's
+// tag in the high half, written with a relaxed device-scope atomic store) and
+// scales its own rows of the chunk kLayerLag chunk steps later, once the other
+// slabs' words of that chunk carry the tag (read with relaxed device-scope
+// atomic loads, which bypass L1).  The state passes' grid (state_grid) puts the
+// eight slabs of a (sequence, head) unit on one XCD and next to each other in
 // that XCD's dispatch order, so all eight are resident together whenever the
 // XCD holds eight workgroups: no slab waits on one that cannot start.  Every
-// wait is bounded; a workgroup whose wait runs out writes NaN rows from then on.
+// wait is bounded; a wave whose wait runs out writes NaN rows from then on.
 constexpr int kLayerLag = 4;             // chunk steps between writing and reading partials
 constexpr int kLayerSpinLimit = 1 << 16; // polls of one chunk's partials before giving up
 

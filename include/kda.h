@@ -339,7 +339,8 @@ kda_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
  * per-row sums of squares through the workspace (64-bit words tagged with a
  * per-call number), each waiting a bounded time for the others'.  They are
  * launched so that the eight are resident together; should a wait still run
- * out, the rows of that workgroup from then on are NaN rather than wrong.
+ * out, the rows that wave of the workgroup writes from then on are NaN rather
+ * than wrong.
  *
  * kda_layer_chunk_fwd_workspace_size -- bytes of device workspace
  * kda_layer_chunk_fwd needs: kda_chunk_fwd_workspace_size(B, T, H, 128, 128,
