@@ -102,6 +102,22 @@ def test_varlen_small_with_resets():
     _check(inp, o, fs, TAU[torch.bfloat16], label="varlen small")
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 16), (32, 32), (64, 64)])
+def test_varlen_many_units_narrow_values(Dk, Dv):
+    """The state passes decode (sequence, head, slab) from a one-dimensional
+    block index with Dv / 16 slabs per unit: 37 sequences x 3 heads = 111 units
+    (not a multiple of eight) at 1, 2 and 4 slabs, lengths 0..300, random
+    initial state, bf16."""
+    log(f"varlen 37x3 Dk={Dk} Dv={Dv}")
+    rng = np.random.default_rng(Dk + Dv)
+    lens = [int(x) for x in rng.integers(0, 301, size=37)]
+    inp = _shrink2(workloads.make_prefill("varlen", "cuda", seed=50 + Dv, H=3, lengths=lens), Dk, Dv)
+    g = torch.Generator(device="cuda").manual_seed(51)
+    inp["init_state"] = 0.02 * torch.randn((len(lens), 3, Dk, Dv), device="cuda", generator=g)
+    o, fs = _gpu(inp)
+    _check(inp, o, fs, TAU[torch.bfloat16], label=f"varlen 37x3 Dk={Dk} Dv={Dv}")
+
+
 def _whole_tensor_check(inp, o, fs, label, group=16):
     """Every head, token and final state against the oracle, a group of heads
     at a time (host copies of the inputs in their own dtypes; the oracle widens
