@@ -399,9 +399,9 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
     }
     a.workspace = static_cast<char *>(workspace);
     a.n_slots = slots; a.pkg_bytes = pkg;
-    a.chunk_offsets = varlen ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
-                             : nullptr;
-    if (gate_mode == 2)  // after the packages and the plan: the last bytes of the workspace
+    a.chunk_offsets = varlen && T > 0 ? reinterpret_cast<int32_t *>(a.workspace + pkg * (size_t)slots * (size_t)H)
+                                      : nullptr;
+    if (gate_mode == 2 && T > 0)  // after the packages and the plan: the last bytes of the workspace
         a.norm_xchg = a.workspace + need_ws - kda::norm_xchg_bytes(chunk_size, Dv) * (size_t)slots * (size_t)H;
     if (T == 0) {
         // Every sequence is empty (cu[N] = T = 0): only final_state <- init_state
