@@ -65,9 +65,11 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 140 /* 1.4.0: adds kda_chunk_fwd_noalloc (1.3.0: kda_dplr_chunk_fwd and
+#define KDA_VERSION 150 /* 1.5.0: adds kda_layer_chunk_fwd_workspace_size (the layer prefill's
+                            workspace now holds its row-norm exchange); 1.4.0:
+                            kda_chunk_fwd_noalloc; 1.3.0: kda_dplr_chunk_fwd and
                             kda_dplr_decode_step; 1.2.0: kda_chunk_bwd; 1.1.0: the gdn_* and
-                            kda_layer_* entry points) */
+                            kda_layer_* entry points */
 
 typedef enum {
     KDA_OK = 0,
